@@ -1,0 +1,128 @@
+"""Oracle: joint replica placement + quota solve (the control plane's planner).
+
+UltraEP article, section "Quota 同时决定专家副本与 token 分流" (quota decides both
+replicas and the token split):
+* a quota is the token load an expert instance receives after rerouting;
+* one search solves replication and quotas together: every step may instantiate a
+  new replica and updates the target quota distribution;
+* constraints: a fixed number of redundant slots per rank, never two instances of one
+  logical expert on one rank, and a new replica must get at least a minimum quota
+  (1024 in production) so that no replica is made for a handful of tokens.
+Section "共享冗余 slot 管理动态专家副本" (shared redundant slots): mains never move; a
+logical expert has one main plus zero or more temporary replicas in the slots.
+Section "在 Gate 之后获取当前层真实负载": every rank runs the same deterministic solve.
+
+The article does not print the search.  Reading used here ("fill to the waterline"):
+
+    c_e   = total load of expert e;  L_r = sum of c_e over the mains homed on r
+    T*    = ceil(sum_e c_e / R)      (the force-balanced per-rank load)
+    start from the identity plan (every main keeps its whole load, no replicas)
+    repeat:
+      h = the most loaded rank (lowest index on ties); stop if L_h <= T*
+      try the mains of h in order (quota descending, expert id ascending), skipping
+      empty ones; for a donor expert e:
+        top-up : among ranks j != h already holding a replica of e with L_j < T*,
+                 take the least loaded (lowest index on ties) and move
+                 d = min(q_main[e], L_h - T*, T* - L_j) from the main to that replica;
+        else new replica: among ranks t != h with a free slot, no instance of e and
+                 L_t < T*, take the least loaded (lowest index on ties);
+                 d = min(q_main[e], L_h - T*, T* - L_t); only if d >= q_min put e into
+                 t's lowest free slot with quota d;
+        the first donor that can move applies its move and the step ends.
+      if no donor of h can move, stop (the peak cannot fall further).
+
+Donors only fall to T* and receivers only rise to T*, so every step exhausts a main,
+brings a donor down to T* or fills a receiver up to T*: at most E + 2R steps.
+Home of expert e: rank e // (E/R) (contiguous EP blocks).  Physical instance ids:
+i = r*(E_loc+S) + j; j < E_loc is the main of expert r*E_loc + j, j >= E_loc is slot j-E_loc.
+
+Pins (tests/test_oracle_quota.py): identity when balanced, S = 0 or q_min too large;
+the one-hot-expert closed form; the constraints of the article as invariants;
+the step bound; brute force over slot assignments on tiny inputs (quality report).
+"""
+
+import numpy as np
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    if E % R != 0:
+        raise ValueError("E must be a multiple of R")
+    E_loc = E // R
+    c = [int(v) for v in counts.sum(axis=0)]
+    L = [sum(c[r * E_loc:(r + 1) * E_loc]) for r in range(R)]
+    t_star = _ceil_div(sum(c), R)
+    q_main = list(c)
+    slot_e = [[-1] * S for _ in range(R)]
+    slot_q = [[0] * S for _ in range(R)]
+    free = [S] * R
+    steps = 0
+    stuck = False
+    while True:
+        h = max(range(R), key=lambda r: (L[r], -r))     # max load, lowest index on ties
+        if L[h] <= t_star:
+            break
+        mains = [e for e in range(h * E_loc, (h + 1) * E_loc) if q_main[e] > 0]
+        mains.sort(key=lambda e: (-q_main[e], e))
+        moved = False
+        for e in mains:
+            over = L[h] - t_star
+            tops = [(L[j], j) for j in range(R) if j != h and e in slot_e[j] and L[j] < t_star]
+            if tops:
+                Lj, j = min(tops)
+                d = min(q_main[e], over, t_star - Lj)
+                s = slot_e[j].index(e)
+                slot_q[j][s] += d
+                q_main[e] -= d
+                L[h] -= d
+                L[j] += d
+                moved = True
+                break
+            news = [(L[t], t) for t in range(R)
+                    if t != h and free[t] > 0 and e not in slot_e[t] and L[t] < t_star]
+            if news:
+                Lt, t = min(news)
+                d = min(q_main[e], over, t_star - Lt)
+                if d >= q_min:
+                    s = S - free[t]          # slots fill in order and are never released
+                    slot_e[t][s] = e
+                    slot_q[t][s] = d
+                    free[t] -= 1
+                    q_main[e] -= d
+                    L[h] -= d
+                    L[t] += d
+                    moved = True
+                    break
+        if not moved:
+            stuck = True
+            break
+        steps += 1
+
+    ipr = E_loc + S
+    inst_expert = np.full(R * ipr, -1, dtype=np.int64)
+    inst_quota = np.zeros(R * ipr, dtype=np.int64)
+    for r in range(R):
+        for j in range(E_loc):
+            e = r * E_loc + j
+            inst_expert[r * ipr + j] = e
+            inst_quota[r * ipr + j] = q_main[e]
+        for s in range(S):
+            inst_expert[r * ipr + E_loc + s] = slot_e[r][s]
+            inst_quota[r * ipr + E_loc + s] = slot_q[r][s]
+    n_rep = sum(1 for r in range(R) for s in range(S) if slot_e[r][s] >= 0)
+    return {
+        "slot_expert": np.array(slot_e, dtype=np.int64).reshape(R, S),
+        "inst_expert": inst_expert,
+        "inst_quota": inst_quota,
+        "rank_load": np.array(L, dtype=np.int64),
+        "n_replicas": n_rep,
+        "n_steps": steps,
+        "t_star": t_star,
+        "stuck": stuck,
+        "inst_per_rank": ipr,
+    }
