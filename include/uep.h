@@ -1,0 +1,270 @@
+/*
+ * uep.h -- C-ABI of libuep.so, the MI355X (gfx950) real-time MoE expert
+ * load-balancing path: load matrix -> quota solve -> local-first reroute and
+ * token assignment -> permute -> redundant-slot staging, plus Waterfill
+ * shared-expert placement and the LPLB min-max replica split.
+ *
+ * Sources (the pages the method comes from):
+ *   [UEP]  "300 微秒调平 MoE 专家负载！小红书 UltraEP 逼近 94.3% 理想训推吞吐"
+ *          (UltraEP technical article, m.163.com)
+ *   [BLOG] "Improving DeepEP MoE Load Balance in SGLang with Waterfill and LPLB"
+ *          (papercache notes of the lmsys blog)
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller, except where a
+ *     call says "host".  The library never allocates, frees or synchronises on
+ *     these calls; work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and ordered with the caller's other work on that stream.
+ *   - Integer arrays are int32, row-major, with the shapes given below.
+ *     bf16 data is passed as raw uint16 bits and moved bit for bit.
+ *   - Geometry: R virtual EP ranks, T tokens per rank, K routing slots per token,
+ *     E logical experts, home(e) = e / (E / R) for the routed experts.  A physical
+ *     instance id is i = r * inst_per_rank + j (rank r, local slot j); instance
+ *     tables `inst_expert[I]` give each instance's logical expert or -1.
+ *   - A top-k id of -1 is an empty routing slot (a padded or absent token).  It is
+ *     not counted and gets bucket position, instance and row -1.
+ *   - Return value: uep_status.  Argument checks run on the host before anything
+ *     is enqueued; on an error nothing is enqueued.  UEP_EHIP reports a launch
+ *     failure (hipGetLastError).
+ *   - Content errors (bad ids, quotas that do not match the load, ...) are found
+ *     on the device and OR-ed as UEP_ERR_* bits into the optional device word
+ *     `err` (may be NULL).  The caller clears it beforehand and reads it after its
+ *     own synchronisation.  Outputs are unspecified when a bit is set.
+ *   - Calls are stateless and re-entrant.  Calls that overlap on one stream-less
+ *     set of buffers race like any other kernels writing the same memory.
+ *   - Limits: R <= 64, E <= 4096, K <= 64, R*T*K < 2^31, total load < 2^31.
+ */
+#ifndef UEP_H
+#define UEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t uep_status;
+enum {
+  UEP_OK = 0,
+  UEP_EINVAL = 1,      /* null pointer, negative size, r_begin/r_end out of range */
+  UEP_EGEOM = 2,       /* unsupported geometry (limits above, E % R != 0, H % 8 != 0 ...) */
+  UEP_EWORKSPACE = 3,  /* workspace missing or smaller than the *_workspace_size query */
+  UEP_EHIP = 4         /* a kernel launch or HIP runtime call failed */
+};
+
+/* device-side content error bits */
+enum {
+  UEP_ERR_ID_RANGE = 1,     /* a top-k id outside [-1, E) */
+  UEP_ERR_DUP_ID = 2,       /* an expert twice in one token's top-k */
+  UEP_ERR_QUOTA_SUM = 4,    /* an expert's instance quotas do not sum to its load */
+  UEP_ERR_INST_DUP = 8,     /* two instances of one expert on one rank */
+  UEP_ERR_BAD_QUOTA = 16,   /* negative quota, or quota on an unused instance */
+  UEP_ERR_COVER = 32,       /* a bucket position not covered by the transfer plan */
+  UEP_ERR_LP = 64           /* LPLB: an expert with load but no instance */
+};
+
+/* Library version string and a static text for a status code (host). */
+const char* uep_version(void);
+const char* uep_status_string(uep_status s);
+
+/* ------------------------------------------------------------------------- *
+ * uep_load_matrix -- the global load matrix of one layer.
+ * [UEP] section "在 Gate 之后获取当前层真实负载" (real load after Gate): once the Gate
+ * has run, every expert's exact token count for this microbatch and layer is known;
+ * the routing metadata of the whole EP group forms the global load matrix.
+ *
+ *   topk_ids   [R][T][K]  in   expert ids in [-1, E), distinct within a token
+ *   counts     [R][E]     out  counts[r][e] = number of (t, k) on rank r routed to e
+ *   bucket_pos [R][T][K]  out  number of tokens t' < t on rank r whose top-k holds
+ *                              the same expert (stable position in its bucket)
+ *   err                   out  optional; UEP_ERR_ID_RANGE, UEP_ERR_DUP_ID
+ *   ws, ws_bytes               device workspace of uep_load_matrix_workspace_size()
+ * ------------------------------------------------------------------------- */
+size_t uep_load_matrix_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E);
+uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                           int32_t E, int32_t* counts, int32_t* bucket_pos, int32_t* err,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_solve_quota -- joint replica placement and quota solve.
+ * [UEP] section "Quota 同时决定专家副本与 token 分流": a quota is the token load an
+ * expert instance receives after rerouting; each search step may instantiate a
+ * replica and updates the quota distribution; at most S redundant slots per rank,
+ * no logical expert twice on one rank, and a new replica gets at least q_min
+ * tokens.  Section "共享冗余 slot 管理动态专家副本": mains never move.
+ * Every caller with the same counts gets the same plan (deterministic, ties to
+ * the lowest index).  Search ("fill to the waterline", T* = ceil(sum c / R)):
+ * the most loaded rank donates from its mains (quota descending) to an existing
+ * replica under T*, else to a new replica on the least loaded rank with a free
+ * slot if that move is >= q_min; donors fall to T*, receivers rise to T*.
+ *
+ *   counts      [R][E]           in   load matrix (E % R == 0, E_loc = E / R)
+ *   S, q_min                          redundant slots per rank (0..8), minimum quota
+ *   slot_expert [R][S]           out  expert held by each slot, -1 if empty
+ *   inst_expert [R*(E_loc+S)]    out  instance table: j < E_loc main of r*E_loc + j,
+ *                                     j >= E_loc slot j - E_loc
+ *   inst_quota  [R*(E_loc+S)]    out  tokens each instance takes
+ *   rank_load   [R]              out  load per rank after the plan
+ *   stats       [4]              out  {replicas placed, steps, T*, 1 if stopped early}
+ * ------------------------------------------------------------------------- */
+uep_status uep_solve_quota(const int32_t* counts, int32_t R, int32_t E, int32_t S,
+                           int32_t q_min, int32_t* slot_expert, int32_t* inst_expert,
+                           int32_t* inst_quota, int32_t* rank_load, int32_t* stats,
+                           void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_identity_quota -- quotas when every expert has exactly one instance
+ * (used with the Waterfill layout of [BLOG] section "共享专家融合作为启用机制",
+ * where each rank has one shared-expert slot next to its routed experts).
+ *
+ *   counts      [R][E]     in
+ *   inst_expert [n_inst]   in   each expert at most once
+ *   inst_quota  [n_inst]   out  total load of the instance's expert (0 if unused)
+ * ------------------------------------------------------------------------- */
+uep_status uep_identity_quota(const int32_t* counts, int32_t R, int32_t E, int32_t n_inst,
+                              const int32_t* inst_expert, int32_t* inst_quota, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_reroute_assign -- local-first reroute and per-token realisation.
+ * [UEP] section "Quota 同时决定专家副本与 token 分流": tokens first use the instance of
+ * their expert on their own rank; what the local quota cannot take goes to remote
+ * instances by their remaining quota; the aggregate quotas are then realised per
+ * token.  Remote fill = interval overlap: residual demands laid end to end in
+ * ascending source rank against remaining capacities in ascending instance id.
+ * Dispatch layout: instance blocks in instance-id order; inside a block source
+ * rank ascending, then token ascending.  The tokens of (r, e) in token order fill
+ * the local instance first, then the remote instances in ascending id.
+ *
+ *   counts, topk_ids, bucket_pos      in   from uep_load_matrix
+ *   inst_per_rank, inst_expert[I],
+ *   inst_quota[I]                     in   the plan; I = R * inst_per_rank
+ *   r_begin, r_end                    in   per-token outputs only for sources in
+ *                                          [r_begin, r_end); xfer/inst_offset always whole
+ *   xfer        [R][I]                out  tokens of source r served by instance i
+ *   inst_offset [I+1]                 out  first dispatch row of every instance
+ *   dest_inst, dest_row [R][T][K]     out  instance and dispatch row of every pair
+ *   err                               out  optional; QUOTA_SUM, INST_DUP, BAD_QUOTA, COVER
+ *   ws, ws_bytes                           uep_reroute_workspace_size()
+ * ------------------------------------------------------------------------- */
+size_t uep_reroute_workspace_size(int32_t R, int32_t E, int32_t inst_per_rank);
+uep_status uep_reroute_assign(const int32_t* counts, const int32_t* topk_ids,
+                              const int32_t* bucket_pos, int32_t R, int32_t T, int32_t K,
+                              int32_t E, int32_t inst_per_rank, const int32_t* inst_expert,
+                              const int32_t* inst_quota, int32_t r_begin, int32_t r_end,
+                              int32_t* xfer, int32_t* inst_offset, int32_t* dest_inst,
+                              int32_t* dest_row, int32_t* err, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_permute -- scatter token activations into the per-instance dispatch buffer.
+ * [UEP] section "流式通信算子加速动态权重分发": once replica weights are in place,
+ * token dispatch follows the reroute plan; this is its on-device permutation.
+ * Each source row is read once and written to each of its K rows.
+ *
+ *   x        [R][T][H] bf16 bits  in   activations (H % 8 == 0, rows 16-byte aligned)
+ *   dest_row [R][T][K]            in   from uep_reroute_assign
+ *   r_begin, r_end                     only sources in [r_begin, r_end) are moved
+ *   out      [P][H] bf16 bits     out  P = number of routed pairs (max dest_row + 1)
+ *   row_src  [P]                  out  optional; (r*T + t)*K + k of the pair in each row
+ * ------------------------------------------------------------------------- */
+uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, int32_t T,
+                       int32_t K, int32_t H, int32_t r_begin, int32_t r_end, uint16_t* out,
+                       int32_t* row_src, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_stage_replica_weights -- redundant-slot weight staging / gradient reduction.
+ * [UEP] section "共享冗余 slot 管理动态专家副本": each rank has S fixed redundant slots
+ * (weights + gradient buffer, no optimizer state) shared by every MoE layer; the
+ * current layer's replica weights are written into them before dispatch.
+ * Section "复用前向方案，完成权重恢复与梯度归约": backward reuses the forward plan,
+ * writes the replica weights again, reduces replica gradients into the main's
+ * gradient buffer and clears the redundant gradient buffer.
+ * Section "流式通信算子加速动态权重分发": fixed-size tiles pulled by a persistent
+ * kernel from a device-side task list derived from the plan.
+ *
+ *   mode = UEP_STAGE_WEIGHTS:     slot_w[r][s] = main_w[slot_expert[r][s]] (bit copy)
+ *                                 for used slots of ranks in [r_begin, r_end)
+ *   mode = UEP_STAGE_GRAD_REDUCE: for each expert e homed in [r_begin, r_end) with
+ *                                 replicas on ranks r1 < r2 < ...:
+ *                                 main_grad[e] = ((main_grad[e] + g_r1) + g_r2) + ...
+ *                                 in fp32 round-to-nearest-even, then those slot
+ *                                 gradients are set to +0.0
+ *   slot_expert [R][S]                       in   from uep_solve_quota
+ *   main_w  [E][expert_elems] bf16, slot_w [R][S][expert_elems] bf16   (WEIGHTS)
+ *   main_grad [E][expert_elems] f32, slot_grad [R][S][expert_elems] f32 (GRAD_REDUCE)
+ *   expert_elems % 8 == 0; unused pointers of the other mode may be NULL.
+ * ------------------------------------------------------------------------- */
+enum { UEP_STAGE_WEIGHTS = 0, UEP_STAGE_GRAD_REDUCE = 1 };
+uep_status uep_stage_replica_weights(int32_t mode, int32_t R, int32_t E, int32_t S,
+                                     const int32_t* slot_expert, int32_t r_begin,
+                                     int32_t r_end, const uint16_t* main_w, uint16_t* slot_w,
+                                     float* main_grad, float* slot_grad,
+                                     int64_t expert_elems, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * uep_waterfill -- place every token's shared-expert slot on a rank.
+ * [BLOG] section "Waterfill算法执行步骤": L_r = routed load on rank r; N shared slots;
+ * waterline H = ceil((sum_r L_r + N) / R); slack S_r = max(H - L_r, 0); each token's
+ * shared slot goes to a candidate rank sampled in proportion to slack with a small
+ * local preference; with zero slack everywhere, a clearly lighter candidate, else
+ * the local rank.  Section "通信权衡与模式选择": candidates are the ranks the token
+ * already visits plus its own rank.
+ * Constants: weights (2^p + 1) * S_r0 for the source rank r0 and 2^p * S_c for the
+ * others (p = local_pref_shift, 0..8); draw = word 0 of Philox4x64-10 with counter
+ * (r0*T + t, 0, 0, 0) and key (seed, layer), v = floor(draw * W / 2^64); the first
+ * candidate (order: r0, then ascending rank) whose running weight exceeds v wins.
+ * Zero total weight: the lightest candidate c with (2^p+1) L_c < 2^p L_r0, else r0.
+ *
+ *   counts     [R][E]      in   routed load matrix (E % R == 0)
+ *   topk_ids   [R][T][K]   in
+ *   batch_size [R]         in   live tokens per rank B_r <= T (N = sum B_r); tokens
+ *                               t >= B_r get shared rank -1
+ *   shared_rank[R][T]      out
+ *   waterline  [1], slack [R], rank_load [R]  out  H, S_r, L_r
+ *   ext_topk   [R][T][K+1] out  optional: top-k plus the column E + shared_rank
+ *                               (-1 for absent tokens), i.e. the fused layout
+ * ------------------------------------------------------------------------- */
+uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
+                         const int32_t* batch_size, int32_t R, int32_t T, int32_t K,
+                         int32_t E, uint64_t seed, uint64_t layer, int32_t local_pref_shift,
+                         int32_t* shared_rank, int32_t* waterline, int32_t* slack,
+                         int32_t* rank_load, int32_t* ext_topk, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * LPLB -- min-max split of replicated experts' load over their copies.
+ * [BLOG] sections "线性规划（LP）公式化构建" and "决策变量与矩阵规模优化": minimise
+ * the peak rank load M subject to, per rank, copy allocation + fixed single-copy
+ * load + slack = M and, per replicated expert, the split summing to its true count;
+ * the structural matrix depends only on the placement and is built once offline,
+ * only the right-hand side changes per batch; a Big-M auxiliary column keeps the
+ * system feasible and is driven to zero.  Section "从全局计数到LP求解的工程实现":
+ * every rank solves the same LP on the GPU with an interior-point method into
+ * preallocated buffers.  Section "从LP解决方案到Token调度": the split decides how a
+ * replicated expert's tokens go to its copies (here: integer quotas by largest
+ * remainder on rint(x * 256), then uep_reroute_assign).
+ *
+ * uep_lplb_prepare (offline): builds the LP structure from a HOST instance table
+ *   inst_expert_host [R*inst_per_rank] (every expert with load needs >= 1 instance,
+ *   at most one per rank) and copies it into the device buffer `lp` of
+ *   uep_lplb_struct_size() bytes (synchronous copy; call outside the hot loop).
+ * uep_lplb (per batch): a fixed number of fp32 Mehrotra predictor-corrector steps.
+ *   counts     [R][E]     in   load matrix
+ *   iters                 in   interior-point iterations (1..200; 30 is plenty)
+ *   x          [n_copies] out  split per copy (token units, copies ordered by expert,
+ *                              then instance id), normalised to sum to each count
+ *   m          [1]        out  max rank load of that split
+ *   inst_quota [I]        out  integer quotas for every instance
+ *   stats      [4]        out  optional: {n_replicated, n_copies, iterations run, 0}
+ * ------------------------------------------------------------------------- */
+size_t uep_lplb_struct_size(int32_t R, int32_t E, int32_t inst_per_rank);
+uep_status uep_lplb_prepare(const int32_t* inst_expert_host, int32_t R, int32_t E,
+                            int32_t inst_per_rank, void* lp, size_t lp_bytes, void* stream);
+uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float* x, float* m,
+                    int32_t* inst_quota, int32_t* stats, int32_t* err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UEP_H */

@@ -1,0 +1,80 @@
+// Shared device helpers for libuep (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/uep.h"
+
+namespace uep {
+
+constexpr int kWave = 64;
+
+// 16-byte vector used for bit-exact row moves (native clang vector so that the
+// non-temporal builtins accept it).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+__device__ __forceinline__ int shfl(int v, int src) { return __shfl(v, src, kWave); }
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the wave (Hillis-Steele on shuffles).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int u = __shfl_up(v, o, kWave);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
+// (value, index) reductions with the lowest index winning ties.  Inactive lanes
+// pass index = INT32_MAX.
+__device__ __forceinline__ void wave_argmax(int& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    int v2 = __shfl_xor(v, o, kWave);
+    int i2 = __shfl_xor(idx, o, kWave);
+    if (v2 > v || (v2 == v && i2 < idx)) { v = v2; idx = i2; }
+  }
+}
+
+__device__ __forceinline__ void wave_argmin(int& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    int v2 = __shfl_xor(v, o, kWave);
+    int i2 = __shfl_xor(idx, o, kWave);
+    if (v2 < v || (v2 == v && i2 < idx)) { v = v2; idx = i2; }
+  }
+}
+
+__device__ __forceinline__ void set_err(int32_t* err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+}  // namespace uep
+
+// Host-side helpers.
+#define UEP_CHECK_LAUNCH()                               \
+  do {                                                   \
+    if (hipGetLastError() != hipSuccess) return UEP_EHIP; \
+  } while (0)
+
+static inline hipStream_t uep_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }

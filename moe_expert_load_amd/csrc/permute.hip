@@ -1,0 +1,72 @@
+// Permute token activations into the per-instance dispatch buffer (UltraEP article,
+// section "流式通信算子加速动态权重分发": dispatch follows the reroute plan once the
+// replica weights are in place).
+//
+// HBM-bound: every source row is read once (non-temporal 16-byte loads) and written
+// to its K destination rows (non-temporal 16-byte stores).  One wave per source
+// token; a 256-thread workgroup moves 4 tokens.  The K destination rows are loaded
+// by lanes 0..K-1 and broadcast with readlane, so store addresses stay uniform per
+// row.  Rows are moved in slices of kVec 16-byte vectors per lane (1 KiB per wave
+// per vector), all loads of a slice issued before its stores.
+#include "common.h"
+
+namespace uep {
+
+constexpr int kPmThreads = 256;
+constexpr int kPmTokPerBlock = kPmThreads / kWave;
+constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
+
+__global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
+                                                             const int32_t* __restrict__ dest_row,
+                                                             u32x4* __restrict__ out,
+                                                             int32_t* __restrict__ row_src,
+                                                             int64_t g0, int64_t g1, int K,
+                                                             int nvec) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t g = g0 + (int64_t)blockIdx.x * kPmTokPerBlock + threadIdx.x / kWave;
+  if (g >= g1) return;
+  const int d_mine = lane < K ? dest_row[g * K + lane] : -1;
+  if (row_src && lane < K && d_mine >= 0) row_src[d_mine] = (int32_t)(g * K + lane);
+  const u32x4* src = x + g * nvec;
+  for (int v0 = 0; v0 < nvec; v0 += kVec * kWave) {
+    u32x4 buf[kVec];
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < nvec) buf[u] = __builtin_nontemporal_load(src + v);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int d = readlane(d_mine, k);
+      if (d < 0) continue;
+      u32x4* dst = out + (int64_t)d * nvec;
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) {
+        const int v = v0 + u * kWave + lane;
+        if (v < nvec) __builtin_nontemporal_store(buf[u], dst + v);
+      }
+    }
+  }
+}
+
+}  // namespace uep
+
+using namespace uep;
+
+extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, int32_t T,
+                                  int32_t K, int32_t H, int32_t r_begin, int32_t r_end,
+                                  uint16_t* out, int32_t* row_src, void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || H <= 0) return UEP_EINVAL;
+  if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
+  if (K > 64 || H % 8 != 0 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
+  const int64_t g0 = (int64_t)r_begin * T, g1 = (int64_t)r_end * T;
+  if (g1 == g0) return UEP_OK;
+  if (!x || !dest_row || !out) return UEP_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) % 16 != 0)
+    return UEP_EGEOM;
+  const int64_t blocks = (g1 - g0 + kPmTokPerBlock - 1) / kPmTokPerBlock;
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)blocks), dim3(kPmThreads), 0,
+                     uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
+                     reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
+  UEP_CHECK_LAUNCH();
+  return UEP_OK;
+}

@@ -1,0 +1,185 @@
+// Redundant-slot weight staging and backward gradient reduction (UltraEP article:
+// section "共享冗余 slot 管理动态专家副本" -- fixed slots per rank shared by all MoE
+// layers, weights + gradient buffer, no optimizer state; section
+// "复用前向方案，完成权重恢复与梯度归约" -- backward reuses the cached plan, re-stages
+// the replica weights, reduces replica gradients into the main's gradient buffer
+// and clears the redundant gradient buffer; section "流式通信算子加速动态权重分发" --
+// persistent kernel pulling fixed-size tiles from a device-side task list).
+//
+// One persistent grid.  Each workgroup first turns the slot table into its task
+// list in LDS (no host round trip: the plan stays on the device), then walks tasks
+// = (slot or replicated expert) x tile with a grid stride.  A tile is 256 threads x
+// kStVec 16-byte vectors = 64 KiB of bf16 weights (or fp32 gradients); all loads of
+// a tile are issued before its stores.
+//
+// GRAD_REDUCE keeps the article's order fixed: for every element the main's
+// gradient is added to the replicas' gradients one at a time in ascending rank
+// (fp32, round to nearest even, no FMA), then each replica gradient is set to +0.
+#include "common.h"
+
+namespace uep {
+
+constexpr int kStThreads = 256;
+constexpr int kStVec = 16;
+constexpr int kStTileVec = kStThreads * kStVec;   // 16-byte vectors per tile
+constexpr int kStMaxSlots = 64 * 8;
+
+__global__ __launch_bounds__(kStThreads) void stage_weights_kernel(
+    const int32_t* __restrict__ slot_expert, int R, int S, int r_begin, int r_end,
+    const u32x4* __restrict__ main_w, u32x4* __restrict__ slot_w, int64_t nvec) {
+  __shared__ int32_t t_slot[kStMaxSlots], t_exp[kStMaxSlots];
+  __shared__ int32_t n_used;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int i = r_begin * S; i < r_end * S; ++i) {
+      const int e = slot_expert[i];
+      if (e >= 0) { t_slot[n] = i; t_exp[n] = e; ++n; }
+    }
+    n_used = n;
+  }
+  __syncthreads();
+  const int64_t tiles = (nvec + kStTileVec - 1) / kStTileVec;
+  const int64_t tasks = n_used * tiles;
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int u = (int)(task / tiles);
+    const int64_t v0 = (task % tiles) * kStTileVec;
+    const u32x4* src = main_w + (int64_t)t_exp[u] * nvec;
+    u32x4* dst = slot_w + (int64_t)t_slot[u] * nvec;
+    u32x4 buf[kStVec];
+#pragma unroll
+    for (int k = 0; k < kStVec; ++k) {
+      const int64_t v = v0 + k * kStThreads + threadIdx.x;
+      if (v < nvec) buf[k] = __builtin_nontemporal_load(src + v);
+    }
+#pragma unroll
+    for (int k = 0; k < kStVec; ++k) {
+      const int64_t v = v0 + k * kStThreads + threadIdx.x;
+      if (v < nvec) __builtin_nontemporal_store(buf[k], dst + v);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kStThreads) void stage_grad_kernel(
+    const int32_t* __restrict__ slot_expert, int R, int E, int S, int r_begin, int r_end,
+    f32x4* __restrict__ main_grad, f32x4* __restrict__ slot_grad, int64_t nvec) {
+  // groups: one per replicated expert homed in [r_begin, r_end), members in slot order
+  __shared__ int32_t g_exp[kStMaxSlots], g_first[kStMaxSlots + 1], g_mem[kStMaxSlots];
+  __shared__ int32_t lead_cnt[kStMaxSlots];   // members of the group a slot leads, else 0
+  __shared__ int32_t grp_of[kStMaxSlots];     // group index of a leading slot
+  __shared__ int32_t n_grp;
+  const int E_loc = E / R;
+  const int n_slots = R * S;
+  // a slot leads its expert's group if no earlier slot holds the same expert
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
+    const int e = slot_expert[i];
+    int cnt = 0;
+    if (e >= 0 && e / E_loc >= r_begin && e / E_loc < r_end) {
+      bool seen = false;
+      for (int i2 = 0; i2 < i; ++i2) seen |= slot_expert[i2] == e;
+      if (!seen)
+        for (int i2 = i; i2 < n_slots; ++i2) cnt += slot_expert[i2] == e;
+    }
+    lead_cnt[i] = cnt;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {          // serial scan over at most 512 counts
+    int ng = 0, nm = 0;
+    for (int i = 0; i < n_slots; ++i) {
+      if (lead_cnt[i] == 0) continue;
+      g_exp[ng] = slot_expert[i];
+      g_first[ng] = nm;
+      grp_of[i] = ng;
+      nm += lead_cnt[i];
+      ++ng;
+    }
+    g_first[ng] = nm;
+    n_grp = ng;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {   // members, in slot order
+    const int e = slot_expert[i];
+    if (e < 0 || e / E_loc < r_begin || e / E_loc >= r_end) continue;
+    int lead = -1, pos = 0;
+    for (int i2 = 0; i2 < i; ++i2)
+      if (slot_expert[i2] == e) {
+        if (lead < 0) lead = i2;
+        ++pos;
+      }
+    if (lead < 0) lead = i;
+    g_mem[g_first[grp_of[lead]] + pos] = i;
+  }
+  __syncthreads();
+  const int64_t tiles = (nvec + kStTileVec - 1) / kStTileVec;
+  const int64_t tasks = n_grp * tiles;
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int gi = (int)(task / tiles);
+    const int64_t v0 = (task % tiles) * kStTileVec;
+    f32x4* mg = main_grad + (int64_t)g_exp[gi] * nvec;
+    const int m0 = g_first[gi], m1 = g_first[gi + 1];
+    for (int k = 0; k < kStVec; ++k) {
+      const int64_t v = v0 + k * kStThreads + threadIdx.x;
+      if (v >= nvec) break;
+      f32x4 acc = mg[v];
+      for (int m = m0; m < m1; ++m) {
+        f32x4* sg = slot_grad + (int64_t)g_mem[m] * nvec + v;
+        const f32x4 add = __builtin_nontemporal_load(sg);
+        acc.x = acc.x + add.x;
+        acc.y = acc.y + add.y;
+        acc.z = acc.z + add.z;
+        acc.w = acc.w + add.w;
+        __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sg);
+      }
+      mg[v] = acc;
+    }
+  }
+}
+
+static int st_grid() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
+      cus = p.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  return cus * 4;
+}
+
+}  // namespace uep
+
+using namespace uep;
+
+extern "C" uep_status uep_stage_replica_weights(int32_t mode, int32_t R, int32_t E, int32_t S,
+                                                const int32_t* slot_expert, int32_t r_begin,
+                                                int32_t r_end, const uint16_t* main_w,
+                                                uint16_t* slot_w, float* main_grad,
+                                                float* slot_grad, int64_t expert_elems,
+                                                void* stream) {
+  if (R <= 0 || E <= 0 || S < 0 || expert_elems < 0) return UEP_EINVAL;
+  if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
+  if (R > 64 || S > 8 || E % R != 0 || expert_elems % 8 != 0) return UEP_EGEOM;
+  if (S == 0 || expert_elems == 0 || r_begin == r_end) return UEP_OK;
+  if (!slot_expert) return UEP_EINVAL;
+  hipStream_t s = uep_stream(stream);
+  if (mode == UEP_STAGE_WEIGHTS) {
+    if (!main_w || !slot_w) return UEP_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(main_w) | reinterpret_cast<uintptr_t>(slot_w)) % 16)
+      return UEP_EGEOM;
+    hipLaunchKernelGGL(stage_weights_kernel, dim3(st_grid()), dim3(kStThreads), 0, s,
+                       slot_expert, R, S, r_begin, r_end,
+                       reinterpret_cast<const u32x4*>(main_w), reinterpret_cast<u32x4*>(slot_w),
+                       expert_elems / 8);
+  } else if (mode == UEP_STAGE_GRAD_REDUCE) {
+    if (!main_grad || !slot_grad) return UEP_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(main_grad) | reinterpret_cast<uintptr_t>(slot_grad)) % 16)
+      return UEP_EGEOM;
+    hipLaunchKernelGGL(stage_grad_kernel, dim3(st_grid()), dim3(kStThreads), 0, s, slot_expert,
+                       R, E, S, r_begin, r_end, reinterpret_cast<f32x4*>(main_grad),
+                       reinterpret_cast<f32x4*>(slot_grad), expert_elems / 4);
+  } else {
+    return UEP_EINVAL;
+  }
+  UEP_CHECK_LAUNCH();
+  return UEP_OK;
+}

@@ -1,0 +1,233 @@
+"""Thin Python binding of libuep.so (the C-ABI in include/uep.h).
+
+Argument marshalling only: torch supplies device memory and the HIP stream; every
+step of the balancing path runs in the library's HIP kernels.  Output tensors the
+caller does not pass are allocated with torch on the input's device.  A non-zero
+status raises UEPError.  Importing this module fails loudly when the library is
+not built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuep.so")
+
+OK, EINVAL, EGEOM, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+ERR_ID_RANGE, ERR_DUP_ID, ERR_QUOTA_SUM, ERR_INST_DUP = 1, 2, 4, 8
+ERR_BAD_QUOTA, ERR_COVER, ERR_LP = 16, 32, 64
+STAGE_WEIGHTS, STAGE_GRAD_REDUCE = 0, 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); the exact list of symbols include/uep.h declares
+SIGNATURES = {
+    "uep_version": (ctypes.c_char_p, []),
+    "uep_status_string": (ctypes.c_char_p, [_I]),
+    "uep_load_matrix_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "uep_load_matrix": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "uep_solve_quota": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "uep_identity_quota": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "uep_reroute_workspace_size": (_SZ, [_I, _I, _I]),
+    "uep_reroute_assign": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "uep_stage_replica_weights": (_I, [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
+    "uep_waterfill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U64, _U64, _I, _P, _P, _P, _P, _P, _P]),
+    "uep_lplb_struct_size": (_SZ, [_I, _I, _I]),
+    "uep_lplb_prepare": (_I, [_P, _I, _I, _I, _P, _SZ, _P]),
+    "uep_lplb": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P]),
+}
+
+
+class UEPError(RuntimeError):
+    pass
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def version() -> str:
+    return LIB.uep_version().decode()
+
+
+def _check(status: int, name: str) -> None:
+    if status != OK:
+        raise UEPError(f"{name}: {LIB.uep_status_string(status).decode()} (status {status})")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def _new(shape, like: torch.Tensor, dtype=torch.int32) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+def load_matrix_workspace_size(R, T, K, E) -> int:
+    return int(LIB.uep_load_matrix_workspace_size(R, T, K, E))
+
+
+def load_matrix(topk_ids, E, counts=None, bucket_pos=None, err=None, ws=None, stream=None):
+    _i32(topk_ids, "topk_ids")
+    R, T, K = topk_ids.shape
+    counts = _new((R, E), topk_ids) if counts is None else counts
+    bucket_pos = _new((R, T, K), topk_ids) if bucket_pos is None else bucket_pos
+    n = load_matrix_workspace_size(R, T, K, E)
+    ws = _new((max(n, 4),), topk_ids, torch.uint8) if ws is None else ws
+    _check(LIB.uep_load_matrix(_p(topk_ids), R, T, K, E, _p(counts), _p(bucket_pos), _p(err),
+                               _p(ws), ws.numel() * ws.element_size(), _s(stream)),
+           "uep_load_matrix")
+    return counts, bucket_pos
+
+
+def solve_quota(counts, S, q_min, out=None, stream=None):
+    _i32(counts, "counts")
+    R, E = counts.shape
+    ipr = E // R + S
+    o = out or {}
+    slot_expert = o.get("slot_expert", _new((R, max(S, 1)), counts))
+    inst_expert = o.get("inst_expert", _new((R * ipr,), counts))
+    inst_quota = o.get("inst_quota", _new((R * ipr,), counts))
+    rank_load = o.get("rank_load", _new((R,), counts))
+    stats = o.get("stats", _new((4,), counts))
+    _check(LIB.uep_solve_quota(_p(counts), R, E, S, q_min, _p(slot_expert), _p(inst_expert),
+                               _p(inst_quota), _p(rank_load), _p(stats), _s(stream)),
+           "uep_solve_quota")
+    return {"slot_expert": slot_expert[:, :S], "inst_expert": inst_expert,
+            "inst_quota": inst_quota, "rank_load": rank_load, "stats": stats,
+            "inst_per_rank": ipr}
+
+
+def identity_quota(counts, inst_expert, inst_quota=None, stream=None):
+    R, E = counts.shape
+    n = inst_expert.numel()
+    inst_quota = _new((n,), counts) if inst_quota is None else inst_quota
+    _check(LIB.uep_identity_quota(_p(counts), R, E, n, _p(inst_expert), _p(inst_quota),
+                                  _s(stream)), "uep_identity_quota")
+    return inst_quota
+
+
+def reroute_workspace_size(R, E, inst_per_rank) -> int:
+    return int(LIB.uep_reroute_workspace_size(R, E, inst_per_rank))
+
+
+def reroute_assign(counts, topk_ids, bucket_pos, inst_per_rank, inst_expert, inst_quota,
+                   r_begin=0, r_end=None, xfer=None, inst_offset=None, dest_inst=None,
+                   dest_row=None, err=None, ws=None, stream=None):
+    R, E = counts.shape
+    _, T, K = topk_ids.shape
+    r_end = R if r_end is None else r_end
+    I = R * inst_per_rank
+    xfer = _new((R, I), counts) if xfer is None else xfer
+    inst_offset = _new((I + 1,), counts) if inst_offset is None else inst_offset
+    dest_inst = _new((R, T, K), counts) if dest_inst is None else dest_inst
+    dest_row = _new((R, T, K), counts) if dest_row is None else dest_row
+    n = reroute_workspace_size(R, E, inst_per_rank)
+    ws = _new((max(n, 4),), counts, torch.uint8) if ws is None else ws
+    _check(LIB.uep_reroute_assign(_p(counts), _p(topk_ids), _p(bucket_pos), R, T, K, E,
+                                  inst_per_rank, _p(inst_expert), _p(inst_quota), r_begin, r_end,
+                                  _p(xfer), _p(inst_offset), _p(dest_inst), _p(dest_row),
+                                  _p(err), _p(ws), ws.numel() * ws.element_size(), _s(stream)),
+           "uep_reroute_assign")
+    return xfer, inst_offset, dest_inst, dest_row
+
+
+def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None):
+    """x [R][T][H] bf16 (or 16-bit) tensor; out [P][H] of the same dtype."""
+    R, T, H = x.shape
+    K = dest_row.shape[2]
+    r_end = R if r_end is None else r_end
+    if x.element_size() != 2 or out.element_size() != 2:
+        raise TypeError("x and out must hold 16-bit elements")
+    _check(LIB.uep_permute(_p(x), _p(dest_row), R, T, K, H, r_begin, r_end, _p(out),
+                           _p(row_src), _s(stream)), "uep_permute")
+    return out, row_src
+
+
+def stage_replica_weights(mode, R, E, S, slot_expert, expert_elems, main_w=None, slot_w=None,
+                          main_grad=None, slot_grad=None, r_begin=0, r_end=None, stream=None):
+    r_end = R if r_end is None else r_end
+    _check(LIB.uep_stage_replica_weights(mode, R, E, S, _p(slot_expert), r_begin, r_end,
+                                         _p(main_w), _p(slot_w), _p(main_grad), _p(slot_grad),
+                                         int(expert_elems), _s(stream)),
+           "uep_stage_replica_weights")
+
+
+def waterfill(counts, topk_ids, batch_size, seed, layer, local_pref_shift=4, shared_rank=None,
+              waterline=None, slack=None, rank_load=None, ext_topk=None, want_ext=True,
+              stream=None):
+    R, E = counts.shape
+    _, T, K = topk_ids.shape
+    shared_rank = _new((R, T), counts) if shared_rank is None else shared_rank
+    waterline = _new((1,), counts) if waterline is None else waterline
+    slack = _new((R,), counts) if slack is None else slack
+    rank_load = _new((R,), counts) if rank_load is None else rank_load
+    if ext_topk is None and want_ext:
+        ext_topk = _new((R, T, K + 1), counts)
+    _check(LIB.uep_waterfill(_p(counts), _p(topk_ids), _p(batch_size), R, T, K, E,
+                             ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                             ctypes.c_uint64(layer & (2 ** 64 - 1)), local_pref_shift,
+                             _p(shared_rank), _p(waterline), _p(slack), _p(rank_load),
+                             _p(ext_topk), _s(stream)), "uep_waterfill")
+    return shared_rank, waterline, slack, rank_load, ext_topk
+
+
+def lplb_struct_size(R, E, inst_per_rank) -> int:
+    return int(LIB.uep_lplb_struct_size(R, E, inst_per_rank))
+
+
+def lplb_prepare(inst_expert_host, R, E, inst_per_rank, device, stream=None) -> torch.Tensor:
+    """Offline: build the LP structure from a host instance table into a device buffer."""
+    import numpy as np
+    ie = np.ascontiguousarray(np.asarray(inst_expert_host, dtype=np.int32))
+    n = lplb_struct_size(R, E, inst_per_rank)
+    buf = torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+    _check(LIB.uep_lplb_prepare(ie.ctypes.data_as(ctypes.c_void_p), R, E, inst_per_rank,
+                                _p(buf), buf.numel(), _s(stream)), "uep_lplb_prepare")
+    return buf
+
+
+def lplb(counts, lp, n_copies, n_inst, iters=30, x=None, m=None, inst_quota=None, stats=None,
+         err=None, stream=None):
+    x = torch.empty((max(n_copies, 1),), dtype=torch.float32, device=counts.device) if x is None else x
+    m = torch.empty((1,), dtype=torch.float32, device=counts.device) if m is None else m
+    inst_quota = _new((n_inst,), counts) if inst_quota is None else inst_quota
+    stats = _new((4,), counts) if stats is None else stats
+    _check(LIB.uep_lplb(_p(counts), _p(lp), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
+                        _p(err), _s(stream)), "uep_lplb")
+    return x[:n_copies], m, inst_quota, stats

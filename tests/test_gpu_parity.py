@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path against the CPU oracle (bit-exact for every integer,
+index and permutation output; fixed-order fp32 for the gradient reduction).
+
+Runs through the C-ABI binding (moe_expert_load_amd.uep -> libuep.so).
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle as O                                       # noqa: E402
+from moe_expert_load_amd import uep as U                 # noqa: E402
+from moe_expert_load_amd import workload as W            # noqa: E402
+from tests.gpu_helpers import (DEV, to_dev, host, err_word, say, plan_on_gpu,  # noqa: E402
+                               random_routing)
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_plan(ids, E, S, q_min):
+    counts, bp = O.load_matrix(ids, E)
+    plan = O.solve_quota(counts, S, q_min)
+    X, io, so = O.reroute(counts, plan["inst_expert"], plan["inst_quota"], plan["inst_per_rank"])
+    di, dr = O.assign(ids, bp, X, plan["inst_expert"], plan["inst_per_rank"], io, so)
+    return dict(counts=counts, bucket_pos=bp, plan=plan, xfer=X, inst_offset=io, dest_inst=di,
+                dest_row=dr)
+
+
+def compare_plan(g, o, S):
+    assert host(g["err"])[0] == 0
+    assert np.array_equal(host(g["counts"]), o["counts"])
+    assert np.array_equal(host(g["bucket_pos"]), o["bucket_pos"])
+    gp, op = g["plan"], o["plan"]
+    assert np.array_equal(host(gp["inst_expert"]), op["inst_expert"])
+    assert np.array_equal(host(gp["inst_quota"]), op["inst_quota"])
+    assert np.array_equal(host(gp["rank_load"]), op["rank_load"])
+    if S:
+        assert np.array_equal(host(gp["slot_expert"]), op["slot_expert"])
+    st = host(gp["stats"])
+    assert st.tolist() == [op["n_replicas"], op["n_steps"], op["t_star"], int(op["stuck"])]
+    assert np.array_equal(host(g["xfer"]), o["xfer"])
+    assert np.array_equal(host(g["inst_offset"]), o["inst_offset"])
+    assert np.array_equal(host(g["dest_inst"]), o["dest_inst"])
+    assert np.array_equal(host(g["dest_row"]), o["dest_row"])
+
+
+def test_library_version():
+    assert "gfx950" in U.version()
+
+
+def test_tiny_full_path():
+    w = W.TINY
+    say("case: tiny full path", w)
+    ids = W.routing(w)
+    o = oracle_plan(ids, w.E, w.S, w.q_min)
+    g = plan_on_gpu(U, to_dev(ids), w.E, w.S, w.q_min)
+    compare_plan(g, o, w.S)
+    # permute, whole group and a rank range
+    x = torch.randn(w.R, w.T, w.H, generator=torch.Generator(device=DEV).manual_seed(1),
+                    device=DEV).to(torch.bfloat16)
+    xh = host(x.view(torch.int16)).view(np.uint16)
+    P = int(o["counts"].sum())
+    out = torch.zeros(P, w.H, dtype=torch.bfloat16, device=DEV)
+    row_src = torch.full((P,), -7, dtype=torch.int32, device=DEV)
+    U.permute(x, g["dest_row"], out, row_src)
+    eo, es, ew = O.permute(xh, o["dest_row"], 0, w.R, P)
+    assert ew.all()
+    assert np.array_equal(host(out.view(torch.int16)).view(np.uint16), eo)
+    assert np.array_equal(host(row_src), es)
+    out2 = torch.zeros_like(out)
+    U.permute(x, g["dest_row"], out2, None, r_begin=1, r_end=3)
+    eo2, _, ew2 = O.permute(xh, o["dest_row"], 1, 3, P)
+    got2 = host(out2.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got2[ew2], eo2[ew2]) and (got2[~ew2] == 0).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_small_plans(seed):
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.integers(1, 9))
+    E = R * int(rng.integers(1, 6))
+    K = int(rng.integers(1, min(E, 9) + 1))
+    T = int(rng.integers(0, 700))
+    S = int(rng.integers(0, 3))
+    q_min = int(rng.integers(0, 60))
+    say(f"case: random plan seed={seed} R={R} E={E} K={K} T={T} S={S} q_min={q_min}")
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.03 * (seed % 2))
+    o = oracle_plan(ids, E, S, q_min)
+    g = plan_on_gpu(U, to_dev(ids), E, S, q_min)
+    compare_plan(g, o, S)
+
+
+def test_plan_edge_cases():
+    say("case: edge cases")
+    # all routing slots empty
+    ids = np.full((3, 5, 2), -1, dtype=np.int32)
+    o = oracle_plan(ids, 6, 1, 1)
+    compare_plan(plan_on_gpu(U, to_dev(ids), 6, 1, 1), o, 1)
+    # one hot expert, many slots
+    R, E, T = 8, 16, 512
+    ids = np.zeros((R, T, 1), dtype=np.int32)
+    o = oracle_plan(ids, E, 2, 10)
+    compare_plan(plan_on_gpu(U, to_dev(ids), E, 2, 10), o, 2)
+    # q_min larger than any move -> identity plan
+    rng = np.random.default_rng(5)
+    ids = random_routing(rng, 4, 300, 2, 8)
+    o = oracle_plan(ids, 8, 1, 10 ** 6)
+    compare_plan(plan_on_gpu(U, to_dev(ids), 8, 1, 10 ** 6), o, 1)
+    # ragged T spanning several load-matrix chunks (4096 pairs each)
+    ids = random_routing(rng, 2, 4096 // 3 * 2 + 17, 3, 10)
+    o = oracle_plan(ids, 10, 1, 5)
+    compare_plan(plan_on_gpu(U, to_dev(ids), 10, 1, 5), o, 1)
+    # T = 0
+    ids = np.zeros((2, 0, 4), dtype=np.int32)
+    err = err_word()
+    counts, bp = U.load_matrix(to_dev(ids), 8, err=err)
+    assert (host(counts) == 0).all() and host(err)[0] == 0
+
+
+def test_content_errors_are_flagged():
+    say("case: content errors")
+    err = err_word()
+    U.load_matrix(to_dev(np.array([[[0, 9]]])), 4, err=err)
+    assert host(err)[0] & U.ERR_ID_RANGE
+    err = err_word()
+    U.load_matrix(to_dev(np.array([[[2, 2]]])), 4, err=err)
+    assert host(err)[0] & U.ERR_DUP_ID
+    # quotas that do not add up to the load
+    counts = to_dev(np.array([[5, 5], [5, 5]]))
+    ids = to_dev(np.zeros((2, 1, 1)))
+    bp = to_dev(np.zeros((2, 1, 1)))
+    err = err_word()
+    U.reroute_assign(counts, ids, bp, 1, to_dev(np.array([0, 1])), to_dev(np.array([10, 9])),
+                     err=err)
+    assert host(err)[0] & U.ERR_QUOTA_SUM
+
+
+def test_host_argument_errors():
+    say("case: host argument errors")
+    t = to_dev(np.zeros((2, 4, 2)))
+    with pytest.raises(U.UEPError):
+        U.load_matrix(t, 0)
+    with pytest.raises(U.UEPError):
+        U.solve_quota(to_dev(np.zeros((3, 7))), 1, 1)          # E % R != 0
+    x = torch.zeros(2, 4, 12, dtype=torch.bfloat16, device=DEV)  # H % 8 != 0
+    with pytest.raises(U.UEPError):
+        U.permute(x, t, torch.zeros(16, 12, dtype=torch.bfloat16, device=DEV))
+
+
+def test_qwen_layer_full_size():
+    """Qwen3-235B-shaped layer: plan bit-exact at full size; permute of one rank's share
+    compared whole, the whole-group permute on sampled rows; staging of 3 slots."""
+    w = W.QWEN_LAYER
+    say("case: qwen layer full size", w)
+    ids = W.routing(w)
+    o = oracle_plan(ids, w.E, w.S, w.q_min)
+    ids_d = to_dev(ids)
+    g = plan_on_gpu(U, ids_d, w.E, w.S, w.q_min)
+    compare_plan(g, o, w.S)
+    P = w.P
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
+    x = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV).to(torch.bfloat16)
+    out = torch.empty(P, w.H, dtype=torch.bfloat16, device=DEV)
+    row_src = torch.empty(P, dtype=torch.int32, device=DEV)
+    U.permute(x, g["dest_row"], out, row_src)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.integers(0, P, 4000), [0, P - 1]]))
+    xh = host(x.view(torch.int16)).view(np.uint16)
+    exp, src = O.permute_rows(xh, o["dest_row"], rows)
+    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)]).view(np.uint16)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(host(row_src)[rows], src)
+    assert np.array_equal(np.sort(host(row_src)), np.arange(P))       # every row written once
+    # one rank's share, compared in full
+    r = 5
+    out_r = torch.zeros(P, w.H, dtype=torch.bfloat16, device=DEV)
+    U.permute(x, g["dest_row"], out_r, None, r_begin=r, r_end=r + 1)
+    rows_r = np.sort(o["dest_row"][r].reshape(-1))
+    exp_r, _ = O.permute_rows(xh, o["dest_row"], rows_r)
+    got_r = host(out_r.view(torch.int16)[torch.from_numpy(rows_r).to(DEV)]).view(np.uint16)
+    assert np.array_equal(got_r, exp_r)
+    del out, out_r
+    # staging: forward weights and the fp32 gradient reduction
+    plan = o["plan"]
+    n = w.expert_elems
+    main_w = torch.randint(-32768, 32767, (w.E, n), dtype=torch.int16, device=DEV)
+    slot_w = torch.zeros(w.R, w.S, n, dtype=torch.int16, device=DEV)
+    U.stage_replica_weights(U.STAGE_WEIGHTS, w.R, w.E, w.S, g["plan"]["slot_expert"].contiguous(),
+                            n, main_w=main_w, slot_w=slot_w)
+    se = plan["slot_expert"]
+    used = [(r_, s_) for r_ in range(w.R) for s_ in range(w.S) if se[r_, s_] >= 0]
+    for (r_, s_) in used[:3]:
+        assert torch.equal(slot_w[r_, s_], main_w[int(se[r_, s_])])
+    for r_ in range(w.R):
+        for s_ in range(w.S):
+            if se[r_, s_] < 0:
+                assert int((slot_w[r_, s_] != 0).sum()) == 0
+    del main_w, slot_w
+
+
+def test_grad_reduce_matches_oracle():
+    say("case: grad reduce")
+    rng = np.random.default_rng(11)
+    R, E, S, n = 8, 16, 2, 8 * 3000 + 8
+    se = np.full((R, S), -1, dtype=np.int32)
+    se[1, 0] = 0; se[2, 1] = 0; se[5, 0] = 0; se[3, 0] = 7; se[6, 1] = 7; se[7, 0] = 15
+    main = rng.standard_normal((E, n)).astype(np.float32)
+    slot = rng.standard_normal((R, S, n)).astype(np.float32) * 1e3
+    mg = to_dev(main, torch.float32)
+    sg = to_dev(slot, torch.float32)
+    U.stage_replica_weights(U.STAGE_GRAD_REDUCE, R, E, S, to_dev(se), n, main_grad=mg, slot_grad=sg)
+    O.grad_reduce(se, main, slot, E // R)
+    assert np.array_equal(host(mg), main)
+    assert np.array_equal(host(sg), slot)
+    # rank-range: only experts homed in [2, 4) (expert 7 lives on rank 3)
+    main2 = rng.standard_normal((E, n)).astype(np.float32)
+    slot2 = rng.standard_normal((R, S, n)).astype(np.float32)
+    mg = to_dev(main2, torch.float32)
+    sg = to_dev(slot2, torch.float32)
+    U.stage_replica_weights(U.STAGE_GRAD_REDUCE, R, E, S, to_dev(se), n, main_grad=mg,
+                            slot_grad=sg, r_begin=2, r_end=4)
+    O.grad_reduce(se, main2, slot2, E // R, 2, 4)
+    assert np.array_equal(host(mg), main2) and np.array_equal(host(sg), slot2)
+
+
+def test_waterfill_layer_full_size():
+    """DeepSeek-V3-shaped layer with Waterfill: H, S_r and every token's shared rank
+    bit-exact; the fused layout (K+1 columns) through load matrix, identity quotas,
+    reroute and assignment bit-exact; permute sampled."""
+    w = W.DSV3_WATERFILL
+    say("case: waterfill full size", w)
+    ids = W.routing(w)
+    seed = W.waterfill_seed(w)
+    counts_o, _ = O.load_matrix(ids, w.E)
+    B = np.full(w.R, w.T, dtype=np.int32)
+    sh_o, H_o, S_o, L_o = O.waterfill(counts_o, ids, B, seed, 0)
+    ids_d = to_dev(ids)
+    counts, _ = U.load_matrix(ids_d, w.E)
+    sh, wl, sl, rl, ext = U.waterfill(counts, ids_d, to_dev(B), seed, 0)
+    assert host(wl)[0] == H_o
+    assert np.array_equal(host(sl), S_o) and np.array_equal(host(rl), L_o)
+    assert np.array_equal(host(sh), sh_o)
+    ext_o = O.extend_topk(ids, sh_o, w.E)
+    assert np.array_equal(host(ext), ext_o)
+    E2 = w.E + w.R
+    ipr = w.E_loc + 1
+    inst = np.full(w.R * ipr, -1, dtype=np.int32)
+    for r in range(w.R):
+        inst[r * ipr:r * ipr + w.E_loc] = np.arange(r * w.E_loc, (r + 1) * w.E_loc)
+        inst[r * ipr + w.E_loc] = w.E + r
+    c2_o, bp2_o = O.load_matrix(ext_o, E2)
+    q_o = O.identity_quota(c2_o, inst)
+    X_o, io_o, so_o = O.reroute(c2_o, inst, q_o, ipr)
+    di_o, dr_o = O.assign(ext_o, bp2_o, X_o, inst, ipr, io_o, so_o)
+    err = err_word()
+    c2, bp2 = U.load_matrix(ext, E2, err=err)
+    inst_d = to_dev(inst)
+    q = U.identity_quota(c2, inst_d)
+    xfer, ioff, di, dr = U.reroute_assign(c2, ext, bp2, ipr, inst_d, q, err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(c2), c2_o) and np.array_equal(host(bp2), bp2_o)
+    assert np.array_equal(host(q), q_o)
+    assert np.array_equal(host(xfer), X_o) and np.array_equal(host(ioff), io_o)
+    assert np.array_equal(host(di), di_o) and np.array_equal(host(dr), dr_o)
+    # permute one rank's share of the fused layout (K+1 rows per token)
+    P = int(c2_o.sum())
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
+    x = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV).to(torch.bfloat16)
+    out = torch.zeros(P, w.H, dtype=torch.bfloat16, device=DEV)
+    r = 9
+    U.permute(x, dr, out, None, r_begin=r, r_end=r + 1)
+    rows = np.sort(dr_o[r].reshape(-1))[::37]
+    xh = host(x.view(torch.int16)).view(np.uint16)
+    exp, _ = O.permute_rows(xh, dr_o, rows)
+    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)]).view(np.uint16)
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_waterfill_random_small(seed):
+    rng = np.random.default_rng(500 + seed)
+    R = int(rng.integers(1, 9))
+    E = R * int(rng.integers(1, 5))
+    K = int(rng.integers(1, min(E, 6) + 1))
+    T = int(rng.integers(1, 300))
+    say(f"case: waterfill random seed={seed} R={R} E={E} K={K} T={T}")
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.05)
+    B = rng.integers(0, T + 1, R).astype(np.int32)
+    counts_o, _ = O.load_matrix(ids, E)
+    for shift in (0, 4):
+        sh_o, H_o, S_o, L_o = O.waterfill(counts_o, ids, B, 12345 + seed, 7, shift)
+        sh, wl, sl, rl, ext = U.waterfill(to_dev(counts_o), to_dev(ids), to_dev(B), 12345 + seed, 7,
+                                          local_pref_shift=shift)
+        assert host(wl)[0] == H_o and np.array_equal(host(sl), S_o)
+        assert np.array_equal(host(sh), sh_o)
