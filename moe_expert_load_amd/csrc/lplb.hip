@@ -1,7 +1,557 @@
-// placeholder until the LPLB kernel lands
+// LPLB: min-max split of replicated experts' load over their copies (Waterfill/LPLB
+// blog, sections "线性规划（LP）公式化构建" and "决策变量与矩阵规模优化": minimise the
+// peak rank load M; per rank, copy allocation + fixed single-copy load + slack = M;
+// per replicated expert, the split sums to its true count; the structural matrix is
+// built offline from the placement, only the right-hand side changes per batch; a
+// Big-M auxiliary column keeps the system feasible and is driven to zero.  Section
+// "从全局计数到LP求解的工程实现": every rank solves the same LP on the GPU with an
+// interior-point method into preallocated buffers.  Section "从LP解决方案到Token调度":
+// the split decides how each replicated expert's tokens go to its copies).
+//
+// Standard form, loads scaled by sigma = max(1, mean rank load):
+//   variables x_p (copies), s_r (rank slacks), M, a (Big-M column, cost 8), all >= 0
+//   rank r  : M + a - s_r - sum_{p on r} x_p = F_r     group g : sum_{p in g} x_p = c_g
+// Solver: Mehrotra predictor-corrector, fp32 iterates, one workgroup.  The normal
+// equations A D A^T dy = rhs are reduced by eliminating the (diagonal) expert rows;
+// the remaining R x R rank matrix P = (d_M + d_a) 11^T + diag(d_s) + sum over groups
+// of a weighted Laplacian of the copies' ranks is assembled and Cholesky-factored in
+// fp64 in LDS.  fp32 is not enough there: the dense M direction (d_M -> inf) swamps
+// the differential entries of copies whose optimal share is a small fraction of the
+// peak.  Diagonal entries are formed as sums of positive terms (no cancellation); a
+// pivot that lost its precision is replaced by a huge one (Cholesky-infinity), which
+// drops that direction.  Iterations stop changing the iterate once mu < 1e-9.
+// Output: x >= 0 normalised so each group sums exactly to its count, m = the max rank
+// load of that split, and integer quotas by largest remainder on rint(x * 256).
+#include <math.h>
+
+#include <vector>
+
 #include "common.h"
-extern "C" size_t uep_lplb_struct_size(int32_t R, int32_t E, int32_t inst_per_rank) { return 0; }
-extern "C" uep_status uep_lplb_prepare(const int32_t* inst_expert_host, int32_t R, int32_t E,
-                            int32_t inst_per_rank, void* lp, size_t lp_bytes, void* stream) { return UEP_EGEOM; }
-extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float* x, float* m,
-                    int32_t* inst_quota, int32_t* stats, int32_t* err, void* stream) { return UEP_EGEOM; }
+
+namespace uep {
+
+constexpr int kLpThreads = 256;
+constexpr int kLpMaxR = 64;
+constexpr int kLpMaxG = 128;
+constexpr int kLpMaxN = 256;
+constexpr int kLpMaxE = 4096;
+constexpr int kLpMaxI = 64 * 40;
+constexpr int kLpMagic = 0x4C50424C;
+constexpr float kBigM = 8.0f;
+constexpr float kEta = 0.99f;
+constexpr float kMuStop = 1e-9f;
+constexpr double kPivTol = 1e-13;
+constexpr int kLpMaxNV = kLpMaxN + kLpMaxR + 2;
+constexpr int kLpMaxRows = kLpMaxR + kLpMaxG;
+
+// device structure (int32 words):
+// [0..7] magic, R, E, ipr, I, G, n, 0
+// grp_expert[G] | grp_start[G+1] | copy_inst[n] | copy_rank[n] | copy_group[n] |
+// rank_start[R+1] | rank_copy[n] | exp_inst[E] | inst_expert[I] | inst_copy[I]
+// exp_inst[e]: instance of a single-copy expert, -2 - g for replicated group g, -1 none
+// inst_copy[i]: copy index of instance i, or -1
+struct LpView {
+  int R, E, ipr, I, G, n;
+  const int32_t *grp_expert, *grp_start, *copy_inst, *copy_rank, *copy_group;
+  const int32_t *rank_start, *rank_copy, *exp_inst, *inst_expert, *inst_copy;
+};
+
+__host__ __device__ inline size_t lp_words(int R, int E, int I, int G, int n) {
+  return 8 + (size_t)G + (G + 1) + 3 * (size_t)n + (R + 1) + n + E + 2 * (size_t)I;
+}
+
+__device__ inline LpView lp_view(const int32_t* w) {
+  LpView v;
+  v.R = w[1]; v.E = w[2]; v.ipr = w[3]; v.I = w[4]; v.G = w[5]; v.n = w[6];
+  const int32_t* p = w + 8;
+  v.grp_expert = p; p += v.G;
+  v.grp_start = p; p += v.G + 1;
+  v.copy_inst = p; p += v.n;
+  v.copy_rank = p; p += v.n;
+  v.copy_group = p; p += v.n;
+  v.rank_start = p; p += v.R + 1;
+  v.rank_copy = p; p += v.n;
+  v.exp_inst = p; p += v.E;
+  v.inst_expert = p; p += v.I;
+  v.inst_copy = p;
+  return v;
+}
+
+struct LpShared {
+  // structure (copied from global)
+  int32_t grp_start[kLpMaxG + 1], copy_rank[kLpMaxN], copy_group[kLpMaxN];
+  int32_t rank_start[kLpMaxR + 1], rank_copy[kLpMaxN];
+  // problem data
+  float f[kLpMaxR], hh[kLpMaxG];
+  int32_t cnt_i[kLpMaxG];
+  // iterates and work vectors (fp32)
+  float v[kLpMaxNV], z[kLpMaxNV], dv[kLpMaxNV], dz[kLpMaxNV], rc[kLpMaxNV], tv[kLpMaxNV];
+  float y[kLpMaxRows], dy[kLpMaxRows], rb[kLpMaxRows], rhs[kLpMaxRows];
+  // normal equations (fp64)
+  double d[kLpMaxNV], beta[kLpMaxG], t64[kLpMaxRows], u64[kLpMaxR];
+  double P[kLpMaxR][kLpMaxR + 1];
+  double Ldiag[kLpMaxR], d0[kLpMaxR];
+  // reductions
+  double red[kLpThreads / kWave];
+  float redf[kLpThreads / kWave];
+  int32_t Fi[kLpMaxR], hc[kLpMaxG];       // fixed load per rank, count per group
+};
+
+__device__ inline double blk_sum(double x, LpShared& S) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) S.red[w] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLpThreads / kWave; ++i) t += S.red[i];
+  return t;
+}
+
+__device__ inline float blk_min(float x, LpShared& S) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, kWave));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) S.redf[w] = x;
+  __syncthreads();
+  float t = S.redf[0];
+#pragma unroll
+  for (int i = 1; i < kLpThreads / kWave; ++i) t = fminf(t, S.redf[i]);
+  return t;
+}
+
+// out[R+G] = A * vec
+__device__ inline void lp_Av(const float* vec, float* out, int n, int R, int G, LpShared& S) {
+  const float Ma = vec[n + R] + vec[n + R + 1];
+  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
+    float acc;
+    if (i < R) {
+      acc = Ma - vec[n + i];
+      for (int k = S.rank_start[i]; k < S.rank_start[i + 1]; ++k) acc -= vec[S.rank_copy[k]];
+    } else {
+      const int g = i - R;
+      acc = 0.0f;
+      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += vec[p];
+    }
+    out[i] = acc;
+  }
+}
+
+// out[nv] = A^T * y ; needs the sum of rank duals
+__device__ inline void lp_ATy(const float* yv, float* out, int n, int R, int G, LpShared& S) {
+  float part = 0.0f;
+  for (int r = threadIdx.x; r < R; r += kLpThreads) part += yv[r];
+  const float ys = (float)blk_sum((double)part, S);
+  for (int i = threadIdx.x; i < n + R + 2; i += kLpThreads) {
+    float val;
+    if (i < n) val = -yv[S.copy_rank[i]] + yv[R + S.copy_group[i]];
+    else if (i < n + R) val = -yv[i - n];
+    else val = ys;
+    out[i] = val;
+  }
+}
+
+__device__ inline float lp_cost(int i, int n, int R) {
+  return i == n + R ? 1.0f : (i == n + R + 1 ? kBigM : 0.0f);
+}
+
+// largest step in [0, 1] keeping u + a du >= 0
+__device__ inline float lp_step(const float* u, const float* du, int nv, LpShared& S) {
+  float a = 1.0f;
+  for (int i = threadIdx.x; i < nv; i += kLpThreads)
+    if (du[i] < 0.0f) a = fminf(a, -u[i] / du[i]);
+  return blk_min(a, S);
+}
+
+// dy = (A D A^T)^{-1} rhs with the factored rank matrix
+__device__ void lp_solve(int n, int R, int G, LpShared& S) {
+  for (int g = threadIdx.x; g < G; g += kLpThreads) S.t64[g] = (double)S.rhs[R + g] / S.beta[g];
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += kLpThreads) {
+    double acc = S.rhs[r];
+    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+      const int p = S.rank_copy[k];
+      acc += S.d[p] * S.t64[S.copy_group[p]];
+    }
+    S.u64[r] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    double b = l < R ? S.u64[l] : 0.0;
+    for (int j = 0; j < R; ++j) {          // L y = r1
+      const double yj = __shfl(b, j, kWave) / S.Ldiag[j];
+      if (l > j && l < R) b -= S.P[l][j] * yj;
+      if (l == j) b = yj;
+    }
+    for (int j = R - 1; j >= 0; --j) {     // L^T u = y
+      const double xj = __shfl(b, j, kWave) / S.Ldiag[j];
+      if (l < j) b -= S.P[j][l] * xj;
+      if (l == j) b = xj;
+    }
+    if (l < R) S.u64[l] = b;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
+    if (i < R) {
+      S.dy[i] = (float)S.u64[i];
+    } else {
+      const int g = i - R;
+      double acc = S.rhs[i];
+      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
+      S.dy[i] = (float)(acc / S.beta[g]);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ void lp_factor(int n, int R, int G, LpShared& S) {
+  const int nv = n + R + 2;
+  for (int i = threadIdx.x; i < nv; i += kLpThreads) S.d[i] = (double)S.v[i] / (double)S.z[i];
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += kLpThreads) {
+    double b = 0.0;
+    for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) b += S.d[p];
+    S.beta[g] = b;
+  }
+  __syncthreads();
+  const double delta = S.d[n + R] + S.d[n + R + 1];
+  for (int idx = threadIdx.x; idx < R * R; idx += kLpThreads) {
+    const int r = idx / R, r2 = idx % R;
+    double val = delta;
+    if (r == r2) {
+      double diag = S.d[n + r];
+      for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+        const int p = S.rank_copy[k], g = S.copy_group[p];
+        double others = 0.0;
+        for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
+          if (q != p) others += S.d[q];
+        diag += S.d[p] * (others / S.beta[g]);
+      }
+      val += diag;
+      S.d0[r] = val;
+    } else {
+      double off = 0.0;
+      for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+        const int p = S.rank_copy[k], g = S.copy_group[p];
+        for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
+          if (S.copy_rank[q] == r2) off += S.d[p] * (S.d[q] / S.beta[g]);
+      }
+      val -= off;
+    }
+    S.P[r][r2] = val;
+  }
+  __syncthreads();
+  for (int j = 0; j < R; ++j) {            // right-looking Cholesky, lower triangle
+    const double pj = S.P[j][j];
+    const bool bad = !(pj > kPivTol * S.d0[j]);
+    const double ljj = bad ? 1e32 : sqrt(pj);
+    if (threadIdx.x == 0) S.Ldiag[j] = ljj;
+    for (int i = j + 1 + threadIdx.x; i < R; i += kLpThreads) S.P[i][j] = bad ? 0.0 : S.P[i][j] / ljj;
+    __syncthreads();
+    const int m = R - j - 1;
+    for (int idx = threadIdx.x; idx < m * m; idx += kLpThreads) {
+      const int i = j + 1 + idx / m, k = j + 1 + idx % m;
+      if (k <= i) S.P[i][k] -= S.P[i][j] * S.P[k][j];
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ lpw,
+                                                          int iters, float* __restrict__ x_out,
+                                                          float* __restrict__ m_out,
+                                                          int32_t* __restrict__ inst_quota,
+                                                          int32_t* __restrict__ stats,
+                                                          int32_t* err) {
+  extern __shared__ __align__(16) unsigned char lp_raw[];
+  LpShared& S = *reinterpret_cast<LpShared*>(lp_raw);
+  const LpView L = lp_view(lpw);
+  const int R = L.R, E = L.E, G = L.G, n = L.n, nv = n + R + 2;
+  const int tid = threadIdx.x;
+
+  for (int i = tid; i <= G; i += kLpThreads) S.grp_start[i] = L.grp_start[i];
+  for (int i = tid; i < n; i += kLpThreads) {
+    S.copy_rank[i] = L.copy_rank[i];
+    S.copy_group[i] = L.copy_group[i];
+    S.rank_copy[i] = L.rank_copy[i];
+  }
+  for (int i = tid; i <= R; i += kLpThreads) S.rank_start[i] = L.rank_start[i];
+  for (int r = tid; r < R; r += kLpThreads) S.Fi[r] = 0;
+  __syncthreads();
+  // expert loads (column sums of the load matrix): fixed load per rank, count per group
+  int bad = 0;
+  for (int e = tid; e < E; e += kLpThreads) {
+    int c = 0;
+    for (int r = 0; r < R; ++r) c += counts[(int64_t)r * E + e];
+    const int i = L.exp_inst[e];
+    if (c > 0 && i == -1) bad |= UEP_ERR_LP;
+    if (c >= (1 << 27)) bad |= UEP_ERR_LP;
+    if (i >= 0) atomicAdd(&S.Fi[i / L.ipr], c);       // integer: exact in any order
+    else if (i <= -2) S.hc[-2 - i] = c;
+  }
+  if (bad) set_err(err, bad);
+  __syncthreads();
+  double part = 0.0;
+  for (int r = tid; r < R; r += kLpThreads) part += S.Fi[r];
+  for (int g = tid; g < G; g += kLpThreads) part += S.hc[g];
+  const double total = blk_sum(part, S);
+  const double sigma = fmax(1.0, total / R);
+  for (int r = tid; r < R; r += kLpThreads) S.f[r] = (float)(S.Fi[r] / sigma);
+  for (int g = tid; g < G; g += kLpThreads) {
+    S.hh[g] = (float)(S.hc[g] / sigma);
+    S.cnt_i[g] = S.grp_start[g + 1] - S.grp_start[g];
+  }
+  __syncthreads();
+
+  int run = 0;
+  if (G > 0) {
+    // starting point: balanced split, slacks >= 1, a = 1; duals y_r = 0.5 / R
+    for (int p = tid; p < n; p += kLpThreads) {
+      const int g = S.copy_group[p];
+      S.tv[p] = S.hh[g] / (float)S.cnt_i[g];
+    }
+    __syncthreads();
+    float lmax = -1e30f;
+    for (int r = tid; r < R; r += kLpThreads) {
+      float ld = S.f[r];
+      for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) ld += S.tv[S.rank_copy[k]];
+      S.rb[r] = ld;
+      lmax = fmaxf(lmax, ld);
+    }
+    const float M0 = -blk_min(-lmax, S);
+    for (int i = tid; i < nv; i += kLpThreads) {
+      float val;
+      if (i < n) val = S.tv[i] + 0.1f;
+      else if (i < n + R) val = M0 - S.rb[i - n] + 1.0f;
+      else if (i == n + R) val = M0;
+      else val = 1.0f;
+      S.v[i] = val;
+    }
+    for (int i = tid; i < R + G; i += kLpThreads) S.y[i] = i < R ? 0.5f / R : 0.0f;
+    __syncthreads();
+    lp_ATy(S.y, S.tv, n, R, G, S);
+    __syncthreads();
+    for (int i = tid; i < nv; i += kLpThreads) S.z[i] = fmaxf(lp_cost(i, n, R) - S.tv[i], 0.0f) + 1.0f;
+    __syncthreads();
+
+    for (int it = 0; it < iters; ++it) {
+      // residuals and complementarity
+      lp_Av(S.v, S.rb, n, R, G, S);
+      __syncthreads();
+      for (int i = tid; i < R + G; i += kLpThreads)
+        S.rb[i] = (i < R ? S.f[i] : S.hh[i - R]) - S.rb[i];
+      lp_ATy(S.y, S.tv, n, R, G, S);
+      __syncthreads();
+      double cz = 0.0;
+      for (int i = tid; i < nv; i += kLpThreads) {
+        S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
+        cz += (double)(S.v[i] * S.z[i]);
+      }
+      const float mu = (float)(blk_sum(cz, S) / nv);
+      if (!(mu >= kMuStop)) break;
+      ++run;
+      lp_factor(n, R, G, S);
+      // predictor: rhs = rb + A (v + D rc)
+      for (int i = tid; i < nv; i += kLpThreads) S.tv[i] = S.v[i] + (float)(S.d[i] * S.rc[i]);
+      __syncthreads();
+      lp_Av(S.tv, S.rhs, n, R, G, S);
+      __syncthreads();
+      for (int i = tid; i < R + G; i += kLpThreads) S.rhs[i] += S.rb[i];
+      __syncthreads();
+      lp_solve(n, R, G, S);
+      lp_ATy(S.dy, S.tv, n, R, G, S);
+      __syncthreads();
+      for (int i = tid; i < nv; i += kLpThreads) {
+        S.dz[i] = S.rc[i] - S.tv[i];
+        S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
+      }
+      __syncthreads();
+      const float ap = lp_step(S.v, S.dv, nv, S);
+      const float ad = lp_step(S.z, S.dz, nv, S);
+      double ca = 0.0;
+      for (int i = tid; i < nv; i += kLpThreads)
+        ca += (double)((S.v[i] + ap * S.dv[i]) * (S.z[i] + ad * S.dz[i]));
+      const float mu_aff = (float)(blk_sum(ca, S) / nv);
+      const float ratio = mu_aff / mu;
+      const float sg = ratio * ratio * ratio;
+      // corrector: rmu = sg mu - v z - dv dz ; rhs = rb + A (D rc - rmu / z)
+      for (int i = tid; i < nv; i += kLpThreads) {
+        const float rmu = sg * mu - S.v[i] * S.z[i] - S.dv[i] * S.dz[i];
+        S.dv[i] = rmu;                       // keep rmu in dv until the new direction
+        S.tv[i] = (float)(S.d[i] * S.rc[i]) - rmu / S.z[i];
+      }
+      __syncthreads();
+      lp_Av(S.tv, S.rhs, n, R, G, S);
+      __syncthreads();
+      for (int i = tid; i < R + G; i += kLpThreads) S.rhs[i] += S.rb[i];
+      __syncthreads();
+      lp_solve(n, R, G, S);
+      lp_ATy(S.dy, S.tv, n, R, G, S);
+      __syncthreads();
+      for (int i = tid; i < nv; i += kLpThreads) {
+        const float rmu = S.dv[i];
+        S.dz[i] = S.rc[i] - S.tv[i];
+        S.dv[i] = rmu / S.z[i] - (float)(S.d[i] * S.dz[i]);
+      }
+      __syncthreads();
+      const float ap2 = lp_step(S.v, S.dv, nv, S);
+      const float ad2 = lp_step(S.z, S.dz, nv, S);
+      for (int i = tid; i < nv; i += kLpThreads) {
+        S.v[i] += kEta * ap2 * S.dv[i];
+        S.z[i] += kEta * ad2 * S.dz[i];
+      }
+      for (int i = tid; i < R + G; i += kLpThreads) S.y[i] += kEta * ad2 * S.dy[i];
+      __syncthreads();
+    }
+  }
+
+  // split: clip, scale back, normalise every group to its count
+  for (int g = tid; g < G; g += kLpThreads) {
+    const int p0 = S.grp_start[g], p1 = S.grp_start[g + 1];
+    const int c = S.hc[g];
+    double sum = 0.0;
+    for (int p = p0; p < p1; ++p) sum += (double)(fmaxf(S.v[p], 0.0f) * (float)sigma);
+    for (int p = p0; p < p1; ++p) {
+      const double xp = (double)(fmaxf(S.v[p], 0.0f) * (float)sigma);
+      S.tv[p] = sum > 0.0 ? (float)(xp * ((double)c / sum)) : (float)((double)c / (p1 - p0));
+      x_out[p] = S.tv[p];
+    }
+  }
+  __syncthreads();
+  double mx = 0.0;
+  for (int r = tid; r < R; r += kLpThreads) {
+    double ld = S.Fi[r];
+    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) ld += S.tv[S.rank_copy[k]];
+    mx = fmax(mx, ld);
+  }
+  {
+    float mxf = (float)mx;
+    mxf = -blk_min(-mxf, S);
+    if (tid == 0) m_out[0] = mxf;
+  }
+  // integer quotas: single-copy instances take the whole load, copies by largest remainder
+  for (int i = tid; i < L.I; i += kLpThreads) {
+    const int e = L.inst_expert[i];
+    if (e < 0) { inst_quota[i] = 0; continue; }
+    if (L.inst_copy[i] < 0) {
+      int c = 0;
+      for (int r = 0; r < R; ++r) c += counts[(int64_t)r * E + e];
+      inst_quota[i] = c;
+      continue;
+    }
+    const int p = L.inst_copy[i], g = S.copy_group[p];
+    const int p0 = S.grp_start[g], p1 = S.grp_start[g + 1];
+    const int64_t c = S.hc[g];
+    int64_t W = 0;
+    for (int q = p0; q < p1; ++q) W += (int64_t)rint((double)fmaxf(S.tv[q], 0.0f) * 256.0);
+    int64_t q_mine;
+    if (W == 0) {
+      const int k = p - p0, cnt = p1 - p0;
+      q_mine = c / cnt + (k < c % cnt ? 1 : 0);
+    } else {
+      int64_t base_sum = 0;
+      const int64_t wp = (int64_t)rint((double)fmaxf(S.tv[p], 0.0f) * 256.0);
+      const int64_t rem_p = (c * wp) % W;
+      int rank_of_p = 0;                    // copies ahead of p in (remainder desc, index asc)
+      for (int q = p0; q < p1; ++q) {
+        const int64_t wq = (int64_t)rint((double)fmaxf(S.tv[q], 0.0f) * 256.0);
+        base_sum += (c * wq) / W;
+        const int64_t rem_q = (c * wq) % W;
+        rank_of_p += (rem_q > rem_p) || (rem_q == rem_p && q < p);
+      }
+      const int64_t left = c - base_sum;
+      q_mine = (c * wp) / W + (rank_of_p < left ? 1 : 0);
+    }
+    inst_quota[i] = (int32_t)q_mine;
+  }
+  if (tid == 0 && stats) {
+    stats[0] = G;
+    stats[1] = n;
+    stats[2] = run;
+    stats[3] = 0;
+  }
+}
+
+}  // namespace uep
+
+using namespace uep;
+
+extern "C" size_t uep_lplb_struct_size(int32_t R, int32_t E, int32_t inst_per_rank) {
+  if (R <= 0 || E <= 0 || inst_per_rank <= 0) return 0;
+  const int I = R * inst_per_rank;
+  return sizeof(int32_t) * lp_words(R, E, I, E, I);
+}
+
+extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
+                                       int32_t inst_per_rank, void* lp, size_t lp_bytes,
+                                       void* stream) {
+  if (R <= 0 || E <= 0 || inst_per_rank <= 0 || !ie || !lp) return UEP_EINVAL;
+  const int I = R * inst_per_rank;
+  if (R > kLpMaxR || E > kLpMaxE || I > kLpMaxI) return UEP_EGEOM;
+  if (lp_bytes < uep_lplb_struct_size(R, E, inst_per_rank)) return UEP_EWORKSPACE;
+  std::vector<std::vector<int>> inst_of(E);
+  for (int i = 0; i < I; ++i) {
+    const int e = ie[i];
+    if (e < -1 || e >= E) return UEP_EINVAL;
+    if (e >= 0) inst_of[e].push_back(i);
+  }
+  std::vector<int> grp_expert, grp_start{0}, copy_inst, copy_rank, copy_group;
+  std::vector<int> exp_inst(E, -1), inst_copy(I, -1);
+  for (int e = 0; e < E; ++e) {
+    const auto& v = inst_of[e];
+    for (size_t a = 0; a < v.size(); ++a)
+      for (size_t b = a + 1; b < v.size(); ++b)
+        if (v[a] / inst_per_rank == v[b] / inst_per_rank) return UEP_EINVAL;
+    if (v.size() == 1) exp_inst[e] = v[0];
+    if (v.size() >= 2) {
+      const int g = (int)grp_expert.size();
+      exp_inst[e] = -2 - g;
+      grp_expert.push_back(e);
+      for (int i : v) {
+        inst_copy[i] = (int)copy_inst.size();
+        copy_inst.push_back(i);
+        copy_rank.push_back(i / inst_per_rank);
+        copy_group.push_back(g);
+      }
+      grp_start.push_back((int)copy_inst.size());
+    }
+  }
+  const int G = (int)grp_expert.size(), n = (int)copy_inst.size();
+  if (G > kLpMaxG || n > kLpMaxN) return UEP_EGEOM;
+  std::vector<int> rank_start(R + 1, 0), rank_copy(n);
+  for (int p = 0; p < n; ++p) rank_start[copy_rank[p] + 1]++;
+  for (int r = 0; r < R; ++r) rank_start[r + 1] += rank_start[r];
+  {
+    std::vector<int> fill(rank_start.begin(), rank_start.end() - 1);
+    for (int p = 0; p < n; ++p) rank_copy[fill[copy_rank[p]]++] = p;
+  }
+  std::vector<int32_t> w(lp_words(R, E, I, G, n), 0);
+  w[0] = kLpMagic; w[1] = R; w[2] = E; w[3] = inst_per_rank; w[4] = I; w[5] = G; w[6] = n;
+  size_t o = 8;
+  auto put = [&](const std::vector<int>& a) { for (int x : a) w[o++] = x; };
+  put(grp_expert); put(grp_start); put(copy_inst); put(copy_rank); put(copy_group);
+  put(rank_start); put(rank_copy); put(exp_inst);
+  for (int i = 0; i < I; ++i) w[o++] = ie[i];
+  put(inst_copy);
+  hipStream_t s = uep_stream(stream);
+  if (hipMemcpyAsync(lp, w.data(), w.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
+      hipSuccess)
+    return UEP_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return UEP_EHIP;
+  return UEP_OK;
+}
+
+extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float* x,
+                               float* m, int32_t* inst_quota, int32_t* stats, int32_t* err,
+                               void* stream) {
+  if (!counts || !lp || !x || !m || !inst_quota || iters < 0 || iters > 200) return UEP_EINVAL;
+  hipLaunchKernelGGL(lplb_kernel, dim3(1), dim3(kLpThreads), sizeof(LpShared), uep_stream(stream),
+                     counts, static_cast<const int32_t*>(lp), iters, x, m, inst_quota, stats, err);
+  UEP_CHECK_LAUNCH();
+  return UEP_OK;
+}

@@ -1,0 +1,73 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function that
+include/uep.h declares, and its host-side argument checks answer without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uep.h")
+LIB = os.path.join(ROOT, "moe_expert_load_amd", "libuep.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uep_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libuep.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("uep_load_matrix", "uep_solve_quota", "uep_reroute_assign", "uep_permute",
+              "uep_stage_replica_weights", "uep_waterfill", "uep_lplb"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_signature_table_matches_header():
+    src = open(os.path.join(ROOT, "moe_expert_load_amd", "uep.py")).read()
+    table = set(re.findall(r'"(uep_[a-z0-9_]+)":', src))
+    assert table == set(declared_functions())
+
+
+def test_host_side_calls_without_gpu(lib):
+    lib.uep_version.restype = ctypes.c_char_p
+    assert b"gfx950" in lib.uep_version()
+    lib.uep_status_string.restype = ctypes.c_char_p
+    assert lib.uep_status_string(3) == b"workspace too small"
+    lib.uep_load_matrix_workspace_size.restype = ctypes.c_size_t
+    # 32 ranks x 16 chunks x 128 experts x 4 bytes
+    assert lib.uep_load_matrix_workspace_size(32, 8192, 8, 128) == 32 * 16 * 128 * 4
+    lib.uep_reroute_workspace_size.restype = ctypes.c_size_t
+    assert lib.uep_reroute_workspace_size(32, 128, 5) > 0
+    lib.uep_lplb_struct_size.restype = ctypes.c_size_t
+    assert lib.uep_lplb_struct_size(64, 256, 5) > 0
+    null = ctypes.c_void_p(None)
+    i32 = ctypes.c_int32
+    # invalid geometry is refused before anything touches a device
+    assert lib.uep_load_matrix(null, i32(0), i32(1), i32(1), i32(4), null, null, null, null,
+                               ctypes.c_size_t(0), null) == 1
+    assert lib.uep_load_matrix(null, i32(65), i32(1), i32(1), i32(4), null, null, null, null,
+                               ctypes.c_size_t(0), null) == 2
+    assert lib.uep_solve_quota(null, i32(3), i32(7), i32(1), i32(1), null, null, null, null, null,
+                               null) == 2
+    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2), null, null,
+                           null) == 2
+    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3), null, null,
+                           null) == 1
+    assert lib.uep_lplb_prepare(null, i32(2), i32(2), i32(2), null, ctypes.c_size_t(0), null) == 1
+    assert lib.uep_stage_replica_weights(i32(0), i32(4), i32(8), i32(9), null, i32(0), i32(4), null,
+                                         null, null, null, ctypes.c_int64(8), null) == 2

@@ -1,0 +1,196 @@
+"""GPU parity of LPLB (Waterfill/LPLB blog, sections "线性规划（LP）公式化构建" and
+"从LP解决方案到Token调度") against the fp64 simplex oracle.
+
+The split x is not unique, so what is compared is: the objective m within 1e-3 of the
+oracle's M* (and never below it), the split's validity (non-negative, each group
+summing to its count), and the integer quotas, which must be exactly the largest
+remainder rounding of the split the kernel returned.  The reroute/assignment driven by
+the quotas is then checked bit-exact against the oracle on the oracle's own quotas, and
+by its properties on the kernel's quotas.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle as O                                       # noqa: E402
+from moe_expert_load_amd import uep as U                 # noqa: E402
+from moe_expert_load_amd import workload as W            # noqa: E402
+from tests.gpu_helpers import DEV, to_dev, host, err_word, say  # noqa: E402
+from tests.test_oracle_reroute_permute import (check_reroute_properties,  # noqa: E402
+                                               check_assign_properties)
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-3
+
+
+def copy_groups(inst_expert, E):
+    """Copies (instance ids) of every replicated expert, ascending expert then instance."""
+    groups = []
+    for e in range(E):
+        insts = [i for i, v in enumerate(inst_expert) if v == e]
+        if len(insts) >= 2:
+            groups.append((e, insts))
+    return groups
+
+
+def check_largest_remainder(x, c, q):
+    """q is the largest-remainder rounding of c over weights rint(max(x, 0) * 256)."""
+    w = [int(np.rint(np.float64(max(float(v), 0.0)) * 256.0)) for v in x]
+    W_ = sum(w)
+    assert sum(q) == c
+    if W_ == 0:
+        n = len(q)
+        assert q == [c // n + (1 if k < c % n else 0) for k in range(n)]
+        return
+    base = [(c * wi) // W_ for wi in w]
+    rem = [(c * wi) % W_ for wi in w]
+    plus = [qi - bi for qi, bi in zip(q, base)]
+    assert all(p in (0, 1) for p in plus)
+    # every +1 goes to a remainder at least as large as any copy without one
+    got = [k for k in range(len(q)) if plus[k]]
+    miss = [k for k in range(len(q)) if not plus[k]]
+    for a in got:
+        for b in miss:
+            assert (rem[a], -a) > (rem[b], -b)
+
+
+def run_lplb(counts_np, inst, ipr, iters=30):
+    R, E = counts_np.shape
+    lp = U.lplb_prepare(inst, R, E, ipr, DEV)
+    groups = copy_groups(inst, E)
+    n = sum(len(g[1]) for g in groups)
+    err = err_word()
+    x, m, q, st = U.lplb(to_dev(counts_np), lp, n, len(inst), iters=iters, err=err)
+    return host(x), float(host(m)[0]), host(q), host(st), int(host(err)[0]), groups
+
+
+def check_lplb(counts_np, inst, ipr, iters=30):
+    R, E = counts_np.shape
+    res = O.lplb(counts_np, inst, ipr)
+    x, m, q, st, err, groups = run_lplb(counts_np, inst, ipr, iters)
+    assert err == 0
+    m_star = res["m_star"]
+    assert m >= m_star * (1 - 1e-6) - 1e-3
+    assert m <= m_star * (1 + REL_TOL) + 1e-3, (m, m_star)
+    c = counts_np.sum(0)
+    k = 0
+    for e, insts in groups:
+        xs = x[k:k + len(insts)]
+        assert (xs >= 0).all()
+        assert abs(float(xs.sum()) - c[e]) <= 1e-5 * max(1.0, c[e]) + 1e-3
+        check_largest_remainder(xs, int(c[e]), [int(q[i]) for i in insts])
+        k += len(insts)
+    for e in range(E):                       # every expert's quotas sum to its load
+        assert q[np.asarray(inst) == e].sum() == c[e]
+    assert (q[np.asarray(inst) < 0] == 0).all()
+    # the integer split stays within one token per copy of the objective
+    ncopy = np.zeros(R, dtype=np.int64)
+    for _, insts in groups:
+        for i in insts:
+            ncopy[i // ipr] += 1
+    qload = np.array([q[r * ipr:(r + 1) * ipr].sum() for r in range(R)])
+    assert (qload <= m_star * (1 + REL_TOL) + ncopy + 1).all()
+    return res, x, m, q, st
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_lplb_random(seed):
+    rng = np.random.default_rng(900 + seed)
+    R = int(rng.choice([2, 3, 5, 8, 16, 31, 64]))
+    E_loc = int(rng.integers(1, 5))
+    E = R * E_loc
+    ipr = E_loc + 1
+    inst = np.full(R * ipr, -1, dtype=np.int32)
+    for r in range(R):
+        inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+    hot = rng.choice(E, size=int(rng.integers(0, R + 1)), replace=False)
+    free = list(rng.permutation(R))
+    for e in hot:
+        for r in free:
+            if r != e // E_loc:
+                inst[r * ipr + E_loc] = e
+                free.remove(r)
+                break
+    counts = rng.multinomial(int(rng.integers(1, 2_000_000)),
+                             rng.dirichlet(np.full(E, rng.choice([0.1, 0.3, 1.0]))), size=R)
+    say(f"case: lplb random seed={seed} R={R} E={E} replicas={int((inst[E_loc::ipr] >= 0).sum())}")
+    check_lplb(counts.astype(np.int32), inst, ipr)
+
+
+def test_lplb_special_cases():
+    say("case: lplb special cases")
+    # red0: no replicas -> M* = max fixed load, quotas = loads
+    R, E_loc = 6, 3
+    ipr = E_loc + 1
+    inst = np.full(R * ipr, -1, dtype=np.int32)
+    for r in range(R):
+        inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+    counts = np.random.default_rng(1).integers(0, 500, (R, R * E_loc)).astype(np.int32)
+    res, x, m, q, st = check_lplb(counts, inst, ipr)
+    assert m == counts.sum(0).reshape(R, E_loc).sum(1).max()
+    assert st[0] == 0 and st[2] == 0
+    # one expert over two otherwise empty ranks: M* = c / 2
+    counts = np.array([[60, 0], [41, 0]], dtype=np.int32)
+    check_lplb(counts, np.array([0, -1, 1, 0], dtype=np.int32), 2)
+    # hand example: M* = 60 with a unique split
+    counts = np.vstack([[90, 30, 60], np.zeros((2, 3))]).astype(np.int32)
+    res, x, m, q, st = check_lplb(counts, np.array([0, 2, 1, 0, 2, -1], dtype=np.int32), 2)
+    assert q.tolist() == [60, 0, 30, 30, 60, 0]
+    # a replicated expert with no load at all
+    counts = np.array([[0, 7], [0, 5]], dtype=np.int32)
+    check_lplb(counts, np.array([0, 1, 1, 0], dtype=np.int32), 2)
+    # all-zero layer
+    check_lplb(np.zeros((4, 8), dtype=np.int32),
+               np.array([0, 1, 5, 2, 3, -1, 4, 5, 0, 6, 7, 2], dtype=np.int32), 3)
+
+
+def test_lplb_layer_full_size():
+    """LPLB-shaped layer: R = 64, 256 experts + 32 static replicas, 16384 tokens per rank."""
+    w = W.LPLB_LAYER
+    say("case: lplb layer full size", w)
+    ids = W.routing(w)
+    inst = W.static_replica_placement(w)
+    ipr = w.E_loc + 1
+    ids_d = to_dev(ids)
+    err = err_word()
+    counts, bp = U.load_matrix(ids_d, w.E, err=err)
+    counts_o, bp_o = O.load_matrix(ids, w.E)
+    assert np.array_equal(host(counts), counts_o)
+    res, x, m, q, st = check_lplb(counts_o.astype(np.int32), inst, ipr)
+    say(f"lplb: m={m} m*={res['m_star']} iterations={st[2]}")
+    # reroute/assign on the oracle's quotas: bit-exact against the oracle
+    inst_d = to_dev(inst)
+    q_o = res["inst_quota"]
+    X_o, io_o, so_o = O.reroute(counts_o, inst, q_o, ipr)
+    di_o, dr_o = O.assign(ids, bp_o, X_o, inst, ipr, io_o, so_o)
+    xfer, ioff, di, dr = U.reroute_assign(counts, ids_d, bp, ipr, inst_d, to_dev(q_o), err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(xfer), X_o) and np.array_equal(host(ioff), io_o)
+    assert np.array_equal(host(di), di_o) and np.array_equal(host(dr), dr_o)
+    # reroute/assign on the kernel's own quotas: properties
+    xfer, ioff, di, dr = U.reroute_assign(counts, ids_d, bp, ipr, inst_d, to_dev(q), err=err)
+    assert host(err)[0] == 0
+    Xg = host(xfer)
+    check_reroute_properties(counts_o, inst, q, ipr, Xg)
+    drh = host(dr)
+    assert np.array_equal(np.sort(drh.reshape(-1)), np.arange(w.P))
+    # permute of the whole group (hidden 7168), sampled rows
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
+    x_act = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV, dtype=torch.bfloat16)
+    out = torch.empty(w.P, w.H, dtype=torch.bfloat16, device=DEV)
+    U.permute(x_act, dr, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.integers(0, w.P, 3000), [0, w.P - 1]]))
+    flat = drh.reshape(-1)
+    pos = np.empty(w.P, dtype=np.int64)
+    pos[flat] = np.arange(w.P)
+    tok = torch.from_numpy(pos[rows] // w.K).to(DEV)
+    exp = host(x_act.view(w.R * w.T, w.H).view(torch.int16)[tok])
+    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)])
+    assert np.array_equal(got, exp)
