@@ -1,20 +1,27 @@
 """Benchmark of the real-time expert load-balancing path on one MI355X.
 
-One step = one pass of the whole per-layer path over one batch of a Qwen3-235B-shaped
-MoE layer simulated as R = 32 virtual EP ranks on one GPU (128 experts, 8192 tokens
-per rank, top-8, hidden 4096 bf16, 1 redundant slot per rank, minimum quota 1024):
+Default (the contract line): one step = one pass of the whole per-layer path over one
+batch of a Qwen3-235B-shaped MoE layer simulated as R = 32 virtual EP ranks on one GPU
+(128 experts, 8192 tokens per rank, top-8, hidden 4096 bf16, 1 redundant slot per
+rank, minimum quota 1024):
 
     load matrix -> quota solve -> reroute + token assignment (all ranks)
     -> forward staging of every used redundant slot (3 x 4096 x 1536 bf16 each)
     -> permute of every rank's activations into the dispatch buffer
 
 value = tokens of the whole EP group per second (R * T / step time), inputs resident
-in HBM.  The JSON line also carries the permute kernel's roofline (algorithmic bytes
-per launch / its event-timed average duration), the per-rank share of a layer in us
-(plan + one rank's permute + its slot staging), and the CPU oracle's throughput on a
-bounded sample of the same workload.
+in HBM.  The line also carries the permute kernel's roofline (algorithmic bytes per
+launch / its event-timed average duration inside the timed region), the per-rank share
+of a layer in us (whole-group plan + one rank's assignment, permute and slot staging,
+replayed from a HIP graph so host launch overhead is not counted), and the CPU
+oracle's throughput on a bounded sample of the same workload.
+
+Other workloads (one JSON line each, not the contract line):
+  --workload tiny | dsv3_waterfill | lplb_layer | qwen3_235b_94layer_sweep
+--kernels prints a per-kernel timing table (graph-replayed) of every workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload NAME] [--kernels]
 """
 
 import argparse
@@ -30,72 +37,169 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "balance-plan+permute µs/layer and tokens/s; permute/stage HBM GB/s (% peak)"
+DEV = "cuda:0"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ----------------------------------------------------------------------------- helpers
+class Timer:
+    """Event pairs on one stream; mean duration in ms."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        self.k = 0
+
+    def start(self, stream):
+        self.ev[self.k][0].record(stream)
+
+    def stop(self, stream):
+        self.ev[self.k][1].record(stream)
+        self.k += 1
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[:self.k]]))
+
+    def all_ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev[:self.k]]
+
+
+def graph_us(torch, fn, reps=20, replays=5):
+    """Mean GPU time of fn() in us: fn is captured `reps` times into one HIP graph and
+    the graph is replayed; host launch overhead is not counted."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(s)                                    # warm (first-call setup outside the graph)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            fn(s)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    a.record(cur)
+    for _ in range(replays):
+        g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * replays)
+
+
 class Layer:
     """Preallocated device buffers of one layer (the library never allocates)."""
 
-    def __init__(self, U, W, torch, w, ids):
-        dev = "cuda:0"
-        self.U, self.w = U, w
-        R, T, K, E, S, H = w.R, w.T, w.K, w.E, w.S, w.H
-        i32 = dict(dtype=torch.int32, device=dev)
-        self.ids = torch.from_numpy(ids).to(dev)
+    def __init__(self, U, W, torch, w, ids, E=None, K=None, ipr=None, weights=True):
+        self.U, self.w, self.torch = U, w, torch
+        R, T, H = w.R, w.T, w.H
+        E = w.E if E is None else E
+        K = w.K if K is None else K
+        self.E, self.K = E, K
+        i32 = dict(dtype=torch.int32, device=DEV)
+        self.ids = torch.from_numpy(np.ascontiguousarray(ids)).to(DEV) if ids is not None else \
+            torch.empty(R, T, K, **i32)
         self.counts = torch.empty(R, E, **i32)
         self.bp = torch.empty(R, T, K, **i32)
-        self.lm_ws = torch.empty(max(U.load_matrix_workspace_size(R, T, K, E), 4), dtype=torch.uint8,
-                                 device=dev)
-        ipr = E // R + S
-        self.ipr = ipr
-        self.plan = {"slot_expert": torch.empty(R, S, **i32), "inst_expert": torch.empty(R * ipr, **i32),
-                     "inst_quota": torch.empty(R * ipr, **i32), "rank_load": torch.empty(R, **i32),
-                     "stats": torch.empty(4, **i32)}
-        self.xfer = torch.empty(R, R * ipr, **i32)
-        self.ioff = torch.empty(R * ipr + 1, **i32)
+        self.lm_ws = torch.empty(max(U.load_matrix_workspace_size(R, T, K, E), 4),
+                                 dtype=torch.uint8, device=DEV)
+        self.ipr = (E // R + w.S) if ipr is None else ipr
+        I = R * self.ipr
+        self.plan = {"slot_expert": torch.full((R, max(w.S, 1)), -1, **i32),
+                     "inst_expert": torch.empty(I, **i32), "inst_quota": torch.empty(I, **i32),
+                     "rank_load": torch.empty(R, **i32), "stats": torch.zeros(4, **i32)}
+        self.xfer = torch.empty(R, I, **i32)
+        self.ioff = torch.empty(I + 1, **i32)
         self.dinst = torch.empty(R, T, K, **i32)
         self.drow = torch.empty(R, T, K, **i32)
-        self.rr_ws = torch.empty(max(U.reroute_workspace_size(R, E, ipr), 4), dtype=torch.uint8,
-                                 device=dev)
-        self.err = torch.zeros(1, **i32)
-        gen = torch.Generator(device=dev).manual_seed(W.tensor_seed(w, 0, 0))
-        self.x = torch.randn(R, T, H, generator=gen, device=dev).to(torch.bfloat16)
-        self.out = torch.empty(w.P, H, dtype=torch.bfloat16, device=dev)
-        self.row_src = torch.empty(w.P, **i32)
-        gen = torch.Generator(device=dev).manual_seed(W.tensor_seed(w, 0, 1))
-        self.main_w = (torch.randn(E, w.expert_elems, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-        self.slot_w = torch.empty(R, S, w.expert_elems, dtype=torch.bfloat16, device=dev)
+        self.rr_ws = torch.empty(max(U.reroute_workspace_size(R, E, self.ipr), 4),
+                                 dtype=torch.uint8, device=DEV)
+        gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
+        self.x = torch.randn(R, T, H, generator=gen, device=DEV, dtype=torch.bfloat16)
+        self.P = R * T * K
+        self.out = torch.empty(self.P, H, dtype=torch.bfloat16, device=DEV)
+        self.row_src = torch.empty(self.P, **i32)
+        if weights and w.S > 0:
+            gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 1))
+            self.main_w = (torch.randn(w.E, w.expert_elems, generator=gen, device=DEV,
+                                       dtype=torch.bfloat16) * 0.02)
+            self.slot_w = torch.empty(R, w.S, w.expert_elems, dtype=torch.bfloat16, device=DEV)
 
-    def plan_step(self, stream):
-        U, w = self.U, self.w
-        U.load_matrix(self.ids, w.E, self.counts, self.bp, None, self.lm_ws, stream)
-        U.solve_quota(self.counts, w.S, w.q_min, out=self.plan, stream=stream)
-        U.reroute_assign(self.counts, self.ids, self.bp, self.ipr, self.plan["inst_expert"],
-                         self.plan["inst_quota"], 0, w.R, self.xfer, self.ioff, self.dinst, self.drow,
-                         None, self.rr_ws, stream)
+    # the steps of the path
+    def load(self, s):
+        self.U.load_matrix(self.ids, self.E, self.counts, self.bp, None, self.lm_ws, s)
 
-    def plan_step_rank(self, stream, r):
-        U, w = self.U, self.w
-        U.load_matrix(self.ids, w.E, self.counts, self.bp, None, self.lm_ws, stream)
-        U.solve_quota(self.counts, w.S, w.q_min, out=self.plan, stream=stream)
-        U.reroute_assign(self.counts, self.ids, self.bp, self.ipr, self.plan["inst_expert"],
-                         self.plan["inst_quota"], r, r + 1, self.xfer, self.ioff, self.dinst,
-                         self.drow, None, self.rr_ws, stream)
+    def solve(self, s):
+        self.U.solve_quota(self.counts, self.w.S, self.w.q_min, out=self.plan, stream=s)
 
-    def stage(self, stream, r_begin=0, r_end=None):
+    def reroute(self, s, r_begin=0, r_end=None):
+        self.U.reroute_assign(self.counts, self.ids, self.bp, self.ipr, self.plan["inst_expert"],
+                              self.plan["inst_quota"], r_begin, r_end, self.xfer, self.ioff,
+                              self.dinst, self.drow, None, self.rr_ws, s)
+
+    def stage(self, s, r_begin=0, r_end=None):
         w = self.w
         self.U.stage_replica_weights(self.U.STAGE_WEIGHTS, w.R, w.E, w.S, self.plan["slot_expert"],
                                      w.expert_elems, main_w=self.main_w, slot_w=self.slot_w,
-                                     r_begin=r_begin, r_end=r_end, stream=stream)
+                                     r_begin=r_begin, r_end=r_end, stream=s)
 
-    def permute(self, stream, r_begin=0, r_end=None):
-        self.U.permute(self.x, self.drow, self.out, self.row_src, r_begin, r_end, stream)
+    def permute(self, s, r_begin=0, r_end=None, row_src=True):
+        self.U.permute(self.x, self.drow, self.out, self.row_src if row_src else None,
+                       r_begin, r_end, s)
+
+    def plan_step(self, s, r_begin=0, r_end=None):
+        self.load(s)
+        self.solve(s)
+        self.reroute(s, r_begin, r_end)
 
 
-def cpu_baseline(w, ids, x_host, slot_expert, n_rank_sample=2):
+def permute_bytes(N, P, H):
+    """Algorithmic bytes of one whole-group permute: every source row read once, every
+    dispatch row written once, plus the 4-byte row_src entry of every row."""
+    return N * H * 2 + P * H * 2 + P * 4
+
+
+def roofline(bytes_, ms, kernel):
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": ms}
+
+
+def base_line(w, W, value, ms, args, dtype, extra_cfg=None):
+    cfg = {"workload": w.name, "R": w.R, "E": w.E, "S": w.S, "tokens_per_rank": w.T,
+           "top_k": w.K, "hidden": w.H, "q_min": w.q_min,
+           "zipf_s": round(W.zipf_exponent(w, 0), 4), "parallelism": f"ep{w.R} virtual ranks on 1 GPU"}
+    if extra_cfg:
+        cfg.update(extra_cfg)
+    return {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": cfg}
+
+
+def timed_steps(torch, args, step, stream, timers=()):
+    for _ in range(args.warmup):
+        step(stream, None)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(args.steps):
+        step(stream, timers)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / args.steps
+
+
+# ----------------------------------------------------------------------------- CPU leg
+def cpu_baseline(w, ids, x_host, n_rank_sample=2):
     """The oracle as it stands, single process, on a bounded sample of the same layer:
     the whole plan (load matrix, quota solve, reroute, assignment) plus the permute of
     n_rank_sample ranks and the staging of one used slot, scaled to the whole layer."""
@@ -125,8 +229,292 @@ def cpu_baseline(w, ids, x_host, slot_expert, n_rank_sample=2):
         "sample": (f"whole-layer plan ({t_plan:.2f} s) + permute of {n_rank_sample} of {w.R} ranks "
                    f"scaled x{w.R // n_rank_sample} ({t_perm:.2f} s) + staging of 1 of {len(used)} "
                    f"used slots scaled ({t_stage:.2f} s); Python+numpy, one thread"),
-        "seconds_per_layer": total,
     }
+
+
+# ----------------------------------------------------------------------------- workloads
+def bench_layer(args, torch, U, W, w, with_cpu):
+    """UltraEP layer: plan + staging + whole-group permute."""
+    log(f"workload {w.name}: R={w.R} E={w.E} S={w.S} T={w.T} K={w.K} H={w.H}")
+    ids = W.routing(w)
+    L = Layer(U, W, torch, w, ids)
+    stream = torch.cuda.current_stream()
+    tq, ts, tp = (Timer(torch, args.steps) for _ in range(3))
+
+    def step(s, timers):
+        if timers:
+            timers[0].start(s)
+        L.plan_step(s)
+        if timers:
+            timers[0].stop(s)
+            timers[1].start(s)
+        L.stage(s)
+        if timers:
+            timers[1].stop(s)
+            timers[2].start(s)
+        L.permute(s)
+        if timers:
+            timers[2].stop(s)
+
+    ms = timed_steps(torch, args, step, stream, (tq, ts, tp))
+    stats = L.plan["stats"].cpu().numpy()
+    n_used = int(stats[0])
+    pb = permute_bytes(w.N, w.P, w.H)
+    perm_ms, stage_ms = tp.mean_ms(), ts.mean_ms()
+    stage_bytes = 2 * n_used * w.expert_elems * 2
+    # per-rank share (rank 0): whole-group plan, its own tokens and slot
+    r = 0
+
+    def rank_share(s):
+        L.plan_step(s, r, r + 1)
+        L.stage(s, r, r + 1)
+        L.permute(s, r, r + 1, row_src=False)
+
+    rank_us = graph_us(torch, rank_share)
+    plan_us = graph_us(torch, lambda s: L.plan_step(s))
+    perm_rank_us = graph_us(torch, lambda s: L.permute(s, r, r + 1, row_src=False))
+    L.plan_step(stream)
+    torch.cuda.synchronize()
+    rl = L.plan["rank_load"].cpu().numpy()
+    c = L.counts.cpu().numpy().sum(0)
+    before = c.reshape(w.R, w.E_loc).sum(1)
+    out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
+                    {"ffn": list(w.ffn_shape)})
+    out["roofline"] = roofline(pb, perm_ms, "permute_kernel<true>")
+    cpu = None
+    if with_cpu:
+        log("cpu baseline (oracle) ...")
+        x_host = L.x.view(torch.int16).cpu().numpy().view(np.uint16)
+        cpu = cpu_baseline(w, ids, x_host)
+    out["cpu_baseline"] = cpu
+    rank_bytes = permute_bytes(w.T, w.T * w.K, w.H) - w.T * w.K * 4
+    out["extra"] = {
+        "us_per_layer_rank_share": rank_us,
+        "plan_us": plan_us,
+        "permute_rank_us": perm_rank_us,
+        "permute_rank_gbs": rank_bytes / (perm_rank_us * 1e-6) / 1e9,
+        "stage_ms": stage_ms,
+        "stage_gbs": stage_bytes / (stage_ms * 1e-3) / 1e9 if n_used else 0.0,
+        "replicas": n_used,
+        "solver_steps": int(stats[1]),
+        "imbalance_before": float(before.max() / before.mean()),
+        "imbalance_after": float(rl.max() / rl.mean()),
+    }
+    out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
+    return out
+
+
+def waterfill_inst(w):
+    ipr = w.E_loc + 1
+    inst = np.full(w.R * ipr, -1, dtype=np.int32)
+    for r in range(w.R):
+        inst[r * ipr:r * ipr + w.E_loc] = np.arange(r * w.E_loc, (r + 1) * w.E_loc)
+        inst[r * ipr + w.E_loc] = w.E + r
+    return inst, ipr
+
+
+def bench_waterfill(args, torch, U, W, w):
+    """DeepSeek-V3 layer with Waterfill: routed load matrix -> Waterfill -> fused
+    (K+1)-column layout -> load matrix -> identity quotas -> reroute/assign -> permute."""
+    log(f"workload {w.name}: R={w.R} E={w.E} T={w.T} K={w.K} H={w.H}")
+    ids = W.routing(w)
+    inst, ipr = waterfill_inst(w)
+    E2, K2 = w.E + w.R, w.K + 1
+    L = Layer(U, W, torch, w, None, E=E2, K=K2, ipr=ipr, weights=False)
+    ids_d = torch.from_numpy(ids).to(DEV)
+    counts1 = torch.empty(w.R, w.E, dtype=torch.int32, device=DEV)
+    bp1 = torch.empty(w.R, w.T, w.K, dtype=torch.int32, device=DEV)
+    ws1 = torch.empty(max(U.load_matrix_workspace_size(w.R, w.T, w.K, w.E), 4), dtype=torch.uint8,
+                      device=DEV)
+    B = torch.full((w.R,), w.T, dtype=torch.int32, device=DEV)
+    sh = torch.empty(w.R, w.T, dtype=torch.int32, device=DEV)
+    wl = torch.empty(1, dtype=torch.int32, device=DEV)
+    sl = torch.empty(w.R, dtype=torch.int32, device=DEV)
+    rl = torch.empty(w.R, dtype=torch.int32, device=DEV)
+    L.plan["inst_expert"].copy_(torch.from_numpy(inst))
+    seed = W.waterfill_seed(w)
+
+    def wf_plan(s, r_begin=0, r_end=None):
+        U.load_matrix(ids_d, w.E, counts1, bp1, None, ws1, s)
+        U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl, L.ids, stream=s)
+        L.load(s)
+        U.identity_quota(L.counts, L.plan["inst_expert"], L.plan["inst_quota"], stream=s)
+        L.reroute(s, r_begin, r_end)
+
+    tp = Timer(torch, args.steps)
+
+    def step(s, timers):
+        wf_plan(s)
+        if timers:
+            timers[0].start(s)
+        L.permute(s)
+        if timers:
+            timers[0].stop(s)
+
+    ms = timed_steps(torch, args, step, torch.cuda.current_stream(), (tp,))
+    N = w.N
+    pb = permute_bytes(N, L.P, w.H)
+    out = base_line(w, W, N / (ms * 1e-3), ms, args, "int32",
+                    {"top_k_fused": K2, "shared_slot_per_rank": 1})
+    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true>")
+    out["cpu_baseline"] = None
+    r = 0
+    plan_us = graph_us(torch, lambda s: wf_plan(s))
+    wf_us = graph_us(torch, lambda s: U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl,
+                                                  L.ids, stream=s))
+    rank_us = graph_us(torch, lambda s: (wf_plan(s, r, r + 1),
+                                         L.permute(s, r, r + 1, row_src=False)))
+    torch.cuda.synchronize()
+    L_r = rl.cpu().numpy().astype(np.float64)
+    shared = np.bincount(sh.cpu().numpy().reshape(-1), minlength=w.R)
+    local = np.full(w.R, w.T, dtype=np.float64)
+    out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "waterfill_us": wf_us,
+                    "waterline": int(wl.item()),
+                    "imbalance_shared_local": float((L_r + local).max() / (L_r + local).mean()),
+                    "imbalance_shared_waterfill": float((L_r + shared).max() / (L_r + shared).mean())}
+    return out
+
+
+def bench_lplb(args, torch, U, W, w):
+    """LPLB layer: load matrix -> LP split -> reroute/assign on its quotas -> permute."""
+    log(f"workload {w.name}: R={w.R} E={w.E} T={w.T} K={w.K} H={w.H} replicas={w.n_static_replicas}")
+    ids = W.routing(w)
+    inst = W.static_replica_placement(w)
+    ipr = w.E_loc + 1
+    L = Layer(U, W, torch, w, ids, ipr=ipr, weights=False)
+    L.plan["inst_expert"].copy_(torch.from_numpy(inst))
+    lp = U.lplb_prepare(inst, w.R, w.E, ipr, DEV)
+    n_copies = int(sum((inst == e).sum() for e in range(w.E) if (inst == e).sum() >= 2))
+    x = torch.empty(max(n_copies, 1), dtype=torch.float32, device=DEV)
+    m = torch.empty(1, dtype=torch.float32, device=DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+
+    def lp_plan(s, r_begin=0, r_end=None):
+        L.load(s)
+        U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x, m, L.plan["inst_quota"], st,
+               None, s)
+        L.reroute(s, r_begin, r_end)
+
+    tp = Timer(torch, args.steps)
+
+    def step(s, timers):
+        lp_plan(s)
+        if timers:
+            timers[0].start(s)
+        L.permute(s)
+        if timers:
+            timers[0].stop(s)
+
+    ms = timed_steps(torch, args, step, torch.cuda.current_stream(), (tp,))
+    pb = permute_bytes(w.N, w.P, w.H)
+    out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
+                    {"static_replicas": w.n_static_replicas, "lp_iters": args.lp_iters})
+    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true>")
+    out["cpu_baseline"] = None
+    lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
+                                             m, L.plan["inst_quota"], st, None, s), reps=5)
+    plan_us = graph_us(torch, lambda s: lp_plan(s), reps=5)
+    r = 0
+    rank_us = graph_us(torch, lambda s: (lp_plan(s, r, r + 1),
+                                         L.permute(s, r, r + 1, row_src=False)), reps=5)
+    torch.cuda.synchronize()
+    c = L.counts.cpu().numpy().sum(0)
+    # uniform split of every replicated expert (the static default the LP replaces)
+    uni = np.zeros(w.R)
+    for e in range(w.E):
+        where = np.nonzero(inst == e)[0]
+        for i in where:
+            uni[i // ipr] += c[e] / len(where)
+    out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "lplb_us": lp_us,
+                    "lp_iterations_run": int(st[2].item()), "m": float(m.item()),
+                    "max_load_uniform_split": float(uni.max()), "mean_load": float(c.sum() / w.R)}
+    return out
+
+
+def bench_sweep(args, torch, U, W, w):
+    """94 Qwen3-235B-shaped layers: forward (plan, staging into the one shared slot set,
+    whole-group permute) in layer order, then backward in reverse order replaying the
+    cached plans (weights staged again, replica gradients reduced into the mains)."""
+    from concurrent.futures import ProcessPoolExecutor
+    log(f"workload {w.name}: {w.layers} layers, R={w.R} E={w.E} T={w.T} K={w.K} H={w.H}")
+    with ProcessPoolExecutor(max_workers=8) as ex:
+        routings = list(ex.map(W.routing, [w] * w.layers, range(w.layers)))
+    layer0 = W.scaled(w, layers=1)
+    L = Layer(U, W, torch, layer0, routings[0])
+    pool = 4        # distinct main weight / gradient sets, cycled over the layers
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 2))
+    mains = [L.main_w] + [(torch.randn(w.E, w.expert_elems, generator=gen, device=DEV,
+                                       dtype=torch.bfloat16) * 0.02) for _ in range(pool - 1)]
+    mgrads = [torch.zeros(w.E, w.expert_elems, dtype=torch.float32, device=DEV) for _ in range(pool)]
+    slot_grad = torch.zeros(w.R, w.S, w.expert_elems, dtype=torch.float32, device=DEV)
+    ids_d = [torch.from_numpy(r).to(DEV) for r in routings]
+    slots = [torch.empty(w.R, w.S, dtype=torch.int32, device=DEV) for _ in range(w.layers)]
+    s = torch.cuda.current_stream()
+    fwd_t = Timer(torch, w.layers * (args.steps + args.warmup))
+    bwd_t = Timer(torch, w.layers * (args.steps + args.warmup))
+
+    def sweep(st, timers):
+        for l in range(w.layers):
+            L.ids = ids_d[l]
+            L.main_w = mains[l % pool]
+            fwd_t.start(st)
+            L.plan_step(st)
+            L.stage(st)
+            L.permute(st)
+            fwd_t.stop(st)
+            slots[l].copy_(L.plan["slot_expert"][:, :w.S])
+        for l in reversed(range(w.layers)):
+            bwd_t.start(st)
+            U.stage_replica_weights(U.STAGE_WEIGHTS, w.R, w.E, w.S, slots[l], w.expert_elems,
+                                    main_w=mains[l % pool], slot_w=L.slot_w, stream=st)
+            U.stage_replica_weights(U.STAGE_GRAD_REDUCE, w.R, w.E, w.S, slots[l], w.expert_elems,
+                                    main_grad=mgrads[l % pool], slot_grad=slot_grad, stream=st)
+            bwd_t.stop(st)
+
+    ms = timed_steps(torch, args, sweep, s)
+    f = np.array(fwd_t.all_ms()[w.layers * args.warmup:]) * 1e3
+    b = np.array(bwd_t.all_ms()[w.layers * args.warmup:]) * 1e3
+    out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
+                    {"layers": w.layers, "weight_sets_cycled": pool, "zipf_s": "0.8+0.6U per layer"})
+    out["roofline"] = None
+    out["cpu_baseline"] = None
+    out["extra"] = {"fwd_us_sum": float(f.sum() / args.steps), "fwd_us_p50": float(np.percentile(f, 50)),
+                    "fwd_us_p99": float(np.percentile(f, 99)),
+                    "bwd_us_sum": float(b.sum() / args.steps), "bwd_us_p50": float(np.percentile(b, 50)),
+                    "bwd_us_p99": float(np.percentile(b, 99)),
+                    "note": "per-layer times include the whole-group permute of 32 virtual ranks"}
+    return out
+
+
+def kernel_report(args, torch, U, W):
+    """Graph-replayed GPU time of every kernel of the path, per workload."""
+    rep = {}
+    for w in (W.TINY, W.QWEN_LAYER):
+        ids = W.routing(w)
+        L = Layer(U, W, torch, w, ids)
+        L.plan_step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        n_used = int(L.plan["stats"][0].item())
+        d = {"load_matrix": graph_us(torch, L.load), "solve_quota": graph_us(torch, L.solve),
+             "reroute_assign": graph_us(torch, L.reroute),
+             "permute_whole": graph_us(torch, lambda s: L.permute(s), reps=5),
+             "permute_rank0": graph_us(torch, lambda s: L.permute(s, 0, 1, row_src=False)),
+             "stage_whole": graph_us(torch, lambda s: L.stage(s), reps=5),
+             "stage_rank0": graph_us(torch, lambda s: L.stage(s, 0, 1)), "replicas": n_used}
+        pb = permute_bytes(w.N, w.P, w.H)
+        d["permute_whole_gbs"] = pb / (d["permute_whole"] * 1e-6) / 1e9
+        d["stage_whole_gbs"] = 4 * n_used * w.expert_elems / (d["stage_whole"] * 1e-6) / 1e9
+        rep[w.name] = d
+        del L
+        torch.cuda.empty_cache()
+    # plain device copy of 4 GiB (the achievable-bandwidth reference)
+    a = torch.empty(1 << 31, dtype=torch.int16, device=DEV)
+    b = torch.empty_like(a)
+    cu = graph_us(torch, lambda s: b.copy_(a), reps=5)
+    rep["device_copy_4GiB"] = {"us": cu, "gbs": 2 * a.numel() * 2 / (cu * 1e-6) / 1e9}
+    del a, b
+    torch.cuda.empty_cache()
+    print(json.dumps(rep), flush=True)
 
 
 def main():
@@ -135,6 +523,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="qwen3_235b_layer")
+    ap.add_argument("--lp-iters", type=int, default=30)
+    ap.add_argument("--kernels", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the EP group is simulated as virtual ranks on a "
@@ -146,119 +537,18 @@ def main():
     from moe_expert_load_amd import uep as U
     from moe_expert_load_amd import workload as W
 
-    w = W.QWEN_LAYER
-    log(f"workload {w.name}: R={w.R} E={w.E} S={w.S} T={w.T} K={w.K} H={w.H}")
-    ids = W.routing(w)
-    L = Layer(U, W, torch, w, ids)
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-
-    # warmup
-    for _ in range(args.warmup):
-        L.plan_step(stream)
-        L.stage(stream)
-        L.permute(stream)
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps; per-kernel events around permute and staging
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    p_ev = [(ev(), ev()) for _ in range(args.steps)]
-    s_ev = [(ev(), ev()) for _ in range(args.steps)]
-    q_ev = [(ev(), ev()) for _ in range(args.steps)]
-    t_start, t_end = ev(), ev()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for k in range(args.steps):
-        q_ev[k][0].record(stream)
-        L.plan_step(stream)
-        q_ev[k][1].record(stream)
-        s_ev[k][0].record(stream)
-        L.stage(stream)
-        s_ev[k][1].record(stream)
-        p_ev[k][0].record(stream)
-        L.permute(stream)
-        p_ev[k][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    perm_ms = float(np.mean([a.elapsed_time(b) for a, b in p_ev]))
-    stage_ms = float(np.mean([a.elapsed_time(b) for a, b in s_ev]))
-    plan_ms = float(np.mean([a.elapsed_time(b) for a, b in q_ev]))
-    stats = L.plan["stats"].cpu().numpy()
-    n_used = int(stats[0])
-    perm_bytes = w.N * w.H * 2 + w.P * w.H * 2 + w.P * 4
-    stage_bytes = 2 * n_used * w.expert_elems * 2
-    perm_gbs = perm_bytes / (perm_ms * 1e-3) / 1e9
-    stage_gbs = stage_bytes / (stage_ms * 1e-3) / 1e9 if n_used else 0.0
-
-    # per-rank share: plan of the whole group + one rank's assignment, permute and slot
-    r = 0
-    n_rep = 50
-    a, b = ev(), ev()
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(n_rep):
-        L.plan_step_rank(stream, r)
-        L.stage(stream, r, r + 1)
-        L.permute(stream, r, r + 1)
-    b.record(stream)
-    torch.cuda.synchronize()
-    rank_us = a.elapsed_time(b) / n_rep * 1e3
-    a2, b2 = ev(), ev()
-    a2.record(stream)
-    for _ in range(n_rep):
-        L.plan_step(stream)
-    b2.record(stream)
-    torch.cuda.synchronize()
-    plan_us = a2.elapsed_time(b2) / n_rep * 1e3
-    rl = L.plan["rank_load"].cpu().numpy()
-    c = L.counts.cpu().numpy().sum(0)
-    before = c.reshape(w.R, w.E_loc).sum(1)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        x_host = L.x.view(torch.int16).cpu().numpy().view(np.uint16)
-        cpu = cpu_baseline(w, ids, x_host, L.plan["slot_expert"].cpu().numpy())
-        cpu.pop("seconds_per_layer")
-
-    out = {
-        "metric": METRIC,
-        "value": w.N / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "R": w.R, "E": w.E, "S": w.S, "tokens_per_rank": w.T,
-                   "top_k": w.K, "hidden": w.H, "q_min": w.q_min, "ffn": list(w.ffn_shape),
-                   "zipf_s": round(W.zipf_exponent(w, 0), 4), "parallelism": "ep32 virtual ranks on 1 GPU"},
-        "roofline": {"bound": "hbm", "kernel": "permute_kernel", "achieved": perm_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": perm_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": perm_bytes,
-                     "avg_launch_ms": perm_ms},
-        "cpu_baseline": cpu,
-        "extra": {
-            "us_per_layer_rank_share": rank_us,
-            "plan_us": plan_us,
-            "plan_ms_in_step": plan_ms,
-            "stage_ms": stage_ms,
-            "stage_gbs": stage_gbs,
-            "stage_frac": stage_gbs / HBM_PEAK_GBS,
-            "replicas": n_used,
-            "solver_steps": int(stats[1]),
-            "imbalance_before": float(before.max() / before.mean()),
-            "imbalance_after": float(rl.max() / rl.mean()),
-            "wall_s_timed": wall,
-        },
-    }
+    if args.kernels:
+        kernel_report(args, torch, U, W)
+        return
+    w = W.ALL[args.workload]
+    if w.name in ("qwen3_235b_layer", "tiny"):
+        out = bench_layer(args, torch, U, W, w, with_cpu=not args.no_cpu_baseline)
+    elif w.name == "dsv3_waterfill":
+        out = bench_waterfill(args, torch, U, W, w)
+    elif w.name == "lplb_layer":
+        out = bench_lplb(args, torch, U, W, w)
+    else:
+        out = bench_sweep(args, torch, U, W, w)
     print(json.dumps(out), flush=True)
 
 

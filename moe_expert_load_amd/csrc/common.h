@@ -65,6 +65,18 @@ __device__ __forceinline__ void wave_argmin(int& v, int& idx) {
   }
 }
 
+// Wave-wide min / max of an int (device-library DPP reductions), result in every lane.
+extern "C" __device__ int __ockl_wfred_max_i32(int);
+extern "C" __device__ int __ockl_wfred_min_i32(int);
+__device__ __forceinline__ int wave_max(int v) { return __ockl_wfred_max_i32(v); }
+__device__ __forceinline__ int wave_min(int v) { return __ockl_wfred_min_i32(v); }
+
+// Lowest lane whose predicate holds (-1 if none).
+__device__ __forceinline__ int first_lane(bool p) {
+  const uint64_t b = __ballot(p);
+  return b ? __ffsll((unsigned long long)b) - 1 : -1;
+}
+
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {
   if (err) atomicOr(err, bits);
 }

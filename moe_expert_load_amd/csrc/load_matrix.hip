@@ -24,6 +24,7 @@ constexpr int kLmItems = 16;                          // pairs per lane
 constexpr int kLmPairs = kLmThreads * kLmItems;       // 4096 pairs per chunk
 constexpr int kLmWaves = kLmThreads / kWave;
 constexpr int kLmMaxE = 4096;
+constexpr int kLmFastK = 16;                         // register path of lm_fix
 
 struct LmGeom {
   int R, T, K, E, tok_per_chunk, n_chunks, id_bits;
@@ -123,11 +124,28 @@ __global__ __launch_bounds__(kLmThreads) void lm_fix(const int32_t* __restrict__
   int dup = 0;
   for (int t = t0 + threadIdx.x; t < t1; t += kLmThreads) {
     const int64_t base = rank_base + (int64_t)t * g.K;
-    for (int k = 0; k < g.K; ++k) {
-      const int e = ids[base + k];
-      if (e < 0 || e >= g.E) continue;
-      for (int k2 = 0; k2 < k; ++k2) dup |= (ids[base + k2] == e);
-      bucket_pos[base + k] += pre[e];
+    if (g.K <= kLmFastK) {
+      // the token's ids and provisional positions in registers, all loads issued first
+      int e[kLmFastK], b[kLmFastK];
+#pragma unroll
+      for (int k = 0; k < kLmFastK; ++k)
+        if (k < g.K) { e[k] = ids[base + k]; b[k] = bucket_pos[base + k]; }
+#pragma unroll
+      for (int k = 0; k < kLmFastK; ++k) {
+        if (k >= g.K) break;
+        const bool valid = e[k] >= 0 && e[k] < g.E;
+#pragma unroll
+        for (int k2 = 0; k2 < kLmFastK; ++k2)
+          if (k2 < k) dup |= valid && e[k2] == e[k];
+        if (valid) bucket_pos[base + k] = b[k] + pre[e[k]];
+      }
+    } else {
+      for (int k = 0; k < g.K; ++k) {
+        const int e = ids[base + k];
+        if (e < 0 || e >= g.E) continue;
+        for (int k2 = 0; k2 < k; ++k2) dup |= (ids[base + k2] == e);
+        bucket_pos[base + k] += pre[e];
+      }
     }
   }
   if (dup) set_err(err, UEP_ERR_DUP_ID);

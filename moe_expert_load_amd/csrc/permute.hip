@@ -16,6 +16,7 @@ constexpr int kPmThreads = 256;
 constexpr int kPmTokPerBlock = kPmThreads / kWave;
 constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
 
+template <bool kRowSrc>
 __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ dest_row,
                                                              u32x4* __restrict__ out,
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
   const int64_t g = g0 + (int64_t)blockIdx.x * kPmTokPerBlock + threadIdx.x / kWave;
   if (g >= g1) return;
   const int d_mine = lane < K ? dest_row[g * K + lane] : -1;
-  if (row_src && lane < K && d_mine >= 0) row_src[d_mine] = (int32_t)(g * K + lane);
+  if (kRowSrc && lane < K && d_mine >= 0) row_src[d_mine] = (int32_t)(g * K + lane);
   const u32x4* src = x + g * nvec;
   for (int v0 = 0; v0 < nvec; v0 += kVec * kWave) {
     u32x4 buf[kVec];
@@ -64,9 +65,14 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) % 16 != 0)
     return UEP_EGEOM;
   const int64_t blocks = (g1 - g0 + kPmTokPerBlock - 1) / kPmTokPerBlock;
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)blocks), dim3(kPmThreads), 0,
-                     uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
-                     reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
+  if (row_src)
+    hipLaunchKernelGGL(permute_kernel<true>, dim3((unsigned)blocks), dim3(kPmThreads), 0,
+                       uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
+                       reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
+  else
+    hipLaunchKernelGGL(permute_kernel<false>, dim3((unsigned)blocks), dim3(kPmThreads), 0,
+                       uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
+                       reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }
