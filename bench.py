@@ -280,7 +280,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     before = c.reshape(w.R, w.E_loc).sum(1)
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"ffn": list(w.ffn_shape)})
-    out["roofline"] = roofline(pb, perm_ms, "permute_kernel<true>")
+    out["roofline"] = roofline(pb, perm_ms, "permute_kernel<true, false>")
     cpu = None
     if with_cpu:
         log("cpu baseline (oracle) ...")
@@ -356,7 +356,7 @@ def bench_waterfill(args, torch, U, W, w):
     pb = permute_bytes(N, L.P, w.H)
     out = base_line(w, W, N / (ms * 1e-3), ms, args, "int32",
                     {"top_k_fused": K2, "shared_slot_per_rank": 1})
-    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true>")
+    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true, true>")
     out["cpu_baseline"] = None
     r = 0
     plan_us = graph_us(torch, lambda s: wf_plan(s))
@@ -409,7 +409,7 @@ def bench_lplb(args, torch, U, W, w):
     pb = permute_bytes(w.N, w.P, w.H)
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"static_replicas": w.n_static_replicas, "lp_iters": args.lp_iters})
-    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true>")
+    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true, true>")
     out["cpu_baseline"] = None
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)

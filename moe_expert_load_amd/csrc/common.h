@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/uep.h"
+#include "uep.h"
 
 namespace uep {
 
@@ -75,6 +75,18 @@ __device__ __forceinline__ int wave_min(int v) { return __ockl_wfred_min_i32(v);
 __device__ __forceinline__ int first_lane(bool p) {
   const uint64_t b = __ballot(p);
   return b ? __ffsll((unsigned long long)b) - 1 : -1;
+}
+
+// sum_r counts[r][e] with 8 independent loads in flight
+__device__ __forceinline__ int column_sum(const int32_t* __restrict__ counts, int R, int E, int e) {
+  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int r = 0;
+  for (; r + 8 <= R; r += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += counts[(int64_t)(r + u) * E + e];
+  }
+  for (; r < R; ++r) acc[0] += counts[(int64_t)r * E + e];
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {

@@ -45,24 +45,31 @@ constexpr int kLpMaxNV = kLpMaxN + kLpMaxR + 2;
 constexpr int kLpMaxRows = kLpMaxR + kLpMaxG;
 
 // device structure (int32 words):
-// [0..7] magic, R, E, ipr, I, G, n, 0
+// [0..7] magic, R, E, ipr, I, G, n, n_ent
 // grp_expert[G] | grp_start[G+1] | copy_inst[n] | copy_rank[n] | copy_group[n] |
-// rank_start[R+1] | rank_copy[n] | exp_inst[E] | inst_expert[I] | inst_copy[I]
+// rank_start[R+1] | rank_copy[n] | exp_inst[E] | inst_expert[I] | inst_copy[I] |
+// ent_rr[n_ent] | ent_start[n_ent+1] | ent_p[n_pair] | ent_q[n_pair]
+// ent_*: the off-diagonal entries (r > r') of the rank matrix that copies of one
+// group touch: entry e = (ent_rr[e] / 64, ent_rr[e] % 64) sums the pairs
+// (ent_p[k] on r, ent_q[k] on r') for k in [ent_start[e], ent_start[e+1]).
 // exp_inst[e]: instance of a single-copy expert, -2 - g for replicated group g, -1 none
 // inst_copy[i]: copy index of instance i, or -1
 struct LpView {
-  int R, E, ipr, I, G, n;
+  int R, E, ipr, I, G, n, n_ent;
   const int32_t *grp_expert, *grp_start, *copy_inst, *copy_rank, *copy_group;
   const int32_t *rank_start, *rank_copy, *exp_inst, *inst_expert, *inst_copy;
+  const int32_t *ent_rr, *ent_start, *ent_p, *ent_q;
 };
 
-__host__ __device__ inline size_t lp_words(int R, int E, int I, int G, int n) {
-  return 8 + (size_t)G + (G + 1) + 3 * (size_t)n + (R + 1) + n + E + 2 * (size_t)I;
+__host__ __device__ inline size_t lp_words(int R, int E, int I, int G, int n, int n_ent,
+                                           int n_pair) {
+  return 8 + (size_t)G + (G + 1) + 3 * (size_t)n + (R + 1) + n + E + 2 * (size_t)I +
+         (size_t)n_ent + (n_ent + 1) + 2 * (size_t)n_pair;
 }
 
 __device__ inline LpView lp_view(const int32_t* w) {
   LpView v;
-  v.R = w[1]; v.E = w[2]; v.ipr = w[3]; v.I = w[4]; v.G = w[5]; v.n = w[6];
+  v.R = w[1]; v.E = w[2]; v.ipr = w[3]; v.I = w[4]; v.G = w[5]; v.n = w[6]; v.n_ent = w[7];
   const int32_t* p = w + 8;
   v.grp_expert = p; p += v.G;
   v.grp_start = p; p += v.G + 1;
@@ -73,8 +80,20 @@ __device__ inline LpView lp_view(const int32_t* w) {
   v.rank_copy = p; p += v.n;
   v.exp_inst = p; p += v.E;
   v.inst_expert = p; p += v.I;
-  v.inst_copy = p;
+  v.inst_copy = p; p += v.I;
+  v.ent_rr = p; p += v.n_ent;
+  v.ent_start = p; p += v.n_ent + 1;
+  const int n_pair = v.ent_start[v.n_ent];
+  v.ent_p = p; p += n_pair;
+  v.ent_q = p;
   return v;
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 struct LpShared {
@@ -90,14 +109,15 @@ struct LpShared {
   // normal equations (fp64)
   double d[kLpMaxNV], beta[kLpMaxG], t64[kLpMaxRows], u64[kLpMaxR];
   double P[kLpMaxR][kLpMaxR + 1];
-  double Ldiag[kLpMaxR], d0[kLpMaxR];
+  double Linv[kLpMaxR], d0[kLpMaxR];
+  double colbuf[2][kLpMaxR];
   // reductions
   double red[kLpThreads / kWave];
   float redf[kLpThreads / kWave];
   int32_t Fi[kLpMaxR], hc[kLpMaxG];       // fixed load per rank, count per group
 };
 
-__device__ inline double blk_sum(double x, LpShared& S) {
+__device__ __forceinline__ double blk_sum(double x, LpShared& S) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
   const int w = threadIdx.x / kWave;
@@ -110,7 +130,7 @@ __device__ inline double blk_sum(double x, LpShared& S) {
   return t;
 }
 
-__device__ inline float blk_min(float x, LpShared& S) {
+__device__ __forceinline__ float blk_min(float x, LpShared& S) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, kWave));
   const int w = threadIdx.x / kWave;
@@ -124,7 +144,7 @@ __device__ inline float blk_min(float x, LpShared& S) {
 }
 
 // out[R+G] = A * vec
-__device__ inline void lp_Av(const float* vec, float* out, int n, int R, int G, LpShared& S) {
+__device__ __forceinline__ void lp_Av(const float* vec, float* out, int n, int R, int G, LpShared& S) {
   const float Ma = vec[n + R] + vec[n + R + 1];
   for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
     float acc;
@@ -141,7 +161,7 @@ __device__ inline void lp_Av(const float* vec, float* out, int n, int R, int G, 
 }
 
 // out[nv] = A^T * y ; needs the sum of rank duals
-__device__ inline void lp_ATy(const float* yv, float* out, int n, int R, int G, LpShared& S) {
+__device__ __forceinline__ void lp_ATy(const float* yv, float* out, int n, int R, int G, LpShared& S) {
   float part = 0.0f;
   for (int r = threadIdx.x; r < R; r += kLpThreads) part += yv[r];
   const float ys = (float)blk_sum((double)part, S);
@@ -159,7 +179,7 @@ __device__ inline float lp_cost(int i, int n, int R) {
 }
 
 // largest step in [0, 1] keeping u + a du >= 0
-__device__ inline float lp_step(const float* u, const float* du, int nv, LpShared& S) {
+__device__ __forceinline__ float lp_step(const float* u, const float* du, int nv, LpShared& S) {
   float a = 1.0f;
   for (int i = threadIdx.x; i < nv; i += kLpThreads)
     if (du[i] < 0.0f) a = fminf(a, -u[i] / du[i]);
@@ -167,7 +187,7 @@ __device__ inline float lp_step(const float* u, const float* du, int nv, LpShare
 }
 
 // dy = (A D A^T)^{-1} rhs with the factored rank matrix
-__device__ void lp_solve(int n, int R, int G, LpShared& S) {
+__device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
   for (int g = threadIdx.x; g < G; g += kLpThreads) S.t64[g] = (double)S.rhs[R + g] / S.beta[g];
   __syncthreads();
   for (int r = threadIdx.x; r < R; r += kLpThreads) {
@@ -181,16 +201,27 @@ __device__ void lp_solve(int n, int R, int G, LpShared& S) {
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
-    double b = l < R ? S.u64[l] : 0.0;
-    for (int j = 0; j < R; ++j) {          // L y = r1
-      const double yj = __shfl(b, j, kWave) / S.Ldiag[j];
-      if (l > j && l < R) b -= S.P[l][j] * yj;
-      if (l == j) b = yj;
+    double b = l < R ? S.u64[l] : 0.0;       // padded rows solve to 0
+    // L = U D^(1/2) with U unit lower triangular: U z = r1, w = D^-1 z, U^T u = w,
+    // so every substitution step is one broadcast and one FMA
+    const double linv_l = S.Linv[l];
+    // Entries outside the triangle are zero, so those lanes' FMAs leave b unchanged:
+    // no branches.  The entries of U are streamed from LDS eight steps at a time
+    // (independent of the substitution chain, so their loads are issued early).
+    for (int j0 = 0; j0 < kLpMaxR; j0 += 8) {        // U z = r1
+      double u[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u[q] = (j0 + q < l) ? S.P[l][j0 + q] * S.Linv[j0 + q] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) b = fma(-u[q], readlane_d(b, j0 + q), b);
     }
-    for (int j = R - 1; j >= 0; --j) {     // L^T u = y
-      const double xj = __shfl(b, j, kWave) / S.Ldiag[j];
-      if (l < j) b -= S.P[j][l] * xj;
-      if (l == j) b = xj;
+    b *= linv_l * linv_l;                             // w = D^-1 z
+    for (int j0 = kLpMaxR - 8; j0 >= 0; j0 -= 8) {   // U^T u = w
+      double u[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u[q] = (j0 + q > l) ? S.P[j0 + q][l] * linv_l : 0.0;
+#pragma unroll
+      for (int q = 7; q >= 0; --q) b = fma(-u[q], readlane_d(b, j0 + q), b);
     }
     if (l < R) S.u64[l] = b;
   }
@@ -208,7 +239,14 @@ __device__ void lp_solve(int n, int R, int G, LpShared& S) {
   __syncthreads();
 }
 
-__device__ void lp_factor(int n, int R, int G, LpShared& S) {
+__device__ __forceinline__ double rsqrt_d(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * (1.5 - 0.5 * x * y * y);          // two Newton steps on the hardware estimate
+  y = y * (1.5 - 0.5 * x * y * y);
+  return y;
+}
+
+__device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, LpShared& S) {
   const int nv = n + R + 2;
   for (int i = threadIdx.x; i < nv; i += kLpThreads) S.d[i] = (double)S.v[i] / (double)S.z[i];
   __syncthreads();
@@ -217,48 +255,104 @@ __device__ void lp_factor(int n, int R, int G, LpShared& S) {
     for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) b += S.d[p];
     S.beta[g] = b;
   }
-  __syncthreads();
   const double delta = S.d[n + R] + S.d[n + R + 1];
-  for (int idx = threadIdx.x; idx < R * R; idx += kLpThreads) {
-    const int r = idx / R, r2 = idx % R;
-    double val = delta;
-    if (r == r2) {
-      double diag = S.d[n + r];
-      for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-        const int p = S.rank_copy[k], g = S.copy_group[p];
-        double others = 0.0;
-        for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
-          if (q != p) others += S.d[q];
-        diag += S.d[p] * (others / S.beta[g]);
-      }
-      val += diag;
-      S.d0[r] = val;
-    } else {
-      double off = 0.0;
-      for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-        const int p = S.rank_copy[k], g = S.copy_group[p];
-        for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
-          if (S.copy_rank[q] == r2) off += S.d[p] * (S.d[q] / S.beta[g]);
-      }
-      val -= off;
+  // every entry starts at the dense M/a term; the matrix is padded to 64 x 64 with
+  // identity rows and columns beyond R so the factorization has no bounds tests
+  for (int idx = threadIdx.x; idx < kLpMaxR * kLpMaxR; idx += kLpThreads) {
+    const int r = idx / kLpMaxR, c = idx % kLpMaxR;
+    S.P[r][c] = (r < R && c < R) ? delta : (r == c ? 1.0 : 0.0);
+  }
+  for (int r = R + threadIdx.x; r < kLpMaxR; r += kLpThreads) S.d0[r] = 1.0;
+  __syncthreads();
+  // diagonal: slack term plus each copy's d_p * (other copies of its group) / beta
+  for (int r = threadIdx.x; r < R; r += kLpThreads) {
+    double diag = delta + S.d[n + r];
+    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+      const int p = S.rank_copy[k], g = S.copy_group[p];
+      double others = 0.0;
+      for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
+        if (q != p) others += S.d[q];
+      diag += S.d[p] * (others / S.beta[g]);
     }
-    S.P[r][r2] = val;
+    S.P[r][r] = diag;
+    S.d0[r] = diag;
+  }
+  // off-diagonal entries touched by copies of one group on both ranks
+  for (int e = threadIdx.x; e < L.n_ent; e += kLpThreads) {
+    double off = 0.0;
+    for (int k = L.ent_start[e]; k < L.ent_start[e + 1]; ++k) {
+      const int p = L.ent_p[k], q = L.ent_q[k];
+      off += S.d[p] * (S.d[q] / S.beta[S.copy_group[p]]);
+    }
+    S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - off;
   }
   __syncthreads();
-  for (int j = 0; j < R; ++j) {            // right-looking Cholesky, lower triangle
-    const double pj = S.P[j][j];
-    const bool bad = !(pj > kPivTol * S.d0[j]);
-    const double ljj = bad ? 1e32 : sqrt(pj);
-    if (threadIdx.x == 0) S.Ldiag[j] = ljj;
-    for (int i = j + 1 + threadIdx.x; i < R; i += kLpThreads) S.P[i][j] = bad ? 0.0 : S.P[i][j] / ljj;
-    __syncthreads();
-    const int m = R - j - 1;
-    for (int idx = threadIdx.x; idx < m * m; idx += kLpThreads) {
-      const int i = j + 1 + idx / m, k = j + 1 + idx % m;
-      if (k <= i) S.P[i][k] -= S.P[i][j] * S.P[k][j];
+  // Right-looking Cholesky with a 4x4 register tile per thread: thread (ti, tk) owns
+  // rows i = ti + 16a and columns k = tk + 16b.  Every thread keeps the diagonal of its
+  // four columns current, so the owners of column j compute the pivot themselves and
+  // one barrier per column suffices (column j is published through a double buffer).
+  const int ti = threadIdx.x / 16, tk = threadIdx.x % 16;
+  double A[4][4], dg[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = ti + 16 * a, k = tk + 16 * b;
+      A[a][b] = S.P[i][k];
     }
-    __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 4; ++b) dg[b] = S.P[tk + 16 * b][tk + 16 * b];
+  // columns are processed in four blocks of 16 so that every tile index is static:
+  // in block jb, rows and columns below 16 * jb are finished and skipped
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll 1
+    for (int jt = 0; jt < 16; ++jt) {
+      const int j = jb * 16 + jt;
+      double* buf = S.colbuf[j & 1];
+      if (tk == jt) {
+        const double pj = dg[jb];
+        const bool bad = !(pj > kPivTol * S.d0[j]);
+        const double inv = bad ? 0.0 : rsqrt_d(pj);
+        if (ti == jt) S.Linv[j] = bad ? 1e-32 : inv;
+#pragma unroll
+        for (int a = jb; a < 4; ++a) {
+          const int i = ti + 16 * a;
+          if (i > j) {
+            A[a][jb] *= inv;
+            buf[i] = A[a][jb];
+          }
+        }
+      }
+      __syncthreads();
+      double li[4], lk[4];
+#pragma unroll
+      for (int a = jb; a < 4; ++a) {
+        const int i = ti + 16 * a;
+        li[a] = i > j ? buf[i] : 0.0;
+      }
+#pragma unroll
+      for (int b = jb; b < 4; ++b) {
+        const int k = tk + 16 * b;
+        lk[b] = k > j ? buf[k] : 0.0;
+      }
+#pragma unroll
+      for (int a = jb; a < 4; ++a)
+#pragma unroll
+        for (int b = jb; b < 4; ++b) A[a][b] = fma(-li[a], lk[b], A[a][b]);
+#pragma unroll
+      for (int b = jb; b < 4; ++b) dg[b] = fma(-lk[b], lk[b], dg[b]);
+    }
   }
+  // the strictly lower factor back to LDS for the triangular solves
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = ti + 16 * a, k = tk + 16 * b;
+      if (k < i) S.P[i][k] = A[a][b];
+    }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
@@ -268,8 +362,7 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ inst_quota,
                                                           int32_t* __restrict__ stats,
                                                           int32_t* err) {
-  extern __shared__ __align__(16) unsigned char lp_raw[];
-  LpShared& S = *reinterpret_cast<LpShared*>(lp_raw);
+  __shared__ LpShared S;                    // static LDS: no dynamic-base lookups
   const LpView L = lp_view(lpw);
   const int R = L.R, E = L.E, G = L.G, n = L.n, nv = n + R + 2;
   const int tid = threadIdx.x;
@@ -286,8 +379,7 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
   // expert loads (column sums of the load matrix): fixed load per rank, count per group
   int bad = 0;
   for (int e = tid; e < E; e += kLpThreads) {
-    int c = 0;
-    for (int r = 0; r < R; ++r) c += counts[(int64_t)r * E + e];
+    const int c = column_sum(counts, R, E, e);
     const int i = L.exp_inst[e];
     if (c > 0 && i == -1) bad |= UEP_ERR_LP;
     if (c >= (1 << 27)) bad |= UEP_ERR_LP;
@@ -355,7 +447,7 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
       const float mu = (float)(blk_sum(cz, S) / nv);
       if (!(mu >= kMuStop)) break;
       ++run;
-      lp_factor(n, R, G, S);
+      lp_factor(n, R, G, L, S);
       // predictor: rhs = rb + A (v + D rc)
       for (int i = tid; i < nv; i += kLpThreads) S.tv[i] = S.v[i] + (float)(S.d[i] * S.rc[i]);
       __syncthreads();
@@ -439,9 +531,7 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     const int e = L.inst_expert[i];
     if (e < 0) { inst_quota[i] = 0; continue; }
     if (L.inst_copy[i] < 0) {
-      int c = 0;
-      for (int r = 0; r < R; ++r) c += counts[(int64_t)r * E + e];
-      inst_quota[i] = c;
+      inst_quota[i] = column_sum(counts, R, E, e);
       continue;
     }
     const int p = L.inst_copy[i], g = S.copy_group[p];
@@ -484,7 +574,9 @@ using namespace uep;
 extern "C" size_t uep_lplb_struct_size(int32_t R, int32_t E, int32_t inst_per_rank) {
   if (R <= 0 || E <= 0 || inst_per_rank <= 0) return 0;
   const int I = R * inst_per_rank;
-  return sizeof(int32_t) * lp_words(R, E, I, E, I);
+  // at most I copies; each copy pairs with at most one copy per other rank
+  const int n_pair = I * (R - 1);
+  return sizeof(int32_t) * lp_words(R, E, I, E, I, R * R, n_pair);
 }
 
 extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
@@ -523,6 +615,20 @@ extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
   }
   const int G = (int)grp_expert.size(), n = (int)copy_inst.size();
   if (G > kLpMaxG || n > kLpMaxN) return UEP_EGEOM;
+  // lower off-diagonal entries of the rank matrix and the copy pairs that form them
+  std::vector<std::vector<std::pair<int, int>>> ent(R * kLpMaxR);
+  for (int g = 0; g < G; ++g)
+    for (int p = grp_start[g]; p < grp_start[g + 1]; ++p)
+      for (int q = grp_start[g]; q < grp_start[g + 1]; ++q)
+        if (copy_rank[p] > copy_rank[q]) ent[copy_rank[p] * kLpMaxR + copy_rank[q]].push_back({p, q});
+  std::vector<int> ent_rr, ent_start{0}, ent_p, ent_q;
+  for (int rr = 0; rr < R * kLpMaxR; ++rr) {
+    if (ent[rr].empty()) continue;
+    ent_rr.push_back(rr);
+    for (auto& pq : ent[rr]) { ent_p.push_back(pq.first); ent_q.push_back(pq.second); }
+    ent_start.push_back((int)ent_p.size());
+  }
+  const int n_ent = (int)ent_rr.size(), n_pair = (int)ent_p.size();
   std::vector<int> rank_start(R + 1, 0), rank_copy(n);
   for (int p = 0; p < n; ++p) rank_start[copy_rank[p] + 1]++;
   for (int r = 0; r < R; ++r) rank_start[r + 1] += rank_start[r];
@@ -530,14 +636,18 @@ extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
     std::vector<int> fill(rank_start.begin(), rank_start.end() - 1);
     for (int p = 0; p < n; ++p) rank_copy[fill[copy_rank[p]]++] = p;
   }
-  std::vector<int32_t> w(lp_words(R, E, I, G, n), 0);
+  const size_t words = lp_words(R, E, I, G, n, n_ent, n_pair);
+  if (lp_bytes < words * sizeof(int32_t)) return UEP_EWORKSPACE;
+  std::vector<int32_t> w(words, 0);
   w[0] = kLpMagic; w[1] = R; w[2] = E; w[3] = inst_per_rank; w[4] = I; w[5] = G; w[6] = n;
+  w[7] = n_ent;
   size_t o = 8;
   auto put = [&](const std::vector<int>& a) { for (int x : a) w[o++] = x; };
   put(grp_expert); put(grp_start); put(copy_inst); put(copy_rank); put(copy_group);
   put(rank_start); put(rank_copy); put(exp_inst);
   for (int i = 0; i < I; ++i) w[o++] = ie[i];
   put(inst_copy);
+  put(ent_rr); put(ent_start); put(ent_p); put(ent_q);
   hipStream_t s = uep_stream(stream);
   if (hipMemcpyAsync(lp, w.data(), w.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
       hipSuccess)
@@ -550,7 +660,7 @@ extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t it
                                float* m, int32_t* inst_quota, int32_t* stats, int32_t* err,
                                void* stream) {
   if (!counts || !lp || !x || !m || !inst_quota || iters < 0 || iters > 200) return UEP_EINVAL;
-  hipLaunchKernelGGL(lplb_kernel, dim3(1), dim3(kLpThreads), sizeof(LpShared), uep_stream(stream),
+  hipLaunchKernelGGL(lplb_kernel, dim3(1), dim3(kLpThreads), 0, uep_stream(stream),
                      counts, static_cast<const int32_t*>(lp), iters, x, m, inst_quota, stats, err);
   UEP_CHECK_LAUNCH();
   return UEP_OK;

@@ -2,8 +2,8 @@
 // section "流式通信算子加速动态权重分发": dispatch follows the reroute plan once the
 // replica weights are in place).
 //
-// HBM-bound: every source row is read once (non-temporal 16-byte loads) and written
-// to its K destination rows (non-temporal 16-byte stores).  One wave per source
+// HBM-bound: every source row is read once and written to its K destination rows
+// with 16-byte vector loads and stores.  One wave per source
 // token; a 256-thread workgroup moves 4 tokens.  The K destination rows are loaded
 // by lanes 0..K-1 and broadcast with readlane, so store addresses stay uniform per
 // row.  Rows are moved in slices of kVec 16-byte vectors per lane (1 KiB per wave
@@ -16,7 +16,7 @@ constexpr int kPmThreads = 256;
 constexpr int kPmTokPerBlock = kPmThreads / kWave;
 constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
 
-template <bool kRowSrc>
+template <bool kRowSrc, bool kNT>
 __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ dest_row,
                                                              u32x4* __restrict__ out,
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
       const int v = v0 + u * kWave + lane;
-      if (v < nvec) buf[u] = __builtin_nontemporal_load(src + v);
+      if (v < nvec) buf[u] = kNT ? __builtin_nontemporal_load(src + v) : src[v];
     }
     for (int k = 0; k < K; ++k) {
       const int d = readlane(d_mine, k);
@@ -43,7 +43,10 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
 #pragma unroll
       for (int u = 0; u < kVec; ++u) {
         const int v = v0 + u * kWave + lane;
-        if (v < nvec) __builtin_nontemporal_store(buf[u], dst + v);
+        if (v < nvec) {
+          if (kNT) __builtin_nontemporal_store(buf[u], dst + v);
+          else dst[v] = buf[u];
+        }
       }
     }
   }
@@ -65,14 +68,21 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) % 16 != 0)
     return UEP_EGEOM;
   const int64_t blocks = (g1 - g0 + kPmTokPerBlock - 1) / kPmTokPerBlock;
-  if (row_src)
-    hipLaunchKernelGGL(permute_kernel<true>, dim3((unsigned)blocks), dim3(kPmThreads), 0,
-                       uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
-                       reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
+  // Rows up to 8 KiB move fastest with plain loads and stores, longer rows with
+  // non-temporal ones (measured on MI355X).
+  const bool nt = H * 2 > 8192;
+  const dim3 grid((unsigned)blocks), block(kPmThreads);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  hipStream_t s = uep_stream(stream);
+  if (row_src && nt)
+    hipLaunchKernelGGL((permute_kernel<true, true>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
+  else if (row_src)
+    hipLaunchKernelGGL((permute_kernel<true, false>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
+  else if (nt)
+    hipLaunchKernelGGL((permute_kernel<false, true>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
   else
-    hipLaunchKernelGGL(permute_kernel<false>, dim3((unsigned)blocks), dim3(kPmThreads), 0,
-                       uep_stream(stream), reinterpret_cast<const u32x4*>(x), dest_row,
-                       reinterpret_cast<u32x4*>(out), row_src, g0, g1, K, H / 8);
+    hipLaunchKernelGGL((permute_kernel<false, false>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }

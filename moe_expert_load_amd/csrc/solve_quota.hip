@@ -146,10 +146,7 @@ __global__ void identity_quota_kernel(const int32_t* __restrict__ counts, int R,
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_inst) return;
   const int e = inst_expert[i];
-  int q = 0;
-  if (e >= 0 && e < E)
-    for (int r = 0; r < R; ++r) q += counts[(int64_t)r * E + e];
-  inst_quota[i] = q;
+  inst_quota[i] = (e >= 0 && e < E) ? column_sum(counts, R, E, e) : 0;
 }
 
 }  // namespace uep

@@ -9,8 +9,9 @@
 // One persistent grid.  Each workgroup first turns the slot table into its task
 // list in LDS (no host round trip: the plan stays on the device), then walks tasks
 // = (slot or replicated expert) x tile with a grid stride.  A tile is 256 threads x
-// kStVec 16-byte vectors = 64 KiB of bf16 weights (or fp32 gradients); all loads of
-// a tile are issued before its stores.
+// kStVec 16-byte vectors = 16 KiB of bf16 weights (or fp32 gradients); all loads of
+// a tile are issued before its stores.  Tile size, grid (16 workgroups per CU) and
+// plain (temporal) loads and stores were picked by measurement on MI355X.
 //
 // GRAD_REDUCE keeps the article's order fixed: for every element the main's
 // gradient is added to the replicas' gradients one at a time in ascending rank
@@ -20,7 +21,7 @@
 namespace uep {
 
 constexpr int kStThreads = 256;
-constexpr int kStVec = 16;
+constexpr int kStVec = 4;                         // 16 KiB tiles (measured best on MI355X)
 constexpr int kStTileVec = kStThreads * kStVec;   // 16-byte vectors per tile
 constexpr int kStMaxSlots = 64 * 8;
 
@@ -49,12 +50,12 @@ __global__ __launch_bounds__(kStThreads) void stage_weights_kernel(
 #pragma unroll
     for (int k = 0; k < kStVec; ++k) {
       const int64_t v = v0 + k * kStThreads + threadIdx.x;
-      if (v < nvec) buf[k] = __builtin_nontemporal_load(src + v);
+      if (v < nvec) buf[k] = src[v];
     }
 #pragma unroll
     for (int k = 0; k < kStVec; ++k) {
       const int64_t v = v0 + k * kStThreads + threadIdx.x;
-      if (v < nvec) __builtin_nontemporal_store(buf[k], dst + v);
+      if (v < nvec) dst[v] = buf[k];
     }
   }
 }
@@ -143,7 +144,7 @@ static int st_grid() {
       cus = p.multiProcessorCount;
     if (cus <= 0) cus = 256;
   }
-  return cus * 4;
+  return cus * 16;
 }
 
 }  // namespace uep

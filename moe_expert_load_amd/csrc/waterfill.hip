@@ -44,11 +44,7 @@ __global__ __launch_bounds__(256) void wf_prologue(const int32_t* __restrict__ c
   __shared__ int32_t s_L[64];
   __shared__ int32_t s_H;
   const int E_loc = E / R;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int r = 0; r < R; ++r) c += counts[(int64_t)r * E + e];
-    wf_lds[e] = c;
-  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) wf_lds[e] = column_sum(counts, R, E, e);
   __syncthreads();
   if (threadIdx.x < R) {
     int L = 0;
