@@ -28,20 +28,22 @@ __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_
 
 __device__ __forceinline__ int shfl(int v, int src) { return __shfl(v, src, kWave); }
 
+__device__ __forceinline__ int wave_incl_scan(int v);
+// wave-wide sum, uniform result
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);
 }
 
-// Inclusive prefix sum across the wave (Hillis-Steele on shuffles).
+// Inclusive prefix sum across the wave: Hillis-Steele inside each row of 16 lanes
+// with DPP row_shr (lanes shifted in from outside the row read 0), then row_bcast:15
+// and row_bcast:31 carry the row totals into the rows above.  All lanes active.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(v, o, kWave);
-    if (l >= o) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -65,11 +67,22 @@ __device__ __forceinline__ void wave_argmin(int& v, int& idx) {
   }
 }
 
-// Wave-wide min / max of an int (device-library DPP reductions), result in every lane.
-extern "C" __device__ int __ockl_wfred_max_i32(int);
-extern "C" __device__ int __ockl_wfred_min_i32(int);
-__device__ __forceinline__ int wave_max(int v) { return __ockl_wfred_max_i32(v); }
-__device__ __forceinline__ int wave_min(int v) { return __ockl_wfred_min_i32(v); }
+// Wave-wide max / min of an int, uniform result: DPP butterflies inside each row of
+// 16 lanes (quad_perm xor 1, xor 2, then row_ror 4 and 8), then the four row results
+// are combined with readlane.  Every lane of the wave must be active.
+template <bool kMax>
+__device__ __forceinline__ int wave_reduce_dpp(int v) {
+  auto op = [](int a, int b) { return kMax ? max(a, b) : min(a, b); };
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ int wave_max(int v) { return wave_reduce_dpp<true>(v); }
+__device__ __forceinline__ int wave_min(int v) { return wave_reduce_dpp<false>(v); }
 
 // Lowest lane whose predicate holds (-1 if none).
 __device__ __forceinline__ int first_lane(bool p) {

@@ -2,19 +2,17 @@
 // "在 Gate 之后获取当前层真实负载": the exact per-expert load of this layer,
 // gathered for the whole EP group into one matrix).
 //
-// Two launches over chunks of one rank's (token, expert) pairs:
-//   lm_chunk: every 256-thread workgroup takes 4096 consecutive pairs (whole
-//     tokens).  Each wave walks its 1024 pairs 64 at a time; lanes holding the same
-//     expert are found with one ballot per id bit (match-any), so a pair's rank
-//     inside the wave is a popcount of lower matching lanes and the last matching
-//     lane bumps the wave's LDS counter -- no atomics, order fixed by pair index.
-//     The 4 wave histograms are scanned in LDS, giving chunk-relative positions and
-//     the chunk histogram (to workspace).
-//   lm_fix: one workgroup per chunk adds the exclusive sum of earlier chunks'
-//     histograms, checks each token for repeated experts, and the last chunk of a
-//     rank writes counts[r][:].
-// Pairs are counted in pair order j = t*K + k; since ids are distinct within a
-// token, pair order inside a bucket is token order.
+// Main path (E <= 1024, K <= 16), two launches over chunks of a rank's tokens:
+//   lm_hist: per-chunk expert histogram with LDS integer atomics (order-free).
+//   lm_rank: each of the 4 waves walks its quarter of the chunk 64 tokens at a time,
+//     lane = token.  Every lane ORs its bit into a per-expert 64-bit lane mask in LDS
+//     for each of its K experts; a pair's rank among the wave's 64 tokens is then the
+//     popcount of its expert's mask below its lane, plus the wave's running count.
+//     Waves are stitched with an LDS scan and earlier chunks' histograms are added,
+//     giving the final positions.  Token order is kept by construction.
+// Fallback (larger E or K): lm_chunk ranks pairs with one ballot per id bit
+//   (match-any), lm_fix adds the earlier chunks' counts.
+// Pairs of one expert are ranked in token order: ids are distinct inside a token.
 #include "common.h"
 
 namespace uep {
@@ -29,6 +27,160 @@ constexpr int kLmFastK = 16;                         // register path of lm_fix
 struct LmGeom {
   int R, T, K, E, tok_per_chunk, n_chunks, id_bits;
 };
+
+constexpr int kLmBitmapMaxE = 1024;
+constexpr int kLmBitmapMaxK = 16;
+
+// K ids of token (base) into registers; 16-byte loads when K % 4 == 0 and aligned
+__device__ __forceinline__ void load_token(const int32_t* __restrict__ p, int K, bool vec,
+                                           int (&v)[kLmBitmapMaxK]) {
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; k += 4)
+      if (k < K) {
+        const int4 q = *reinterpret_cast<const int4*>(p + k);
+        v[k] = q.x; v[k + 1] = q.y; v[k + 2] = q.z; v[k + 3] = q.w;
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k)
+      if (k < K) v[k] = p[k];
+  }
+}
+
+__device__ __forceinline__ void store_token(int32_t* __restrict__ p, int K, bool vec,
+                                            const int (&v)[kLmBitmapMaxK]) {
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; k += 4)
+      if (k < K) *reinterpret_cast<int4*>(p + k) = make_int4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k)
+      if (k < K) p[k] = v[k];
+  }
+}
+
+__global__ __launch_bounds__(256) void lm_hist(const int32_t* __restrict__ ids,
+                                               int32_t* __restrict__ chunk_hist, int32_t* err,
+                                               LmGeom g, bool vec) {
+  extern __shared__ int32_t lh_lds[];                 // [E]
+  const int r = blockIdx.y, c = blockIdx.x;
+  for (int e = threadIdx.x; e < g.E; e += 256) lh_lds[e] = 0;
+  __syncthreads();
+  const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
+  int bad = 0;
+  for (int t = t0 + threadIdx.x; t < t1; t += 256) {
+    int v[kLmBitmapMaxK];
+    load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+      if (k >= g.K) break;
+      const int e = v[k];
+      if (e < -1 || e >= g.E) bad = 1;
+      else if (e >= 0) atomicAdd(&lh_lds[e], 1);
+    }
+  }
+  if (bad) set_err(err, UEP_ERR_ID_RANGE);
+  __syncthreads();
+  int32_t* ch = chunk_hist + ((int64_t)r * g.n_chunks + c) * g.E;
+  for (int e = threadIdx.x; e < g.E; e += 256) ch[e] = lh_lds[e];
+}
+
+__global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
+                                               int32_t* __restrict__ bucket_pos,
+                                               const int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts, int32_t* err,
+                                               LmGeom g, bool vec) {
+  extern __shared__ uint64_t lr_lds[];
+  uint64_t* mask = lr_lds;                                             // [4][E]
+  int32_t* whist = reinterpret_cast<int32_t*>(lr_lds + 4 * g.E);       // [4][E]
+  int32_t* pre = whist + 4 * g.E;                                      // [E]
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
+  for (int e = threadIdx.x; e < g.E; e += 256) {
+    int s = 0;
+    for (int cc = 0; cc < c; ++cc) s += ch[(int64_t)cc * g.E + e];
+    pre[e] = s;
+    if (c == g.n_chunks - 1)
+      counts[(int64_t)r * g.E + e] = s + (g.T > 0 ? ch[(int64_t)c * g.E + e] : 0);
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) { mask[ww * g.E + e] = 0; whist[ww * g.E + e] = 0; }
+  }
+  __syncthreads();
+  const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
+  const int tpw = g.tok_per_chunk / 4;
+  const int tw0 = t0 + w * tpw, tw1 = min(t1, tw0 + tpw);
+  uint64_t* vmask = mask + w * g.E;       // this wave's masks and running counts
+  int32_t* vhist = whist + w * g.E;
+  const uint64_t below = lanemask_lt();
+  // pass 1: ranks among the wave's tokens (provisional, relative to the wave)
+  for (int tb = tw0; tb < tw1; tb += kWave) {
+    const int t = tb + lane;
+    const bool live = t < tw1;
+    int v[kLmBitmapMaxK];
+    int32_t* bp = bucket_pos + ((int64_t)r * g.T + t) * g.K;
+    if (live) load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+      if (k >= g.K) break;
+      if (live && v[k] >= 0 && v[k] < g.E) atomicOr((unsigned long long*)&mask[w * g.E + v[k]], 1ull << lane);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int pos[kLmBitmapMaxK];
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+      if (k >= g.K) break;
+      pos[k] = -1;
+      if (live && v[k] >= 0 && v[k] < g.E)
+        pos[k] = vhist[v[k]] + __popcll(vmask[v[k]] & below);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int e = lane; e < g.E; e += kWave) {
+      const uint64_t m = vmask[e];
+      if (m) {
+        vhist[e] = vhist[e] + __popcll(m);
+        vmask[e] = 0;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (live) store_token(bp, g.K, vec, pos);
+  }
+  __syncthreads();
+  // wave offsets: earlier chunks + earlier waves of this chunk
+  for (int e = threadIdx.x; e < g.E; e += 256) {
+    int run = pre[e];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const int x = whist[ww * g.E + e];
+      whist[ww * g.E + e] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  // pass 2: final positions, and the check for an expert twice in one token
+  int dup = 0;
+  for (int tb = tw0; tb < tw1; tb += kWave) {
+    const int t = tb + lane;
+    if (t >= tw1) continue;
+    int v[kLmBitmapMaxK], pos[kLmBitmapMaxK];
+    const int64_t base = ((int64_t)r * g.T + t) * g.K;
+    load_token(ids + base, g.K, vec, v);
+    load_token(bucket_pos + base, g.K, vec, pos);
+#pragma unroll
+    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+      if (k >= g.K) break;
+      const bool ok = v[k] >= 0 && v[k] < g.E;
+#pragma unroll
+      for (int k2 = 0; k2 < kLmBitmapMaxK; ++k2)
+        if (k2 < k) dup |= ok && v[k2] == v[k];
+      if (ok) pos[k] += whist[w * g.E + v[k]];
+    }
+    store_token(bucket_pos + base, g.K, vec, pos);
+  }
+  if (dup) set_err(err, UEP_ERR_DUP_ID);
+}
 
 __global__ __launch_bounds__(kLmThreads) void lm_chunk(const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ bucket_pos,
@@ -151,10 +303,17 @@ __global__ __launch_bounds__(kLmThreads) void lm_fix(const int32_t* __restrict__
   if (dup) set_err(err, UEP_ERR_DUP_ID);
 }
 
+static bool lm_bitmap(int K, int E) { return E <= kLmBitmapMaxE && K <= kLmBitmapMaxK; }
+
 static LmGeom lm_geom(int R, int T, int K, int E) {
   LmGeom g;
   g.R = R; g.T = T; g.K = K; g.E = E;
-  g.tok_per_chunk = kLmPairs / K;
+  if (lm_bitmap(K, E)) {
+    // whole waves of tokens: 256 * max(1, floor(8 / K)) tokens, at most 2048 per chunk
+    g.tok_per_chunk = 256 * (K >= 8 ? 1 : 8 / K);
+  } else {
+    g.tok_per_chunk = kLmPairs / K;
+  }
   g.n_chunks = T > 0 ? (T + g.tok_per_chunk - 1) / g.tok_per_chunk : 1;
   int bits = 0;
   while ((1 << bits) < E) ++bits;
@@ -182,6 +341,20 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
   LmGeom g = lm_geom(R, T, K, E);
   hipStream_t s = uep_stream(stream);
   dim3 grid(g.n_chunks, R);
+  if (lm_bitmap(K, E)) {
+    const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
+                     (T == 0 || reinterpret_cast<uintptr_t>(bucket_pos) % 16 == 0);
+    if (T > 0) {
+      hipLaunchKernelGGL(lm_hist, grid, dim3(256), sizeof(int32_t) * E, s, topk_ids, (int32_t*)ws,
+                         err, g, vec);
+      UEP_CHECK_LAUNCH();
+    }
+    const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
+    hipLaunchKernelGGL(lm_rank, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
+                       counts, err, g, vec);
+    UEP_CHECK_LAUNCH();
+    return UEP_OK;
+  }
   if (T > 0) {
     hipLaunchKernelGGL(lm_chunk, grid, dim3(kLmThreads), sizeof(int32_t) * kLmWaves * E, s,
                        topk_ids, bucket_pos, (int32_t*)ws, err, g);

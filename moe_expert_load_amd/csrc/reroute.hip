@@ -10,8 +10,9 @@
 //   (ascending instance) with two wave scans, and every owner lane writes its
 //   column of the transfer matrix X as interval overlaps.  Every source lane then
 //   emits its segments {first bucket position, instance, row base, length}:
-//   local first, then remote instances in ascending id.  Blocks beyond E zero the
-//   columns of unused instances.
+//   local first, then remote instances in ascending id.  Lanes exchange values only
+//   by readlane (no LDS, no barrier).  Blocks beyond E zero the columns of unused
+//   instances.
 // rr_assign: one thread per (token, expert) pair; a short backwards scan over the
 //   pair's (rank, expert) segments gives instance and dispatch row.
 #include "common.h"
@@ -22,6 +23,10 @@ struct RrGeom {
   int R, T, K, E, ipr, I, seg_cap;
 };
 
+__device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) {
+  return max(0, min(a1, b1) - max(a0, b0));
+}
+
 __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ counts,
                                                 const int32_t* __restrict__ inst_expert,
                                                 const int32_t* __restrict__ inst_quota,
@@ -30,9 +35,6 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
                                                 int32_t* __restrict__ seg_base,
                                                 int32_t* __restrict__ seg_cnt,
                                                 int4* __restrict__ segs, int32_t* err, RrGeom g) {
-  __shared__ int32_t o_inst[kWave], o_qlo[kWave], o_qhi[kWave], o_off[kWave];
-  __shared__ int32_t s_dlo[kWave], s_dhi[kWave];
-  __shared__ int32_t so[kWave * kWave];   // so[src][owner] = rows of earlier sources in owner's instance
   const int e = blockIdx.x, lane = threadIdx.x;
   const int R = g.R, I = g.I, E = g.E;
 
@@ -80,54 +82,72 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   const int d_lo = d_incl - D, q_lo = q_incl - Q;
   if (lane == 0 && readlane(d_incl, kWave - 1) != readlane(q_incl, kWave - 1))
     set_err(err, UEP_ERR_QUOTA_SUM);
-  o_inst[lane] = my_i;
-  o_qlo[lane] = q_lo;
-  o_qhi[lane] = q_lo + Q;
-  o_off[lane] = my_off;
-  s_dlo[lane] = d_lo;
-  s_dhi[lane] = d_lo + D;
-  __syncthreads();
 
-  // owner lane: its column of X and the running row offset of every source in it
-  if (active && my_i >= 0) {
-    int run = 0;
-    for (int s = 0; s < R; ++s) {
-      int x = max(0, min(s_dhi[s], q_lo + Q) - max(s_dlo[s], q_lo));
-      if (s == lane) x += xl;
-      xfer[(int64_t)s * I + my_i] = x;
-      so[s * kWave + lane] = run;
-      run += x;
-    }
-  }
-  __syncthreads();
-
-  // segments of source lane: local, then remote owners in ascending rank
-  int n = 0;
-  if (active) {
-    n = xl > 0;
-    for (int o = 0; o < R; ++o) {
-      if (o == lane || o_inst[o] < 0) continue;
-      const int lo = max(d_lo, o_qlo[o]), hi = min(d_lo + D, o_qhi[o]);
-      n += hi > lo;
+  // Only ranks holding an instance of e matter (usually one or two).  For each such
+  // owner o, in ascending rank, every source lane s computes the tokens it sends o:
+  // the overlap of its demand interval [d_lo_s, d_lo_s + D_s) with o's capacity
+  // interval [q_lo_o, q_lo_o + Q_o), plus o's local tokens when s == o, and writes
+  // its entry of o's column of X.  Rows of an instance are ordered by source rank, so
+  // source s starts in o's block after the overlap of [0, d_lo_s) with o's interval,
+  // plus o's local tokens when o < s.  Segments of a source: its local instance first,
+  // then the remote owners in ascending rank.
+  const uint64_t owners = ballot(active && my_i >= 0);
+  int n = active ? (xl > 0) : 0;
+  for (uint64_t m = owners; m; m &= m - 1) {
+    const int o = __ffsll((unsigned long long)m) - 1;
+    const int oi = readlane(my_i, o), oql = readlane(q_lo, o), oqh = oql + readlane(Q, o);
+    const int oxl = readlane(xl, o);
+    if (active) {
+      const int x = overlap(d_lo, d_lo + D, oql, oqh);
+      xfer[(int64_t)lane * I + oi] = x + (lane == o ? oxl : 0);
+      n += (lane != o && x > 0);
     }
   }
   const int n_incl = wave_incl_scan(n);
-  if (lane == 0 && readlane(n_incl, kWave - 1) > g.seg_cap) set_err(err, UEP_ERR_COVER);
-  if (active && readlane(n_incl, kWave - 1) <= g.seg_cap) {
-    int k = e * g.seg_cap + (n_incl - n);
+  const int n_tot = readlane(n_incl, kWave - 1);
+  if (lane == 0 && n_tot > g.seg_cap) set_err(err, UEP_ERR_COVER);
+  const bool fits = n_tot <= g.seg_cap;
+  int k = e * g.seg_cap + (n_incl - n);
+  if (active) {
     seg_base[(int64_t)lane * E + e] = k;
-    seg_cnt[(int64_t)lane * E + e] = n;
-    if (xl > 0) segs[k++] = make_int4(0, my_i, my_off + so[lane * kWave + lane], xl);
-    for (int o = 0; o < R; ++o) {
-      if (o == lane || o_inst[o] < 0) continue;
-      const int lo = max(d_lo, o_qlo[o]), hi = min(d_lo + D, o_qhi[o]);
+    seg_cnt[(int64_t)lane * E + e] = fits ? n : 0;
+    if (fits && xl > 0) segs[k++] = make_int4(0, my_i, my_off + overlap(0, d_lo, q_lo, q_lo + Q), xl);
+  }
+  for (uint64_t m = owners; m; m &= m - 1) {
+    const int o = __ffsll((unsigned long long)m) - 1;
+    const int oi = readlane(my_i, o), oql = readlane(q_lo, o), oqh = oql + readlane(Q, o);
+    const int ooff = readlane(my_off, o), oxl = readlane(xl, o);
+    if (fits && active && o != lane) {
+      const int lo = max(d_lo, oql), hi = min(d_lo + D, oqh);
       if (hi > lo) {
         const int b0 = xl + (lo - d_lo);
-        segs[k++] = make_int4(b0, o_inst[o], o_off[o] + so[lane * kWave + o] - b0, hi - lo);
+        const int before = overlap(0, d_lo, oql, oqh) + (o < lane ? oxl : 0);
+        segs[k++] = make_int4(b0, oi, ooff + before - b0, hi - lo);
       }
     }
-  } else if (active) {
-    seg_cnt[(int64_t)lane * E + e] = 0;
+  }
+}
+
+__device__ __forceinline__ void assign_one(int e, int b, int r, const int32_t* __restrict__ seg_base,
+                                           const int32_t* __restrict__ seg_cnt,
+                                           const int4* __restrict__ segs, int32_t* err,
+                                           const RrGeom& g, int& di, int& dr) {
+  di = -1;
+  dr = -1;
+  if (e < 0 || e >= g.E) return;
+  const int sb = seg_base[(int64_t)r * g.E + e];
+  const int n = seg_cnt[(int64_t)r * g.E + e];
+  int k = n - 1;
+  int4 sg = make_int4(0, -1, 0, 0);
+  for (; k >= 0; --k) {
+    sg = segs[sb + k];
+    if (sg.x <= b) break;
+  }
+  if (k >= 0 && b < sg.x + sg.w) {
+    di = sg.y;
+    dr = sg.z + b;
+  } else {
+    set_err(err, UEP_ERR_COVER);
   }
 }
 
@@ -141,28 +161,34 @@ __global__ __launch_bounds__(256) void rr_assign(const int32_t* __restrict__ ids
                                                  int64_t j0, int64_t j1, RrGeom g) {
   const int64_t j = j0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= j1) return;
-  const int e = ids[j];
-  int di = -1, dr = -1;
-  if (e >= 0 && e < g.E) {
-    const int r = (int)(j / ((int64_t)g.T * g.K));
-    const int b = bucket_pos[j];
-    const int sb = seg_base[(int64_t)r * g.E + e];
-    const int n = seg_cnt[(int64_t)r * g.E + e];
-    int k = n - 1;
-    int4 sg = make_int4(0, -1, 0, 0);
-    for (; k >= 0; --k) {
-      sg = segs[sb + k];
-      if (sg.x <= b) break;
-    }
-    if (k >= 0 && b < sg.x + sg.w) {
-      di = sg.y;
-      dr = sg.z + b;
-    } else {
-      set_err(err, UEP_ERR_COVER);
-    }
-  }
+  int di, dr;
+  assign_one(ids[j], bucket_pos[j], (int)(j / ((int64_t)g.T * g.K)), seg_base, seg_cnt, segs, err,
+             g, di, dr);
   dest_inst[j] = di;
   dest_row[j] = dr;
+}
+
+// four consecutive pairs per thread (16-byte loads and stores); needs T*K % 4 == 0 so
+// the four pairs share a rank and j0 is aligned
+__global__ __launch_bounds__(256) void rr_assign4(const int4* __restrict__ ids,
+                                                  const int4* __restrict__ bucket_pos,
+                                                  const int32_t* __restrict__ seg_base,
+                                                  const int32_t* __restrict__ seg_cnt,
+                                                  const int4* __restrict__ segs,
+                                                  int4* __restrict__ dest_inst,
+                                                  int4* __restrict__ dest_row, int32_t* err,
+                                                  int64_t q0, int64_t q1, RrGeom g) {
+  const int64_t qd = q0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (qd >= q1) return;
+  const int r = (int)(qd * 4 / ((int64_t)g.T * g.K));
+  const int4 e = ids[qd], b = bucket_pos[qd];
+  int4 di, dr;
+  assign_one(e.x, b.x, r, seg_base, seg_cnt, segs, err, g, di.x, dr.x);
+  assign_one(e.y, b.y, r, seg_base, seg_cnt, segs, err, g, di.y, dr.y);
+  assign_one(e.z, b.z, r, seg_base, seg_cnt, segs, err, g, di.z, dr.z);
+  assign_one(e.w, b.w, r, seg_base, seg_cnt, segs, err, g, di.w, dr.w);
+  dest_inst[qd] = di;
+  dest_row[qd] = dr;
 }
 
 static void rr_ws_layout(int R, int E, size_t* off_cnt, size_t* off_segs, size_t* total,
@@ -218,9 +244,23 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
   UEP_CHECK_LAUNCH();
   if (pairs) {
     const int64_t j0 = (int64_t)r_begin * T * K, j1 = (int64_t)r_end * T * K;
-    const int64_t nb = (j1 - j0 + 255) / 256;
-    hipLaunchKernelGGL(rr_assign, dim3((unsigned)nb), dim3(256), 0, s, topk_ids, bucket_pos,
-                       seg_base, seg_cnt, segs, dest_inst, dest_row, err, j0, j1, g);
+    const bool vec = ((int64_t)T * K) % 4 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(topk_ids) | reinterpret_cast<uintptr_t>(bucket_pos) |
+                       reinterpret_cast<uintptr_t>(dest_inst) | reinterpret_cast<uintptr_t>(dest_row)) %
+                      16) == 0;
+    if (vec) {
+      const int64_t q0 = j0 / 4, q1 = j1 / 4;
+      const int64_t nb = (q1 - q0 + 255) / 256;
+      hipLaunchKernelGGL(rr_assign4, dim3((unsigned)nb), dim3(256), 0, s,
+                         reinterpret_cast<const int4*>(topk_ids),
+                         reinterpret_cast<const int4*>(bucket_pos), seg_base, seg_cnt, segs,
+                         reinterpret_cast<int4*>(dest_inst), reinterpret_cast<int4*>(dest_row), err,
+                         q0, q1, g);
+    } else {
+      const int64_t nb = (j1 - j0 + 255) / 256;
+      hipLaunchKernelGGL(rr_assign, dim3((unsigned)nb), dim3(256), 0, s, topk_ids, bucket_pos,
+                         seg_base, seg_cnt, segs, dest_inst, dest_row, err, j0, j1, g);
+    }
     UEP_CHECK_LAUNCH();
   }
   return UEP_OK;

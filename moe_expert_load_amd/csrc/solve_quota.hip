@@ -35,11 +35,27 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
   const int E_loc = E / R;
   for (int e = tid; e < E; e += kSqThreads) sq_lds[e] = 0;
   __syncthreads();
-  for (int i = tid; i < R * E; i += kSqThreads) atomicAdd(&sq_lds[i % E], counts[i]);
+  {
+    // per = threads per expert; each sums every per-th rank with loads in flight
+    const int per = E >= kSqThreads ? 1 : kSqThreads / E;
+    const int part = tid % per;
+    for (int e = tid / per; e < E; e += kSqThreads / per) {
+      int acc[4] = {0, 0, 0, 0};
+      int r = part;
+      for (; r + 3 * per < R; r += 4 * per) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += counts[(int64_t)(r + u * per) * E + e];
+      }
+      for (; r < R; r += per) acc[0] += counts[(int64_t)r * E + e];
+      atomicAdd(&sq_lds[e], (acc[0] + acc[1]) + (acc[2] + acc[3]));
+    }
+  }
   __syncthreads();
   if (tid >= kWave) return;                 // the search itself is one wave
 
-  volatile int32_t* q_main = sq_lds;
+  // Only this wave touches the quotas from here on; its LDS accesses execute in
+  // program order, so plain loads and stores are enough.
+  int32_t* q_main = sq_lds;
   const int lane = tid;
   const bool active = lane < R;
   int L = 0;

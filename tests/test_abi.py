@@ -49,8 +49,10 @@ def test_host_side_calls_without_gpu(lib):
     lib.uep_status_string.restype = ctypes.c_char_p
     assert lib.uep_status_string(3) == b"workspace too small"
     lib.uep_load_matrix_workspace_size.restype = ctypes.c_size_t
-    # 32 ranks x 16 chunks x 128 experts x 4 bytes
-    assert lib.uep_load_matrix_workspace_size(32, 8192, 8, 128) == 32 * 16 * 128 * 4
+    # one int32 histogram per (rank, chunk of tokens): grows with the token count
+    small = lib.uep_load_matrix_workspace_size(32, 1024, 8, 128)
+    big = lib.uep_load_matrix_workspace_size(32, 8192, 8, 128)
+    assert small > 0 and big > small and big % (32 * 128 * 4) == 0
     lib.uep_reroute_workspace_size.restype = ctypes.c_size_t
     assert lib.uep_reroute_workspace_size(32, 128, 5) > 0
     lib.uep_lplb_struct_size.restype = ctypes.c_size_t

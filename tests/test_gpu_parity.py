@@ -113,6 +113,11 @@ def test_plan_edge_cases():
     ids = random_routing(rng, 2, 4096 // 3 * 2 + 17, 3, 10)
     o = oracle_plan(ids, 10, 1, 5)
     compare_plan(plan_on_gpu(U, to_dev(ids), 10, 1, 5), o, 1)
+    # many experts / many routing slots: the ballot ranking path
+    for (R_, T_, K_, E_) in ((32, 40, 4, 2048), (4, 200, 20, 64)):
+        ids = random_routing(rng, R_, T_, K_, E_, p=np.full(E_, 1.0 / E_), empty_frac=0.02)
+        o = oracle_plan(ids, E_, 1, 3)
+        compare_plan(plan_on_gpu(U, to_dev(ids), E_, 1, 3), o, 1)
     # T = 0
     ids = np.zeros((2, 0, 4), dtype=np.int32)
     err = err_word()
