@@ -165,11 +165,68 @@ def permute_bytes(N, P, H):
     return N * H * 2 + P * H * 2 + P * 4
 
 
-def roofline(bytes_, ms, kernel):
+PERMUTE_CALL = "permute_kernel<false> + row_src_kernel (one uep_permute call)"
+PERMUTE_CALL_NT = "permute_kernel<true> + row_src_kernel (one uep_permute call)"
+PERMUTE_SOURCES = ("moe_expert_load_amd/csrc/permute.hip", "moe_expert_load_amd/csrc/common.h")
+
+
+def source_digest(paths=PERMUTE_SOURCES):
+    """sha256 over the kernel's source files: ties stored counter figures to the code."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the permute call from the committed counter summary
+    profiles/permute_<workload>_pmc.md, or None when there is none or the permute
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"permute_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and " = " in line:
+            k, v = line[2:].split(" = ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline(bytes_, ms, kernel, traffic=None):
     gbs = bytes_ / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": ms}
+
+
+def copy_reference(torch, U, nbytes=1 << 30, reps=5):
+    """Event-timed plain device copy (uep_device_copy) of nbytes: the achievable
+    bandwidth line, and the known-size kernel that calibrates byte counters."""
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=DEV)
+    b = torch.empty_like(a)
+    s = torch.cuda.current_stream()
+    U.device_copy(a, b, s)
+    torch.cuda.synchronize()
+    t = Timer(torch, reps)
+    for _ in range(reps):
+        t.start(s)
+        U.device_copy(a, b, s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": 2 * nbytes, "avg_launch_ms": ms,
+            "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
 def base_line(w, W, value, ms, args, dtype, extra_cfg=None):
@@ -199,10 +256,10 @@ def timed_steps(torch, args, step, stream, timers=()):
 
 
 # ----------------------------------------------------------------------------- CPU leg
-def cpu_baseline(w, ids, x_host, n_rank_sample=2):
+def cpu_baseline(w, ids, x_host, n_rank_sample=8):
     """The oracle as it stands, single process, on a bounded sample of the same layer:
-    the whole plan (load matrix, quota solve, reroute, assignment) plus the permute of
-    n_rank_sample ranks and the staging of one used slot, scaled to the whole layer."""
+    the whole plan (load matrix, quota solve, reroute, assignment), the permute of
+    n_rank_sample ranks scaled to all ranks, and the staging of every used slot."""
     import oracle as O
     t0 = time.perf_counter()
     counts, bp = O.load_matrix(ids, w.E)
@@ -217,18 +274,15 @@ def cpu_baseline(w, ids, x_host, n_rank_sample=2):
     n = w.expert_elems
     mw = np.zeros((w.E, n), dtype=np.uint16)
     sw = np.zeros((w.R, w.S, n), dtype=np.uint16)
-    one = np.full((w.R, w.S), -1, dtype=np.int64)
-    if used:
-        one[used[0]] = plan["slot_expert"][used[0]]
     t0 = time.perf_counter()
-    O.stage_forward(one, mw, sw)
-    t_stage = (time.perf_counter() - t0) * len(used)
+    O.stage_forward(plan["slot_expert"], mw, sw)
+    t_stage = time.perf_counter() - t0
     total = t_plan + t_perm + t_stage
     return {
         "value": w.N / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
         "sample": (f"whole-layer plan ({t_plan:.2f} s) + permute of {n_rank_sample} of {w.R} ranks "
-                   f"scaled x{w.R // n_rank_sample} ({t_perm:.2f} s) + staging of 1 of {len(used)} "
-                   f"used slots scaled ({t_stage:.2f} s); Python+numpy, one thread"),
+                   f"scaled x{w.R / n_rank_sample:g} ({t_perm:.2f} s) + staging of all {len(used)} "
+                   f"used slots ({t_stage:.2f} s); Python+numpy, one thread"),
     }
 
 
@@ -262,6 +316,13 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     pb = permute_bytes(w.N, w.P, w.H)
     perm_ms, stage_ms = tp.mean_ms(), ts.mean_ms()
     stage_bytes = 2 * n_used * w.expert_elems * 2
+    copy = copy_reference(torch, U)
+    if args.roofline_only:
+        out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32", {"ffn": list(w.ffn_shape)})
+        out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
+        out["cpu_baseline"] = None
+        out["extra"] = {"device_copy_gbs": copy["gbs"], "stage_ms": stage_ms}
+        return out
     # per-rank share (rank 0): whole-group plan, its own tokens and slot
     r = 0
 
@@ -280,7 +341,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     before = c.reshape(w.R, w.E_loc).sum(1)
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"ffn": list(w.ffn_shape)})
-    out["roofline"] = roofline(pb, perm_ms, "permute_kernel<true, false>")
+    out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
     cpu = None
     if with_cpu:
         log("cpu baseline (oracle) ...")
@@ -299,6 +360,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "solver_steps": int(stats[1]),
         "imbalance_before": float(before.max() / before.mean()),
         "imbalance_after": float(rl.max() / rl.mean()),
+        "device_copy_gbs": copy["gbs"],
     }
     out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
     return out
@@ -356,7 +418,8 @@ def bench_waterfill(args, torch, U, W, w):
     pb = permute_bytes(N, L.P, w.H)
     out = base_line(w, W, N / (ms * 1e-3), ms, args, "int32",
                     {"top_k_fused": K2, "shared_slot_per_rank": 1})
-    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true, true>")
+    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
+                               measured_traffic(w.name))
     out["cpu_baseline"] = None
     r = 0
     plan_us = graph_us(torch, lambda s: wf_plan(s))
@@ -409,7 +472,8 @@ def bench_lplb(args, torch, U, W, w):
     pb = permute_bytes(w.N, w.P, w.H)
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"static_replicas": w.n_static_replicas, "lp_iters": args.lp_iters})
-    out["roofline"] = roofline(pb, tp.mean_ms(), "permute_kernel<true, true>")
+    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
+                               measured_traffic(w.name))
     out["cpu_baseline"] = None
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)
@@ -517,6 +581,99 @@ def kernel_report(args, torch, U, W):
     print(json.dumps(rep), flush=True)
 
 
+# ----------------------------------------------------------------------------- profiles
+def _short(name):
+    name = name.replace("void ", "")
+    head = name.split("(")[0]
+    return head if len(head) <= 60 else head[:57] + "..."
+
+
+def _csv(directory, suffix):
+    import csv
+    import glob
+    found = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not found:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(found[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def trace_summary(directory):
+    """Markdown table of a rocprofv3 --kernel-trace --stats CSV run: rocprofv3's own
+    per-name statistics, then the trace split by (kernel, workgroup count), since one
+    kernel runs at several sizes in one bench (whole group vs one rank's share)."""
+    stats = _csv(directory, "kernel_stats.csv")
+    print("rocprofv3 kernel statistics (by kernel name, all launches):\n")
+    print("| kernel | calls | avg us | min us | max us | % time |")
+    print("|---|---|---|---|---|---|")
+    for r in stats:
+        if not r["Name"].startswith(("uep::", "void uep::")):
+            continue
+        print(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']} |")
+    trace = _csv(directory, "kernel_trace.csv")
+    agg = {}
+    for r in trace:
+        if "uep::" not in r["Kernel_Name"]:
+            continue
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        blocks = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+        key = (_short(r["Kernel_Name"]), blocks, wg)
+        agg.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("\nkernel trace by (kernel, workgroups):\n")
+    print("| kernel | workgroups x threads | launches | avg us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (k, b, wg), d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(d, dtype=np.float64) / 1e3
+        print(f"| {k} | {b} x {wg} | {len(d)} | {d.mean():.2f} | {np.median(d):.2f} | "
+              f"{d.min():.2f} | {d.max():.2f} |")
+
+
+def pmc_summary(fetch_dir, write_dir, workload="qwen3_235b_layer"):
+    """Copy-calibrated HBM traffic of the permute call from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    true bytes / counter reading of uep_device_copy's 1 GiB copy in the same run."""
+    w = None
+    from moe_expert_load_amd import workload as W
+    w = W.ALL[workload]
+
+    def per_kernel(rows, counter):
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] != counter or "uep::" not in r["Kernel_Name"]:
+                continue
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1))
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: float(np.median(v)) for k, v in out.items()}
+
+    fetch = per_kernel(_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = per_kernel(_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024
+    ck = [k for k in fetch if k[0].endswith("device_copy_kernel")]
+    f_fetch = copy_kib / fetch[ck[0]]
+    f_write = copy_kib / write[ck[0]]
+    print("| kernel | workgroups | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated MiB read | "
+          "calibrated MiB written |")
+    print("|---|---|---|---|---|---|")
+    for k in sorted(fetch, key=lambda k: -fetch[k] - write.get(k, 0)):
+        fw = write.get(k, float("nan"))
+        print(f"| {k[0]} | {k[1]} | {fetch[k]:.1f} | {fw:.1f} | {fetch[k] * f_fetch / 1024:.1f} | "
+              f"{fw * f_write / 1024:.1f} |")
+    pk = [k for k in fetch if "permute_kernel" in k[0] and k[1] == (w.N + 3) // 4]
+    rk = [k for k in fetch if "row_src_kernel" in k[0] and k[1] == (w.P + 255) // 256]
+    kib = sum(fetch[k] * f_fetch + write[k] * f_write for k in pk + rk)
+    traffic = int(round(kib * 1024))
+    alg = permute_bytes(w.N, w.P, w.H)
+    print(f"\ncalibration (uep_device_copy, 1 GiB read + 1 GiB written): FETCH_SIZE x {f_fetch:.5f}, "
+          f"WRITE_SIZE x {f_write:.5f}\n")
+    print(f"- workload = {workload}")
+    print(f"- kernels = {', '.join(f'{k[0]} ({k[1]} workgroups)' for k in pk + rk)}")
+    print(f"- algorithmic_bytes_per_launch = {alg}")
+    print(f"- traffic_bytes_per_launch = {traffic}")
+    print(f"- traffic_over_algorithmic = {traffic / alg:.4f}")
+    print(f"- source_sha256 = {source_digest()}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,7 +683,19 @@ def main():
     ap.add_argument("--workload", default="qwen3_235b_layer")
     ap.add_argument("--lp-iters", type=int, default=30)
     ap.add_argument("--kernels", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="timed steps, roofline and copy reference only (for counter passes)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print the markdown summary of a rocprofv3 kernel-trace CSV run")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the copy-calibrated traffic of two rocprofv3 --pmc CSV runs")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, workload=args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the EP group is simulated as virtual ranks on a "
               "single device, so --gpus above 1 is not supported.", file=sys.stderr)

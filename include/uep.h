@@ -69,6 +69,21 @@ const char* uep_version(void);
 const char* uep_status_string(uep_status s);
 
 /* ------------------------------------------------------------------------- *
+ * uep_device_copy -- plain device-to-device copy, the measured HBM reference line.
+ * Not a step of the balancing path: it is the "achievable bandwidth" kernel against
+ * which the permute and staging kernels are read, and the known-size kernel that
+ * calibrates hardware byte counters.  Each workgroup copies 16 KiB with 16-byte
+ * vector loads, all issued before its stores.
+ *
+ *   src   [bytes]  in   device memory, 16-byte aligned
+ *   dst   [bytes]  out  device memory, 16-byte aligned, not overlapping src
+ *   bytes               multiple of 16; 0 is a no-op
+ * Returns UEP_EINVAL for null pointers or negative size, UEP_EGEOM for misaligned
+ * pointers or a size that is not a multiple of 16.
+ * ------------------------------------------------------------------------- */
+uep_status uep_device_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_load_matrix -- the global load matrix of one layer.
  * [UEP] section "在 Gate 之后获取当前层真实负载" (real load after Gate): once the Gate
  * has run, every expert's exact token count for this microbatch and layer is known;

@@ -3,11 +3,19 @@
 // replica weights are in place).
 //
 // HBM-bound: every source row is read once and written to its K destination rows
-// with 16-byte vector loads and stores.  One wave per source
-// token; a 256-thread workgroup moves 4 tokens.  The K destination rows are loaded
-// by lanes 0..K-1 and broadcast with readlane, so store addresses stay uniform per
-// row.  Rows are moved in slices of kVec 16-byte vectors per lane (1 KiB per wave
-// per vector), all loads of a slice issued before its stores.
+// with 16-byte vector loads and stores.  One wave per source token; a 256-thread
+// workgroup moves 4 tokens.  The K destination rows are loaded by lanes 0..K-1 and
+// broadcast with readlane, so store addresses stay uniform per row.  Rows are moved
+// in slices of kVec 16-byte vectors per lane (1 KiB per wave per vector), all loads
+// of a slice issued before its stores.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs; the block -> token map
+// gives each XCD one contiguous token range, so rows that consecutive tokens write
+// into the same instance block meet in one L2.
+//
+// The inverse map row_src is written by a second, separate launch: 4-byte scattered
+// stores mixed into the row stream cost several times more than on their own
+// (measured on MI355X: about 4 % of the whole-group permute inline, under 1 % apart).
 #include "common.h"
 
 namespace uep {
@@ -16,18 +24,23 @@ constexpr int kPmThreads = 256;
 constexpr int kPmTokPerBlock = kPmThreads / kWave;
 constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
 
-template <bool kRowSrc, bool kNT>
+// Bijection of [0, nb): block b runs on XCD b % 8; that XCD's blocks take one
+// contiguous range of logical block ids, the first nb % 8 XCDs one block more.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
+  const int64_t q = nb / 8, rem = nb % 8, xcd = b % 8, idx = b / 8;
+  return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
+}
+
+template <bool kNT>
 __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ dest_row,
-                                                             u32x4* __restrict__ out,
-                                                             int32_t* __restrict__ row_src,
-                                                             int64_t g0, int64_t g1, int K,
-                                                             int nvec) {
+                                                             u32x4* __restrict__ out, int64_t g0,
+                                                             int64_t g1, int K, int nvec) {
   const int lane = threadIdx.x % kWave;
-  const int64_t g = g0 + (int64_t)blockIdx.x * kPmTokPerBlock + threadIdx.x / kWave;
+  const int64_t b = xcd_block(blockIdx.x, gridDim.x);
+  const int64_t g = g0 + b * kPmTokPerBlock + threadIdx.x / kWave;
   if (g >= g1) return;
   const int d_mine = lane < K ? dest_row[g * K + lane] : -1;
-  if (kRowSrc && lane < K && d_mine >= 0) row_src[d_mine] = (int32_t)(g * K + lane);
   const u32x4* src = x + g * nvec;
   for (int v0 = 0; v0 < nvec; v0 += kVec * kWave) {
     u32x4 buf[kVec];
@@ -50,6 +63,17 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
       }
     }
   }
+}
+
+// row_src[dest_row[j]] = j for the pairs j in [j0, j1), one thread per pair.
+__global__ __launch_bounds__(kPmThreads) void row_src_kernel(const int32_t* __restrict__ dest_row,
+                                                             int32_t* __restrict__ row_src,
+                                                             int64_t j0, int64_t j1, int swizzle) {
+  const int64_t b = swizzle ? xcd_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  const int64_t j = j0 + b * kPmThreads + threadIdx.x;
+  if (j >= j1) return;
+  const int32_t d = dest_row[j];
+  if (d >= 0) row_src[d] = (int32_t)j;
 }
 
 }  // namespace uep
@@ -75,14 +99,20 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x4* ov = reinterpret_cast<u32x4*>(out);
   hipStream_t s = uep_stream(stream);
-  if (row_src && nt)
-    hipLaunchKernelGGL((permute_kernel<true, true>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
-  else if (row_src)
-    hipLaunchKernelGGL((permute_kernel<true, false>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
-  else if (nt)
-    hipLaunchKernelGGL((permute_kernel<false, true>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
+  if (nt)
+    hipLaunchKernelGGL(permute_kernel<true>, grid, block, 0, s, xv, dest_row, ov, g0, g1, K, H / 8);
   else
-    hipLaunchKernelGGL((permute_kernel<false, false>), grid, block, 0, s, xv, dest_row, ov, row_src, g0, g1, K, H / 8);
+    hipLaunchKernelGGL(permute_kernel<false>, grid, block, 0, s, xv, dest_row, ov, g0, g1, K, H / 8);
   UEP_CHECK_LAUNCH();
+  if (row_src) {
+    const int64_t j0 = g0 * K, j1 = g1 * K;
+    const int64_t rblocks = (j1 - j0 + kPmThreads - 1) / kPmThreads;
+    // The XCD map helps once the scatter spans many blocks (measured: whole
+    // Qwen-layer group faster, one rank's share slower).
+    const int swizzle = rblocks >= 4096;
+    hipLaunchKernelGGL(row_src_kernel, dim3((unsigned)rblocks), block, 0, s, dest_row, row_src, j0,
+                       j1, swizzle);
+    UEP_CHECK_LAUNCH();
+  }
   return UEP_OK;
 }

@@ -33,6 +33,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "uep_version": (ctypes.c_char_p, []),
     "uep_status_string": (ctypes.c_char_p, [_I]),
+    "uep_device_copy": (_I, [_P, _P, _I64, _P]),
     "uep_load_matrix_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "uep_load_matrix": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "uep_solve_quota": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
@@ -177,6 +178,15 @@ def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None):
     _check(LIB.uep_permute(_p(x), _p(dest_row), R, T, K, H, r_begin, r_end, _p(out),
                            _p(row_src), _s(stream)), "uep_permute")
     return out, row_src
+
+
+def device_copy(src, dst, stream=None):
+    """Plain copy of src into dst (same byte size, both contiguous device tensors)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_contiguous() and dst.is_contiguous()):
+        raise TypeError("device_copy needs two contiguous tensors of the same byte size")
+    _check(LIB.uep_device_copy(_p(src), _p(dst), n, _s(stream)), "uep_device_copy")
+    return dst
 
 
 def stage_replica_weights(mode, R, E, S, slot_expert, expert_elems, main_w=None, slot_w=None,

@@ -73,3 +73,10 @@ def test_host_side_calls_without_gpu(lib):
     assert lib.uep_lplb_prepare(null, i32(2), i32(2), i32(2), null, ctypes.c_size_t(0), null) == 1
     assert lib.uep_stage_replica_weights(i32(0), i32(4), i32(8), i32(9), null, i32(0), i32(4), null,
                                          null, null, null, ctypes.c_int64(8), null) == 2
+    i64 = ctypes.c_int64
+    assert lib.uep_device_copy(null, null, i64(0), null) == 0
+    assert lib.uep_device_copy(null, null, i64(-16), null) == 1
+    assert lib.uep_device_copy(null, null, i64(32), null) == 1
+    fake_a, fake_b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert lib.uep_device_copy(fake_a, fake_b, i64(24), null) == 2
+    assert lib.uep_device_copy(ctypes.c_void_p(4100), fake_b, i64(32), null) == 2

@@ -118,6 +118,15 @@ def test_plan_edge_cases():
         ids = random_routing(rng, R_, T_, K_, E_, p=np.full(E_, 1.0 / E_), empty_frac=0.02)
         o = oracle_plan(ids, E_, 1, 3)
         compare_plan(plan_on_gpu(U, to_dev(ids), E_, 1, 3), o, 1)
+    # a single rank: nothing to balance, identity plan
+    ids = random_routing(rng, 1, 100, 2, 4)
+    o = oracle_plan(ids, 4, 1, 1)
+    compare_plan(plan_on_gpu(U, to_dev(ids), 4, 1, 1), o, 1)
+    # no redundant slots on a skewed layer: identity quotas, the solver reports stuck
+    ids = random_routing(rng, 4, 300, 2, 8, p=np.array([.6, .2, .05, .05, .04, .03, .02, .01]))
+    o = oracle_plan(ids, 8, 0, 1)
+    assert o["plan"]["stuck"] and o["plan"]["n_replicas"] == 0
+    compare_plan(plan_on_gpu(U, to_dev(ids), 8, 0, 1), o, 0)
     # T = 0
     ids = np.zeros((2, 0, 4), dtype=np.int32)
     err = err_word()
@@ -153,6 +162,19 @@ def test_host_argument_errors():
     x = torch.zeros(2, 4, 12, dtype=torch.bfloat16, device=DEV)  # H % 8 != 0
     with pytest.raises(U.UEPError):
         U.permute(x, t, torch.zeros(16, 12, dtype=torch.bfloat16, device=DEV))
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 4096, 16 * (3 * 4096 + 17)])
+def test_device_copy_reference(nbytes):
+    """The plain copy used as the bandwidth reference is bitwise, ragged tail included."""
+    say("case: device copy", nbytes)
+    g = torch.Generator(device=DEV).manual_seed(nbytes)
+    a = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32,
+                      device=DEV)
+    b = torch.full_like(a, -7)
+    U.device_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 def test_qwen_layer_full_size():
