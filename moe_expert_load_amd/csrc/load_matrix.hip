@@ -99,29 +99,55 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   const int r = blockIdx.y, c = blockIdx.x;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
+  const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
+  const int tpw = g.tok_per_chunk / 4;
+  const int tw0 = t0 + w * tpw, tw1 = min(t1, tw0 + tpw);
+  // the wave's first 64 tokens: loads issued before anything else
+  int v0[kLmBitmapMaxK], pos0[kLmBitmapMaxK];
+  if (tw0 + lane < tw1) load_token(ids + ((int64_t)r * g.T + tw0 + lane) * g.K, g.K, vec, v0);
   for (int e = threadIdx.x; e < g.E; e += 256) {
-    int s = 0;
-    for (int cc = 0; cc < c; ++cc) s += ch[(int64_t)cc * g.E + e];
-    pre[e] = s;
-    if (c == g.n_chunks - 1)
-      counts[(int64_t)r * g.E + e] = s + (g.T > 0 ? ch[(int64_t)c * g.E + e] : 0);
+    pre[e] = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) { mask[ww * g.E + e] = 0; whist[ww * g.E + e] = 0; }
   }
   __syncthreads();
-  const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
-  const int tpw = g.tok_per_chunk / 4;
-  const int tw0 = t0 + w * tpw, tw1 = min(t1, tw0 + tpw);
+  // pre[e] = sum of the earlier chunks' histograms: `per` threads per expert, each
+  // with up to 16 independent loads in flight, combined by LDS integer atomics
+  {
+    const int per = g.E >= 256 ? 1 : 256 / g.E;
+    const int part = threadIdx.x % per;
+    for (int e = threadIdx.x / per; e < g.E; e += 256 / per) {
+      int s = 0;
+      for (int cc0 = part; cc0 < c; cc0 += 16 * per) {
+        int acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int cc = cc0 + u * per;
+          acc[u] = cc < c ? ch[(int64_t)cc * g.E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += acc[u];
+      }
+      if (s) atomicAdd(&pre[e], s);
+    }
+  }
   uint64_t* vmask = mask + w * g.E;       // this wave's masks and running counts
   int32_t* vhist = whist + w * g.E;
   const uint64_t below = lanemask_lt();
-  // pass 1: ranks among the wave's tokens (provisional, relative to the wave)
+  // pass 1: ranks among the wave's tokens (provisional, relative to the wave).  The
+  // first 64 tokens of the wave stay in registers for pass 2; later ones (only when a
+  // wave has more than 64 tokens) go through bucket_pos.
   for (int tb = tw0; tb < tw1; tb += kWave) {
     const int t = tb + lane;
     const bool live = t < tw1;
     int v[kLmBitmapMaxK];
     int32_t* bp = bucket_pos + ((int64_t)r * g.T + t) * g.K;
-    if (live) load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+    if (tb == tw0) {
+#pragma unroll
+      for (int k = 0; k < kLmBitmapMaxK; ++k) v[k] = v0[k];
+    } else if (live) {
+      load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+    }
 #pragma unroll
     for (int k = 0; k < kLmBitmapMaxK; ++k) {
       if (k >= g.K) break;
@@ -145,10 +171,16 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (live) store_token(bp, g.K, vec, pos);
+    if (tb == tw0) {
+#pragma unroll
+      for (int k = 0; k < kLmBitmapMaxK; ++k) { v0[k] = v[k]; pos0[k] = pos[k]; }
+    } else if (live) {
+      store_token(bp, g.K, vec, pos);
+    }
   }
   __syncthreads();
-  // wave offsets: earlier chunks + earlier waves of this chunk
+  // wave offsets: earlier chunks + earlier waves of this chunk; the last chunk also
+  // writes the rank's row of the load matrix
   for (int e = threadIdx.x; e < g.E; e += 256) {
     int run = pre[e];
 #pragma unroll
@@ -157,6 +189,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
       whist[ww * g.E + e] = run;
       run += x;
     }
+    if (c == g.n_chunks - 1) counts[(int64_t)r * g.E + e] = run;
   }
   __syncthreads();
   // pass 2: final positions, and the check for an expert twice in one token
@@ -166,8 +199,13 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
     if (t >= tw1) continue;
     int v[kLmBitmapMaxK], pos[kLmBitmapMaxK];
     const int64_t base = ((int64_t)r * g.T + t) * g.K;
-    load_token(ids + base, g.K, vec, v);
-    load_token(bucket_pos + base, g.K, vec, pos);
+    if (tb == tw0) {
+#pragma unroll
+      for (int k = 0; k < kLmBitmapMaxK; ++k) { v[k] = v0[k]; pos[k] = pos0[k]; }
+    } else {
+      load_token(ids + base, g.K, vec, v);
+      load_token(bucket_pos + base, g.K, vec, pos);
+    }
 #pragma unroll
     for (int k = 0; k < kLmBitmapMaxK; ++k) {
       if (k >= g.K) break;

@@ -13,8 +13,9 @@
 //   local first, then remote instances in ascending id.  Lanes exchange values only
 //   by readlane (no LDS, no barrier).  Blocks beyond E zero the columns of unused
 //   instances.
-// rr_assign: one thread per (token, expert) pair; a short backwards scan over the
-//   pair's (rank, expert) segments gives instance and dispatch row.
+// rr_assign: a workgroup takes 2048 pairs of one rank, stages that rank's segments in
+//   LDS, and gives every pair its instance and dispatch row by a short backwards scan
+//   over its (rank, expert) segments.
 #include "common.h"
 
 namespace uep {
@@ -128,67 +129,169 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   }
 }
 
-__device__ __forceinline__ void assign_one(int e, int b, int r, const int32_t* __restrict__ seg_base,
-                                           const int32_t* __restrict__ seg_cnt,
-                                           const int4* __restrict__ segs, int32_t* err,
-                                           const RrGeom& g, int& di, int& dr) {
-  di = -1;
-  dr = -1;
-  if (e < 0 || e >= g.E) return;
-  const int sb = seg_base[(int64_t)r * g.E + e];
-  const int n = seg_cnt[(int64_t)r * g.E + e];
-  int k = n - 1;
-  int4 sg = make_int4(0, -1, 0, 0);
-  for (; k >= 0; --k) {
-    sg = segs[sb + k];
-    if (sg.x <= b) break;
-  }
-  if (k >= 0 && b < sg.x + sg.w) {
-    di = sg.y;
-    dr = sg.z + b;
-  } else {
-    set_err(err, UEP_ERR_COVER);
-  }
-}
-
-__global__ __launch_bounds__(256) void rr_assign(const int32_t* __restrict__ ids,
-                                                 const int32_t* __restrict__ bucket_pos,
-                                                 const int32_t* __restrict__ seg_base,
-                                                 const int32_t* __restrict__ seg_cnt,
-                                                 const int4* __restrict__ segs,
-                                                 int32_t* __restrict__ dest_inst,
-                                                 int32_t* __restrict__ dest_row, int32_t* err,
-                                                 int64_t j0, int64_t j1, RrGeom g) {
+// Fallback for geometries whose segment table does not fit in LDS: one thread per
+// pair, the (rank, expert) list walked backwards in global memory.
+__global__ __launch_bounds__(256) void rr_assign_flat(const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ bucket_pos,
+                                                      const int32_t* __restrict__ seg_base,
+                                                      const int32_t* __restrict__ seg_cnt,
+                                                      const int4* __restrict__ segs,
+                                                      int32_t* __restrict__ dest_inst,
+                                                      int32_t* __restrict__ dest_row, int32_t* err,
+                                                      int64_t j0, int64_t j1, RrGeom g) {
   const int64_t j = j0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= j1) return;
-  int di, dr;
-  assign_one(ids[j], bucket_pos[j], (int)(j / ((int64_t)g.T * g.K)), seg_base, seg_cnt, segs, err,
-             g, di, dr);
+  const int e = ids[j], b = bucket_pos[j];
+  const int r = (int)(j / ((int64_t)g.T * g.K));
+  int di = -1, dr = -1;
+  if (e >= 0 && e < g.E) {
+    const int sb = seg_base[(int64_t)r * g.E + e];
+    int k = seg_cnt[(int64_t)r * g.E + e] - 1;
+    int4 sg = make_int4(0, -1, 0, 0);
+    for (; k >= 0; --k) {
+      sg = segs[sb + k];
+      if (sg.x <= b) break;
+    }
+    if (k >= 0 && b < sg.x + sg.w) {
+      di = sg.y;
+      dr = sg.z + b;
+    } else {
+      set_err(err, UEP_ERR_COVER);
+    }
+  }
   dest_inst[j] = di;
   dest_row[j] = dr;
 }
 
-// four consecutive pairs per thread (16-byte loads and stores); needs T*K % 4 == 0 so
-// the four pairs share a rank and j0 is aligned
-__global__ __launch_bounds__(256) void rr_assign4(const int4* __restrict__ ids,
-                                                  const int4* __restrict__ bucket_pos,
-                                                  const int32_t* __restrict__ seg_base,
-                                                  const int32_t* __restrict__ seg_cnt,
-                                                  const int4* __restrict__ segs,
-                                                  int4* __restrict__ dest_inst,
-                                                  int4* __restrict__ dest_row, int32_t* err,
-                                                  int64_t q0, int64_t q1, RrGeom g) {
-  const int64_t qd = q0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (qd >= q1) return;
-  const int r = (int)(qd * 4 / ((int64_t)g.T * g.K));
-  const int4 e = ids[qd], b = bucket_pos[qd];
-  int4 di, dr;
-  assign_one(e.x, b.x, r, seg_base, seg_cnt, segs, err, g, di.x, dr.x);
-  assign_one(e.y, b.y, r, seg_base, seg_cnt, segs, err, g, di.y, dr.y);
-  assign_one(e.z, b.z, r, seg_base, seg_cnt, segs, err, g, di.z, dr.z);
-  assign_one(e.w, b.w, r, seg_base, seg_cnt, segs, err, g, di.w, dr.w);
-  dest_inst[qd] = di;
-  dest_row[qd] = dr;
+constexpr int kRaThreads = 256;
+constexpr size_t kRaMaxLds = 60 * 1024;               // staged segment table limit
+
+// One workgroup = 256 * kPer consecutive pairs of one source rank r.  The rank's
+// segment lists (every expert's) are first copied into LDS, compacted by an
+// exclusive scan of their lengths: each instance receives r's tokens of one expert
+// only, so the rank has at most I segments.  The pairs' ids and bucket positions are
+// loaded before that staging; each pair then walks its (r, expert) list backwards in
+// LDS to the segment holding its bucket position.
+template <bool kVec4, int kPer>
+__global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restrict__ ids,
+                                                        const int32_t* __restrict__ bucket_pos,
+                                                        const int32_t* __restrict__ seg_base,
+                                                        const int32_t* __restrict__ seg_cnt,
+                                                        const int4* __restrict__ segs,
+                                                        int32_t* __restrict__ dest_inst,
+                                                        int32_t* __restrict__ dest_row, int32_t* err,
+                                                        int r_begin, RrGeom g) {
+  extern __shared__ int4 ra_lds[];
+  int4* lsegs = ra_lds;                                          // [I]
+  int32_t* loff = reinterpret_cast<int32_t*>(ra_lds + g.I);      // [E]
+  int32_t* lcnt = loff + g.E;                                    // [E]
+  __shared__ int32_t wave_tot[kRaThreads / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int r = r_begin + blockIdx.y;
+  const int64_t n_pairs = (int64_t)g.T * g.K;
+  const int64_t p0 = (int64_t)blockIdx.x * kRaThreads * kPer;
+  const int64_t p1 = min(n_pairs, p0 + kRaThreads * kPer);
+  const int64_t rbase = (int64_t)r * n_pairs;
+
+  // 1. this thread's pairs (issued first; consumed after the staging)
+  int e_[kPer], b_[kPer];
+  if (kVec4) {
+#pragma unroll
+    for (int it = 0; it < kPer / 4; ++it) {
+      const int64_t j = p0 + 4 * ((int64_t)it * kRaThreads + tid);
+      int4 ev = make_int4(-1, -1, -1, -1), bv = make_int4(0, 0, 0, 0);
+      if (j < p1) {
+        ev = *reinterpret_cast<const int4*>(ids + rbase + j);
+        bv = *reinterpret_cast<const int4*>(bucket_pos + rbase + j);
+      }
+      e_[4 * it] = ev.x; e_[4 * it + 1] = ev.y; e_[4 * it + 2] = ev.z; e_[4 * it + 3] = ev.w;
+      b_[4 * it] = bv.x; b_[4 * it + 1] = bv.y; b_[4 * it + 2] = bv.z; b_[4 * it + 3] = bv.w;
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int64_t j = p0 + (int64_t)it * kRaThreads + tid;
+      e_[it] = j < p1 ? ids[rbase + j] : -1;
+      b_[it] = j < p1 ? bucket_pos[rbase + j] : 0;
+    }
+  }
+
+  // 2. segment counts of rank r: thread t owns experts [t*m, t*m + m)
+  const int m = (g.E + kRaThreads - 1) / kRaThreads;
+  const int ea = min(g.E, tid * m), eb = min(g.E, ea + m);
+  int mine = 0;
+  for (int e = ea; e < eb; ++e) {
+    const int n = seg_cnt[(int64_t)r * g.E + e];
+    lcnt[e] = n;
+    mine += n;
+  }
+  const int incl = wave_incl_scan(mine);
+  if (lane == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int ww = 0; ww < w; ++ww) run += wave_tot[ww];
+  // 3. copy the lists into LDS, compacted
+  for (int e = ea; e < eb; ++e) {
+    int n = lcnt[e];
+    if (run + n > g.I) {                    // cannot happen for a consistent plan
+      set_err(err, UEP_ERR_COVER);
+      n = max(0, g.I - run);
+      lcnt[e] = n;
+    }
+    loff[e] = run;
+    const int sb = seg_base[(int64_t)r * g.E + e];
+    for (int k = 0; k < n; ++k) lsegs[run + k] = segs[sb + k];
+    run += n;
+  }
+  __syncthreads();
+
+  // 4. look the pairs up
+  int di_[kPer], dr_[kPer];
+  int bad = 0;
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = e_[it], b = b_[it];
+    di_[it] = -1;
+    dr_[it] = -1;
+    if (e < 0 || e >= g.E) continue;
+    const int o = loff[e];
+    int k = lcnt[e] - 1;
+    int4 sg = make_int4(0, -1, 0, 0);
+    for (; k >= 0; --k) {
+      sg = lsegs[o + k];
+      if (sg.x <= b) break;
+    }
+    if (k >= 0 && b < sg.x + sg.w) {
+      di_[it] = sg.y;
+      dr_[it] = sg.z + b;
+    } else {
+      bad = 1;
+    }
+  }
+  if (bad) set_err(err, UEP_ERR_COVER);
+
+  // 5. store
+  if (kVec4) {
+#pragma unroll
+    for (int it = 0; it < kPer / 4; ++it) {
+      const int64_t j = p0 + 4 * ((int64_t)it * kRaThreads + tid);
+      if (j < p1) {
+        *reinterpret_cast<int4*>(dest_inst + rbase + j) =
+            make_int4(di_[4 * it], di_[4 * it + 1], di_[4 * it + 2], di_[4 * it + 3]);
+        *reinterpret_cast<int4*>(dest_row + rbase + j) =
+            make_int4(dr_[4 * it], dr_[4 * it + 1], dr_[4 * it + 2], dr_[4 * it + 3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int64_t j = p0 + (int64_t)it * kRaThreads + tid;
+      if (j < p1) {
+        dest_inst[rbase + j] = di_[it];
+        dest_row[rbase + j] = dr_[it];
+      }
+    }
+  }
 }
 
 static void rr_ws_layout(int R, int E, size_t* off_cnt, size_t* off_segs, size_t* total,
@@ -243,23 +346,33 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
                      xfer, inst_offset, seg_base, seg_cnt, segs, err, g);
   UEP_CHECK_LAUNCH();
   if (pairs) {
-    const int64_t j0 = (int64_t)r_begin * T * K, j1 = (int64_t)r_end * T * K;
     const bool vec = ((int64_t)T * K) % 4 == 0 &&
                      ((reinterpret_cast<uintptr_t>(topk_ids) | reinterpret_cast<uintptr_t>(bucket_pos) |
                        reinterpret_cast<uintptr_t>(dest_inst) | reinterpret_cast<uintptr_t>(dest_row)) %
                       16) == 0;
-    if (vec) {
-      const int64_t q0 = j0 / 4, q1 = j1 / 4;
-      const int64_t nb = (q1 - q0 + 255) / 256;
-      hipLaunchKernelGGL(rr_assign4, dim3((unsigned)nb), dim3(256), 0, s,
-                         reinterpret_cast<const int4*>(topk_ids),
-                         reinterpret_cast<const int4*>(bucket_pos), seg_base, seg_cnt, segs,
-                         reinterpret_cast<int4*>(dest_inst), reinterpret_cast<int4*>(dest_row), err,
-                         q0, q1, g);
+    // 8 pairs per thread when that still gives >= 512 workgroups, else 4
+    const int64_t pairs_all = (int64_t)T * K * (r_end - r_begin);
+    const int per = pairs_all >= 512ll * kRaThreads * 8 ? 8 : 4;
+    const int64_t chunks = ((int64_t)T * K + kRaThreads * per - 1) / (kRaThreads * per);
+    const dim3 grid((unsigned)chunks, (unsigned)(r_end - r_begin));
+    const size_t lds = sizeof(int4) * (size_t)g.I + 2 * sizeof(int32_t) * (size_t)E;
+    if (lds > kRaMaxLds) {
+      const int64_t j0 = (int64_t)r_begin * T * K, j1 = (int64_t)r_end * T * K;
+      hipLaunchKernelGGL(rr_assign_flat, dim3((unsigned)((j1 - j0 + 255) / 256)), dim3(256), 0, s,
+                         topk_ids, bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err,
+                         j0, j1, g);
+    } else if (vec && per == 8) {
+      hipLaunchKernelGGL((rr_assign<true, 8>), grid, dim3(kRaThreads), lds, s, topk_ids,
+                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
+    } else if (vec) {
+      hipLaunchKernelGGL((rr_assign<true, 4>), grid, dim3(kRaThreads), lds, s, topk_ids,
+                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
+    } else if (per == 8) {
+      hipLaunchKernelGGL((rr_assign<false, 8>), grid, dim3(kRaThreads), lds, s, topk_ids,
+                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
     } else {
-      const int64_t nb = (j1 - j0 + 255) / 256;
-      hipLaunchKernelGGL(rr_assign, dim3((unsigned)nb), dim3(256), 0, s, topk_ids, bucket_pos,
-                         seg_base, seg_cnt, segs, dest_inst, dest_row, err, j0, j1, g);
+      hipLaunchKernelGGL((rr_assign<false, 4>), grid, dim3(kRaThreads), lds, s, topk_ids,
+                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
     }
     UEP_CHECK_LAUNCH();
   }

@@ -5,10 +5,10 @@
 //
 // Expert loads are summed by the whole workgroup (LDS integer atomics, exact in any
 // order); the search is one wave64, lane r = rank r: L_r, free slots and the rank's
-// slot table live in registers, per-expert main quotas in LDS.  Each step is a handful of wave
-// DPP wave reductions + a ballot (argmax over ranks, argmin over receivers), so the whole
-// solve is a strictly sequential loop of at most E + 2R steps with no barrier
-// other than the wave itself.
+// slot table live in registers, per-expert main quotas in LDS.  A step is a few DPP
+// wave reductions (argmax over ranks, argmax over donors, argmin over receivers), so
+// the whole solve is a strictly sequential loop of at most E + 2R steps with no
+// barrier other than the wave itself.
 //
 // Step rule ("fill to the waterline", T* = ceil(sum_e c_e / R)): h = most loaded
 // rank (lowest index on ties); stop if L_h <= T*.  Donors are h's mains with a
@@ -24,7 +24,163 @@ namespace uep {
 constexpr int kSqMaxS = 8;
 constexpr int kSqThreads = 256;
 constexpr int kBig = 0x7fffffff;
+constexpr int kPackBits = 25;               // loads below 2^25 fit a (load, lane) key
 
+// Unsigned wave minimum (same DPP pattern as wave_reduce_dpp).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// One rank's search state, held by lane r (kS >= S slots in registers).
+template <int kS>
+struct SqLane {
+  int L;                 // current load of the rank
+  int sl_e[kS], sl_q[kS];
+  int free_slots;
+};
+
+template <int kS>
+__device__ __forceinline__ int slot_of(const SqLane<kS>& st, int S, int e) {
+  int has = -1;
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+    if (s < S && st.sl_e[s] == e) has = s;
+  return has;
+}
+
+template <int kS>
+__device__ __forceinline__ void add_to_slot(SqLane<kS>& st, int slot, int delta) {
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+    if (s == slot) st.sl_q[s] += delta;
+}
+
+template <int kS>
+__device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delta) {
+  const int slot = S - st.free_slots;
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+    if (s == slot) { st.sl_e[s] = e; st.sl_q[s] = delta; }
+  st.free_slots -= 1;
+}
+
+// The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
+// reduction give value and lowest lane together; top-up candidates (keys below
+// 2^31) sort before new-replica candidates, so one unsigned minimum picks the
+// receiver of either kind with the rule's precedence.
+template <int kS>
+__device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
+                                              int R, int E_loc, int S, int q_min, int t_star,
+                                              int& steps, int& n_rep, int& stuck) {
+  for (;;) {
+    const int kh = wave_max(active ? (st.L << 6) | (63 - lane) : -1);
+    const int Lh = kh >> 6;
+    if (Lh <= t_star) break;
+    const int h = 63 - (kh & 63);
+    const int over = Lh - t_star;
+    const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
+    bool tried = false, moved = false;
+    for (;;) {
+      // next donor: largest untried main quota on h, lowest expert id on ties
+      const int kd = wave_max((lane < E_loc && qj > 0 && !tried) ? (qj << 6) | (63 - lane) : -1);
+      if (kd < 0) break;
+      const int qd = kd >> 6, jd = 63 - (kd & 63);
+      const int e = h * E_loc + jd;
+      const int has = slot_of<kS>(st, S, e);
+      const bool below = active && lane != h && st.L < t_star;
+      const bool c1 = below && has >= 0;
+      const bool c2 = below && has < 0 && st.free_slots > 0;
+      const uint32_t key = c1   ? ((uint32_t)st.L << 6) | (uint32_t)lane
+                           : c2 ? 0x80000000u | ((uint32_t)st.L << 6) | (uint32_t)lane
+                                : 0xFFFFFFFFu;
+      const uint32_t km = wave_min_u32(key);
+      if (km != 0xFFFFFFFFu) {
+        const int tgt = (int)(km & 63u);
+        const int Lt = (int)((km >> 6) & ((1u << kPackBits) - 1));
+        const int delta = min(qd, min(over, t_star - Lt));
+        if (km < 0x80000000u) {                       // top up an existing replica
+          if (lane == tgt) { add_to_slot<kS>(st, has, delta); st.L += delta; }
+          if (lane == h) st.L -= delta;
+          if (lane == 0) q_main[e] = qd - delta;
+          moved = true;
+          break;
+        }
+        if (delta >= q_min) {                         // open a new replica
+          if (lane == tgt) { open_slot<kS>(st, S, e, delta); st.L += delta; }
+          if (lane == h) st.L -= delta;
+          if (lane == 0) q_main[e] = qd - delta;
+          ++n_rep;
+          moved = true;
+          break;
+        }
+      }
+      if (lane == jd) tried = true;
+    }
+    if (!moved) { stuck = 1; break; }
+    ++steps;
+  }
+}
+
+// The same rule for any load below 2^31: value reductions, then ballots.
+template <int kS>
+__device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
+                                            int R, int E_loc, int S, int q_min, int t_star,
+                                            int& steps, int& n_rep, int& stuck) {
+  for (;;) {
+    const int Lh = wave_max(active ? st.L : INT32_MIN);
+    if (Lh <= t_star) break;
+    const int h = first_lane(active && st.L == Lh);
+    const int over = Lh - t_star;
+    const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
+    bool tried = false, moved = false;
+    for (;;) {
+      const int dk = (lane < E_loc && qj > 0 && !tried) ? qj : -1;
+      const int qd = wave_max(dk);
+      if (qd <= 0) break;
+      const int jd = first_lane(dk == qd);
+      const int e = h * E_loc + jd;
+      const int has = slot_of<kS>(st, S, e);
+      const bool c1 = active && lane != h && has >= 0 && st.L < t_star;
+      const int kj = wave_min(c1 ? st.L : kBig);
+      if (kj != kBig) {
+        const int j = first_lane(c1 && st.L == kj);
+        const int delta = min(qd, min(over, t_star - kj));
+        if (lane == j) { add_to_slot<kS>(st, has, delta); st.L += delta; }
+        if (lane == h) st.L -= delta;
+        if (lane == 0) q_main[e] = qd - delta;
+        moved = true;
+        break;
+      }
+      const bool c2 = active && lane != h && st.free_slots > 0 && has < 0 && st.L < t_star;
+      const int kt = wave_min(c2 ? st.L : kBig);
+      if (kt != kBig) {
+        const int delta = min(qd, min(over, t_star - kt));
+        if (delta >= q_min) {
+          const int t = first_lane(c2 && st.L == kt);
+          if (lane == t) { open_slot<kS>(st, S, e, delta); st.L += delta; }
+          if (lane == h) st.L -= delta;
+          if (lane == 0) q_main[e] = qd - delta;
+          ++n_rep;
+          moved = true;
+          break;
+        }
+      }
+      if (lane == jd) tried = true;
+    }
+    if (!moved) { stuck = 1; break; }
+    ++steps;
+  }
+}
+
+template <int kS>
 __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
     const int32_t* __restrict__ counts, int R, int E, int S, int q_min,
     int32_t* __restrict__ slot_expert, int32_t* __restrict__ inst_expert,
@@ -58,79 +214,21 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
   int32_t* q_main = sq_lds;
   const int lane = tid;
   const bool active = lane < R;
-  int L = 0;
+  SqLane<kS> st;
+  st.L = 0;
   if (active)
-    for (int j = 0; j < E_loc; ++j) L += q_main[lane * E_loc + j];
-  int sl_e[kSqMaxS], sl_q[kSqMaxS];         // this rank's slots
+    for (int j = 0; j < E_loc; ++j) st.L += q_main[lane * E_loc + j];
 #pragma unroll
-  for (int s = 0; s < kSqMaxS; ++s) { sl_e[s] = -1; sl_q[s] = 0; }
-  int free_slots = active ? S : 0;
-  const int total = wave_sum(L);
+  for (int s = 0; s < kS; ++s) { st.sl_e[s] = -1; st.sl_q[s] = 0; }
+  st.free_slots = active ? S : 0;
+  const int total = wave_sum(st.L);
   const int t_star = (total + R - 1) / R;
 
   int steps = 0, n_rep = 0, stuck = 0;
-  for (;;) {
-    const int Lh = wave_max(active ? L : INT32_MIN);
-    if (Lh <= t_star) break;
-    const int h = first_lane(active && L == Lh);
-    const int over = Lh - t_star;
-    const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
-    bool tried = false, moved = false;
-    for (;;) {
-      // next donor: largest untried main quota on h, lowest expert id on ties
-      const int dk = (lane < E_loc && qj > 0 && !tried) ? qj : -1;
-      const int qd = wave_max(dk);
-      if (qd <= 0) break;
-      const int jd = first_lane(dk == qd);
-      const int e = h * E_loc + jd;
-      int has = -1;
-#pragma unroll
-      for (int s = 0; s < kSqMaxS; ++s)
-        if (s < S && sl_e[s] == e) has = s;
-      // top up an existing replica below the waterline
-      const bool c1 = active && lane != h && has >= 0 && L < t_star;
-      const int kj = wave_min(c1 ? L : kBig);
-      if (kj != kBig) {
-        const int j = first_lane(c1 && L == kj);
-        const int delta = min(qd, min(over, t_star - kj));
-        if (lane == j) {
-#pragma unroll
-          for (int s = 0; s < kSqMaxS; ++s)
-            if (s == has) sl_q[s] += delta;
-          L += delta;
-        }
-        if (lane == h) L -= delta;
-        if (lane == 0) q_main[e] = qd - delta;
-        moved = true;
-        break;
-      }
-      // open a new replica on the least loaded eligible rank
-      const bool c2 = active && lane != h && free_slots > 0 && has < 0 && L < t_star;
-      const int kt = wave_min(c2 ? L : kBig);
-      if (kt != kBig) {
-        const int delta = min(qd, min(over, t_star - kt));
-        if (delta >= q_min) {
-          const int t = first_lane(c2 && L == kt);
-          if (lane == t) {
-            const int slot = S - free_slots;
-#pragma unroll
-            for (int s = 0; s < kSqMaxS; ++s)
-              if (s == slot) { sl_e[s] = e; sl_q[s] = delta; }
-            free_slots -= 1;
-            L += delta;
-          }
-          if (lane == h) L -= delta;
-          if (lane == 0) q_main[e] = qd - delta;
-          ++n_rep;
-          moved = true;
-          break;
-        }
-      }
-      if (lane == jd) tried = true;
-    }
-    if (!moved) { stuck = 1; break; }
-    ++steps;
-  }
+  if (total < (1 << kPackBits))
+    search_packed<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+  else
+    search_wide<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
 
   const int ipr = E_loc + S;
   for (int i = lane; i < R * E_loc; i += kWave) {
@@ -140,13 +238,13 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
   }
   if (active) {
 #pragma unroll
-    for (int s = 0; s < kSqMaxS; ++s)
+    for (int s = 0; s < kS; ++s)
       if (s < S) {
-        inst_expert[lane * ipr + E_loc + s] = sl_e[s];
-        inst_quota[lane * ipr + E_loc + s] = sl_q[s];
-        slot_expert[lane * S + s] = sl_e[s];
+        inst_expert[lane * ipr + E_loc + s] = st.sl_e[s];
+        inst_quota[lane * ipr + E_loc + s] = st.sl_q[s];
+        slot_expert[lane * S + s] = st.sl_e[s];
       }
-    rank_load[lane] = L;
+    rank_load[lane] = st.L;
   }
   if (lane == 0) {
     stats[0] = n_rep;
@@ -178,8 +276,15 @@ extern "C" uep_status uep_solve_quota(const int32_t* counts, int32_t R, int32_t 
   if (!counts || !inst_expert || !inst_quota || !rank_load || !stats || (S > 0 && !slot_expert))
     return UEP_EINVAL;
   const size_t lds = sizeof(int32_t) * E;
-  hipLaunchKernelGGL(solve_quota_kernel, dim3(1), dim3(kSqThreads), lds, uep_stream(stream), counts, R, E,
-                     S, q_min, slot_expert, inst_expert, inst_quota, rank_load, stats);
+  hipStream_t st = uep_stream(stream);
+#define UEP_SQ_LAUNCH(KS)                                                                     \
+  hipLaunchKernelGGL(solve_quota_kernel<KS>, dim3(1), dim3(kSqThreads), lds, st, counts, R, E, \
+                     S, q_min, slot_expert, inst_expert, inst_quota, rank_load, stats)
+  if (S <= 1) UEP_SQ_LAUNCH(1);
+  else if (S <= 2) UEP_SQ_LAUNCH(2);
+  else if (S <= 4) UEP_SQ_LAUNCH(4);
+  else UEP_SQ_LAUNCH(8);
+#undef UEP_SQ_LAUNCH
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }

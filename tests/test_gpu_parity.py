@@ -134,6 +134,39 @@ def test_plan_edge_cases():
     assert (host(counts) == 0).all() and host(err)[0] == 0
 
 
+def test_plan_largest_geometry():
+    """E = 4096 experts on R = 64 ranks: the ballot-ranking load matrix and the
+    assignment kernel whose segment table does not fit in LDS."""
+    say("case: largest geometry R=64 E=4096")
+    rng = np.random.default_rng(21)
+    R, T, K, E = 64, 16, 4, 4096
+    p = rng.dirichlet(np.full(E, 0.05))
+    ids = random_routing(rng, R, T, K, E, p=p, empty_frac=0.01)
+    o = oracle_plan(ids, E, 1, 1)
+    assert o["plan"]["n_replicas"] > 0
+    compare_plan(plan_on_gpu(U, to_dev(ids), E, 1, 1), o, 1)
+
+
+@pytest.mark.parametrize("total", [(1 << 25) - 977, 1 << 27, (1 << 31) - 4096])
+def test_solve_quota_large_loads(total):
+    """The solver alone on synthetic load matrices whose total is just below the
+    packed-key limit (2^25), above it, and near the int32 limit."""
+    say("case: solve_quota total", total)
+    rng = np.random.default_rng(total % 1000)
+    R, E, S = 32, 128, 2
+    w = rng.dirichlet(np.full(R * E, 0.2))
+    counts = np.floor(w * total).astype(np.int64)
+    counts.flat[0] += total - counts.sum()
+    counts = counts.reshape(R, E).astype(np.int32)
+    q_min = total // 4000
+    o = O.solve_quota(counts, S, q_min)
+    g = U.solve_quota(to_dev(counts), S, q_min)
+    assert np.array_equal(host(g["inst_quota"]), o["inst_quota"])
+    assert np.array_equal(host(g["slot_expert"]), o["slot_expert"])
+    assert np.array_equal(host(g["rank_load"]), o["rank_load"])
+    assert host(g["stats"]).tolist() == [o["n_replicas"], o["n_steps"], o["t_star"], int(o["stuck"])]
+
+
 def test_content_errors_are_flagged():
     say("case: content errors")
     err = err_word()
