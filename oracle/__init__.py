@@ -21,6 +21,7 @@ the path itself fixes fp32).  Sources:
     - "共享专家融合作为启用机制" (shared-expert fusion)                     -> waterfill
     - "线性规划（LP）公式化构建", "决策变量与矩阵规模优化" (LP, variables)  -> lplb
     - "从LP解决方案到Token调度" (from LP to token dispatch)               -> lplb
+    - "背景知识与设计原则", "共享专家融合作为启用机制" (dispatch and combine) -> combine
 
 Parity status of each function (what pins it) is listed in the module headers.
 """
@@ -29,6 +30,7 @@ from .load_matrix import load_matrix, OracleInputError
 from .quota import solve_quota
 from .reroute import reroute, assign, identity_quota
 from .permute import permute, permute_rows
+from .combine import combine, combine_f32, combine_tokens, f32_to_bf16_bits, bf16_bits_to_f32
 from .stage import stage_forward, grad_reduce
 from .philox import philox4x64_10, philox4x64_10_np
 from .waterfill import waterfill, extend_topk
@@ -36,6 +38,7 @@ from .lplb import lplb_structure, lplb_lp, simplex, hamilton_quotas, lplb
 
 __all__ = [
     "load_matrix", "OracleInputError", "solve_quota", "reroute", "assign", "identity_quota",
-    "permute", "permute_rows", "stage_forward", "grad_reduce", "philox4x64_10", "philox4x64_10_np",
+    "permute", "permute_rows", "combine", "combine_f32", "combine_tokens", "f32_to_bf16_bits",
+    "bf16_bits_to_f32", "stage_forward", "grad_reduce", "philox4x64_10", "philox4x64_10_np",
     "waterfill", "extend_topk", "lplb_structure", "lplb_lp", "simplex", "hamilton_quotas", "lplb",
 ]
