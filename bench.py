@@ -200,6 +200,12 @@ def measured_traffic(workload):
         return None
 
 
+def combine_bytes(N, P, H):
+    """Algorithmic bytes of one whole-group combine: every dispatch row read once,
+    every token row written once, plus each pair's row index and weight."""
+    return N * H * 2 + P * H * 2 + P * 8
+
+
 def roofline(bytes_, ms, kernel, traffic=None):
     gbs = bytes_ / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
@@ -253,6 +259,32 @@ def timed_steps(torch, args, step, stream, timers=()):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / args.steps
+
+
+def combine_figures(torch, U, W, L, reps=5):
+    """Combine (the step after the experts: dispatch rows back to token order with the
+    router weights), timed outside the step: whole group event-timed, one rank's share
+    graph-replayed.  Its input here is the permuted buffer of the step."""
+    w = L.w
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 5))
+    gate = torch.rand(w.R, w.T, L.K, generator=gen, device=DEV)
+    y = torch.empty(w.R, w.T, w.H, dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.current_stream()
+    U.combine(L.out, L.drow, gate, y, stream=s)
+    torch.cuda.synchronize()
+    t = Timer(torch, reps)
+    for _ in range(reps):
+        t.start(s)
+        U.combine(L.out, L.drow, gate, y, stream=s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    rank_us = graph_us(torch, lambda st: U.combine(L.out, L.drow, gate, y, 0, 1, stream=st))
+    cb = combine_bytes(w.N, L.P, w.H)
+    del y, gate
+    torch.cuda.empty_cache()
+    return {"combine_ms": ms, "combine_gbs": cb / (ms * 1e-3) / 1e9,
+            "combine_frac": cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "combine_rank_us": rank_us}
 
 
 # ----------------------------------------------------------------------------- CPU leg
@@ -317,6 +349,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     perm_ms, stage_ms = tp.mean_ms(), ts.mean_ms()
     stage_bytes = 2 * n_used * w.expert_elems * 2
     copy = copy_reference(torch, U)
+    comb = combine_figures(torch, U, W, L)
     if args.roofline_only:
         out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32", {"ffn": list(w.ffn_shape)})
         out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
@@ -361,6 +394,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "imbalance_before": float(before.max() / before.mean()),
         "imbalance_after": float(rl.max() / rl.mean()),
         "device_copy_gbs": copy["gbs"],
+        **comb,
     }
     out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
     return out

@@ -188,6 +188,29 @@ uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, in
                        int32_t* row_src, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * uep_combine -- expert outputs from the dispatch buffer back to token order.
+ * [BLOG] section "背景知识与设计原则": DeepEP's combine brings each token's routed-
+ * expert outputs back after dispatch; section "共享专家融合作为启用机制": a fused
+ * shared slot is one more column of the same layout and goes through the same
+ * combine.  The pages do not write it out; this is the standard MoE output with the
+ * router weights as input:
+ *   y[r][t] = bf16( sum_k w[r][t][k] * out[dest_row[r][t][k]] ),  slots with row -1 skipped,
+ * each product and addition rounded to nearest even in fp32, k ascending from +0.0,
+ * no fused multiply-add, then nearest-even rounding to bf16 (a NaN stays a NaN).
+ *
+ *   out      [P][H] bf16 bits     in   dispatch buffer (layout of uep_permute's out),
+ *                                      16-byte aligned
+ *   dest_row [R][T][K]            in   from uep_reroute_assign
+ *   gate_w   [R][T][K] fp32       in   combine weights
+ *   r_begin, r_end                     only tokens of ranks in [r_begin, r_end) are written
+ *   y        [R][T][H] bf16 bits  out  16-byte aligned; other ranks' rows are untouched
+ * Returns UEP_EINVAL / UEP_EGEOM like uep_permute.
+ * ------------------------------------------------------------------------- */
+uep_status uep_combine(const uint16_t* out, const int32_t* dest_row, const float* gate_w,
+                       int32_t R, int32_t T, int32_t K, int32_t H, int32_t r_begin,
+                       int32_t r_end, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_stage_replica_weights -- redundant-slot weight staging / gradient reduction.
  * [UEP] section "共享冗余 slot 管理动态专家副本": each rank has S fixed redundant slots
  * (weights + gradient buffer, no optimizer state) shared by every MoE layer; the

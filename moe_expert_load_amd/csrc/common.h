@@ -102,6 +102,14 @@ __device__ __forceinline__ int column_sum(const int32_t* __restrict__ counts, in
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
+// Bijection of [0, nb) for HBM-streaming grids: workgroup b runs on XCD b % 8; that
+// XCD's workgroups take one contiguous range of logical block ids (the first nb % 8
+// XCDs one more), so neighbouring blocks share an L2.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
+  const int64_t q = nb / 8, rem = nb % 8, xcd = b % 8, idx = b / 8;
+  return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
+}
+
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {
   if (err) atomicOr(err, bits);
 }

@@ -24,13 +24,6 @@ constexpr int kPmThreads = 256;
 constexpr int kPmTokPerBlock = kPmThreads / kWave;
 constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
 
-// Bijection of [0, nb): block b runs on XCD b % 8; that XCD's blocks take one
-// contiguous range of logical block ids, the first nb % 8 XCDs one block more.
-__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
-  const int64_t q = nb / 8, rem = nb % 8, xcd = b % 8, idx = b / 8;
-  return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
-}
-
 template <bool kNT>
 __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ dest_row,

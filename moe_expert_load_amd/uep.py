@@ -42,6 +42,7 @@ SIGNATURES = {
     "uep_reroute_assign": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "uep_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "uep_stage_replica_weights": (_I, [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
     "uep_waterfill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U64, _U64, _I, _P, _P, _P, _P, _P, _P]),
     "uep_lplb_struct_size": (_SZ, [_I, _I, _I]),
@@ -178,6 +179,23 @@ def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None):
     _check(LIB.uep_permute(_p(x), _p(dest_row), R, T, K, H, r_begin, r_end, _p(out),
                            _p(row_src), _s(stream)), "uep_permute")
     return out, row_src
+
+
+def combine(out, dest_row, gate_w, y, r_begin=0, r_end=None, stream=None):
+    """out [P][H] 16-bit dispatch buffer; dest_row [R][T][K] int32; gate_w [R][T][K]
+    float32; y [R][T][H] 16-bit (rows of ranks in [r_begin, r_end) are written)."""
+    R, T, K = dest_row.shape
+    H = out.shape[1]
+    r_end = R if r_end is None else r_end
+    if out.element_size() != 2 or y.element_size() != 2:
+        raise TypeError("out and y must hold 16-bit elements")
+    if gate_w.dtype != torch.float32 or tuple(gate_w.shape) != (R, T, K):
+        raise TypeError("gate_w must be float32 [R][T][K]")
+    if tuple(y.shape) != (R, T, H):
+        raise TypeError("y must be [R][T][H]")
+    _check(LIB.uep_combine(_p(out), _p(dest_row), _p(gate_w), R, T, K, H, r_begin, r_end, _p(y),
+                           _s(stream)), "uep_combine")
+    return y
 
 
 def device_copy(src, dst, stream=None):

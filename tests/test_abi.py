@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ("uep_load_matrix", "uep_solve_quota", "uep_reroute_assign", "uep_permute",
-              "uep_stage_replica_weights", "uep_waterfill", "uep_lplb"):
+              "uep_stage_replica_weights", "uep_waterfill", "uep_lplb", "uep_combine"):
         assert n in names
 
 
@@ -73,6 +73,12 @@ def test_host_side_calls_without_gpu(lib):
     assert lib.uep_lplb_prepare(null, i32(2), i32(2), i32(2), null, ctypes.c_size_t(0), null) == 1
     assert lib.uep_stage_replica_weights(i32(0), i32(4), i32(8), i32(9), null, i32(0), i32(4), null,
                                          null, null, null, ctypes.c_int64(8), null) == 2
+    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2),
+                           null, null) == 2
+    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3),
+                           null, null) == 1
+    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(16), i32(0), i32(2),
+                           null, null) == 1
     i64 = ctypes.c_int64
     assert lib.uep_device_copy(null, null, i64(0), null) == 0
     assert lib.uep_device_copy(null, null, i64(-16), null) == 1

@@ -1,0 +1,124 @@
+"""GPU parity of uep_combine (weighted un-permute to token order) against the oracle:
+bit-exact bf16 outputs on the same seeded inputs; dispatch rows come from the
+oracle's own plan."""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle as O                                       # noqa: E402
+from moe_expert_load_amd import uep as U                 # noqa: E402
+from moe_expert_load_amd import workload as W            # noqa: E402
+from tests.gpu_helpers import DEV, to_dev, host, say, random_routing  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_dest_row(ids, E, S, q_min):
+    counts, bp = O.load_matrix(ids, E)
+    plan = O.solve_quota(counts, S, q_min)
+    X, io, so = O.reroute(counts, plan["inst_expert"], plan["inst_quota"], plan["inst_per_rank"])
+    _, dr = O.assign(ids, bp, X, plan["inst_expert"], plan["inst_per_rank"], io, so)
+    return dr
+
+
+def bits(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def random_case(seed, R, T, K, E, H, empty, S=1, q_min=2):
+    rng = np.random.default_rng(seed)
+    ids = random_routing(rng, R, T, K, E, empty_frac=empty)
+    dr = oracle_dest_row(ids, E, S, q_min)
+    P = max(int((dr >= 0).sum()), 1)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    y_disp = torch.randn(P, H, generator=g, device=DEV).to(torch.bfloat16)
+    w = rng.random((R, T, K)).astype(np.float32) * 2 - 0.5
+    return dr, y_disp, w
+
+
+@pytest.mark.parametrize("seed,R,T,K,E,H,empty", [
+    (0, 4, 512, 2, 8, 256, 0.0),          # tiny shape
+    (1, 3, 97, 3, 9, 8 * 300, 0.1),       # K % 4 != 0, ragged slices
+    (2, 2, 40, 5, 10, 7168, 0.2),         # 14 KiB rows (two slices), empty slots
+    (3, 5, 33, 9, 15, 1032, 0.05),        # K = 9 (fused shared column), odd row length
+    (4, 1, 64, 1, 1, 64, 0.3),            # one rank, one expert
+])
+def test_combine_random(seed, R, T, K, E, H, empty):
+    say("case: combine", seed, R, T, K, E, H, empty)
+    dr, y_disp, w = random_case(seed, R, T, K, E, H, empty)
+    y = torch.full((R, T, H), 77, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    U.combine(y_disp, to_dev(dr), to_dev(w, torch.float32), y)
+    exp = O.combine(bits(y_disp), dr, w)
+    assert np.array_equal(bits(y), exp)
+
+
+def test_combine_rank_range_and_noops():
+    say("case: combine rank ranges")
+    R, T, K, E, H = 4, 50, 4, 8, 512
+    dr, y_disp, w = random_case(7, R, T, K, E, H, 0.1)
+    exp = O.combine(bits(y_disp), dr, w)
+    fill = torch.full((R, T, H), 77, dtype=torch.int16, device=DEV)
+    y = fill.clone().view(torch.bfloat16)
+    U.combine(y_disp, to_dev(dr), to_dev(w, torch.float32), y, r_begin=1, r_end=3)
+    got = bits(y)
+    assert np.array_equal(got[1:3], exp[1:3])
+    assert (got[[0, 3]] == 77).all()                            # untouched
+    U.combine(y_disp, to_dev(dr), to_dev(w, torch.float32), y, r_begin=2, r_end=2)
+    assert np.array_equal(bits(y), got)                         # empty range: no-op
+    # every slot empty: +0.0 everywhere
+    none = np.full((R, T, K), -1, dtype=np.int32)
+    U.combine(y_disp, to_dev(none), to_dev(w, torch.float32), y)
+    assert (bits(y) == 0).all()
+
+
+def test_combine_inverts_permute_with_one_hot_weights():
+    """permute then combine with weight 1 on one live slot (0 elsewhere) returns x bit
+    for bit, at the Tiny shape through the device plan and permute."""
+    w_ = W.TINY
+    say("case: permute/combine round trip", w_)
+    ids = W.routing(w_)
+    dr = oracle_dest_row(ids, w_.E, w_.S, w_.q_min)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn(w_.R, w_.T, w_.H, generator=g, device=DEV).to(torch.bfloat16)
+    P = int((dr >= 0).sum())
+    out = torch.empty(P, w_.H, dtype=torch.bfloat16, device=DEV)
+    dr_d = to_dev(dr)
+    U.permute(x, dr_d, out)
+    rng = np.random.default_rng(5)
+    onehot = np.zeros(dr.shape, dtype=np.float32)
+    onehot[np.arange(w_.R)[:, None], np.arange(w_.T)[None, :], rng.integers(0, w_.K, (w_.R, w_.T))] = 1
+    y = torch.empty_like(x)
+    U.combine(out, dr_d, to_dev(onehot, torch.float32), y)
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
+def test_combine_qwen_layer_full_size():
+    """Qwen3-235B-shaped layer, whole group: 16 GiB dispatch buffer in, 2 GiB out;
+    compared on sampled tokens (and every token of one rank's first 512)."""
+    w_ = W.QWEN_LAYER
+    say("case: combine qwen full size", w_)
+    ids = W.routing(w_)
+    dr = oracle_dest_row(ids, w_.E, w_.S, w_.q_min)
+    g = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w_, 0, 4))
+    y_disp = torch.randn(w_.P, w_.H, generator=g, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(9)
+    gate = rng.dirichlet(np.ones(w_.K), size=(w_.R, w_.T)).astype(np.float32)
+    y = torch.empty(w_.R, w_.T, w_.H, dtype=torch.bfloat16, device=DEV)
+    U.combine(y_disp, to_dev(dr), to_dev(gate, torch.float32), y)
+    torch.cuda.synchronize()
+    tok = np.unique(np.concatenate([rng.integers(0, w_.N, 1500), np.arange(512) + 17 * w_.T,
+                                    [0, w_.N - 1]]))
+    rows = np.unique(dr.reshape(w_.N, w_.K)[tok].reshape(-1))
+    rows = rows[rows >= 0]
+    # host copy of only the dispatch rows the sampled tokens read
+    sub = bits(y_disp[torch.from_numpy(rows).to(DEV)])
+    remap = np.full(w_.P, -1, dtype=np.int64)
+    remap[rows] = np.arange(len(rows))
+    d_small = np.where(dr >= 0, remap[np.maximum(dr, 0)], -1).astype(np.int32)
+    exp = O.combine_tokens(sub, d_small, gate, tok)
+    got = bits(y.view(w_.N, w_.H)[torch.from_numpy(tok).to(DEV)])
+    assert np.array_equal(got, exp)
