@@ -247,7 +247,8 @@ uep_status uep_stage_replica_weights(int32_t mode, int32_t R, int32_t E, int32_t
  * shared slot goes to a candidate rank sampled in proportion to slack with a small
  * local preference; with zero slack everywhere, a clearly lighter candidate, else
  * the local rank.  Section "通信权衡与模式选择": candidates are the ranks the token
- * already visits plus its own rank.
+ * already visits plus its own rank (all_ranks = 0), or every rank of the EP group in
+ * the all-rank mode (all_ranks != 0).
  * Constants: weights (2^p + 1) * S_r0 for the source rank r0 and 2^p * S_c for the
  * others (p = local_pref_shift, 0..8); draw = word 0 of Philox4x64-10 with counter
  * (r0*T + t, 0, 0, 0) and key (seed, layer), v = floor(draw * W / 2^64); the first
@@ -266,8 +267,8 @@ uep_status uep_stage_replica_weights(int32_t mode, int32_t R, int32_t E, int32_t
 uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
                          const int32_t* batch_size, int32_t R, int32_t T, int32_t K,
                          int32_t E, uint64_t seed, uint64_t layer, int32_t local_pref_shift,
-                         int32_t* shared_rank, int32_t* waterline, int32_t* slack,
-                         int32_t* rank_load, int32_t* ext_topk, void* stream);
+                         int32_t all_ranks, int32_t* shared_rank, int32_t* waterline,
+                         int32_t* slack, int32_t* rank_load, int32_t* ext_topk, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * LPLB -- min-max split of replicated experts' load over their copies.

@@ -3,8 +3,8 @@
 // H = ceil((sum_r L_r + N) / R), slack S_r = max(H - L_r, 0), per-token sampling in
 // proportion to slack with a small local preference, zero-slack fallback to a
 // clearly lighter candidate; section "通信权衡与模式选择": candidates are the ranks
-// the token already visits plus its own; section "共享专家融合作为启用机制": the
-// top-k output gains one column for the shared expert).
+// the token already visits plus its own, or every rank in the all-rank mode; section
+// "共享专家融合作为启用机制": the top-k output gains one column for the shared expert).
 //
 // wf_prologue: one workgroup turns the load matrix into L_r, H and S_r.
 // wf_sample: one thread per token.  The candidate set is a 64-bit mask of visited
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids
                                                  const int32_t* __restrict__ slack,
                                                  const int32_t* __restrict__ rank_load, int R,
                                                  int T, int K, int E, uint64_t seed,
-                                                 uint64_t layer, int shift,
+                                                 uint64_t layer, int shift, int all_ranks,
                                                  int32_t* __restrict__ shared_rank,
                                                  int32_t* __restrict__ ext) {
   __shared__ int32_t s_S[64], s_L[64], s_B[64];
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids
     if (e >= 0 && e < E) visited |= 1ull << (e / E_loc);
   }
   if (t < s_B[r0]) {
+    if (all_ranks) visited = R == 64 ? ~0ull : (1ull << R) - 1;
     visited &= ~(1ull << r0);
     const int64_t big = 1ll << shift;
     const int64_t w0 = (big + 1) * s_S[r0];
@@ -139,7 +140,8 @@ using namespace uep;
 extern "C" uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
                                     const int32_t* batch_size, int32_t R, int32_t T, int32_t K,
                                     int32_t E, uint64_t seed, uint64_t layer,
-                                    int32_t local_pref_shift, int32_t* shared_rank,
+                                    int32_t local_pref_shift, int32_t all_ranks,
+                                    int32_t* shared_rank,
                                     int32_t* waterline, int32_t* slack, int32_t* rank_load,
                                     int32_t* ext_topk, void* stream) {
   if (R <= 0 || T < 0 || K <= 0 || E <= 0) return UEP_EINVAL;
@@ -156,7 +158,7 @@ extern "C" uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_i
     const int64_t n = (int64_t)R * T;
     hipLaunchKernelGGL(wf_sample, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, topk_ids,
                        batch_size, slack, rank_load, R, T, K, E, seed, layer, local_pref_shift,
-                       shared_rank, ext_topk);
+                       all_ranks ? 1 : 0, shared_rank, ext_topk);
     UEP_CHECK_LAUNCH();
   }
   return UEP_OK;

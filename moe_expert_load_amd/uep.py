@@ -44,7 +44,8 @@ SIGNATURES = {
     "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "uep_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "uep_stage_replica_weights": (_I, [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
-    "uep_waterfill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U64, _U64, _I, _P, _P, _P, _P, _P, _P]),
+    "uep_waterfill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U64, _U64, _I, _I, _P, _P, _P, _P, _P,
+                           _P]),
     "uep_lplb_struct_size": (_SZ, [_I, _I, _I]),
     "uep_lplb_prepare": (_I, [_P, _I, _I, _I, _P, _SZ, _P]),
     "uep_lplb": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P]),
@@ -218,7 +219,7 @@ def stage_replica_weights(mode, R, E, S, slot_expert, expert_elems, main_w=None,
 
 def waterfill(counts, topk_ids, batch_size, seed, layer, local_pref_shift=4, shared_rank=None,
               waterline=None, slack=None, rank_load=None, ext_topk=None, want_ext=True,
-              stream=None):
+              stream=None, all_ranks=False):
     R, E = counts.shape
     _, T, K = topk_ids.shape
     shared_rank = _new((R, T), counts) if shared_rank is None else shared_rank
@@ -230,7 +231,7 @@ def waterfill(counts, topk_ids, batch_size, seed, layer, local_pref_shift=4, sha
     _check(LIB.uep_waterfill(_p(counts), _p(topk_ids), _p(batch_size), R, T, K, E,
                              ctypes.c_uint64(seed & (2 ** 64 - 1)),
                              ctypes.c_uint64(layer & (2 ** 64 - 1)), local_pref_shift,
-                             _p(shared_rank), _p(waterline), _p(slack), _p(rank_load),
+                             1 if all_ranks else 0, _p(shared_rank), _p(waterline), _p(slack), _p(rank_load),
                              _p(ext_topk), _s(stream)), "uep_waterfill")
     return shared_rank, waterline, slack, rank_load, ext_topk
 

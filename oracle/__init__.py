@@ -34,11 +34,12 @@ from .combine import combine, combine_f32, combine_tokens, f32_to_bf16_bits, bf1
 from .stage import stage_forward, grad_reduce
 from .philox import philox4x64_10, philox4x64_10_np
 from .waterfill import waterfill, extend_topk
-from .lplb import lplb_structure, lplb_lp, simplex, hamilton_quotas, lplb
+from .lplb import lplb_structure, lplb_lp, simplex, hamilton_quotas, lplb, lplb_sample
 
 __all__ = [
     "load_matrix", "OracleInputError", "solve_quota", "reroute", "assign", "identity_quota",
     "permute", "permute_rows", "combine", "combine_f32", "combine_tokens", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "stage_forward", "grad_reduce", "philox4x64_10", "philox4x64_10_np",
     "waterfill", "extend_topk", "lplb_structure", "lplb_lp", "simplex", "hamilton_quotas", "lplb",
+    "lplb_sample",
 ]

@@ -26,9 +26,17 @@ Solver: a dense two-phase primal simplex in fp64 with Bland's rule (no cycling).
 Pins: scipy's HiGHS, the max-flow/min-cut closed form
 M* = max over rank sets T of (sum_{r in T} F_r + sum_{e: all copies in T} c_e) / |T|
 on small R, red0 -> M* = max_r F_r, one expert split over two empty ranks -> c/2.
+
+lplb_sample is the per-token variant of the same section "从LP解决方案到Token调度"
+(each token draws a copy from the normalised split; see its docstring for the
+readings).  Pins: Philox against numpy (full counters), the draw frequencies within
+4 sigma of w_p / W, W = 0 -> uniform over copies, a zero-weight copy never drawn,
+single-copy experts and empty slots mapped deterministically.
 """
 
 import numpy as np
+
+from .philox import philox4x64_10_np
 
 
 def lplb_structure(inst_expert, inst_per_rank: int, E: int) -> dict:
@@ -215,3 +223,62 @@ def lplb(counts, inst_expert, inst_per_rank: int):
         inst_quota[i] = qc[p]
     return {"m_star": m_star, "x": x, "inst_quota": inst_quota, "F": F, "c": c,
             "structure": st, "groups": groups}
+
+
+def lplb_sample(topk_ids, inst_expert, inst_per_rank: int, E: int, x, seed: int, layer: int,
+                ranks=None):
+    """LPLB's dispatch-time copy draw (blog section "从LP解决方案到Token调度"): the LP
+    split, normalised per replicated expert, is a probability distribution over its
+    physical copies; every token routed to a replicated expert draws one copy from it,
+    and a single-copy expert maps to its only instance.
+
+    Readings: the distribution is taken on the integer weights w_p = rint(max(x_p, 0) *
+    256) of the quota step (exact on both sides); the draw for slot k of global token
+    g is word 0 u of Philox4x64-10 at counter (g, k, 1, 0), key (seed, layer);
+    v = floor(u * W / 2^64) with W = sum w_p, and the first copy (instance order) whose
+    running weight exceeds v wins; with W = 0 the copy floor(u * n / 2^64) of the n
+    copies.  x is indexed like lplb_structure's copies (replicated experts ascending,
+    each expert's copies in instance order).
+
+    Returns dest_inst [R][T][K] int64 (-1 for empty slots; ranks outside ``ranks``,
+    if given, stay -1)."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    R, T, K = ids.shape
+    st = lplb_structure(inst_expert, inst_per_rank, E)
+    x = np.asarray(x)
+    copies_of = {}
+    for g_, e in enumerate(st["replicated"]):
+        idx = np.nonzero(st["copy_group"] == g_)[0]
+        w = [int(np.rint(np.float64(max(x[p], 0)) * 256.0)) for p in idx]
+        copies_of[e] = ([int(st["copy_inst"][p]) for p in idx], w)
+    out = np.full((R, T, K), -1, dtype=np.int64)
+    for r in (range(R) if ranks is None else ranks):
+        g = np.arange(r * T, (r + 1) * T, dtype=np.uint64)
+        u = [philox4x64_10_np(g, (seed, layer), c1=k, c2=1)[:, 0] for k in range(K)]
+        for t in range(T):
+            for k in range(K):
+                e = int(ids[r, t, k])
+                if e < 0:
+                    continue
+                if e >= E:
+                    raise ValueError("expert id out of range")
+                lst = st["copies"][e]
+                if len(lst) == 0:
+                    raise ValueError("an expert with load has no instance")
+                if len(lst) == 1:
+                    out[r, t, k] = lst[0]
+                    continue
+                inst, w = copies_of[e]
+                W = sum(w)
+                uu = int(u[k][t])
+                if W == 0:
+                    out[r, t, k] = inst[(uu * len(inst)) >> 64]
+                    continue
+                v = (uu * W) >> 64
+                run = 0
+                for i, wi in zip(inst, w):
+                    run += wi
+                    if run > v:
+                        out[r, t, k] = i
+                        break
+    return out

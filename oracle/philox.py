@@ -5,7 +5,9 @@ Published definition: J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
 4x64 multipliers and Weyl key increments given there.  Waterfill samples the shared
 expert's rank at random (Waterfill/LPLB blog, section "Waterfill算法执行步骤"); the
 pages name no generator, so this counter-based one is the reading (one draw per
-token, counter = (token, 0, 0, 0), key = (seed, layer)).
+token, counter = (token, 0, 0, 0), key = (seed, layer)).  LPLB's dispatch-time copy
+draw (blog section "从LP解决方案到Token调度") uses counter (token, slot, 1, 0), the
+same key.
 
 Pins: numpy.random.Philox (an independent implementation of the same generator)
 at many counters and keys, and the scalar and vectorised forms against each other.
@@ -46,12 +48,13 @@ def _mulhilo(a: np.ndarray, m: int):
     return hi, lo
 
 
-def philox4x64_10_np(c0: np.ndarray, key) -> np.ndarray:
-    """Word 0..3 for counters (c0[i], 0, 0, 0); returns uint64 [n][4]."""
+def philox4x64_10_np(c0: np.ndarray, key, c1=0, c2=0, c3=0) -> np.ndarray:
+    """Word 0..3 for counters (c0[i], c1[i], c2[i], c3[i]) (c1..c3 arrays or scalars,
+    default 0); returns uint64 [n][4]."""
     c0 = np.asarray(c0, dtype=np.uint64)
-    c1 = np.zeros_like(c0)
-    c2 = np.zeros_like(c0)
-    c3 = np.zeros_like(c0)
+    c1 = np.broadcast_to(np.asarray(c1, dtype=np.uint64), c0.shape).copy()
+    c2 = np.broadcast_to(np.asarray(c2, dtype=np.uint64), c0.shape).copy()
+    c3 = np.broadcast_to(np.asarray(c3, dtype=np.uint64), c0.shape).copy()
     k0, k1 = int(key[0]) & _MASK, int(key[1]) & _MASK
     with np.errstate(over="ignore"):
         for _ in range(10):

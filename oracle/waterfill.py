@@ -12,7 +12,9 @@ Waterfill/LPLB blog, section "Waterfill算法执行步骤" (Waterfill steps):
    if every candidate has zero slack, fall back to a clearly lighter candidate, again
    preferring the local rank.
 Section "通信权衡与模式选择": the communication-conservative candidates are the ranks
-the token already visits for its routed experts, with its source rank as fallback.
+the token already visits for its routed experts, with its source rank as fallback;
+the all-rank mode lets every EP rank take the shared slot (more freedom to balance,
+possibly one more destination per token).
 Section "共享专家融合作为启用机制": the top-k output gains one extra column for the
 shared expert and every rank keeps one shared-expert slot beside its routed experts.
 
@@ -20,8 +22,8 @@ Readings (the page gives no constants):
 * L_r = routed pairs whose expert is homed on r (home(e) = e // (E/R)); the local batch
   sizes B_r enter only through N = sum_r B_r (adding them to L_r too would count the
   shared slots twice);
-* candidates = the deduplicated set {home(e_k)} plus the source rank r0, in the order
-  r0 first, then the others ascending;
+* candidates = the deduplicated set {home(e_k)} plus the source rank r0 (all-rank
+  mode: every rank), in the order r0 first, then the others ascending;
 * weights: 2^p * S_c for c != r0 and (2^p + 1) * S_r0 for the source (p = 4: a 1/16 bonus);
 * with W = sum of weights > 0: u = word 0 of Philox4x64-10(counter = (g, 0, 0, 0),
   key = (seed, layer)) for the global token index g = r0*T + t; v = floor(u * W / 2^64);
@@ -32,7 +34,9 @@ Readings (the page gives no constants):
 * tokens t >= B_r0 are absent: shared rank -1.
 
 Pins: H and S_r closed form, sum_r S_r >= N, candidate set {r0} -> r0, the zero-slack
-fallback on hand-made cases, the sampled distribution within 4 sigma of the weights.
+fallback on hand-made cases, the sampled distribution within 4 sigma of the weights;
+all-rank mode without the local bonus: each rank's share of the shared slots within
+4 sigma of N * S_r / sum S, so the expected load L_r + shared_r stays at or below H.
 """
 
 import numpy as np
@@ -40,8 +44,12 @@ import numpy as np
 from .philox import philox4x64_10_np
 
 
-def waterfill(counts, topk_ids, batch_size, seed: int, layer: int, local_pref_shift: int = 4):
-    """Returns (shared_rank [R][T] int64, H, S [R] int64, L [R] int64)."""
+def waterfill(counts, topk_ids, batch_size, seed: int, layer: int, local_pref_shift: int = 4,
+              all_ranks: bool = False, ranks=None):
+    """Returns (shared_rank [R][T] int64, H, S [R] int64, L [R] int64).
+
+    ``ranks`` limits the per-token draws to those source ranks (others stay -1);
+    H, S and L always cover the whole group."""
     counts = np.asarray(counts, dtype=np.int64)
     ids = np.asarray(topk_ids, dtype=np.int64)
     B = np.asarray(batch_size, dtype=np.int64)
@@ -61,9 +69,12 @@ def waterfill(counts, topk_ids, batch_size, seed: int, layer: int, local_pref_sh
     g = np.arange(R * T, dtype=np.uint64)
     u_all = philox4x64_10_np(g, (seed, layer))[:, 0]
     shared = np.full((R, T), -1, dtype=np.int64)
-    for r0 in range(R):
+    for r0 in (range(R) if ranks is None else ranks):
         for t in range(int(B[r0])):
-            visited = sorted(set(int(e) // E_loc for e in ids[r0, t] if e >= 0) - {r0})
+            if all_ranks:
+                visited = [c_ for c_ in range(R) if c_ != r0]
+            else:
+                visited = sorted(set(int(e) // E_loc for e in ids[r0, t] if e >= 0) - {r0})
             cands = [r0] + visited
             w = [(big + 1) * int(S[r0])] + [big * int(S[c_]) for c_ in visited]
             W = sum(w)

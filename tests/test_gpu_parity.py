@@ -306,6 +306,11 @@ def test_waterfill_layer_full_size():
     assert np.array_equal(host(sh), sh_o)
     ext_o = O.extend_topk(ids, sh_o, w.E)
     assert np.array_equal(host(ext), ext_o)
+    # all-rank mode, three source ranks compared
+    some = [0, 17, w.R - 1]
+    sh_a, *_ = O.waterfill(counts_o, ids, B, seed, 0, all_ranks=True, ranks=some)
+    sh_g, *_ = U.waterfill(counts, ids_d, to_dev(B), seed, 0, all_ranks=True, want_ext=False)
+    assert np.array_equal(host(sh_g)[some], sh_a[some])
     E2 = w.E + w.R
     ipr = w.E_loc + 1
     inst = np.full(w.R * ipr, -1, dtype=np.int32)
@@ -351,9 +356,9 @@ def test_waterfill_random_small(seed):
     ids = random_routing(rng, R, T, K, E, empty_frac=0.05)
     B = rng.integers(0, T + 1, R).astype(np.int32)
     counts_o, _ = O.load_matrix(ids, E)
-    for shift in (0, 4):
-        sh_o, H_o, S_o, L_o = O.waterfill(counts_o, ids, B, 12345 + seed, 7, shift)
+    for shift, mode in ((0, False), (4, False), (0, True), (4, True)):
+        sh_o, H_o, S_o, L_o = O.waterfill(counts_o, ids, B, 12345 + seed, 7, shift, all_ranks=mode)
         sh, wl, sl, rl, ext = U.waterfill(to_dev(counts_o), to_dev(ids), to_dev(B), 12345 + seed, 7,
-                                          local_pref_shift=shift)
+                                          local_pref_shift=shift, all_ranks=mode)
         assert host(wl)[0] == H_o and np.array_equal(host(sl), S_o)
         assert np.array_equal(host(sh), sh_o)

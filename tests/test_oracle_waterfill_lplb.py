@@ -32,6 +32,20 @@ def test_philox_matches_numpy(key):
         assert tuple(int(v) for v in vec[n]) == O.philox4x64_10((int(gi), 0, 0, 0), key)
 
 
+@pytest.mark.parametrize("key", [(3, 5), (MASK, 0)])
+def test_philox_full_counters_match_numpy(key):
+    """All four counter words (the LPLB draw uses (g, k, 1, 0)): numpy's Philox started
+    at counter (g - 1, w1, w2, w3) outputs the block at (g, w1, w2, w3)."""
+    cases = [(1, 0, 1, 0), (77, 5, 1, 0), (2 ** 40, 63, 1, 0), (9, 2 ** 63, 7, 2 ** 50)]
+    for g, w1, w2, w3 in cases:
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                              counter=np.array([g - 1, w1, w2, w3], dtype=np.uint64))
+        want = tuple(int(bg.random_raw()) for _ in range(4))
+        assert O.philox4x64_10((g, w1, w2, w3), key) == want
+        vec = O.philox4x64_10_np(np.array([g], dtype=np.uint64), key, c1=w1, c2=w2, c3=w3)
+        assert tuple(int(v) for v in vec[0]) == want
+
+
 # ---------------------------------------------------------------- Waterfill
 
 def test_waterfill_closed_form():
@@ -94,6 +108,39 @@ def test_waterfill_sampling_distribution():
     got = np.array([(sh[r0] == c).sum() for c in (3, 1, 2)])
     sigma = np.sqrt(T * p * (1 - p))
     assert (np.abs(got - T * p) <= 4 * sigma + 1).all()
+
+
+def test_waterfill_all_rank_mode_without_bonus_follows_slack():
+    """All-rank mode with no local bonus (shift 0): every token draws its shared rank
+    with probability S_r / sum S, whatever it visits, so each rank's count lies within
+    4 sigma of N S_r / sum S and the expected load L_r + N S_r / sum S is <= H."""
+    R, E, T = 6, 12, 6000
+    rng = np.random.default_rng(4)
+    counts = np.zeros((R, E), dtype=np.int64)
+    counts[0] = rng.integers(0, 4000, E)
+    ids = np.zeros((R, T, 1), dtype=np.int64)        # every token visits rank 0 only
+    B = np.full(R, T)
+    sh, H, S, L = O.waterfill(counts, ids, B, seed=3, layer=5, local_pref_shift=0,
+                              all_ranks=True)
+    N = R * T
+    p = S / S.sum()
+    got = np.array([(sh == r).sum() for r in range(R)])
+    sigma = np.sqrt(N * p * (1 - p))
+    assert (np.abs(got - N * p) <= 4 * sigma + 1).all()
+    assert (L + N * p <= H + 1e-9).all()
+    # the conservative mode keeps these tokens on {r0, 0}
+    sh_c, *_ = O.waterfill(counts, ids, B, seed=3, layer=5, local_pref_shift=0)
+    for r0 in range(R):
+        assert set(np.unique(sh_c[r0])) <= {r0, 0}
+
+
+def test_waterfill_all_rank_mode_single_rank_candidates():
+    """With R = 1 both modes reduce to the source rank."""
+    counts = np.array([[5, 7]])
+    ids = np.array([[[0, 1], [1, -1]]])
+    for mode in (False, True):
+        sh, H, S, L = O.waterfill(counts, ids, np.array([2]), seed=1, layer=0, all_ranks=mode)
+        assert sh.tolist() == [[0, 0]]
 
 
 def test_waterfill_extend_topk():
@@ -226,3 +273,66 @@ def test_lplb_layer_matches_highs():
     hi = linprog(cost, A_eq=A, b_eq=b, bounds=(0, None), method="highs")
     assert res["m_star"] == pytest.approx(hi.fun, rel=1e-9)
     _check_lplb_solution(res, counts, inst, w.E_loc + 1)
+
+
+# ---------------------------------------------------------------- LPLB per-token draw
+
+def _two_copy_table():
+    # R = 4, E = 8 (2 mains per rank), one redundant slot per rank: expert 0 has
+    # replicas on ranks 1 and 3, expert 5 one on rank 0
+    ipr = 3
+    inst = np.full(4 * ipr, -1, dtype=np.int64)
+    for r in range(4):
+        inst[r * ipr:r * ipr + 2] = [2 * r, 2 * r + 1]
+    inst[1 * ipr + 2] = 0
+    inst[3 * ipr + 2] = 0
+    inst[0 * ipr + 2] = 5
+    return inst, ipr
+
+
+def test_lplb_sample_frequencies_follow_the_split():
+    inst, ipr = _two_copy_table()
+    st = O.lplb_structure(inst, ipr, 8)
+    assert st["replicated"] == [0, 5]
+    # copies in order: expert 0 -> instances 0, 5, 11; expert 5 -> instances 2, 7
+    x = np.array([100.0, 300.0, 600.0, 0.25, 0.0], dtype=np.float32)
+    R, T = 4, 20000
+    ids = np.zeros((R, T, 2), dtype=np.int64)
+    ids[:, :, 1] = 5
+    ids[:, :5, 1] = -1
+    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=11, layer=2)
+    assert (out[:, :5, 1] == -1).all()
+    # expert 5: the copy with x = 0 (instance 7) is never drawn
+    assert set(np.unique(out[:, 5:, 1])) == {2}
+    got = np.array([(out[:, :, 0] == i).sum() for i in (0, 5, 11)])
+    p = np.array([100, 300, 600], dtype=np.float64) / 1000
+    n = R * T
+    sigma = np.sqrt(n * p * (1 - p))
+    assert (np.abs(got - n * p) <= 4 * sigma + 1).all()
+
+
+def test_lplb_sample_zero_weights_uniform_and_single_copies():
+    inst, ipr = _two_copy_table()
+    x = np.zeros(5, dtype=np.float32)
+    R, T = 4, 9000
+    ids = np.zeros((R, T, 2), dtype=np.int64)
+    ids[:, :, 1] = 3                       # single-copy expert 3 -> its main, instance 4
+    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=1, layer=0)
+    assert (out[:, :, 1] == 4).all()
+    got = np.array([(out[:, :, 0] == i).sum() for i in (0, 5, 11)])
+    n, p = R * T, 1 / 3
+    assert (np.abs(got - n * p) <= 4 * np.sqrt(n * p * (1 - p)) + 1).all()
+
+
+def test_lplb_sample_draw_is_the_published_generator():
+    """The copy of one pair, recomputed by hand from the scalar Philox."""
+    inst, ipr = _two_copy_table()
+    x = np.array([1.0, 2.0, 5.0, 1.0, 1.0], dtype=np.float32)
+    ids = np.zeros((4, 3, 2), dtype=np.int64)
+    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=123, layer=9)
+    r, t, k = 2, 1, 1
+    g = r * 3 + t
+    u = O.philox4x64_10((g, k, 1, 0), (123, 9))[0]
+    v = (u * (256 + 512 + 1280)) >> 64
+    want = 0 if v < 256 else (5 if v < 768 else 11)
+    assert out[r, t, k] == want
