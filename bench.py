@@ -465,10 +465,16 @@ def bench_waterfill(args, torch, U, W, w):
     L_r = rl.cpu().numpy().astype(np.float64)
     shared = np.bincount(sh.cpu().numpy().reshape(-1), minlength=w.R)
     local = np.full(w.R, w.T, dtype=np.float64)
+    sh_all = torch.empty_like(sh)
+    U.waterfill(counts1, ids_d, B, seed, 0, 4, sh_all, wl, sl, rl, None, want_ext=False,
+                all_ranks=True)
+    shared_all = np.bincount(sh_all.cpu().numpy().reshape(-1), minlength=w.R)
     out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "waterfill_us": wf_us,
                     "waterline": int(wl.item()),
                     "imbalance_shared_local": float((L_r + local).max() / (L_r + local).mean()),
-                    "imbalance_shared_waterfill": float((L_r + shared).max() / (L_r + shared).mean())}
+                    "imbalance_shared_waterfill": float((L_r + shared).max() / (L_r + shared).mean()),
+                    "imbalance_shared_waterfill_all_ranks":
+                        float((L_r + shared_all).max() / (L_r + shared_all).mean())}
     return out
 
 
@@ -515,6 +521,32 @@ def bench_lplb(args, torch, U, W, w):
     r = 0
     rank_us = graph_us(torch, lambda s: (lp_plan(s, r, r + 1),
                                          L.permute(s, r, r + 1, row_src=False)), reps=5)
+    # the per-token draw variant: LP split -> copy draw -> instance dispatch layout
+    I = len(inst)
+    di = torch.empty_like(L.ids)
+    ident = torch.arange(I, dtype=torch.int32, device=DEV)
+    ci = torch.empty(w.R, I, dtype=torch.int32, device=DEV)
+    bpi = torch.empty_like(L.ids)
+    wsi = torch.empty(max(U.load_matrix_workspace_size(w.R, w.T, w.K, I), 4), dtype=torch.uint8,
+                      device=DEV)
+    qi = torch.empty(I, dtype=torch.int32, device=DEV)
+    xfi = torch.empty(w.R, I, dtype=torch.int32, device=DEV)
+    ioi = torch.empty(I + 1, dtype=torch.int32, device=DEV)
+    dii, dri = torch.empty_like(L.ids), torch.empty_like(L.ids)
+    rri = torch.empty(max(U.reroute_workspace_size(w.R, I, ipr), 4), dtype=torch.uint8, device=DEV)
+
+    def sample_plan(s):
+        L.load(s)
+        U.lplb(L.counts, lp, n_copies, I, args.lp_iters, x, m, L.plan["inst_quota"], st, None, s)
+        U.lplb_sample(L.ids, lp, x, 99, 0, di, None, s)
+        U.load_matrix(di, I, ci, bpi, None, wsi, s)
+        U.identity_quota(ci, ident, qi, stream=s)
+        U.reroute_assign(ci, di, bpi, ipr, ident, qi, 0, None, xfi, ioi, dii, dri, None, rri, s)
+
+    sample_us = graph_us(torch, sample_plan, reps=5)
+    torch.cuda.synchronize()
+    qs = qi.cpu().numpy()
+    load_sampled = np.array([qs[r * ipr:(r + 1) * ipr].sum() for r in range(w.R)])
     torch.cuda.synchronize()
     c = L.counts.cpu().numpy().sum(0)
     # uniform split of every replicated expert (the static default the LP replaces)
@@ -525,7 +557,8 @@ def bench_lplb(args, torch, U, W, w):
             uni[i // ipr] += c[e] / len(where)
     out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "lplb_us": lp_us,
                     "lp_iterations_run": int(st[2].item()), "m": float(m.item()),
-                    "max_load_uniform_split": float(uni.max()), "mean_load": float(c.sum() / w.R)}
+                    "max_load_uniform_split": float(uni.max()), "mean_load": float(c.sum() / w.R),
+                    "sample_plan_us": sample_us, "max_load_sampled": int(load_sampled.max())}
     return out
 
 

@@ -302,6 +302,31 @@ uep_status uep_lplb_prepare(const int32_t* inst_expert_host, int32_t R, int32_t 
 uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float* x, float* m,
                     int32_t* inst_quota, int32_t* stats, int32_t* err, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * uep_lplb_sample -- LPLB's per-token copy draw.
+ * [BLOG] section "从LP解决方案到Token调度": the split, normalised per replicated expert,
+ * is a probability distribution over its physical copies; every token routed to a
+ * replicated expert draws one copy from it, and a single-copy expert keeps its only
+ * instance.  Weights are the integers w_p = rint(max(x_p, 0) * 256) of uep_lplb's
+ * quota step; the draw for slot k of global token g = r*T + t is word 0 u of
+ * Philox4x64-10 at counter (g, k, 1, 0), key (seed, layer); v = floor(u * W / 2^64)
+ * with W = sum w_p, and the first copy (instance order) whose running weight exceeds
+ * v wins; W = 0: copy floor(u * n / 2^64) of the expert's n copies.
+ * The dispatch layout then follows from uep_load_matrix on dest_inst (instances as
+ * experts, E' = I), uep_identity_quota with the identity table and
+ * uep_reroute_assign.
+ *
+ *   topk_ids  [R][T][K]   in   expert ids (-1: empty slot -> -1)
+ *   lp                    in   device structure from uep_lplb_prepare (same R)
+ *   x         [n_copies]  in   per-copy split (uep_lplb's x, same copy order)
+ *   dest_inst [R][T][K]   out  physical instance of every pair
+ *   err                   optional: UEP_ERR_ID_RANGE, UEP_ERR_LP (no instance, or
+ *                         a structure that is not one for R ranks)
+ * ------------------------------------------------------------------------- */
+uep_status uep_lplb_sample(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                           const void* lp, const float* x, uint64_t seed, uint64_t layer,
+                           int32_t* dest_inst, int32_t* err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "common.h"
+#include "philox.h"
 
 namespace uep {
 
@@ -567,6 +568,65 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
   }
 }
 
+// LPLB's per-token copy draw (section "从LP解决方案到Token调度": the split,
+// normalised per replicated expert, is a distribution over its physical copies from
+// which every token routed to that expert draws one; a single-copy expert keeps its
+// only instance).  Weights are the integers w_p = rint(max(x_p, 0) * 256) of the
+// quota step; the draw for slot k of global token g is word 0 of Philox4x64-10 at
+// counter (g, k, 1, 0), key (seed, layer), scaled by a 64x64->128-bit product, so
+// the choice is exact integer arithmetic.  One thread per (token, slot) pair.
+__device__ __forceinline__ uint64_t copy_weight(float x) {
+  return (uint64_t)rintf(fmaxf(x, 0.0f) * 256.0f);
+}
+
+__global__ __launch_bounds__(256) void lplb_sample_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t n_pairs, int K, int R,
+                                                          const int32_t* __restrict__ lpw,
+                                                          const float* __restrict__ x,
+                                                          uint64_t seed, uint64_t layer,
+                                                          int32_t* __restrict__ dest_inst,
+                                                          int32_t* err) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n_pairs) return;
+  if (lpw[0] != kLpMagic || lpw[1] != R) {
+    dest_inst[j] = -1;
+    set_err(err, UEP_ERR_LP);
+    return;
+  }
+  const LpView L = lp_view(lpw);
+  const int e = ids[j];
+  int out = -1;
+  if (e >= L.E || e < -1) {
+    set_err(err, UEP_ERR_ID_RANGE);
+  } else if (e >= 0) {
+    const int ei = L.exp_inst[e];
+    if (ei >= 0) {
+      out = ei;
+    } else if (ei == -1) {
+      set_err(err, UEP_ERR_LP);
+    } else {
+      const int gi = -2 - ei;
+      const int c0 = L.grp_start[gi], c1 = L.grp_start[gi + 1];
+      uint64_t W = 0;
+      for (int c = c0; c < c1; ++c) W += copy_weight(x[c]);
+      const uint64_t u = philox4x64_10_w0((uint64_t)(j / K), (uint64_t)(j % K), 1, 0, seed, layer);
+      int pick = c0;
+      if (W == 0) {
+        pick = c0 + (int)__umul64hi(u, (uint64_t)(c1 - c0));
+      } else {
+        const uint64_t v = __umul64hi(u, W);
+        uint64_t run = 0;
+        for (int c = c0; c < c1; ++c) {
+          run += copy_weight(x[c]);
+          if (run > v) { pick = c; break; }
+        }
+      }
+      out = L.copy_inst[pick];
+    }
+  }
+  dest_inst[j] = out;
+}
+
 }  // namespace uep
 
 using namespace uep;
@@ -662,6 +722,22 @@ extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t it
   if (!counts || !lp || !x || !m || !inst_quota || iters < 0 || iters > 200) return UEP_EINVAL;
   hipLaunchKernelGGL(lplb_kernel, dim3(1), dim3(kLpThreads), 0, uep_stream(stream),
                      counts, static_cast<const int32_t*>(lp), iters, x, m, inst_quota, stats, err);
+  UEP_CHECK_LAUNCH();
+  return UEP_OK;
+}
+
+extern "C" uep_status uep_lplb_sample(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                                      const void* lp, const float* x, uint64_t seed,
+                                      uint64_t layer, int32_t* dest_inst, int32_t* err,
+                                      void* stream) {
+  if (R <= 0 || T < 0 || K <= 0) return UEP_EINVAL;
+  if (R > kLpMaxR || K > 64 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
+  const int64_t n = (int64_t)R * T * K;
+  if (n == 0) return UEP_OK;
+  if (!topk_ids || !lp || !x || !dest_inst) return UEP_EINVAL;
+  hipLaunchKernelGGL(lplb_sample_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     uep_stream(stream), topk_ids, n, K, R, static_cast<const int32_t*>(lp), x,
+                     seed, layer, dest_inst, err);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }

@@ -13,27 +13,9 @@
 //   (global token index, 0, 0, 0) and key (seed, layer), scaled to the total weight
 //   with a 64x64->128-bit multiply, so the choice is exact integer arithmetic.
 #include "common.h"
+#include "philox.h"
 
 namespace uep {
-
-__device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t ctr0, uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-  uint64_t c0 = ctr0, c1 = 0, c2 = 0, c3 = 0;
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += W0;
-    k1 += W1;
-  }
-  return c0;
-}
 
 __global__ __launch_bounds__(256) void wf_prologue(const int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ batch_size, int R,
@@ -104,7 +86,7 @@ __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids
     int64_t W = w0;
     for (uint64_t m = visited; m; m &= m - 1) W += big * s_S[__ffsll((unsigned long long)m) - 1];
     if (W > 0) {
-      const uint64_t u = philox4x64_10_w0((uint64_t)g, seed, layer);
+      const uint64_t u = philox4x64_10_w0((uint64_t)g, 0, 0, 0, seed, layer);
       const uint64_t v = __umul64hi(u, (uint64_t)W);
       uint64_t run = (uint64_t)w0;
       choice = r0;

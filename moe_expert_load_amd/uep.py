@@ -48,6 +48,7 @@ SIGNATURES = {
                            _P]),
     "uep_lplb_struct_size": (_SZ, [_I, _I, _I]),
     "uep_lplb_prepare": (_I, [_P, _I, _I, _I, _P, _SZ, _P]),
+    "uep_lplb_sample": (_I, [_P, _I, _I, _I, _P, _P, _U64, _U64, _P, _P, _P]),
     "uep_lplb": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -260,3 +261,17 @@ def lplb(counts, lp, n_copies, n_inst, iters=30, x=None, m=None, inst_quota=None
     _check(LIB.uep_lplb(_p(counts), _p(lp), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
                         _p(err), _s(stream)), "uep_lplb")
     return x[:n_copies], m, inst_quota, stats
+
+
+def lplb_sample(topk_ids, lp, x, seed, layer, dest_inst=None, err=None, stream=None):
+    """Per-token copy draw from LPLB's split: dest_inst [R][T][K] int32."""
+    _i32(topk_ids, "topk_ids")
+    R, T, K = topk_ids.shape
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    dest_inst = _new((R, T, K), topk_ids) if dest_inst is None else dest_inst
+    _check(LIB.uep_lplb_sample(_p(topk_ids), R, T, K, _p(lp), _p(x),
+                               ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                               ctypes.c_uint64(layer & (2 ** 64 - 1)), _p(dest_inst), _p(err),
+                               _s(stream)), "uep_lplb_sample")
+    return dest_inst

@@ -194,3 +194,110 @@ def test_lplb_layer_full_size():
     exp = host(x_act.view(w.R * w.T, w.H).view(torch.int16)[tok])
     got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)])
     assert np.array_equal(got, exp)
+
+
+# ---------------------------------------------------------------- per-token copy draw
+
+def random_lplb_case(rng, R, E_loc, T, K, n_hot):
+    E = R * E_loc
+    ipr = E_loc + 1
+    inst = np.full(R * ipr, -1, dtype=np.int32)
+    for r in range(R):
+        inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+    hot = rng.choice(E, size=n_hot, replace=False)
+    free = list(rng.permutation(R))
+    for e in hot:
+        for r in free:
+            if r != e // E_loc:
+                inst[r * ipr + E_loc] = e
+                free.remove(r)
+                break
+    p = rng.dirichlet(np.full(E, 0.3))
+    ids = np.stack([np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)])
+                    for _ in range(R)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.03] = -1
+    return ids, inst, ipr, E
+
+
+def instance_dispatch_oracle(dest_inst, inst_len, ipr):
+    """Dispatch layout of sampled instance ids: each instance is a one-copy pseudo-expert."""
+    ident = np.arange(inst_len, dtype=np.int64)
+    c, bp = O.load_matrix(dest_inst, inst_len)
+    q = O.identity_quota(c, ident)
+    X, io, so = O.reroute(c, ident, q, ipr)
+    _, dr = O.assign(dest_inst, bp, X, ident, ipr, io, so)
+    return c, q, dr
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_lplb_sample_random(seed):
+    rng = np.random.default_rng(1300 + seed)
+    R = int(rng.choice([2, 4, 8, 16]))
+    E_loc = int(rng.integers(1, 4))
+    T, K = int(rng.integers(1, 200)), int(rng.integers(1, min(R * E_loc, 6) + 1))
+    n_hot = int(rng.integers(0, R + 1))
+    ids, inst, ipr, E = random_lplb_case(rng, R, E_loc, T, K, n_hot)
+    say(f"case: lplb sample seed={seed} R={R} E={E} T={T} K={K} replicas={n_hot}")
+    counts_o, _ = O.load_matrix(ids, E)
+    x32 = np.asarray(O.lplb(counts_o, inst, ipr)["x"], dtype=np.float32)
+    lp = U.lplb_prepare(inst, R, E, ipr, DEV)
+    err = err_word()
+    seed_, layer = 77 + seed, 3
+    di = U.lplb_sample(to_dev(ids), lp, to_dev(x32 if x32.size else np.zeros(1), torch.float32),
+                       seed_, layer, err=err)
+    di_o = O.lplb_sample(ids, inst, ipr, E, x32, seed_, layer)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(di), di_o)
+    # the dispatch layout of the drawn instances, bit-exact
+    I = len(inst)
+    c_o, q_o, dr_o = instance_dispatch_oracle(di_o, I, ipr)
+    c, bp = U.load_matrix(di, I, err=err)
+    ident = to_dev(np.arange(I))
+    q = U.identity_quota(c, ident)
+    _, _, _, dr = U.reroute_assign(c, di, bp, ipr, ident, q, err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(c), c_o) and np.array_equal(host(q), q_o)
+    assert np.array_equal(host(dr), dr_o)
+
+
+def test_lplb_sample_layer_full_size():
+    """LPLB layer: the draw of three source ranks bit-exact on the oracle's split; with
+    the kernel's own split, every pair lands on a copy of its expert and each copy's
+    share of a replicated expert's tokens is within 5 sigma of w_p / W."""
+    w = W.LPLB_LAYER
+    say("case: lplb sample full size", w)
+    ids = W.routing(w)
+    inst = W.static_replica_placement(w)
+    ipr = w.E_loc + 1
+    counts_o, _ = O.load_matrix(ids, w.E)
+    x32 = np.asarray(O.lplb(counts_o, inst, ipr)["x"], dtype=np.float32)
+    lp = U.lplb_prepare(inst, w.R, w.E, ipr, DEV)
+    ids_d = to_dev(ids)
+    err = err_word()
+    seed_, layer = 2024, 11
+    di = U.lplb_sample(ids_d, lp, to_dev(x32, torch.float32), seed_, layer, err=err)
+    some = [0, 40, w.R - 1]
+    di_o = O.lplb_sample(ids, inst, ipr, w.E, x32, seed_, layer, ranks=some)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(di)[some], di_o[some])
+    # the kernel's own split, end to end
+    groups = copy_groups(inst, w.E)
+    n = sum(len(g[1]) for g in groups)
+    x, m, q, st = U.lplb(to_dev(counts_o), lp, n, len(inst), iters=30, err=err)
+    di = host(U.lplb_sample(ids_d, lp, x, seed_, layer, err=err))
+    assert host(err)[0] == 0
+    inst_np = np.asarray(inst)
+    live = ids >= 0
+    assert (inst_np[di[live]] == ids[live]).all() and (di[~live] == -1).all()
+    xh = host(x)
+    k = 0
+    for e, insts in groups:
+        wts = np.array([np.rint(max(float(v), 0.0) * 256.0) for v in xh[k:k + len(insts)]])
+        k += len(insts)
+        tot = int((ids == e).sum())
+        if wts.sum() == 0 or tot == 0:
+            continue
+        p = wts / wts.sum()
+        got = np.array([(di == i).sum() for i in insts])
+        sigma = np.sqrt(tot * p * (1 - p))
+        assert (np.abs(got - tot * p) <= 5 * sigma + 1).all()
