@@ -19,7 +19,8 @@
 // the differential entries of copies whose optimal share is a small fraction of the
 // peak.  Diagonal entries are formed as sums of positive terms (no cancellation); a
 // pivot that lost its precision is replaced by a huge one (Cholesky-infinity), which
-// drops that direction.  Iterations stop changing the iterate once mu < 1e-9.
+// drops that direction.  Iterations stop once the duality gap is below 1e-4 of the
+// objective M (or mu < 1e-9), at most `iters` of them.
 // Output: x >= 0 normalised so each group sums exactly to its count, m = the max rank
 // load of that split, and integer quotas by largest remainder on rint(x * 256).
 #include <math.h>
@@ -41,6 +42,7 @@ constexpr int kLpMagic = 0x4C50424C;
 constexpr float kBigM = 8.0f;
 constexpr float kEta = 0.99f;
 constexpr float kMuStop = 1e-9f;
+constexpr double kGapRel = 1e-4;
 constexpr double kPivTol = 1e-13;
 constexpr int kLpMaxNV = kLpMaxN + kLpMaxR + 2;
 constexpr int kLpMaxRows = kLpMaxR + kLpMaxG;
@@ -204,26 +206,20 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
     const int l = threadIdx.x;
     double b = l < R ? S.u64[l] : 0.0;       // padded rows solve to 0
     // L = U D^(1/2) with U unit lower triangular: U z = r1, w = D^-1 z, U^T u = w,
-    // so every substitution step is one broadcast and one FMA
+    // so every substitution step is one broadcast and one FMA.  P holds U's strictly
+    // lower part and zeros elsewhere, so lanes outside the triangle add 0: no
+    // branches, and each pass loads its 64 entries in one burst before the chain.
     const double linv_l = S.Linv[l];
-    // Entries outside the triangle are zero, so those lanes' FMAs leave b unchanged:
-    // no branches.  The entries of U are streamed from LDS eight steps at a time
-    // (independent of the substitution chain, so their loads are issued early).
-    for (int j0 = 0; j0 < kLpMaxR; j0 += 8) {        // U z = r1
-      double u[8];
+    double u[kLpMaxR];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) u[q] = (j0 + q < l) ? S.P[l][j0 + q] * S.Linv[j0 + q] : 0.0;
+    for (int q = 0; q < kLpMaxR; ++q) u[q] = S.P[l][q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) b = fma(-u[q], readlane_d(b, j0 + q), b);
-    }
-    b *= linv_l * linv_l;                             // w = D^-1 z
-    for (int j0 = kLpMaxR - 8; j0 >= 0; j0 -= 8) {   // U^T u = w
-      double u[8];
+    for (int q = 0; q < kLpMaxR; ++q) b = fma(-u[q], readlane_d(b, q), b);   // U z = r1
+    b *= linv_l * linv_l;                                                   // w = D^-1 z
 #pragma unroll
-      for (int q = 0; q < 8; ++q) u[q] = (j0 + q > l) ? S.P[j0 + q][l] * linv_l : 0.0;
+    for (int q = 0; q < kLpMaxR; ++q) u[q] = S.P[q][l];
 #pragma unroll
-      for (int q = 7; q >= 0; --q) b = fma(-u[q], readlane_d(b, j0 + q), b);
-    }
+    for (int q = kLpMaxR - 1; q >= 0; --q) b = fma(-u[q], readlane_d(b, q), b);  // U^T u = w
     if (l < R) S.u64[l] = b;
   }
   __syncthreads();
@@ -288,72 +284,71 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
     S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - off;
   }
   __syncthreads();
-  // Right-looking Cholesky with a 4x4 register tile per thread: thread (ti, tk) owns
-  // rows i = ti + 16a and columns k = tk + 16b.  Every thread keeps the diagonal of its
-  // four columns current, so the owners of column j compute the pivot themselves and
-  // one barrier per column suffices (column j is published through a double buffer).
+  // Blocked right-looking Cholesky, four panels of 16 columns.  Thread (ti, tk) keeps
+  // a 4x4 register tile of the trailing matrix: rows i = ti + 16a, columns
+  // k = tk + 16b.  For panel p: the tiles of column block p are published to LDS;
+  // wave 0 factors the 64 x 16 panel with one row per lane (pivots and column
+  // entries broadcast by readlane, no barriers) and stores U = L diag(Linv) strictly
+  // below the diagonal, zeros above, and the pivots; then every thread subtracts the
+  // panel's rank-16 product from its trailing tiles, L_ij L_kj = U_ij U_kj p_j.
+  // Eight barriers in all.  A pivot that lost its precision (p_j <= tol * original
+  // diagonal) drops its direction: its column of U is 0 and Linv = 1e-32.
   const int ti = threadIdx.x / 16, tk = threadIdx.x % 16;
-  double A[4][4], dg[4];
+  double* piv = S.colbuf[0];
+  double A[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = ti + 16 * a, k = tk + 16 * b;
-      A[a][b] = S.P[i][k];
-    }
+    for (int b = 0; b < 4; ++b) A[a][b] = S.P[ti + 16 * a][tk + 16 * b];
+  __syncthreads();
 #pragma unroll
-  for (int b = 0; b < 4; ++b) dg[b] = S.P[tk + 16 * b][tk + 16 * b];
-  // columns are processed in four blocks of 16 so that every tile index is static:
-  // in block jb, rows and columns below 16 * jb are finished and skipped
+  for (int pb = 0; pb < 4; ++pb) {
+    const int c0 = 16 * pb;
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-#pragma unroll 1
-    for (int jt = 0; jt < 16; ++jt) {
-      const int j = jb * 16 + jt;
-      double* buf = S.colbuf[j & 1];
-      if (tk == jt) {
-        const double pj = dg[jb];
-        const bool bad = !(pj > kPivTol * S.d0[j]);
+    for (int a = pb; a < 4; ++a) S.P[ti + 16 * a][c0 + tk] = A[a][pb];
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      // the lane index is re-read per panel (empty asm, no instruction) so the 64
+      // lane-vs-column compares stay inside the loop instead of being hoisted out of
+      // the interior-point loop as 64 live masks
+      int l = threadIdx.x;
+      asm volatile("" : "+v"(l));
+      double r[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) r[j] = S.P[l][c0 + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c = c0 + j;
+        const double pj = readlane_d(r[j], c);
+        const bool bad = !(pj > kPivTol * S.d0[c]);
         const double inv = bad ? 0.0 : rsqrt_d(pj);
-        if (ti == jt) S.Linv[j] = bad ? 1e-32 : inv;
-#pragma unroll
-        for (int a = jb; a < 4; ++a) {
-          const int i = ti + 16 * a;
-          if (i > j) {
-            A[a][jb] *= inv;
-            buf[i] = A[a][jb];
-          }
+        if (l == c) {
+          S.Linv[c] = bad ? 1e-32 : inv;
+          piv[c] = pj;
         }
+        const double lic = l > c ? r[j] * inv : 0.0;        // L_lc (0 on and above)
+        S.P[l][c] = lic * inv;                               // U = L Linv
+#pragma unroll
+        for (int j2 = j + 1; j2 < 16; ++j2) r[j2] = fma(-lic, readlane_d(lic, c0 + j2), r[j2]);
       }
-      __syncthreads();
-      double li[4], lk[4];
+    }
+    __syncthreads();
+    if (pb < 3) {
 #pragma unroll
-      for (int a = jb; a < 4; ++a) {
-        const int i = ti + 16 * a;
-        li[a] = i > j ? buf[i] : 0.0;
+      for (int j = 0; j < 16; ++j) {
+        const double pj = piv[c0 + j];
+        double ui[4], uk[4];
+#pragma unroll
+        for (int a = pb + 1; a < 4; ++a) ui[a] = S.P[ti + 16 * a][c0 + j];
+#pragma unroll
+        for (int b2 = pb + 1; b2 < 4; ++b2) uk[b2] = S.P[tk + 16 * b2][c0 + j] * pj;
+#pragma unroll
+        for (int a = pb + 1; a < 4; ++a)
+#pragma unroll
+          for (int b2 = pb + 1; b2 < 4; ++b2) A[a][b2] = fma(-ui[a], uk[b2], A[a][b2]);
       }
-#pragma unroll
-      for (int b = jb; b < 4; ++b) {
-        const int k = tk + 16 * b;
-        lk[b] = k > j ? buf[k] : 0.0;
-      }
-#pragma unroll
-      for (int a = jb; a < 4; ++a)
-#pragma unroll
-        for (int b = jb; b < 4; ++b) A[a][b] = fma(-li[a], lk[b], A[a][b]);
-#pragma unroll
-      for (int b = jb; b < 4; ++b) dg[b] = fma(-lk[b], lk[b], dg[b]);
     }
   }
-  // the strictly lower factor back to LDS for the triangular solves
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = ti + 16 * a, k = tk + 16 * b;
-      if (k < i) S.P[i][k] = A[a][b];
-    }
-  __syncthreads();
 }
 
 __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
@@ -445,8 +440,11 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
         S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
         cz += (double)(S.v[i] * S.z[i]);
       }
-      const float mu = (float)(blk_sum(cz, S) / nv);
-      if (!(mu >= kMuStop)) break;
+      const double gap = blk_sum(cz, S);
+      const float mu = (float)(gap / nv);
+      // stop once the duality gap, which bounds the objective error of a feasible
+      // iterate, is below kGapRel of the objective (fp32 iterates gain nothing beyond)
+      if (!(mu >= kMuStop) || gap <= kGapRel * fmax(1.0, (double)S.v[n + R])) break;
       ++run;
       lp_factor(n, R, G, L, S);
       // predictor: rhs = rb + A (v + D rc)
