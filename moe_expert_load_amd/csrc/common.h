@@ -90,16 +90,19 @@ __device__ __forceinline__ int first_lane(bool p) {
   return b ? __ffsll((unsigned long long)b) - 1 : -1;
 }
 
-// sum_r counts[r][e] with 8 independent loads in flight
+// sum_r counts[r][e] with up to 32 predicated loads in flight (two rounds for
+// R <= 64): the matrix was just written by another kernel, so each round costs a
+// full trip to the last-level cache
 __device__ __forceinline__ int column_sum(const int32_t* __restrict__ counts, int R, int E, int e) {
-  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int r = 0;
-  for (; r + 8 <= R; r += 8) {
+  int s = 0;
+  for (int r0 = 0; r0 < R; r0 += 32) {
+    int v[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += counts[(int64_t)(r + u) * E + e];
+    for (int u = 0; u < 32; ++u) v[u] = r0 + u < R ? counts[(int64_t)(r0 + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s += v[u];
   }
-  for (; r < R; ++r) acc[0] += counts[(int64_t)r * E + e];
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  return s;
 }
 
 // Bijection of [0, nb) for HBM-streaming grids: workgroup b runs on XCD b % 8; that

@@ -192,18 +192,23 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
   for (int e = tid; e < E; e += kSqThreads) sq_lds[e] = 0;
   __syncthreads();
   {
-    // per = threads per expert; each sums every per-th rank with loads in flight
+    // per = threads per expert; each sums every per-th rank, up to 16 predicated
+    // loads in flight (one round whenever R <= 16 * per)
     const int per = E >= kSqThreads ? 1 : kSqThreads / E;
     const int part = tid % per;
     for (int e = tid / per; e < E; e += kSqThreads / per) {
-      int acc[4] = {0, 0, 0, 0};
-      int r = part;
-      for (; r + 3 * per < R; r += 4 * per) {
+      int acc = 0;
+      for (int r0 = part; r0 < R; r0 += 16 * per) {
+        int v[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] += counts[(int64_t)(r + u * per) * E + e];
+        for (int u = 0; u < 16; ++u) {
+          const int r = r0 + u * per;
+          v[u] = r < R ? counts[(int64_t)r * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
       }
-      for (; r < R; r += per) acc[0] += counts[(int64_t)r * E + e];
-      atomicAdd(&sq_lds[e], (acc[0] + acc[1]) + (acc[2] + acc[3]));
+      atomicAdd(&sq_lds[e], acc);
     }
   }
   __syncthreads();

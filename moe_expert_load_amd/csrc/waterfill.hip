@@ -9,9 +9,11 @@
 // wf_prologue: one workgroup turns the load matrix into L_r, H and S_r.
 // wf_sample: one thread per token.  The candidate set is a 64-bit mask of visited
 //   ranks (R <= 64) minus the source rank, walked in ascending order after the
-//   source; the draw is word 0 of Philox4x64-10 (Salmon et al., SC'11) at counter
-//   (global token index, 0, 0, 0) and key (seed, layer), scaled to the total weight
-//   with a 64x64->128-bit multiply, so the choice is exact integer arithmetic.
+//   source; in the all-rank mode the running weights are prefix sums of the slack,
+//   searched by bisection.  The draw is word 0 of Philox4x64-10 (Salmon et al.,
+//   SC'11) at counter (global token index, 0, 0, 0) and key (seed, layer), scaled to
+//   the total weight with a 64x64->128-bit multiply, so the choice is exact integer
+//   arithmetic.
 #include "common.h"
 #include "philox.h"
 
@@ -23,10 +25,14 @@ __global__ __launch_bounds__(256) void wf_prologue(const int32_t* __restrict__ c
                                                    int32_t* __restrict__ slack,
                                                    int32_t* __restrict__ rank_load) {
   extern __shared__ int32_t wf_lds[];   // [E] expert loads
-  __shared__ int32_t s_L[64];
+  __shared__ int32_t s_L[64], s_B[64];
   __shared__ int32_t s_H;
   const int E_loc = E / R;
   for (int e = threadIdx.x; e < E; e += blockDim.x) wf_lds[e] = column_sum(counts, R, E, e);
+  if (threadIdx.x < R) {
+    const int b = batch_size[threadIdx.x];
+    s_B[threadIdx.x] = b < 0 ? 0 : (b > T ? T : b);
+  }
   __syncthreads();
   if (threadIdx.x < R) {
     int L = 0;
@@ -36,10 +42,7 @@ __global__ __launch_bounds__(256) void wf_prologue(const int32_t* __restrict__ c
   __syncthreads();
   if (threadIdx.x == 0) {
     int64_t tot = 0;
-    for (int r = 0; r < R; ++r) {
-      const int b = batch_size[r];
-      tot += s_L[r] + (b < 0 ? 0 : (b > T ? T : b));
-    }
+    for (int r = 0; r < R; ++r) tot += (int64_t)s_L[r] + s_B[r];
     s_H = (int)((tot + R - 1) / R);
     waterline[0] = s_H;
   }
@@ -51,6 +54,11 @@ __global__ __launch_bounds__(256) void wf_prologue(const int32_t* __restrict__ c
   }
 }
 
+// One workgroup = up to 256 consecutive tokens of rank r0 = blockIdx.y, one thread
+// per token.  The block's top-k rows are read coalesced into an LDS tile with K + 1
+// columns; the thread's choice fills the extra column and the tile is written back
+// coalesced as the fused top-(K+1) rows.  Home ranks come from an LDS table.
+template <bool kStage>
 __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids,
                                                  const int32_t* __restrict__ batch_size,
                                                  const int32_t* __restrict__ slack,
@@ -59,60 +67,123 @@ __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids
                                                  uint64_t layer, int shift, int all_ranks,
                                                  int32_t* __restrict__ shared_rank,
                                                  int32_t* __restrict__ ext) {
-  __shared__ int32_t s_S[64], s_L[64], s_B[64];
+  __shared__ int32_t s_S[64], s_L[64];
+  __shared__ int64_t s_cum[65];           // prefix sums of slack (all-rank mode)
+  __shared__ int32_t s_B;
+  extern __shared__ int32_t wf_dyn[];     // home[E], then the [256][K+1] tile
+  int32_t* home = wf_dyn;
+  int32_t* tile = wf_dyn + E;
+  const int r0 = blockIdx.y;
+  const int t_base = blockIdx.x * 256;
+  const int n_tok = min(256, T - t_base);
+  const int E_loc = E / R;
+  const int K1 = K + 1;
+  const int64_t g_base = (int64_t)r0 * T + t_base;
+  for (int e = threadIdx.x; e < E; e += 256) home[e] = e / E_loc;
   if (threadIdx.x < R) {
     s_S[threadIdx.x] = slack[threadIdx.x];
     s_L[threadIdx.x] = rank_load[threadIdx.x];
-    s_B[threadIdx.x] = batch_size[threadIdx.x];
+  }
+  if (threadIdx.x == 0) s_B = batch_size[r0];
+  if (kStage) {
+    const int32_t* src = ids + g_base * K;
+    for (int j = threadIdx.x; j < n_tok * K; j += 256) {
+      const int tt = j / K;
+      tile[tt * K1 + (j - tt * K)] = src[j];
+    }
   }
   __syncthreads();
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (int64_t)R * T) return;
-  const int r0 = (int)(g / T), t = (int)(g % T);
-  const int E_loc = E / R;
-  const int32_t* tok = ids + g * K;
-  int choice = -1;
-  uint64_t visited = 0;
-  for (int k = 0; k < K; ++k) {
-    const int e = tok[k];
-    if (ext) ext[g * (K + 1) + k] = e;
-    if (e >= 0 && e < E) visited |= 1ull << (e / E_loc);
+  if (all_ranks && threadIdx.x == 0) {
+    int64_t c = 0;
+    for (int r = 0; r < R; ++r) { s_cum[r] = c; c += s_S[r]; }
+    s_cum[R] = c;
   }
-  if (t < s_B[r0]) {
-    if (all_ranks) visited = R == 64 ? ~0ull : (1ull << R) - 1;
-    visited &= ~(1ull << r0);
-    const int64_t big = 1ll << shift;
-    const int64_t w0 = (big + 1) * s_S[r0];
-    int64_t W = w0;
-    for (uint64_t m = visited; m; m &= m - 1) W += big * s_S[__ffsll((unsigned long long)m) - 1];
-    if (W > 0) {
-      const uint64_t u = philox4x64_10_w0((uint64_t)g, 0, 0, 0, seed, layer);
-      const uint64_t v = __umul64hi(u, (uint64_t)W);
-      uint64_t run = (uint64_t)w0;
-      choice = r0;
-      if (!(run > v)) {
-        for (uint64_t m = visited; m; m &= m - 1) {
-          const int c = __ffsll((unsigned long long)m) - 1;
-          run += (uint64_t)(big * s_S[c]);
-          if (run > v) { choice = c; break; }
+  if (all_ranks) __syncthreads();
+  const int t = t_base + threadIdx.x;
+  if (threadIdx.x < n_tok) {
+    const int64_t g = g_base + threadIdx.x;
+    int choice = -1;
+    uint64_t visited = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = kStage ? tile[threadIdx.x * K1 + k] : ids[g * K + k];
+      if (!kStage && ext) ext[g * K1 + k] = e;
+      if (e >= 0 && e < E) visited |= 1ull << home[e];
+    }
+    if (t < s_B) {
+      const int64_t big = 1ll << shift;
+      const int64_t w0 = (big + 1) * s_S[r0];
+      if (all_ranks) {
+        const int64_t tot = s_cum[R] - s_S[r0];
+        const int64_t W = w0 + big * tot;
+        if (W > 0) {
+          const uint64_t u = philox4x64_10_w0((uint64_t)g, 0, 0, 0, seed, layer);
+          const uint64_t v = __umul64hi(u, (uint64_t)W);
+          if (v < (uint64_t)w0) {
+            choice = r0;
+          } else {
+            // first c != r0 with big * (slack of ranks <= c, r0 excluded) > v - w0
+            const uint64_t vr = v - (uint64_t)w0;
+            int lo = 0, hi = R - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi) / 2;
+              const int64_t cm = s_cum[mid + 1] - (r0 <= mid ? s_S[r0] : 0);
+              if ((uint64_t)(big * cm) > vr) hi = mid; else lo = mid + 1;
+            }
+            choice = lo;
+          }
+        } else {
+          choice = r0;
+          int64_t bestL = -1;
+          const int64_t lr0 = s_L[r0];
+          for (int c = 0; c < R; ++c) {
+            const int64_t lc = s_L[c];
+            if (c != r0 && (big + 1) * lc < big * lr0 && (bestL < 0 || lc < bestL)) {
+              bestL = lc;
+              choice = c;
+            }
+          }
         }
-      }
-    } else {
-      choice = r0;
-      int64_t bestL = -1;
-      const int64_t lr0 = s_L[r0];
-      for (uint64_t m = visited; m; m &= m - 1) {
-        const int c = __ffsll((unsigned long long)m) - 1;
-        const int64_t lc = s_L[c];
-        if ((big + 1) * lc < big * lr0 && (bestL < 0 || lc < bestL)) {
-          bestL = lc;
-          choice = c;
+      } else {
+        visited &= ~(1ull << r0);
+        int64_t W = w0;
+        for (uint64_t m = visited; m; m &= m - 1) W += big * s_S[__ffsll((unsigned long long)m) - 1];
+        if (W > 0) {
+          const uint64_t u = philox4x64_10_w0((uint64_t)g, 0, 0, 0, seed, layer);
+          const uint64_t v = __umul64hi(u, (uint64_t)W);
+          uint64_t run = (uint64_t)w0;
+          choice = r0;
+          if (!(run > v)) {
+            for (uint64_t m = visited; m; m &= m - 1) {
+              const int c = __ffsll((unsigned long long)m) - 1;
+              run += (uint64_t)(big * s_S[c]);
+              if (run > v) { choice = c; break; }
+            }
+          }
+        } else {
+          choice = r0;
+          int64_t bestL = -1;
+          const int64_t lr0 = s_L[r0];
+          for (uint64_t m = visited; m; m &= m - 1) {
+            const int c = __ffsll((unsigned long long)m) - 1;
+            const int64_t lc = s_L[c];
+            if ((big + 1) * lc < big * lr0 && (bestL < 0 || lc < bestL)) {
+              bestL = lc;
+              choice = c;
+            }
+          }
         }
       }
     }
+    shared_rank[g] = choice;
+    const int col = choice >= 0 ? E + choice : -1;
+    if (kStage) tile[threadIdx.x * K1 + K] = col;
+    else if (ext) ext[g * K1 + K] = col;
   }
-  shared_rank[g] = choice;
-  if (ext) ext[g * (K + 1) + K] = choice >= 0 ? E + choice : -1;
+  if (kStage && ext) {
+    __syncthreads();
+    int32_t* dst = ext + g_base * K1;
+    for (int j = threadIdx.x; j < n_tok * K1; j += 256) dst[j] = tile[j];
+  }
 }
 
 }  // namespace uep
@@ -137,10 +208,16 @@ extern "C" uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_i
                      R, E, T, waterline, slack, rank_load);
   UEP_CHECK_LAUNCH();
   if (T > 0) {
-    const int64_t n = (int64_t)R * T;
-    hipLaunchKernelGGL(wf_sample, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, topk_ids,
-                       batch_size, slack, rank_load, R, T, K, E, seed, layer, local_pref_shift,
-                       all_ranks ? 1 : 0, shared_rank, ext_topk);
+    const dim3 grid((unsigned)((T + 255) / 256), (unsigned)R);
+    const size_t tile = sizeof(int32_t) * (size_t)(E + 256 * (K + 1));
+    if (tile <= 48 * 1024)
+      hipLaunchKernelGGL(wf_sample<true>, grid, dim3(256), tile, s, topk_ids, batch_size, slack,
+                         rank_load, R, T, K, E, seed, layer, local_pref_shift, all_ranks ? 1 : 0,
+                         shared_rank, ext_topk);
+    else
+      hipLaunchKernelGGL(wf_sample<false>, grid, dim3(256), sizeof(int32_t) * E, s, topk_ids,
+                         batch_size, slack, rank_load, R, T, K, E, seed, layer, local_pref_shift,
+                         all_ranks ? 1 : 0, shared_rank, ext_topk);
     UEP_CHECK_LAUNCH();
   }
   return UEP_OK;
