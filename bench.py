@@ -214,6 +214,25 @@ def roofline(bytes_, ms, kernel, traffic=None):
             "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": ms}
 
 
+def launch_floor(torch, U, n=1000):
+    """The launch floor the latency-bound kernels are read against: the library's
+    smallest launch (a 16-byte uep_device_copy, one workgroup) on the bench stream,
+    as the mean of graph-replayed back-to-back launches and as the median of n
+    event-timed single launches."""
+    a = torch.zeros(4, dtype=torch.int32, device=DEV)
+    b = torch.empty_like(a)
+    graph = graph_us(torch, lambda st: U.device_copy(a, b, st), reps=100, replays=10)
+    s = torch.cuda.current_stream()
+    t = Timer(torch, n)
+    for _ in range(n):
+        t.start(s)
+        U.device_copy(a, b, s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    return {"launch_floor_us_graph": graph,
+            "launch_floor_us_event_median": float(np.median(t.all_ms()) * 1e3)}
+
+
 def copy_reference(torch, U, nbytes=1 << 30, reps=5):
     """Event-timed plain device copy (uep_device_copy) of nbytes: the achievable
     bandwidth line, and the known-size kernel that calibrates byte counters."""
@@ -288,33 +307,39 @@ def combine_figures(torch, U, W, L, reps=5):
 
 
 # ----------------------------------------------------------------------------- CPU leg
-def cpu_baseline(w, ids, x_host, n_rank_sample=8):
-    """The oracle as it stands, single process, on a bounded sample of the same layer:
-    the whole plan (load matrix, quota solve, reroute, assignment), the permute of
-    n_rank_sample ranks scaled to all ranks, and the staging of every used slot."""
+def cpu_baseline(w, ids, x_host, passes=3):
+    """The oracle as it stands, single process: the whole step of the layer (load
+    matrix, quota solve, reroute, assignment, permute of every rank, staging of every
+    used slot), repeated `passes` times; value = tokens per second of the mean pass."""
     import oracle as O
-    t0 = time.perf_counter()
-    counts, bp = O.load_matrix(ids, w.E)
-    plan = O.solve_quota(counts, w.S, w.q_min)
-    X, io, so = O.reroute(counts, plan["inst_expert"], plan["inst_quota"], plan["inst_per_rank"])
-    _, dr = O.assign(ids, bp, X, plan["inst_expert"], plan["inst_per_rank"], io, so)
-    t_plan = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.permute(x_host, dr, 0, n_rank_sample, w.P)
-    t_perm = (time.perf_counter() - t0) * w.R / n_rank_sample
-    used = [(r, s) for r in range(w.R) for s in range(w.S) if plan["slot_expert"][r, s] >= 0]
     n = w.expert_elems
     mw = np.zeros((w.E, n), dtype=np.uint16)
     sw = np.zeros((w.R, w.S, n), dtype=np.uint16)
-    t0 = time.perf_counter()
-    O.stage_forward(plan["slot_expert"], mw, sw)
-    t_stage = time.perf_counter() - t0
-    total = t_plan + t_perm + t_stage
+    t_plan = t_perm = t_stage = 0.0
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        counts, bp = O.load_matrix(ids, w.E)
+        plan = O.solve_quota(counts, w.S, w.q_min)
+        X, io, so = O.reroute(counts, plan["inst_expert"], plan["inst_quota"],
+                              plan["inst_per_rank"])
+        _, dr = O.assign(ids, bp, X, plan["inst_expert"], plan["inst_per_rank"], io, so)
+        t1 = time.perf_counter()
+        out = O.permute(x_host, dr, 0, w.R, w.P)
+        del out
+        t2 = time.perf_counter()
+        O.stage_forward(plan["slot_expert"], mw, sw)
+        t3 = time.perf_counter()
+        t_plan += t1 - t0
+        t_perm += t2 - t1
+        t_stage += t3 - t2
+    total = (t_plan + t_perm + t_stage) / passes
+    used = int((plan["slot_expert"] >= 0).sum())
     return {
         "value": w.N / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": (f"whole-layer plan ({t_plan:.2f} s) + permute of {n_rank_sample} of {w.R} ranks "
-                   f"scaled x{w.R / n_rank_sample:g} ({t_perm:.2f} s) + staging of all {len(used)} "
-                   f"used slots ({t_stage:.2f} s); Python+numpy, one thread"),
+        "sample": (f"the whole layer step {passes} times ({t_plan + t_perm + t_stage:.1f} s of CPU "
+                   f"work): plan {t_plan / passes:.2f} s, permute of all {w.R} ranks "
+                   f"{t_perm / passes:.2f} s, staging of all {used} used slots "
+                   f"{t_stage / passes:.2f} s per pass; Python+numpy, one thread"),
     }
 
 
@@ -350,6 +375,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     stage_bytes = 2 * n_used * w.expert_elems * 2
     copy = copy_reference(torch, U)
     comb = combine_figures(torch, U, W, L)
+    floor = launch_floor(torch, U)
     if args.roofline_only:
         out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32", {"ffn": list(w.ffn_shape)})
         out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
@@ -395,6 +421,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "imbalance_after": float(rl.max() / rl.mean()),
         "device_copy_gbs": copy["gbs"],
         **comb,
+        **floor,
     }
     out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
     return out
