@@ -214,6 +214,37 @@ def roofline(bytes_, ms, kernel, traffic=None):
             "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": ms}
 
 
+def grad_reduce_figures(torch, U, L, reps=3):
+    """Backward replica-gradient reduction (fp32) on the step's plan, event-timed.
+    Algorithmic bytes: per replicated expert its main gradient read and written once,
+    per replica its gradient read once and zeroed once."""
+    w = L.w
+    se = L.plan["slot_expert"][:, :w.S].contiguous()
+    gen = torch.Generator(device=DEV).manual_seed(17)
+    main_grad = torch.zeros(w.E, w.expert_elems, dtype=torch.float32, device=DEV)
+    slot_grad = torch.randn(w.R, w.S, w.expert_elems, generator=gen, dtype=torch.float32,
+                            device=DEV)
+    sh = se.cpu().numpy()
+    reps_of = {}
+    for e in sh[sh >= 0]:
+        reps_of[int(e)] = reps_of.get(int(e), 0) + 1
+    nbytes = sum((2 + 2 * n) * w.expert_elems * 4 for n in reps_of.values())
+    s = torch.cuda.current_stream()
+    t = Timer(torch, reps)
+    for _ in range(reps):
+        t.start(s)
+        U.stage_replica_weights(U.STAGE_GRAD_REDUCE, w.R, w.E, w.S, se, w.expert_elems,
+                                main_grad=main_grad, slot_grad=slot_grad, stream=s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del main_grad, slot_grad
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9 if nbytes else 0.0
+    return {"grad_reduce_ms": ms, "grad_reduce_gbs": gbs, "grad_reduce_frac": gbs / HBM_PEAK_GBS,
+            "replicated_experts": len(reps_of)}
+
+
 def launch_floor(torch, U, n=1000):
     """The launch floor the latency-bound kernels are read against: the library's
     smallest launch (a 16-byte uep_device_copy, one workgroup) on the bench stream,
@@ -376,6 +407,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     copy = copy_reference(torch, U)
     comb = combine_figures(torch, U, W, L)
     floor = launch_floor(torch, U)
+    grad = grad_reduce_figures(torch, U, L)
     if args.roofline_only:
         out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32", {"ffn": list(w.ffn_shape)})
         out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
@@ -422,6 +454,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "device_copy_gbs": copy["gbs"],
         **comb,
         **floor,
+        **grad,
     }
     out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
     return out

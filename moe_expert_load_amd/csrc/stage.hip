@@ -117,20 +117,36 @@ __global__ __launch_bounds__(kStThreads) void stage_grad_kernel(
     const int64_t v0 = (task % tiles) * kStTileVec;
     f32x4* mg = main_grad + (int64_t)g_exp[gi] * nvec;
     const int m0 = g_first[gi], m1 = g_first[gi + 1];
+    // the tile's main vectors, then each replica's vectors, all loads of one
+    // operand in flight together; sums in slot order, one fp32 add at a time
+    f32x4 acc[kStVec];
+#pragma unroll
     for (int k = 0; k < kStVec; ++k) {
       const int64_t v = v0 + k * kStThreads + threadIdx.x;
-      if (v >= nvec) break;
-      f32x4 acc = mg[v];
-      for (int m = m0; m < m1; ++m) {
-        f32x4* sg = slot_grad + (int64_t)g_mem[m] * nvec + v;
-        const f32x4 add = __builtin_nontemporal_load(sg);
-        acc.x = acc.x + add.x;
-        acc.y = acc.y + add.y;
-        acc.z = acc.z + add.z;
-        acc.w = acc.w + add.w;
-        __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sg);
+      acc[k] = v < nvec ? mg[v] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int m = m0; m < m1; ++m) {
+      f32x4* sg = slot_grad + (int64_t)g_mem[m] * nvec;
+      f32x4 add[kStVec];
+#pragma unroll
+      for (int k = 0; k < kStVec; ++k) {
+        const int64_t v = v0 + k * kStThreads + threadIdx.x;
+        add[k] = v < nvec ? __builtin_nontemporal_load(sg + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      mg[v] = acc;
+#pragma unroll
+      for (int k = 0; k < kStVec; ++k) {
+        const int64_t v = v0 + k * kStThreads + threadIdx.x;
+        acc[k].x = acc[k].x + add[k].x;
+        acc[k].y = acc[k].y + add[k].y;
+        acc[k].z = acc[k].z + add[k].z;
+        acc[k].w = acc[k].w + add[k].w;
+        if (v < nvec) __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sg + v);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kStVec; ++k) {
+      const int64_t v = v0 + k * kStThreads + threadIdx.x;
+      if (v < nvec) mg[v] = acc[k];
     }
   }
 }
