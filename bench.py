@@ -338,7 +338,7 @@ def combine_figures(torch, U, W, L, reps=5):
 
 
 # ----------------------------------------------------------------------------- CPU leg
-def cpu_baseline(w, ids, x_host, passes=3):
+def cpu_baseline(w, ids, x_host, passes=5):
     """The oracle as it stands, single process: the whole step of the layer (load
     matrix, quota solve, reroute, assignment, permute of every rank, staging of every
     used slot), repeated `passes` times; value = tokens per second of the mean pass."""

@@ -98,9 +98,10 @@ __device__ __forceinline__ int column_sum(const int32_t* __restrict__ counts, in
   for (int r0 = 0; r0 < R; r0 += 32) {
     int v[32];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) v[u] = r0 + u < R ? counts[(int64_t)(r0 + u) * E + e] : 0;
+    for (int u = 0; u < 32; ++u)       // clamped address, no branch: every load issues
+      v[u] = counts[(int64_t)min(r0 + u, R - 1) * E + e];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) s += v[u];
+    for (int u = 0; u < 32; ++u) s += r0 + u < R ? v[u] : 0;
   }
   return s;
 }

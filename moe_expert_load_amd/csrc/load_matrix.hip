@@ -32,31 +32,33 @@ constexpr int kLmBitmapMaxE = 1024;
 constexpr int kLmBitmapMaxK = 16;
 
 // K ids of token (base) into registers; 16-byte loads when K % 4 == 0 and aligned
+template <int kN>
 __device__ __forceinline__ void load_token(const int32_t* __restrict__ p, int K, bool vec,
-                                           int (&v)[kLmBitmapMaxK]) {
+                                           int (&v)[kN]) {
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; k += 4)
+    for (int k = 0; k < kN; k += 4)
       if (k < K) {
         const int4 q = *reinterpret_cast<const int4*>(p + k);
         v[k] = q.x; v[k + 1] = q.y; v[k + 2] = q.z; v[k + 3] = q.w;
       }
   } else {
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k)
+    for (int k = 0; k < kN; ++k)
       if (k < K) v[k] = p[k];
   }
 }
 
+template <int kN>
 __device__ __forceinline__ void store_token(int32_t* __restrict__ p, int K, bool vec,
-                                            const int (&v)[kLmBitmapMaxK]) {
+                                            const int (&v)[kN]) {
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; k += 4)
+    for (int k = 0; k < kN; k += 4)
       if (k < K) *reinterpret_cast<int4*>(p + k) = make_int4(v[k], v[k + 1], v[k + 2], v[k + 3]);
   } else {
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k)
+    for (int k = 0; k < kN; ++k)
       if (k < K) p[k] = v[k];
   }
 }
@@ -87,6 +89,9 @@ __global__ __launch_bounds__(256) void lm_hist(const int32_t* __restrict__ ids,
   for (int e = threadIdx.x; e < g.E; e += 256) ch[e] = lh_lds[e];
 }
 
+// kMaxK bounds K (8, 12 or 16): per-token arrays stay small enough for four waves per
+// SIMD, so the 1024 workgroups of a 32-rank layer fit the chip in one round
+template <int kMaxK>
 __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
                                                int32_t* __restrict__ bucket_pos,
                                                const int32_t* __restrict__ chunk_hist,
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   const int tpw = g.tok_per_chunk / 4;
   const int tw0 = t0 + w * tpw, tw1 = min(t1, tw0 + tpw);
   // the wave's first 64 tokens: loads issued before anything else
-  int v0[kLmBitmapMaxK], pos0[kLmBitmapMaxK];
+  int v0[kMaxK], pos0[kMaxK];
   if (tw0 + lane < tw1) load_token(ids + ((int64_t)r * g.T + tw0 + lane) * g.K, g.K, vec, v0);
   for (int e = threadIdx.x; e < g.E; e += 256) {
     pre[e] = 0;
@@ -134,46 +139,51 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   uint64_t* vmask = mask + w * g.E;       // this wave's masks and running counts
   int32_t* vhist = whist + w * g.E;
   const uint64_t below = lanemask_lt();
+  // one batch of at most 64 tokens per wave: running counts stay 0 and the wave's
+  // per-expert counts are read from its masks afterwards
+  const bool one = tpw <= kWave;
   // pass 1: ranks among the wave's tokens (provisional, relative to the wave).  The
   // first 64 tokens of the wave stay in registers for pass 2; later ones (only when a
   // wave has more than 64 tokens) go through bucket_pos.
   for (int tb = tw0; tb < tw1; tb += kWave) {
     const int t = tb + lane;
     const bool live = t < tw1;
-    int v[kLmBitmapMaxK];
+    int v[kMaxK];
     int32_t* bp = bucket_pos + ((int64_t)r * g.T + t) * g.K;
     if (tb == tw0) {
 #pragma unroll
-      for (int k = 0; k < kLmBitmapMaxK; ++k) v[k] = v0[k];
+      for (int k = 0; k < kMaxK; ++k) v[k] = v0[k];
     } else if (live) {
       load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
     }
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+    for (int k = 0; k < kMaxK; ++k) {
       if (k >= g.K) break;
       if (live && v[k] >= 0 && v[k] < g.E) atomicOr((unsigned long long*)&mask[w * g.E + v[k]], 1ull << lane);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    int pos[kLmBitmapMaxK];
+    int pos[kMaxK];
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+    for (int k = 0; k < kMaxK; ++k) {
       if (k >= g.K) break;
       pos[k] = -1;
       if (live && v[k] >= 0 && v[k] < g.E)
-        pos[k] = vhist[v[k]] + __popcll(vmask[v[k]] & below);
+        pos[k] = (one ? 0 : vhist[v[k]]) + __popcll(vmask[v[k]] & below);
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    for (int e = lane; e < g.E; e += kWave) {
-      const uint64_t m = vmask[e];
-      if (m) {
-        vhist[e] = vhist[e] + __popcll(m);
-        vmask[e] = 0;
+    if (!one) {       // fold the batch into the running counts, clear the masks
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      for (int e = lane; e < g.E; e += kWave) {
+        const uint64_t m = vmask[e];
+        if (m) {
+          vhist[e] = vhist[e] + __popcll(m);
+          vmask[e] = 0;
+        }
       }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (tb == tw0) {
 #pragma unroll
-      for (int k = 0; k < kLmBitmapMaxK; ++k) { v0[k] = v[k]; pos0[k] = pos[k]; }
+      for (int k = 0; k < kMaxK; ++k) { v0[k] = v[k]; pos0[k] = pos[k]; }
     } else if (live) {
       store_token(bp, g.K, vec, pos);
     }
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
     int run = pre[e];
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const int x = whist[ww * g.E + e];
+      const int x = one ? (int)__popcll(mask[ww * g.E + e]) : whist[ww * g.E + e];
       whist[ww * g.E + e] = run;
       run += x;
     }
@@ -197,21 +207,21 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   for (int tb = tw0; tb < tw1; tb += kWave) {
     const int t = tb + lane;
     if (t >= tw1) continue;
-    int v[kLmBitmapMaxK], pos[kLmBitmapMaxK];
+    int v[kMaxK], pos[kMaxK];
     const int64_t base = ((int64_t)r * g.T + t) * g.K;
     if (tb == tw0) {
 #pragma unroll
-      for (int k = 0; k < kLmBitmapMaxK; ++k) { v[k] = v0[k]; pos[k] = pos0[k]; }
+      for (int k = 0; k < kMaxK; ++k) { v[k] = v0[k]; pos[k] = pos0[k]; }
     } else {
       load_token(ids + base, g.K, vec, v);
       load_token(bucket_pos + base, g.K, vec, pos);
     }
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k) {
+    for (int k = 0; k < kMaxK; ++k) {
       if (k >= g.K) break;
       const bool ok = v[k] >= 0 && v[k] < g.E;
 #pragma unroll
-      for (int k2 = 0; k2 < kLmBitmapMaxK; ++k2)
+      for (int k2 = 0; k2 < kMaxK; ++k2)
         if (k2 < k) dup |= ok && v[k2] == v[k];
       if (ok) pos[k] += whist[w * g.E + v[k]];
     }
@@ -388,8 +398,15 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
       UEP_CHECK_LAUNCH();
     }
     const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
-    hipLaunchKernelGGL(lm_rank, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
-                       counts, err, g, vec);
+    if (K <= 8)
+      hipLaunchKernelGGL(lm_rank<8>, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
+                         counts, err, g, vec);
+    else if (K <= 12)
+      hipLaunchKernelGGL(lm_rank<12>, grid, dim3(256), lds, s, topk_ids, bucket_pos,
+                         (const int32_t*)ws, counts, err, g, vec);
+    else
+      hipLaunchKernelGGL(lm_rank<16>, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
+                         counts, err, g, vec);
     UEP_CHECK_LAUNCH();
     return UEP_OK;
   }

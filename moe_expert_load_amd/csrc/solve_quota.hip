@@ -201,12 +201,10 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
       for (int r0 = part; r0 < R; r0 += 16 * per) {
         int v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int r = r0 + u * per;
-          v[u] = r < R ? counts[(int64_t)r * E + e] : 0;
-        }
+        for (int u = 0; u < 16; ++u)     // clamped address, no branch: every load issues
+          v[u] = counts[(int64_t)min(r0 + u * per, R - 1) * E + e];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) acc += v[u];
+        for (int u = 0; u < 16; ++u) acc += r0 + u * per < R ? v[u] : 0;
       }
       atomicAdd(&sq_lds[e], acc);
     }

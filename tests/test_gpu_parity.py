@@ -93,6 +93,22 @@ def test_random_small_plans(seed):
     compare_plan(g, o, S)
 
 
+@pytest.mark.parametrize("K", [3, 7, 8, 9, 12, 13, 16])
+def test_load_matrix_k_variants(K):
+    """Every register-size variant of the ranking kernel (K <= 8, <= 12, <= 16) at its
+    edges, several chunks per rank; K = 3 gives waves more than one batch of tokens."""
+    say("case: load matrix K variant", K)
+    rng = np.random.default_rng(40 + K)
+    R, T, E = 4, 700, 32
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
+    counts_o, bp_o = O.load_matrix(ids, E)
+    err = err_word()
+    counts, bp = U.load_matrix(to_dev(ids), E, err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(counts), counts_o)
+    assert np.array_equal(host(bp), bp_o)
+
+
 def test_plan_edge_cases():
     say("case: edge cases")
     # all routing slots empty
