@@ -183,6 +183,53 @@ def test_solve_quota_large_loads(total):
     assert host(g["stats"]).tolist() == [o["n_replicas"], o["n_steps"], o["t_star"], int(o["stuck"])]
 
 
+def test_plan_already_balanced_and_max_k():
+    """A layer already at the waterline gets the identity plan in zero steps; K = 64,
+    the largest top-k the library takes, through the ballot-ranking path."""
+    say("case: balanced layer, K = 64")
+    R, E, T = 4, 8, 64
+    ids = np.zeros((R, T, 2), dtype=np.int32)
+    for r in range(R):                       # every rank routes to its own two experts
+        ids[r, :, 0], ids[r, :, 1] = 2 * r, 2 * r + 1
+    o = oracle_plan(ids, E, 1, 1)
+    assert o["plan"]["n_steps"] == 0 and o["plan"]["n_replicas"] == 0
+    compare_plan(plan_on_gpu(U, to_dev(ids), E, 1, 1), o, 1)
+    rng = np.random.default_rng(64)
+    ids = random_routing(rng, 2, 40, 64, 128, empty_frac=0.05)
+    o = oracle_plan(ids, 128, 1, 4)
+    compare_plan(plan_on_gpu(U, to_dev(ids), 128, 1, 4), o, 1)
+
+
+def test_permute_with_empty_slots():
+    """Empty top-k slots (-1) get no row; every live pair's row is its token's row."""
+    say("case: permute with empty slots")
+    rng = np.random.default_rng(77)
+    R, T, K, E, H = 3, 150, 4, 12, 136
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.2)
+    o = oracle_plan(ids, E, 1, 2)
+    P = int((o["dest_row"] >= 0).sum())
+    g = torch.Generator(device=DEV).manual_seed(77)
+    x = torch.randn(R, T, H, generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.zeros(P, H, dtype=torch.bfloat16, device=DEV)
+    row_src = torch.full((P,), -9, dtype=torch.int32, device=DEV)
+    U.permute(x, to_dev(o["dest_row"]), out, row_src)
+    exp, exp_src, written = O.permute(host(x.view(torch.int16)).view(np.uint16), o["dest_row"], 0, R, P)
+    assert written.all()
+    assert np.array_equal(host(out.view(torch.int16)).view(np.uint16), exp)
+    assert np.array_equal(host(row_src), exp_src)
+
+
+@pytest.mark.parametrize("layer", [0, 47, 93])
+def test_sweep_layers_plan(layer):
+    """Layers of the 94-layer Qwen3-235B-shaped sweep, each with its own Zipf skew:
+    the whole-group plan bit-exact."""
+    w = W.QWEN_SWEEP
+    say("case: sweep layer", layer, "s =", round(W.zipf_exponent(w, layer), 3))
+    ids = W.routing(w, layer)
+    o = oracle_plan(ids, w.E, w.S, w.q_min)
+    compare_plan(plan_on_gpu(U, to_dev(ids), w.E, w.S, w.q_min), o, w.S)
+
+
 def test_content_errors_are_flagged():
     say("case: content errors")
     err = err_word()
