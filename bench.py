@@ -67,19 +67,21 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.ev[:self.k]]
 
 
-def graph_us(torch, fn, reps=20, replays=5):
+def graph_us(torch, fn, reps=20, replays=5, indexed=False):
     """Mean GPU time of fn() in us: fn is captured `reps` times into one HIP graph and
-    the graph is replayed; host launch overhead is not counted."""
+    the graph is replayed; host launch overhead is not counted.  With indexed=True,
+    fn(stream, i) gets the repetition index, so per-rank work can rotate over ranks and
+    no repetition re-reads the previous one's inputs from the 256 MB last-level cache."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn(s)                                    # warm (first-call setup outside the graph)
+        fn(s, 0) if indexed else fn(s)           # warm (first-call setup outside the graph)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        for _ in range(reps):
-            fn(s)
+        for i in range(reps):
+            fn(s, i) if indexed else fn(s)
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
@@ -329,7 +331,8 @@ def combine_figures(torch, U, W, L, reps=5):
         t.stop(s)
     torch.cuda.synchronize()
     ms = t.mean_ms()
-    rank_us = graph_us(torch, lambda st: U.combine(L.out, L.drow, gate, y, 0, 1, stream=st))
+    rank_us = graph_us(torch, lambda st, i: U.combine(L.out, L.drow, gate, y, i % w.R,
+                                                      i % w.R + 1, stream=st), indexed=True)
     cb = combine_bytes(w.N, L.P, w.H)
     del y, gate
     torch.cuda.empty_cache()
@@ -414,17 +417,19 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         out["cpu_baseline"] = None
         out["extra"] = {"device_copy_gbs": copy["gbs"], "stage_ms": stage_ms}
         return out
-    # per-rank share (rank 0): whole-group plan, its own tokens and slot
-    r = 0
+    # per-rank share, averaged over ranks (repetition i takes rank i mod R): the
+    # whole-group plan, that rank's assignment, slot staging and permute
 
-    def rank_share(s):
+    def rank_share(s, i):
+        r = i % w.R
         L.plan_step(s, r, r + 1)
         L.stage(s, r, r + 1)
         L.permute(s, r, r + 1, row_src=False)
 
-    rank_us = graph_us(torch, rank_share)
+    rank_us = graph_us(torch, rank_share, reps=w.R, replays=2, indexed=True)
     plan_us = graph_us(torch, lambda s: L.plan_step(s))
-    perm_rank_us = graph_us(torch, lambda s: L.permute(s, r, r + 1, row_src=False))
+    perm_rank_us = graph_us(torch, lambda s, i: L.permute(s, i % w.R, i % w.R + 1, row_src=False),
+                            reps=w.R, replays=2, indexed=True)
     L.plan_step(stream)
     torch.cuda.synchronize()
     rl = L.plan["rank_load"].cpu().numpy()
@@ -515,12 +520,12 @@ def bench_waterfill(args, torch, U, W, w):
     out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
                                measured_traffic(w.name))
     out["cpu_baseline"] = None
-    r = 0
     plan_us = graph_us(torch, lambda s: wf_plan(s))
     wf_us = graph_us(torch, lambda s: U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl,
                                                   L.ids, stream=s))
-    rank_us = graph_us(torch, lambda s: (wf_plan(s, r, r + 1),
-                                         L.permute(s, r, r + 1, row_src=False)))
+    rank_us = graph_us(torch, lambda s, i: (wf_plan(s, i % w.R, i % w.R + 1),
+                                            L.permute(s, i % w.R, i % w.R + 1, row_src=False)),
+                       reps=w.R, replays=2, indexed=True)
     torch.cuda.synchronize()
     L_r = rl.cpu().numpy().astype(np.float64)
     shared = np.bincount(sh.cpu().numpy().reshape(-1), minlength=w.R)
@@ -578,9 +583,9 @@ def bench_lplb(args, torch, U, W, w):
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)
     plan_us = graph_us(torch, lambda s: lp_plan(s), reps=5)
-    r = 0
-    rank_us = graph_us(torch, lambda s: (lp_plan(s, r, r + 1),
-                                         L.permute(s, r, r + 1, row_src=False)), reps=5)
+    rank_us = graph_us(torch, lambda s, i: (lp_plan(s, i % w.R, i % w.R + 1),
+                                            L.permute(s, i % w.R, i % w.R + 1, row_src=False)),
+                       reps=8, replays=2, indexed=True)
     # the per-token draw variant: LP split -> copy draw -> instance dispatch layout
     I = len(inst)
     di = torch.empty_like(L.ids)
@@ -689,9 +694,12 @@ def kernel_report(args, torch, U, W):
         d = {"load_matrix": graph_us(torch, L.load), "solve_quota": graph_us(torch, L.solve),
              "reroute_assign": graph_us(torch, L.reroute),
              "permute_whole": graph_us(torch, lambda s: L.permute(s), reps=5),
-             "permute_rank0": graph_us(torch, lambda s: L.permute(s, 0, 1, row_src=False)),
+             "permute_rank": graph_us(torch, lambda s, i: L.permute(s, i % w.R, i % w.R + 1,
+                                                                     row_src=False),
+                                      reps=w.R, indexed=True),
              "stage_whole": graph_us(torch, lambda s: L.stage(s), reps=5),
-             "stage_rank0": graph_us(torch, lambda s: L.stage(s, 0, 1)), "replicas": n_used}
+             "stage_rank": graph_us(torch, lambda s, i: L.stage(s, i % w.R, i % w.R + 1),
+                                    reps=w.R, indexed=True), "replicas": n_used}
         pb = permute_bytes(w.N, w.P, w.H)
         d["permute_whole_gbs"] = pb / (d["permute_whole"] * 1e-6) / 1e9
         d["stage_whole_gbs"] = 4 * n_used * w.expert_elems / (d["stage_whole"] * 1e-6) / 1e9
