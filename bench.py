@@ -406,7 +406,10 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     n_used = int(stats[0])
     pb = permute_bytes(w.N, w.P, w.H)
     perm_ms, stage_ms = tp.mean_ms(), ts.mean_ms()
-    stage_bytes = 2 * n_used * w.expert_elems * 2
+    se_h = L.plan["slot_expert"].cpu().numpy()
+    n_distinct = len(np.unique(se_h[se_h >= 0]))
+    # each staged expert's main read once, each used slot written once
+    stage_bytes = (n_distinct + n_used) * w.expert_elems * 2
     copy = copy_reference(torch, U)
     comb = combine_figures(torch, U, W, L)
     floor = launch_floor(torch, U)
@@ -702,7 +705,10 @@ def kernel_report(args, torch, U, W):
                                     reps=w.R, indexed=True), "replicas": n_used}
         pb = permute_bytes(w.N, w.P, w.H)
         d["permute_whole_gbs"] = pb / (d["permute_whole"] * 1e-6) / 1e9
-        d["stage_whole_gbs"] = 4 * n_used * w.expert_elems / (d["stage_whole"] * 1e-6) / 1e9
+        se_h = L.plan["slot_expert"].cpu().numpy()
+        n_distinct = len(np.unique(se_h[se_h >= 0]))
+        d["stage_whole_gbs"] = ((n_distinct + n_used) * w.expert_elems * 2
+                                / (d["stage_whole"] * 1e-6) / 1e9)
         rep[w.name] = d
         del L
         torch.cuda.empty_cache()

@@ -7,8 +7,8 @@
 // persistent kernel pulling fixed-size tiles from a device-side task list).
 //
 // One persistent grid.  Each workgroup first turns the slot table into its task
-// list in LDS (no host round trip: the plan stays on the device), then walks tasks
-// = (slot or replicated expert) x tile with a grid stride.  A tile is 256 threads x
+// list in LDS (no host round trip: the plan stays on the device): the selected slots
+// grouped by expert.  It then walks tasks = (expert group) x tile with a grid stride.  A tile is 256 threads x
 // kStVec 16-byte vectors = 16 KiB of bf16 weights (or fp32 gradients); all loads of
 // a tile are issued before its stores.  Tile size, grid (16 workgroups per CU) and
 // plain (temporal) loads and stores were picked by measurement on MI355X.
@@ -25,37 +25,97 @@ constexpr int kStVec = 4;                         // 16 KiB tiles (measured best
 constexpr int kStTileVec = kStThreads * kStVec;   // 16-byte vectors per tile
 constexpr int kStMaxSlots = 64 * 8;
 
-__global__ __launch_bounds__(kStThreads) void stage_weights_kernel(
-    const int32_t* __restrict__ slot_expert, int R, int S, int r_begin, int r_end,
-    const u32x4* __restrict__ main_w, u32x4* __restrict__ slot_w, int64_t nvec) {
-  __shared__ int32_t t_slot[kStMaxSlots], t_exp[kStMaxSlots];
-  __shared__ int32_t n_used;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int i = r_begin * S; i < r_end * S; ++i) {
-      const int e = slot_expert[i];
-      if (e >= 0) { t_slot[n] = i; t_exp[n] = e; ++n; }
+// Slot groups, one per expert among the selected slots, members in slot order, built
+// in LDS by the whole workgroup.  kByHome selects slots whose expert is homed in
+// [r_begin, r_end) (gradients go to the main's rank), else slots of ranks in
+// [r_begin, r_end) (weights go to the slot's rank).
+struct StGroups {
+  int32_t g_exp[kStMaxSlots], g_first[kStMaxSlots + 1], g_mem[kStMaxSlots];
+  int32_t lead_cnt[kStMaxSlots], grp_of[kStMaxSlots];
+  int32_t n_grp;
+};
+
+template <bool kByHome>
+__device__ __forceinline__ bool st_selected(int i, int e, int S, int E_loc, int r_begin, int r_end) {
+  if (e < 0) return false;
+  const int r = kByHome ? e / E_loc : i / S;
+  return r >= r_begin && r < r_end;
+}
+
+template <bool kByHome>
+__device__ __forceinline__ void st_build_groups(const int32_t* __restrict__ slot_expert, int n_slots,
+                                                int S, int E_loc, int r_begin, int r_end,
+                                                StGroups& G) {
+  // a selected slot leads its expert's group if no earlier selected slot holds it
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
+    const int e = slot_expert[i];
+    int cnt = 0;
+    if (st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end)) {
+      bool seen = false;
+      for (int i2 = 0; i2 < i; ++i2)
+        seen |= slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end);
+      if (!seen)
+        for (int i2 = i; i2 < n_slots; ++i2)
+          cnt += slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end);
     }
-    n_used = n;
+    G.lead_cnt[i] = cnt;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {          // serial scan over at most 512 counts
+    int ng = 0, nm = 0;
+    for (int i = 0; i < n_slots; ++i) {
+      if (G.lead_cnt[i] == 0) continue;
+      G.g_exp[ng] = slot_expert[i];
+      G.g_first[ng] = nm;
+      G.grp_of[i] = ng;
+      nm += G.lead_cnt[i];
+      ++ng;
+    }
+    G.g_first[ng] = nm;
+    G.n_grp = ng;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {   // members, in slot order
+    const int e = slot_expert[i];
+    if (!st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end)) continue;
+    int lead = -1, pos = 0;
+    for (int i2 = 0; i2 < i; ++i2)
+      if (slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end)) {
+        if (lead < 0) lead = i2;
+        ++pos;
+      }
+    if (lead < 0) lead = i;
+    G.g_mem[G.g_first[G.grp_of[lead]] + pos] = i;
+  }
+  __syncthreads();
+}
+
+// Weights: each tile of an expert's main is read once and written to every slot of
+// its group, so an expert replicated n times costs one read and n writes.
+__global__ __launch_bounds__(kStThreads) void stage_weights_kernel(
+    const int32_t* __restrict__ slot_expert, int R, int E, int S, int r_begin, int r_end,
+    const u32x4* __restrict__ main_w, u32x4* __restrict__ slot_w, int64_t nvec) {
+  __shared__ StGroups G;
+  st_build_groups<false>(slot_expert, R * S, S, E / R, r_begin, r_end, G);
   const int64_t tiles = (nvec + kStTileVec - 1) / kStTileVec;
-  const int64_t tasks = n_used * tiles;
+  const int64_t tasks = G.n_grp * tiles;
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
-    const int u = (int)(task / tiles);
+    const int gi = (int)(task / tiles);
     const int64_t v0 = (task % tiles) * kStTileVec;
-    const u32x4* src = main_w + (int64_t)t_exp[u] * nvec;
-    u32x4* dst = slot_w + (int64_t)t_slot[u] * nvec;
+    const u32x4* src = main_w + (int64_t)G.g_exp[gi] * nvec;
     u32x4 buf[kStVec];
 #pragma unroll
     for (int k = 0; k < kStVec; ++k) {
       const int64_t v = v0 + k * kStThreads + threadIdx.x;
       if (v < nvec) buf[k] = src[v];
     }
+    for (int m = G.g_first[gi]; m < G.g_first[gi + 1]; ++m) {
+      u32x4* dst = slot_w + (int64_t)G.g_mem[m] * nvec;
 #pragma unroll
-    for (int k = 0; k < kStVec; ++k) {
-      const int64_t v = v0 + k * kStThreads + threadIdx.x;
-      if (v < nvec) dst[v] = buf[k];
+      for (int k = 0; k < kStVec; ++k) {
+        const int64_t v = v0 + k * kStThreads + threadIdx.x;
+        if (v < nvec) dst[v] = buf[k];
+      }
     }
   }
 }
@@ -64,52 +124,12 @@ __global__ __launch_bounds__(kStThreads) void stage_grad_kernel(
     const int32_t* __restrict__ slot_expert, int R, int E, int S, int r_begin, int r_end,
     f32x4* __restrict__ main_grad, f32x4* __restrict__ slot_grad, int64_t nvec) {
   // groups: one per replicated expert homed in [r_begin, r_end), members in slot order
-  __shared__ int32_t g_exp[kStMaxSlots], g_first[kStMaxSlots + 1], g_mem[kStMaxSlots];
-  __shared__ int32_t lead_cnt[kStMaxSlots];   // members of the group a slot leads, else 0
-  __shared__ int32_t grp_of[kStMaxSlots];     // group index of a leading slot
-  __shared__ int32_t n_grp;
-  const int E_loc = E / R;
-  const int n_slots = R * S;
-  // a slot leads its expert's group if no earlier slot holds the same expert
-  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
-    const int e = slot_expert[i];
-    int cnt = 0;
-    if (e >= 0 && e / E_loc >= r_begin && e / E_loc < r_end) {
-      bool seen = false;
-      for (int i2 = 0; i2 < i; ++i2) seen |= slot_expert[i2] == e;
-      if (!seen)
-        for (int i2 = i; i2 < n_slots; ++i2) cnt += slot_expert[i2] == e;
-    }
-    lead_cnt[i] = cnt;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {          // serial scan over at most 512 counts
-    int ng = 0, nm = 0;
-    for (int i = 0; i < n_slots; ++i) {
-      if (lead_cnt[i] == 0) continue;
-      g_exp[ng] = slot_expert[i];
-      g_first[ng] = nm;
-      grp_of[i] = ng;
-      nm += lead_cnt[i];
-      ++ng;
-    }
-    g_first[ng] = nm;
-    n_grp = ng;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {   // members, in slot order
-    const int e = slot_expert[i];
-    if (e < 0 || e / E_loc < r_begin || e / E_loc >= r_end) continue;
-    int lead = -1, pos = 0;
-    for (int i2 = 0; i2 < i; ++i2)
-      if (slot_expert[i2] == e) {
-        if (lead < 0) lead = i2;
-        ++pos;
-      }
-    if (lead < 0) lead = i;
-    g_mem[g_first[grp_of[lead]] + pos] = i;
-  }
-  __syncthreads();
+  __shared__ StGroups G;
+  st_build_groups<true>(slot_expert, R * S, S, E / R, r_begin, r_end, G);
+  const int n_grp = G.n_grp;
+  const int32_t* g_exp = G.g_exp;
+  const int32_t* g_first = G.g_first;
+  const int32_t* g_mem = G.g_mem;
   const int64_t tiles = (nvec + kStTileVec - 1) / kStTileVec;
   const int64_t tasks = n_grp * tiles;
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
@@ -184,7 +204,7 @@ extern "C" uep_status uep_stage_replica_weights(int32_t mode, int32_t R, int32_t
     if ((reinterpret_cast<uintptr_t>(main_w) | reinterpret_cast<uintptr_t>(slot_w)) % 16)
       return UEP_EGEOM;
     hipLaunchKernelGGL(stage_weights_kernel, dim3(st_grid()), dim3(kStThreads), 0, s,
-                       slot_expert, R, S, r_begin, r_end,
+                       slot_expert, R, E, S, r_begin, r_end,
                        reinterpret_cast<const u32x4*>(main_w), reinterpret_cast<u32x4*>(slot_w),
                        expert_elems / 8);
   } else if (mode == UEP_STAGE_GRAD_REDUCE) {

@@ -325,6 +325,26 @@ def test_qwen_layer_full_size():
     del main_w, slot_w
 
 
+def test_stage_weights_matches_oracle():
+    """Forward staging with one expert in several slots (one read, fan-out writes),
+    rank sub-ranges and a ragged tile; every slot compared, untouched ones included."""
+    say("case: stage weights")
+    rng = np.random.default_rng(12)
+    R, E, S, n = 8, 16, 2, 8 * 3000 + 8
+    se = np.full((R, S), -1, dtype=np.int32)
+    se[1, 0] = 0; se[2, 1] = 0; se[5, 0] = 0; se[3, 0] = 7; se[6, 1] = 7; se[7, 0] = 15
+    se[0, 1] = 9
+    main = rng.integers(0, 1 << 16, (E, n), dtype=np.uint16)
+    for (r0, r1) in ((0, R), (2, 6), (5, 6), (3, 3)):
+        slot = rng.integers(0, 1 << 16, (R, S, n), dtype=np.uint16)
+        slot_d = to_dev(slot.view(np.int16), torch.int16)
+        U.stage_replica_weights(U.STAGE_WEIGHTS, R, E, S, to_dev(se), n,
+                                main_w=to_dev(main.view(np.int16), torch.int16), slot_w=slot_d,
+                                r_begin=r0, r_end=r1)
+        O.stage_forward(se, main, slot, r0, r1)
+        assert np.array_equal(host(slot_d).view(np.uint16), slot), (r0, r1)
+
+
 def test_grad_reduce_matches_oracle():
     say("case: grad reduce")
     rng = np.random.default_rng(11)
