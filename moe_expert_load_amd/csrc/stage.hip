@@ -16,6 +16,8 @@
 // GRAD_REDUCE keeps the article's order fixed: for every element the main's
 // gradient is added to the replicas' gradients one at a time in ascending rank
 // (fp32, round to nearest even, no FMA), then each replica gradient is set to +0.
+#include <atomic>
+
 #include "common.h"
 
 namespace uep {
@@ -171,16 +173,19 @@ __global__ __launch_bounds__(kStThreads) void stage_grad_kernel(
   }
 }
 
+// 16 workgroups per CU of the current device (the CU count is looked up once per device)
 static int st_grid() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 16;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     hipDeviceProp_t p;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
-      cus = p.multiProcessorCount;
-    if (cus <= 0) cus = 256;
+    n = (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
+            ? p.multiProcessorCount : 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus * 16;
+  return n * 16;
 }
 
 }  // namespace uep

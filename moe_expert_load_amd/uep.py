@@ -82,7 +82,15 @@ def _check(status: int, name: str) -> None:
 
 
 def _p(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a contiguous GPU tensor (None stays NULL).  A host tensor is
+    refused here: its address handed to a kernel would fault the device."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("the library takes device memory: got a tensor on " + str(t.device))
+    if not t.is_contiguous():
+        raise TypeError("the library takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _s(stream) -> ctypes.c_void_p:

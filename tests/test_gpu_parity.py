@@ -258,6 +258,11 @@ def test_host_argument_errors():
     x = torch.zeros(2, 4, 12, dtype=torch.bfloat16, device=DEV)  # H % 8 != 0
     with pytest.raises(U.UEPError):
         U.permute(x, t, torch.zeros(16, 12, dtype=torch.bfloat16, device=DEV))
+    # host memory and strided views are refused before anything reaches a kernel
+    with pytest.raises(TypeError):
+        U.load_matrix(torch.zeros(2, 4, 2, dtype=torch.int32), 8)
+    with pytest.raises(TypeError):
+        U.load_matrix(torch.zeros(2, 4, 4, dtype=torch.int32, device=DEV)[:, :, ::2], 8)
 
 
 @pytest.mark.parametrize("nbytes", [16, 16 * 4096, 16 * (3 * 4096 + 17)])
