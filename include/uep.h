@@ -287,9 +287,10 @@ uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
  *   inst_expert_host [R*inst_per_rank] (every expert with load needs >= 1 instance,
  *   at most one per rank) and copies it into the device buffer `lp` of
  *   uep_lplb_struct_size() bytes (synchronous copy; call outside the hot loop).
- * uep_lplb (per batch): a fixed number of fp32 Mehrotra predictor-corrector steps.
+ * uep_lplb (per batch): fp32 Mehrotra predictor-corrector steps, at most `iters`.
  *   counts     [R][E]     in   load matrix
- *   iters                 in   interior-point iterations (1..200; 30 is plenty)
+ *   iters                 in   iteration cap (0..200; the solve stops earlier once the
+ *                              duality gap is at most 1e-4 of M; 30 is plenty)
  *   x          [n_copies] out  split per copy (token units, copies ordered by expert,
  *                              then instance id), normalised to sum to each count
  *   m          [1]        out  max rank load of that split
