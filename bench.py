@@ -341,6 +341,20 @@ def combine_figures(torch, U, W, L, reps=5):
 
 
 # ----------------------------------------------------------------------------- CPU leg
+def host_cpu():
+    """CPU model name and logical CPU count of this host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def cpu_baseline(w, ids, x_host, passes=5):
     """The oracle as it stands, single process: the whole step of the layer (load
     matrix, quota solve, reroute, assignment, permute of every rank, staging of every
@@ -367,6 +381,7 @@ def cpu_baseline(w, ids, x_host, passes=5):
         t_perm += t2 - t1
         t_stage += t3 - t2
     total = (t_plan + t_perm + t_stage) / passes
+    model, ncpu = host_cpu()
     used = int((plan["slot_expert"] >= 0).sum())
     return {
         "value": w.N / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -374,6 +389,7 @@ def cpu_baseline(w, ids, x_host, passes=5):
                    f"work): plan {t_plan / passes:.2f} s, permute of all {w.R} ranks "
                    f"{t_perm / passes:.2f} s, staging of all {used} used slots "
                    f"{t_stage / passes:.2f} s per pass; Python+numpy, one thread"),
+        "host": {"cpu_model": model, "logical_cpus": ncpu},
     }
 
 
@@ -539,6 +555,7 @@ def bench_waterfill(args, torch, U, W, w):
     shared_all = np.bincount(sh_all.cpu().numpy().reshape(-1), minlength=w.R)
     out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "waterfill_us": wf_us,
                     "waterline": int(wl.item()),
+                    "imbalance_routed_only": float(L_r.max() / L_r.mean()),
                     "imbalance_shared_local": float((L_r + local).max() / (L_r + local).mean()),
                     "imbalance_shared_waterfill": float((L_r + shared).max() / (L_r + shared).mean()),
                     "imbalance_shared_waterfill_all_ranks":
