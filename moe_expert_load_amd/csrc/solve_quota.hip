@@ -12,11 +12,12 @@
 //
 // Step rule ("fill to the waterline", T* = ceil(sum_e c_e / R)): h = most loaded
 // rank (lowest index on ties); stop if L_h <= T*.  Donors are h's mains with a
-// non-zero quota, quota descending then id ascending.  For a donor e: top up the
-// least loaded rank (< T*) already holding a replica of e, moving
-// min(q_e, L_h - T*, T* - L_j); otherwise open a replica in the lowest free slot of
-// the least loaded rank (< T*, free slot, no copy of e) if that move is >= q_min.
-// The first donor that can move ends the step; none -> stop.
+// non-zero quota, quota descending then id ascending.  For a donor e: open a replica
+// in the lowest free slot of the least loaded rank t (L_t < T*, a free slot, no copy
+// of e), moving min(q_e, L_h - T*, T* - L_t) if that is >= q_min.  The first donor
+// that can move ends the step; none -> stop.  Every move empties the donor main,
+// brings h down to T* or brings t up to T*, so a placed replica never takes more
+// tokens later and there is no "add to an existing replica" case.
 #include "common.h"
 
 namespace uep {
@@ -57,13 +58,6 @@ __device__ __forceinline__ int slot_of(const SqLane<kS>& st, int S, int e) {
 }
 
 template <int kS>
-__device__ __forceinline__ void add_to_slot(SqLane<kS>& st, int slot, int delta) {
-#pragma unroll
-  for (int s = 0; s < kS; ++s)
-    if (s == slot) st.sl_q[s] += delta;
-}
-
-template <int kS>
 __device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delta) {
   const int slot = S - st.free_slots;
 #pragma unroll
@@ -73,9 +67,7 @@ __device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delt
 }
 
 // The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
-// reduction give value and lowest lane together; top-up candidates (keys below
-// 2^31) sort before new-replica candidates, so one unsigned minimum picks the
-// receiver of either kind with the rule's precedence.
+// reduction give value and lowest lane together.
 template <int kS>
 __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
                                               int R, int E_loc, int S, int q_min, int t_star,
@@ -94,25 +86,13 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       if (kd < 0) break;
       const int qd = kd >> 6, jd = 63 - (kd & 63);
       const int e = h * E_loc + jd;
-      const int has = slot_of<kS>(st, S, e);
-      const bool below = active && lane != h && st.L < t_star;
-      const bool c1 = below && has >= 0;
-      const bool c2 = below && has < 0 && st.free_slots > 0;
-      const uint32_t key = c1   ? ((uint32_t)st.L << 6) | (uint32_t)lane
-                           : c2 ? 0x80000000u | ((uint32_t)st.L << 6) | (uint32_t)lane
-                                : 0xFFFFFFFFu;
-      const uint32_t km = wave_min_u32(key);
+      const bool c2 = active && lane != h && st.L < t_star && st.free_slots > 0 &&
+                      slot_of<kS>(st, S, e) < 0;
+      const uint32_t km = wave_min_u32(c2 ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
       if (km != 0xFFFFFFFFu) {
         const int tgt = (int)(km & 63u);
-        const int Lt = (int)((km >> 6) & ((1u << kPackBits) - 1));
+        const int Lt = (int)(km >> 6);
         const int delta = min(qd, min(over, t_star - Lt));
-        if (km < 0x80000000u) {                       // top up an existing replica
-          if (lane == tgt) { add_to_slot<kS>(st, has, delta); st.L += delta; }
-          if (lane == h) st.L -= delta;
-          if (lane == 0) q_main[e] = qd - delta;
-          moved = true;
-          break;
-        }
         if (delta >= q_min) {                         // open a new replica
           if (lane == tgt) { open_slot<kS>(st, S, e, delta); st.L += delta; }
           if (lane == h) st.L -= delta;
@@ -147,19 +127,8 @@ __device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, int
       if (qd <= 0) break;
       const int jd = first_lane(dk == qd);
       const int e = h * E_loc + jd;
-      const int has = slot_of<kS>(st, S, e);
-      const bool c1 = active && lane != h && has >= 0 && st.L < t_star;
-      const int kj = wave_min(c1 ? st.L : kBig);
-      if (kj != kBig) {
-        const int j = first_lane(c1 && st.L == kj);
-        const int delta = min(qd, min(over, t_star - kj));
-        if (lane == j) { add_to_slot<kS>(st, has, delta); st.L += delta; }
-        if (lane == h) st.L -= delta;
-        if (lane == 0) q_main[e] = qd - delta;
-        moved = true;
-        break;
-      }
-      const bool c2 = active && lane != h && st.free_slots > 0 && has < 0 && st.L < t_star;
+      const bool c2 = active && lane != h && st.free_slots > 0 && st.L < t_star &&
+                      slot_of<kS>(st, S, e) < 0;
       const int kt = wave_min(c2 ? st.L : kBig);
       if (kt != kBig) {
         const int delta = min(qd, min(over, t_star - kt));

@@ -20,23 +20,23 @@ The article does not print the search.  Reading used here ("fill to the waterlin
     repeat:
       h = the most loaded rank (lowest index on ties); stop if L_h <= T*
       try the mains of h in order (quota descending, expert id ascending), skipping
-      empty ones; for a donor expert e:
-        top-up : among ranks j != h already holding a replica of e with L_j < T*,
-                 take the least loaded (lowest index on ties) and move
-                 d = min(q_main[e], L_h - T*, T* - L_j) from the main to that replica;
-        else new replica: among ranks t != h with a free slot, no instance of e and
-                 L_t < T*, take the least loaded (lowest index on ties);
-                 d = min(q_main[e], L_h - T*, T* - L_t); only if d >= q_min put e into
-                 t's lowest free slot with quota d;
-        the first donor that can move applies its move and the step ends.
+      empty ones; for a donor expert e: among ranks t != h with a free slot, no
+      instance of e and L_t < T*, take the least loaded (lowest index on ties);
+      d = min(q_main[e], L_h - T*, T* - L_t); only if d >= q_min put e into t's
+      lowest free slot with quota d; the first donor that can move applies its move
+      and the step ends.
       if no donor of h can move, stop (the peak cannot fall further).
 
 Donors only fall to T* and receivers only rise to T*, so every step exhausts a main,
-brings a donor down to T* or fills a receiver up to T*: at most E + 2R steps.
+brings a donor down to T* or fills a receiver up to T*: at most E + 2R steps.  The
+same fact means a replica, once placed, never receives more: its expert's main is
+empty, or its home rank sits at T* (never again the heaviest above T*), or the
+replica's rank sits at T* (never again a receiver).  So "adding to an existing
+replica" never arises, and every move opens a new replica.
 Home of expert e: rank e // (E/R) (contiguous EP blocks).  Physical instance ids:
 i = r*(E_loc+S) + j; j < E_loc is the main of expert r*E_loc + j, j >= E_loc is slot j-E_loc.
 
-Pins (tests/test_oracle_quota.py): identity when balanced, S = 0 or q_min too large;
+Pins (tests/test_oracle_load_quota.py): identity when balanced, S = 0 or q_min too large;
 the one-hot-expert closed form; the constraints of the article as invariants;
 the step bound; brute force over slot assignments on tiny inputs (quality report).
 """
@@ -72,17 +72,6 @@ def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
         moved = False
         for e in mains:
             over = L[h] - t_star
-            tops = [(L[j], j) for j in range(R) if j != h and e in slot_e[j] and L[j] < t_star]
-            if tops:
-                Lj, j = min(tops)
-                d = min(q_main[e], over, t_star - Lj)
-                s = slot_e[j].index(e)
-                slot_q[j][s] += d
-                q_main[e] -= d
-                L[h] -= d
-                L[j] += d
-                moved = True
-                break
             news = [(L[t], t) for t in range(R)
                     if t != h and free[t] > 0 and e not in slot_e[t] and L[t] < t_star]
             if news:

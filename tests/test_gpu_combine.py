@@ -75,6 +75,23 @@ def test_combine_rank_range_and_noops():
     assert (bits(y) == 0).all()
 
 
+def test_combine_summation_order_hand_case():
+    """Terms 1, 2^-8, 0.75*2^-24, 0.75*2^-24: summed in ascending k in fp32 the small
+    terms are lost and the bf16 tie rounds to even (0x3F80); the reversed slot order
+    makes them meet first and gives 0x3F81.  Same on the GPU as in the oracle."""
+    say("case: combine summation order")
+    H = 64
+    rows = np.repeat(np.array([[0x3F80], [0x3B80], [0x3380], [0x3380]], dtype=np.int16), H, axis=1)
+    y_disp = torch.from_numpy(rows).to(DEV).view(torch.bfloat16)
+    dr = np.array([[[0, 1, 2, 3]], [[3, 2, 1, 0]]], dtype=np.int32)
+    g = np.array([[[1.0, 1.0, 0.75, 0.75]], [[0.75, 0.75, 1.0, 1.0]]], dtype=np.float32)
+    y = torch.empty(2, 1, H, dtype=torch.bfloat16, device=DEV)
+    U.combine(y_disp, to_dev(dr), to_dev(g, torch.float32), y)
+    got = bits(y)
+    assert (got[0] == 0x3F80).all() and (got[1] == 0x3F81).all()
+    assert np.array_equal(got, O.combine(rows.view(np.uint16), dr, g))
+
+
 def test_combine_inverts_permute_with_one_hot_weights():
     """permute then combine with weight 1 on one live slot (0 elsewhere) returns x bit
     for bit, at the Tiny shape through the device plan and permute."""

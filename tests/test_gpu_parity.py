@@ -16,6 +16,7 @@ from moe_expert_load_amd import uep as U                 # noqa: E402
 from moe_expert_load_amd import workload as W            # noqa: E402
 from tests.gpu_helpers import (DEV, to_dev, host, err_word, say, plan_on_gpu,  # noqa: E402
                                random_routing)
+from tests.conftest import golden                        # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -181,6 +182,25 @@ def test_solve_quota_large_loads(total):
     assert np.array_equal(host(g["slot_expert"]), o["slot_expert"])
     assert np.array_equal(host(g["rank_load"]), o["rank_load"])
     assert host(g["stats"]).tolist() == [o["n_replicas"], o["n_steps"], o["t_star"], int(o["stuck"])]
+
+
+QUOTA_RULE_CASES = golden("quota_rule_cases.json")["cases"]
+
+
+@pytest.mark.parametrize("case", QUOTA_RULE_CASES, ids=[c["name"] for c in QUOTA_RULE_CASES])
+def test_solve_quota_tie_and_order_rules(case):
+    """Hand-worked plans that each hinge on one rule (rank ties, donor ties, the strict
+    'below T*' receiver test with q_min = 0, the slot fill order): the kernel's plan
+    equals the hand result and the oracle's."""
+    say("case: solve_quota rule", case["name"])
+    counts = np.zeros((case["R"], case["E"]), dtype=np.int32)
+    counts[0] = case["c"]
+    o = O.solve_quota(counts, case["S"], case["q_min"])
+    g = U.solve_quota(to_dev(counts), case["S"], case["q_min"])
+    for key in ("slot_expert", "inst_expert", "inst_quota", "rank_load"):
+        assert host(g[key]).tolist() == case[key] == o[key].tolist(), key
+    assert host(g["stats"]).tolist() == [case["n_replicas"], case["n_steps"], case["t_star"],
+                                         int(case["stuck"])]
 
 
 def test_plan_already_balanced_and_max_k():
@@ -450,3 +470,33 @@ def test_waterfill_random_small(seed):
                                           local_pref_shift=shift, all_ranks=mode)
         assert host(wl)[0] == H_o and np.array_equal(host(sl), S_o)
         assert np.array_equal(host(sh), sh_o)
+
+
+def test_waterfill_zero_slack_and_fallback_cases():
+    """Two hand cases (the oracle's pins): W = 16 with a zero-weight source, where the
+    draw must never pick the source even at v = 0; and W = 0, where the token goes to
+    the lightest clearly lighter (17:16) candidate or stays home."""
+    say("case: waterfill zero slack / fallback")
+    R, E, T = 3, 3, 256
+    ids = np.full((R, T, 1), -1, dtype=np.int32)
+    ids[0, :, 0] = 1
+    ids[1, :, 0] = 0
+    ids[2, 0, 0] = 1
+    counts, _ = O.load_matrix(ids, E)
+    B = np.array([0, T, 0], dtype=np.int32)
+    sh_o, H_o, S_o, _ = O.waterfill(counts, ids, B, 8, 3)
+    sh, wl, sl, rl, _ = U.waterfill(to_dev(counts), to_dev(ids), to_dev(B), 8, 3)
+    assert host(wl)[0] == H_o == 257 and host(sl).tolist() == S_o.tolist() == [1, 0, 257]
+    assert np.array_equal(host(sh), sh_o) and (sh_o[1] == 0).all()
+
+    R, E, T = 8, 8, 2
+    counts = np.zeros((R, E), dtype=np.int32)
+    counts[0, :4] = [100, 95, 80, 60]
+    ids = np.full((R, T, 3), -1, dtype=np.int32)
+    ids[0, 0] = [1, 2, 3]
+    ids[0, 1, 0] = 1
+    B = np.array([2, 0, 0, 0, 0, 0, 0, 0], dtype=np.int32)
+    sh_o, H_o, _, _ = O.waterfill(counts, ids, B, 0, 0)
+    sh, wl, _, _, _ = U.waterfill(to_dev(counts), to_dev(ids), to_dev(B), 0, 0)
+    assert host(wl)[0] == H_o == 43
+    assert np.array_equal(host(sh), sh_o) and sh_o[0].tolist() == [3, 0]

@@ -103,6 +103,26 @@ def test_hand_example():
     assert (y[1] == 0).all()
 
 
+def test_summation_order_is_ascending_k_in_fp32():
+    """Terms 1, 2^-8, 0.75*2^-24, 0.75*2^-24 (rows 1.0, 2^-8, 2^-24, 2^-24; weights 1, 1,
+    0.75, 0.75).  In k order each small term is below half an ulp of 1 + 2^-8 (2^-24)
+    and is lost: the fp32 sum is 1 + 2^-8, the exact midpoint of the bf16 neighbours
+    1.0 and 1 + 2^-7, which rounds to even, 0x3F80.  Adding the two small terms first
+    (any other order) or in a wider type gives 1 + 2^-8 + 1.5*2^-24, which rounds to
+    1 + 2^-8 + 2^-23 in fp32 and to 0x3F81 in bf16."""
+    y_disp = np.array([[0x3F80], [0x3B80], [0x3380], [0x3380]], dtype=np.uint16)
+    assert bf16_bits_to_f32(y_disp).ravel().tolist() == [1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24]
+    dr = np.arange(4, dtype=np.int32).reshape(1, 1, 4)
+    g = np.array([[[1.0, 1.0, 0.75, 0.75]]], dtype=np.float32)
+    assert combine_f32(y_disp, dr, g)[0, 0, 0] == np.float32(1 + 2.0 ** -8)
+    assert O.combine(y_disp, dr, g)[0, 0].tolist() == [0x3F80]
+    # the same terms in reverse slot order: the small ones meet first
+    dr_rev = dr[:, :, ::-1].copy()
+    g_rev = g[:, :, ::-1].copy()
+    assert combine_f32(y_disp, dr_rev, g_rev)[0, 0, 0] == np.float32(1 + 2.0 ** -8 + 2.0 ** -23)
+    assert O.combine(y_disp, dr_rev, g_rev)[0, 0].tolist() == [0x3F81]
+
+
 def test_fp32_sum_within_recursive_summation_bound():
     """|fl(sum) - exact| <= gamma_K * sum |g_k x_k| with gamma_K = K u / (1 - K u),
     u = 2^-24: the bound for K rounded products summed left to right."""
@@ -122,6 +142,17 @@ def test_fp32_sum_within_recursive_summation_bound():
                 exact = math.fsum(terms)
                 bound = gamma * sum(abs(v) for v in terms)
                 assert abs(float(acc[r, t, h]) - exact) <= bound
+
+
+def test_rank_range_leaves_other_ranks_zero():
+    rng = np.random.default_rng(9)
+    ids, dr, x, out = _toy(rng)
+    R, T, K = dr.shape
+    g = rng.random((R, T, K)).astype(np.float32)
+    whole = O.combine(out, dr, g)
+    part = O.combine(out, dr, g, 1, 2)
+    assert np.array_equal(part[1], whole[1])
+    assert (part[0] == 0).all() and (part[2] == 0).all()
 
 
 def test_combine_tokens_matches_whole():

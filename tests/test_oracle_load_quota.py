@@ -95,6 +95,8 @@ def _check_plan_invariants(counts, S, q_min, plan):
         assert len(set(used.tolist())) == len(used)                              # no duplicate
         slots = block[E_loc:]
         assert (slots >= 0).sum() <= S
+        used_slots = (slots >= 0).tolist()                     # slots fill from slot 0 up
+        assert used_slots == sorted(used_slots, reverse=True)
         for s in range(S):
             if slots[s] >= 0:
                 assert iq[r * ipr + E_loc + s] >= max(q_min, 1)                  # replica quota
@@ -121,6 +123,23 @@ def test_quota_hand_example():
     for key in ("slot_expert", "inst_expert", "inst_quota", "rank_load"):
         assert plan[key].tolist() == g[key], key
     _check_plan_invariants(counts, g["S"], g["q_min"], plan)
+
+
+QUOTA_RULE_CASES = golden("quota_rule_cases.json")["cases"]
+
+
+@pytest.mark.parametrize("case", QUOTA_RULE_CASES, ids=[c["name"] for c in QUOTA_RULE_CASES])
+def test_quota_tie_and_order_rules_by_hand(case):
+    """Hand-worked plans that each hinge on one rule: rank ties, donor ties, the strict
+    'below T*' receiver test with q_min = 0, and the slot fill order."""
+    counts = np.zeros((case["R"], case["E"]), dtype=np.int64)
+    counts[0] = case["c"]
+    plan = O.solve_quota(counts, case["S"], case["q_min"])
+    for key in ("slot_expert", "inst_expert", "inst_quota", "rank_load"):
+        assert plan[key].tolist() == case[key], key
+    for key in ("t_star", "n_steps", "n_replicas", "stuck"):
+        assert plan[key] == case[key], key
+    _check_plan_invariants(counts, case["S"], case["q_min"], plan)
 
 
 def test_quota_identity_when_balanced():

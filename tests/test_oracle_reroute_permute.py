@@ -58,6 +58,13 @@ def check_assign_properties(ids, bp, X, inst_offset, src_offset, ipr, dest_inst,
                 t_idx, _ = np.nonzero(sel)
                 order = np.argsort(dest_row[r][sel])
                 assert (np.diff(t_idx[order]) > 0).all()               # token order inside
+    # per (rank, expert), in token order: the local instance first, then the remote
+    # instances in ascending physical id
+    for r in range(R):
+        for e in np.unique(ids[r][ok[r]]):
+            t_idx, k_idx = np.nonzero(ids[r] == e)                     # ascending t
+            seq = [(0 if int(i) // ipr == r else 1, int(i)) for i in dest_inst[r][t_idx, k_idx]]
+            assert seq == sorted(seq)
 
 
 def test_reroute_hand_example():
@@ -66,6 +73,30 @@ def test_reroute_hand_example():
                           np.array(g["inst_quota"]), 3)
     assert X.tolist() == g["xfer"]
     assert io.tolist() == g["inst_offset"]
+
+
+def test_assign_hand_example_two_remote_instances():
+    """R = 3, one main per rank, one slot per rank (4 physical ids = r*2 + j).  Expert 0
+    has its main (instance 0) and replicas on ranks 1 (instance 3) and 2 (instance 5)
+    with quotas 1, 2, 2.  Rank 0 routes tokens 0..3 to expert 0, rank 2 routes token 0.
+    Local pass: rank 0 keeps 1 (instance 0), rank 2 keeps 1 (instance 5, 1 left).
+    Remote pass: rank 0's 3 remaining tokens fill instance 3 (2) then instance 5 (1).
+    Rows: instance blocks at offsets 0 (i0), 1 (i3), 3 (i5); inside i5 rank 0 first."""
+    ipr = 2
+    ie = np.array([0, -1, 1, 0, 2, 0])
+    q = np.array([1, 0, 0, 2, 0, 2])
+    ids = np.full((3, 4, 1), -1, dtype=np.int64)
+    ids[0, :, 0] = 0
+    ids[2, 0, 0] = 0
+    counts, bp = O.load_matrix(ids, 3)
+    X, io, so = O.reroute(counts, ie, q, ipr)
+    assert X[0].tolist() == [1, 0, 0, 2, 0, 1] and X[2].tolist() == [0, 0, 0, 0, 0, 1]
+    assert io.tolist() == [0, 1, 1, 1, 3, 3, 5]
+    di, dr = O.assign(ids, bp, X, ie, ipr, io, so)
+    assert di[0, :, 0].tolist() == [0, 3, 3, 5] and dr[0, :, 0].tolist() == [0, 1, 2, 3]
+    assert di[2, 0, 0] == 5 and dr[2, 0, 0] == 4
+    assert (di[1] == -1).all() and (dr[2, 1:] == -1).all()
+    check_assign_properties(ids, bp, X, io, so, ipr, di, dr)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -129,6 +160,11 @@ def test_permute_matches_fancy_index():
     assert np.array_equal(out1[wr1], out[wr1])
     exp, src = O.permute_rows(x, dr, np.array([0, 5, w.P - 1]))
     assert np.array_equal(exp, out[[0, 5, w.P - 1]]) and np.array_equal(src, row_src[[0, 5, w.P - 1]])
+    # two pairs aimed at one row is an invalid plan, and the oracle says so
+    bad = dr.copy()
+    bad[0, 1, 0] = bad[0, 0, 0]
+    with pytest.raises(ValueError):
+        O.permute(x, bad, 0, w.R, w.P)
 
 
 def test_slot_memory_arithmetic():
@@ -155,6 +191,12 @@ def test_stage_forward_and_grad_reduce():
         for s in range(S):
             e = slot_expert[r, s]
             assert np.array_equal(slot_w[r, s], main_w[e] if e >= 0 else np.zeros(n, np.uint16))
+    # a rank range fills only its own ranks' slots
+    part = np.full((R, S, n), 7, dtype=np.uint16)
+    O.stage_forward(slot_expert, main_w, part, 1, 3)
+    assert (part[[0, 3]] == 7).all()
+    assert np.array_equal(part[1], slot_w[1]) and np.array_equal(part[2, 0], slot_w[2, 0])
+    assert (part[2, 1] == 7).all()                       # empty slot untouched
     # integer-valued fp32 data: every partial sum is exact, so the result is the exact sum
     mg = rng.integers(-1000, 1000, (R * E_loc, n)).astype(np.float32)
     sg = rng.integers(-1000, 1000, (R, S, n)).astype(np.float32)

@@ -89,6 +89,90 @@ def test_waterfill_candidates_and_fallback():
     assert (sh[:, 1:] == -1).all()             # absent tokens (t >= B_r)
 
 
+def test_waterfill_zero_slack_candidate_never_drawn():
+    """Rank 1's tokens visit rank 0 only; S_1 = 0 and S_0 = 1, so the weights are
+    [17*0, 16*1] and W = 16 is small enough that v = 0 comes up: even then the draw
+    takes the first candidate whose running weight EXCEEDS v, never the zero-weight
+    source.  L = [256, 257, 0], N = 256, H = ceil(769/3) = 257, S = [1, 0, 257]."""
+    R, E, T = 3, 3, 256
+    ids = np.full((R, T, 1), -1, dtype=np.int64)
+    ids[0, :, 0] = 1
+    ids[1, :, 0] = 0
+    ids[2, 0, 0] = 1
+    counts = np.zeros((R, E), dtype=np.int64)
+    for r in range(R):
+        counts[r] = np.bincount(ids[r][ids[r] >= 0], minlength=E)
+    B = np.array([0, T, 0])
+    sh, H, S, L = O.waterfill(counts, ids, B, seed=8, layer=3)
+    assert L.tolist() == [256, 257, 0] and H == 257 and S.tolist() == [1, 0, 257]
+    assert (sh[1] == 0).all()
+    assert (sh[0] == -1).all() and (sh[2] == -1).all()
+
+
+def test_waterfill_fallback_takes_the_lightest_clearly_lighter_candidate():
+    """W = 0: every candidate of rank 0's tokens is at or above H.  L = [100, 95, 80,
+    60, 0, 0, 0, 0], N = 2, H = ceil(337/8) = 43.  Token 0 visits ranks 1, 2, 3: ranks
+    2 (17*80 < 16*100) and 3 (17*60 < 1600) are clearly lighter, rank 1 (17*95 = 1615)
+    is not; the lightest, rank 3, wins.  Token 1 visits rank 1 only: 95 < 100 but not
+    by the 1/16 margin, so the token stays on rank 0."""
+    R, E, T = 8, 8, 2
+    counts = np.zeros((R, E), dtype=np.int64)
+    counts[0, :4] = [100, 95, 80, 60]
+    ids = np.full((R, T, 3), -1, dtype=np.int64)
+    ids[0, 0] = [1, 2, 3]
+    ids[0, 1, 0] = 1
+    B = np.array([2, 0, 0, 0, 0, 0, 0, 0])
+    sh, H, S, L = O.waterfill(counts, ids, B, seed=0, layer=0)
+    assert H == 43 and S[:4].tolist() == [0, 0, 0, 0]
+    assert sh[0].tolist() == [3, 0]
+    assert (sh[1:] == -1).all()
+
+
+def _numpy_philox_word0(seed, layer, c0, c1=0, c2=0, c3=0):
+    """Word 0 of Philox4x64-10 at counter (c0, c1, c2, c3) from numpy's own generator,
+    which outputs the block at its counter + 1 (so it starts one below, with the borrow
+    carried through the four words)."""
+    c = (c0 | (c1 << 64) | (c2 << 128) | (c3 << 192)) - 1
+    c %= 1 << 256
+    start = [(c >> (64 * j)) & MASK for j in range(4)]
+    bg = np.random.Philox(key=np.array([seed, layer], dtype=np.uint64),
+                          counter=np.array(start, dtype=np.uint64))
+    return int(bg.random_raw())
+
+
+@pytest.mark.parametrize("shift,all_ranks", [(4, False), (0, False), (2, False), (4, True)])
+def test_waterfill_draws_come_from_numpy_philox(shift, all_ranks):
+    """Every token's shared rank recomputed from numpy's own Philox4x64-10 (key (seed,
+    layer), counter (g, 0, 0, 0) for g = r0*T + t), word 0 u, v = floor(u*W/2^64),
+    candidates r0 first then the others ascending (the visited ranks, or every rank in
+    the all-rank mode) with weights (2^shift + 1) S_r0 and 2^shift S_c."""
+    R, E, T, seed, layer = 4, 4, 16, 2024, 7
+    counts = np.zeros((R, E), dtype=np.int64)
+    counts[0] = [40, 10, 25, 0]                        # L = [40, 10, 25, 0]
+    rng = np.random.default_rng(5)
+    ids = np.stack([np.stack([rng.choice(E, 2, replace=False) for _ in range(T)])
+                    for _ in range(R)]).astype(np.int64)
+    ids[rng.random(ids.shape) < 0.2] = -1
+    B = np.full(R, T)
+    sh, H, S, L = O.waterfill(counts, ids, B, seed=seed, layer=layer, local_pref_shift=shift,
+                              all_ranks=all_ranks)
+    assert H == 35 and S.tolist() == [0, 25, 10, 35]   # ceil((75 + 64) / 4) = 35
+    big = 1 << shift
+    drawn = 0
+    for r0 in range(R):
+        for t in range(T):
+            others = set(range(R)) if all_ranks else {int(e) for e in ids[r0, t] if e >= 0}
+            cands = [r0] + sorted(others - {r0})
+            w = [(big + 1) * int(S[r0])] + [big * int(S[c]) for c in cands[1:]]
+            if sum(w) == 0:
+                continue
+            v = (_numpy_philox_word0(seed, layer, r0 * T + t) * sum(w)) >> 64
+            run = np.cumsum(w)
+            assert sh[r0, t] == cands[int(np.nonzero(run > v)[0][0])]
+            drawn += 1
+    assert drawn >= 48
+
+
 def test_waterfill_sampling_distribution():
     """Per-token choice frequencies follow the weights (within 4 sigma)."""
     R, E, T = 4, 8, 20000
@@ -147,6 +231,10 @@ def test_waterfill_extend_topk():
     ids = np.array([[[1, 2], [3, 0]]])
     ext = O.extend_topk(ids, np.array([[0, -1]]), 4)
     assert ext.tolist() == [[[1, 2, 4], [3, 0, -1]]]
+    ids = np.array([[[1, 2], [3, 0], [0, 1]]] * 3)
+    ext = O.extend_topk(ids, np.array([[2, 1, 0], [0, 0, -1], [1, 2, 2]]), 4)
+    assert ext[:, :, 2].tolist() == [[6, 5, 4], [4, 4, -1], [5, 6, 6]]   # E + shared rank
+    assert np.array_equal(ext[:, :, :2], ids)
 
 
 # ---------------------------------------------------------------- LPLB
@@ -259,6 +347,16 @@ def test_hamilton_quotas():
     assert q.tolist() == [3, 0, 8]                    # 11*640/2560 = 2.75, 11*1920/2560 = 8.25
     q = O.hamilton_quotas(np.array([1.0 / 3, 2.0 / 3], dtype=np.float32), [1000], [[0, 1]])
     assert q.sum() == 1000 and abs(q[0] - 333) <= 1
+    # quotas are floors plus leftover units, not rounded shares: 5 * 1/3 = 1.67 each ->
+    # floors 1, 1, 1, remainders equal, the 2 leftover units to the lowest copies
+    q = O.hamilton_quotas(np.array([1.0, 1.0, 1.0]), [5], [[0, 1, 2]])
+    assert q.tolist() == [2, 2, 1]
+    # weights round to nearest (x*256 = 1.6 -> 2, 1.2 -> 1): 9 * 2/3 = 6, 9 * 1/3 = 3
+    q = O.hamilton_quotas(np.array([1.6, 1.2], dtype=np.float32) / 256, [9], [[0, 1]])
+    assert q.tolist() == [6, 3]
+    # ties round to even (x*256 = 2.5 -> 2, 3.5 -> 4): 12 * 2/6 = 4, 12 * 4/6 = 8
+    q = O.hamilton_quotas(np.array([2.5, 3.5], dtype=np.float32) / 256, [12], [[0, 1]])
+    assert q.tolist() == [4, 8]
 
 
 def test_lplb_layer_matches_highs():
@@ -325,14 +423,20 @@ def test_lplb_sample_zero_weights_uniform_and_single_copies():
 
 
 def test_lplb_sample_draw_is_the_published_generator():
-    """The copy of one pair, recomputed by hand from the scalar Philox."""
+    """Every pair recomputed from numpy's own Philox4x64-10 at counter (g, k, 1, 0), key
+    (seed, layer): expert 0's copies (instances 0, 5, 11) carry weights 256, 512, 1280
+    and expert 5's (instances 2, 7) weight 0 each, so expert 5 takes the uniform branch,
+    copy floor(u * 2 / 2^64)."""
     inst, ipr = _two_copy_table()
-    x = np.array([1.0, 2.0, 5.0, 1.0, 1.0], dtype=np.float32)
-    ids = np.zeros((4, 3, 2), dtype=np.int64)
-    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=123, layer=9)
-    r, t, k = 2, 1, 1
-    g = r * 3 + t
-    u = O.philox4x64_10((g, k, 1, 0), (123, 9))[0]
-    v = (u * (256 + 512 + 1280)) >> 64
-    want = 0 if v < 256 else (5 if v < 768 else 11)
-    assert out[r, t, k] == want
+    x = np.array([1.0, 2.0, 5.0, 0.0, 0.0], dtype=np.float32)
+    R, T, seed, layer = 4, 6, 123, 9
+    ids = np.zeros((R, T, 2), dtype=np.int64)
+    ids[:, :, 1] = 5
+    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=seed, layer=layer)
+    for r in range(R):
+        for t in range(T):
+            g = r * T + t
+            v = (_numpy_philox_word0(seed, layer, g, 0, 1) * 2048) >> 64
+            assert out[r, t, 0] == (0 if v < 256 else (5 if v < 768 else 11))
+            u = _numpy_philox_word0(seed, layer, g, 1, 1)
+            assert out[r, t, 1] == (2, 7)[(u * 2) >> 64]
