@@ -4,6 +4,8 @@ include/uep.h declares, and its host-side argument checks answer without a GPU."
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -86,3 +88,50 @@ def test_host_side_calls_without_gpu(lib):
     fake_a, fake_b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     assert lib.uep_device_copy(fake_a, fake_b, i64(24), null) == 2
     assert lib.uep_device_copy(ctypes.c_void_p(4100), fake_b, i64(32), null) == 2
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "uep.h"
+
+typedef void (*any_fn)(void);
+static const any_fn table[] = {
+%(table)s
+};
+
+int main(void) {
+  const char* v = uep_version();
+  if (!v || !strstr(v, "gfx950")) { printf("version: %%s\n", v ? v : "(null)"); return 1; }
+  if (strcmp(uep_status_string(UEP_EWORKSPACE), "workspace too small") != 0) return 2;
+  /* geometry errors are answered on the host, before any device work */
+  if (uep_load_matrix(NULL, 0, 1, 1, 4, NULL, NULL, NULL, NULL, 0, NULL) != UEP_EINVAL) return 3;
+  if (uep_load_matrix(NULL, 65, 1, 1, 4, NULL, NULL, NULL, NULL, 0, NULL) != UEP_EGEOM) return 4;
+  if (uep_permute(NULL, NULL, 2, 4, 2, 12, 0, 2, NULL, NULL, NULL) != UEP_EGEOM) return 5;
+  printf("%%d functions, %%s\n", (int)(sizeof table / sizeof table[0]), v);
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler,std,suffix", [("gcc", "-std=c99", ".c"),
+                                                  ("g++", "-std=c++17", ".cpp")])
+def test_header_compiles_and_links_from_c_and_cpp(lib, tmp_path, compiler, std, suffix):
+    """A plain C99 (and C++17) program, -pedantic -Werror, that names every declared
+    function and calls the host-side checks links against libuep.so and runs."""
+    cc = shutil.which(compiler)
+    if cc is None:
+        pytest.skip(f"{compiler} not available")
+    names = declared_functions()
+    src = tmp_path / f"abi_check{suffix}"
+    src.write_text(C_PROGRAM % {"table": ",\n".join(f"  (any_fn){n}" for n in names)})
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(LIB)
+    build = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                            "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                            "-L", libdir, "-l:libuep.so", f"-Wl,-rpath,{libdir}"],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert run.stdout.startswith(f"{len(names)} functions")
