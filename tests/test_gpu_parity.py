@@ -239,6 +239,37 @@ def test_permute_with_empty_slots():
     assert np.array_equal(host(row_src), exp_src)
 
 
+@pytest.mark.parametrize("H", [8, 4104, 8192])
+def test_permute_row_lengths(H):
+    """Row lengths at the edges of the kernel's slicing: one 16-byte vector; one vector
+    past 8 KiB (the non-temporal path with a one-vector tail); exactly two slices.
+    Rows of the other ranks and row_src entries outside the range stay untouched."""
+    say("case: permute H", H)
+    rng = np.random.default_rng(H)
+    R, T, K, E = 3, 41, 3, 6
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.1)
+    o = oracle_plan(ids, E, 1, 2)
+    P = int((o["dest_row"] >= 0).sum())
+    g = torch.Generator(device=DEV).manual_seed(H)
+    x = torch.randn(R, T, H, generator=g, device=DEV).to(torch.bfloat16)
+    xb = host(x.view(torch.int16)).view(np.uint16)
+    dr = to_dev(o["dest_row"])
+    out = torch.full((P, H), 5, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    row_src = torch.full((P,), -9, dtype=torch.int32, device=DEV)
+    U.permute(x, dr, out, row_src)
+    exp, exp_src, _ = O.permute(xb, o["dest_row"], 0, R, P)
+    assert np.array_equal(host(out.view(torch.int16)).view(np.uint16), exp)
+    assert np.array_equal(host(row_src), exp_src)
+    part = torch.full((P, H), 5, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    part_src = torch.full((P,), -9, dtype=torch.int32, device=DEV)
+    U.permute(x, dr, part, part_src, r_begin=1, r_end=2)
+    exp1, src1, wr1 = O.permute(xb, o["dest_row"], 1, 2, P)
+    got = host(part.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got[wr1], exp1[wr1]) and (got[~wr1] == 5).all()
+    gs = host(part_src)
+    assert np.array_equal(gs[wr1], src1[wr1]) and (gs[~wr1] == -9).all()
+
+
 @pytest.mark.parametrize("layer", [0, 47, 93])
 def test_sweep_layers_plan(layer):
     """Layers of the 94-layer Qwen3-235B-shaped sweep, each with its own Zipf skew:
