@@ -287,6 +287,25 @@ def copy_reference(torch, U, nbytes=1 << 30, reps=5):
             "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def fill_reference(torch, U, nbytes=1 << 30, reps=5):
+    """Event-timed uep_device_fill of nbytes: the write-only bandwidth line (the permute
+    and staging streams are mostly writes)."""
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device=DEV)
+    s = torch.cuda.current_stream()
+    U.device_fill(a, 0, s)
+    torch.cuda.synchronize()
+    t = Timer(torch, reps)
+    for _ in range(reps):
+        t.start(s)
+        U.device_fill(a, 0x01010101, s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del a
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": nbytes, "avg_launch_ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
+
+
 def base_line(w, W, value, ms, args, dtype, extra_cfg=None):
     cfg = {"workload": w.name, "R": w.R, "E": w.E, "S": w.S, "tokens_per_rank": w.T,
            "top_k": w.K, "hidden": w.H, "q_min": w.q_min,
@@ -427,6 +446,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     # each staged expert's main read once, each used slot written once
     stage_bytes = (n_distinct + n_used) * w.expert_elems * 2
     copy = copy_reference(torch, U)
+    fill = fill_reference(torch, U)
     comb = combine_figures(torch, U, W, L)
     floor = launch_floor(torch, U)
     grad = grad_reduce_figures(torch, U, L)
@@ -434,7 +454,8 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32", {"ffn": list(w.ffn_shape)})
         out["roofline"] = roofline(pb, perm_ms, PERMUTE_CALL, measured_traffic(w.name))
         out["cpu_baseline"] = None
-        out["extra"] = {"device_copy_gbs": copy["gbs"], "stage_ms": stage_ms}
+        out["extra"] = {"device_copy_gbs": copy["gbs"], "device_fill_gbs": fill["gbs"],
+                        "stage_ms": stage_ms}
         return out
     # per-rank share, averaged over ranks (repetition i takes rank i mod R): the
     # whole-group plan, that rank's assignment, slot staging and permute
@@ -476,6 +497,8 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "imbalance_before": float(before.max() / before.mean()),
         "imbalance_after": float(rl.max() / rl.mean()),
         "device_copy_gbs": copy["gbs"],
+        "device_fill_gbs": fill["gbs"],
+        "permute_over_fill_line": (pb / (perm_ms * 1e-3) / 1e9) / fill["gbs"],
         **comb,
         **floor,
         **grad,
@@ -729,11 +752,13 @@ def kernel_report(args, torch, U, W):
         rep[w.name] = d
         del L
         torch.cuda.empty_cache()
-    # plain device copy of 4 GiB (the achievable-bandwidth reference)
+    # uep_device_copy and uep_device_fill of 4 GiB (the copy and write-only lines)
     a = torch.empty(1 << 31, dtype=torch.int16, device=DEV)
     b = torch.empty_like(a)
-    cu = graph_us(torch, lambda s: b.copy_(a), reps=5)
+    cu = graph_us(torch, lambda s: U.device_copy(a, b, s), reps=5)
     rep["device_copy_4GiB"] = {"us": cu, "gbs": 2 * a.numel() * 2 / (cu * 1e-6) / 1e9}
+    fu = graph_us(torch, lambda s: U.device_fill(b, 0, s), reps=5)
+    rep["device_fill_4GiB"] = {"us": fu, "gbs": b.numel() * 2 / (fu * 1e-6) / 1e9}
     del a, b
     torch.cuda.empty_cache()
     print(json.dumps(rep), flush=True)

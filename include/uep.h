@@ -84,6 +84,21 @@ const char* uep_status_string(uep_status s);
 uep_status uep_device_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * uep_device_fill -- writes a 32-bit pattern over device memory.  Not a step of the
+ * balancing path: the write-only HBM reference line (the permute and staging
+ * streams are mostly writes), and a fill kernel for callers that clear buffers
+ * inside a captured graph and want no memset node there.  Same workgroup shape as
+ * uep_device_copy (16 KiB per workgroup, 16-byte vector stores).
+ *
+ *   dst    [bytes]  out  device memory, 16-byte aligned
+ *   bytes                multiple of 16; 0 is a no-op
+ *   value                the 32-bit word written at every 4-byte offset
+ * Returns UEP_EINVAL for a null pointer or negative size, UEP_EGEOM for a misaligned
+ * pointer or a size that is not a multiple of 16.
+ * ------------------------------------------------------------------------- */
+uep_status uep_device_fill(void* dst, int64_t bytes, uint32_t value, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_load_matrix -- the global load matrix of one layer.
  * [UEP] section "在 Gate 之后获取当前层真实负载" (real load after Gate): once the Gate
  * has run, every expert's exact token count for this microbatch and layer is known;

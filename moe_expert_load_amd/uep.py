@@ -34,6 +34,7 @@ SIGNATURES = {
     "uep_version": (ctypes.c_char_p, []),
     "uep_status_string": (ctypes.c_char_p, [_I]),
     "uep_device_copy": (_I, [_P, _P, _I64, _P]),
+    "uep_device_fill": (_I, [_P, _I64, ctypes.c_uint32, _P]),
     "uep_load_matrix_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "uep_load_matrix": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "uep_solve_quota": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
@@ -214,6 +215,16 @@ def device_copy(src, dst, stream=None):
     if dst.numel() * dst.element_size() != n or not (src.is_contiguous() and dst.is_contiguous()):
         raise TypeError("device_copy needs two contiguous tensors of the same byte size")
     _check(LIB.uep_device_copy(_p(src), _p(dst), n, _s(stream)), "uep_device_copy")
+    return dst
+
+
+def device_fill(dst, value=0, stream=None):
+    """Writes the 32-bit word `value` over the contiguous device tensor dst (a byte size
+    that is a multiple of 16)."""
+    if not dst.is_contiguous():
+        raise TypeError("device_fill needs a contiguous tensor")
+    n = dst.numel() * dst.element_size()
+    _check(LIB.uep_device_fill(_p(dst), n, value & 0xFFFFFFFF, _s(stream)), "uep_device_fill")
     return dst
 
 

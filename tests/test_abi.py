@@ -88,6 +88,12 @@ def test_host_side_calls_without_gpu(lib):
     fake_a, fake_b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     assert lib.uep_device_copy(fake_a, fake_b, i64(24), null) == 2
     assert lib.uep_device_copy(ctypes.c_void_p(4100), fake_b, i64(32), null) == 2
+    u32 = ctypes.c_uint32
+    assert lib.uep_device_fill(null, i64(0), u32(7), null) == 0
+    assert lib.uep_device_fill(null, i64(-16), u32(7), null) == 1
+    assert lib.uep_device_fill(null, i64(32), u32(7), null) == 1
+    assert lib.uep_device_fill(fake_a, i64(24), u32(7), null) == 2
+    assert lib.uep_device_fill(ctypes.c_void_p(4100), i64(32), u32(7), null) == 2
 
 
 C_PROGRAM = r"""

@@ -329,6 +329,19 @@ def test_device_copy_reference(nbytes):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("nbytes", [16, 16 * 4096, 16 * (3 * 4096 + 17)])
+def test_device_fill(nbytes):
+    """The fill writes its 32-bit word over exactly the given bytes, ragged tail
+    included, and nothing past them."""
+    say("case: device fill", nbytes)
+    buf = torch.full((nbytes // 4 + 8,), -7, dtype=torch.int32, device=DEV)
+    U.device_fill(buf[:nbytes // 4], 0x9E3779B9)
+    torch.cuda.synchronize()
+    h = host(buf).view(np.uint32)
+    assert (h[:nbytes // 4] == 0x9E3779B9).all()
+    assert (h[nbytes // 4:] == np.uint32(2**32 - 7)).all()
+
+
 def test_qwen_layer_full_size():
     """Qwen3-235B-shaped layer: plan bit-exact at full size; permute of one rank's share
     compared whole, the whole-group permute on sampled rows; staging of 3 slots."""
