@@ -517,8 +517,9 @@ def waterfill_inst(w):
 
 
 def bench_waterfill(args, torch, U, W, w):
-    """DeepSeek-V3 layer with Waterfill: routed load matrix -> Waterfill -> fused
-    (K+1)-column layout -> load matrix -> identity quotas -> reroute/assign -> permute."""
+    """DeepSeek-V3 layer with Waterfill: routed load matrix (counts only) -> Waterfill ->
+    fused (K+1)-column layout -> load matrix -> identity quotas -> reroute/assign ->
+    permute."""
     log(f"workload {w.name}: R={w.R} E={w.E} T={w.T} K={w.K} H={w.H}")
     ids = W.routing(w)
     inst, ipr = waterfill_inst(w)
@@ -526,7 +527,6 @@ def bench_waterfill(args, torch, U, W, w):
     L = Layer(U, W, torch, w, None, E=E2, K=K2, ipr=ipr, weights=False)
     ids_d = torch.from_numpy(ids).to(DEV)
     counts1 = torch.empty(w.R, w.E, dtype=torch.int32, device=DEV)
-    bp1 = torch.empty(w.R, w.T, w.K, dtype=torch.int32, device=DEV)
     ws1 = torch.empty(max(U.load_matrix_workspace_size(w.R, w.T, w.K, w.E), 4), dtype=torch.uint8,
                       device=DEV)
     B = torch.full((w.R,), w.T, dtype=torch.int32, device=DEV)
@@ -538,7 +538,7 @@ def bench_waterfill(args, torch, U, W, w):
     seed = W.waterfill_seed(w)
 
     def wf_plan(s, r_begin=0, r_end=None):
-        U.load_matrix(ids_d, w.E, counts1, bp1, None, ws1, s)
+        U.load_matrix(ids_d, w.E, counts1, None, None, ws1, s, counts_only=True)
         U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl, L.ids, stream=s)
         L.load(s)
         U.identity_quota(L.counts, L.plan["inst_expert"], L.plan["inst_quota"], stream=s)

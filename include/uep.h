@@ -107,7 +107,11 @@ uep_status uep_device_fill(void* dst, int64_t bytes, uint32_t value, void* strea
  *   topk_ids   [R][T][K]  in   expert ids in [-1, E), distinct within a token
  *   counts     [R][E]     out  counts[r][e] = number of (t, k) on rank r routed to e
  *   bucket_pos [R][T][K]  out  number of tokens t' < t on rank r whose top-k holds
- *                              the same expert (stable position in its bucket)
+ *                              the same expert (stable position in its bucket);
+ *                              may be NULL: then only counts are computed (a layer
+ *                              that needs the loads but no positions, e.g. the routed
+ *                              loads Waterfill starts from), and duplicate ids are
+ *                              not checked
  *   err                   out  optional; UEP_ERR_ID_RANGE, UEP_ERR_DUP_ID
  *   ws, ws_bytes               device workspace of uep_load_matrix_workspace_size()
  * ------------------------------------------------------------------------- */

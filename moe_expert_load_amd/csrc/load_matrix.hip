@@ -3,7 +3,8 @@
 // gathered for the whole EP group into one matrix).
 //
 // Main path (E <= 1024, K <= 16), two launches over chunks of a rank's tokens:
-//   lm_hist: per-chunk expert histogram with LDS integer atomics (order-free).
+//   lm_hist: per-chunk expert histogram with LDS integer atomics (order-free), the
+//     chunk's ids read as one flat coalesced range.
 //   lm_rank: each of the 4 waves walks its quarter of the chunk 64 tokens at a time,
 //     lane = token.  Every lane ORs its bit into a per-expert 64-bit lane mask in LDS
 //     for each of its K experts; a pair's rank among the wave's 64 tokens is then the
@@ -12,6 +13,7 @@
 //     giving the final positions.  Token order is kept by construction.
 // Fallback (larger E or K): lm_chunk ranks pairs with one ballot per id bit
 //   (match-any), lm_fix adds the earlier chunks' counts.
+// Counts only (no bucket_pos): lm_hist, then lm_counts sums each rank's chunks.
 // Pairs of one expert are ranked in token order: ids are distinct inside a token.
 #include "common.h"
 
@@ -63,35 +65,75 @@ __device__ __forceinline__ void store_token(int32_t* __restrict__ p, int K, bool
   }
 }
 
+// Per-chunk expert histogram.  A histogram has no token order, so the chunk's
+// (t1 - t0) * K ids are read as one flat range: every load instruction of a wave
+// covers 256 consecutive bytes, whatever K is, and the first 8 loads of each thread
+// are issued before the LDS is cleared.
 __global__ __launch_bounds__(256) void lm_hist(const int32_t* __restrict__ ids,
                                                int32_t* __restrict__ chunk_hist, int32_t* err,
-                                               LmGeom g, bool vec) {
+                                               LmGeom g) {
   extern __shared__ int32_t lh_lds[];                 // [E]
   const int r = blockIdx.y, c = blockIdx.x;
-  for (int e = threadIdx.x; e < g.E; e += 256) lh_lds[e] = 0;
-  __syncthreads();
+  const int tid = threadIdx.x;
   const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
-  int bad = 0;
-  for (int t = t0 + threadIdx.x; t < t1; t += 256) {
-    int v[kLmBitmapMaxK];
-    load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+  const int32_t* p = ids + ((int64_t)r * g.T + t0) * g.K;
+  const int n = (t1 - t0) * g.K;                      // >= K >= 1: launched only for T > 0
+  int v[8];
 #pragma unroll
-    for (int k = 0; k < kLmBitmapMaxK; ++k) {
-      if (k >= g.K) break;
-      const int e = v[k];
-      if (e < -1 || e >= g.E) bad = 1;
-      else if (e >= 0) atomicAdd(&lh_lds[e], 1);
+  for (int u = 0; u < 8; ++u) v[u] = p[min(u * 256 + tid, n - 1)];
+  for (int e = tid; e < g.E; e += 256) lh_lds[e] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int i0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = v[u];
+      if (i0 + u * 256 + tid < n) {
+        if (e < -1 || e >= g.E) bad = 1;
+        else if (e >= 0) atomicAdd(&lh_lds[e], 1);
+      }
     }
+    i0 += 8 * 256;
+    if (i0 >= n) break;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[min(i0 + u * 256 + tid, n - 1)];
   }
   if (bad) set_err(err, UEP_ERR_ID_RANGE);
   __syncthreads();
   int32_t* ch = chunk_hist + ((int64_t)r * g.n_chunks + c) * g.E;
-  for (int e = threadIdx.x; e < g.E; e += 256) ch[e] = lh_lds[e];
+  for (int e = tid; e < g.E; e += 256) ch[e] = lh_lds[e];
+}
+
+// Counts only: counts[r][e] = sum of rank r's chunk histograms (one workgroup per rank,
+// up to 16 loads in flight per thread).
+__global__ __launch_bounds__(256) void lm_counts(const int32_t* __restrict__ chunk_hist,
+                                                 int32_t* __restrict__ counts, LmGeom g) {
+  const int r = blockIdx.x;
+  const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
+  for (int e = threadIdx.x; e < g.E; e += 256) {
+    int s = 0;
+    if (g.T > 0)
+      for (int c0 = 0; c0 < g.n_chunks; c0 += 16) {
+        int acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = ch[(int64_t)min(c0 + u, g.n_chunks - 1) * g.E + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += c0 + u < g.n_chunks ? acc[u] : 0;
+      }
+    counts[(int64_t)r * g.E + e] = s;
+  }
 }
 
 // kMaxK bounds K (8, 12 or 16): per-token arrays stay small enough for four waves per
-// SIMD, so the 1024 workgroups of a 32-rank layer fit the chip in one round
-template <int kMaxK>
+// SIMD, so the 1024 workgroups of a 32-rank layer fit the chip in one round.
+// kTile (for K % 4 != 0, where a token's ids are not 16-byte vectors): the chunk's ids
+// come in through one flat coalesced read into an LDS tile, the lanes read their
+// tokens' ids from it, and the final positions leave through a second tile and one
+// flat coalesced write, instead of K strided 4-byte accesses per lane.
+constexpr int kLmTileLd = 16;                          // flat loads per thread: 4096 ids
+constexpr size_t kLmTileMaxLds = 64 * 1024;            // tiles only while the LDS fits 64 KiB
+
+template <int kMaxK, bool kTile>
 __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
                                                int32_t* __restrict__ bucket_pos,
                                                const int32_t* __restrict__ chunk_hist,
@@ -101,21 +143,43 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   uint64_t* mask = lr_lds;                                             // [4][E]
   int32_t* whist = reinterpret_cast<int32_t*>(lr_lds + 4 * g.E);       // [4][E]
   int32_t* pre = whist + 4 * g.E;                                      // [E]
+  int32_t* idt = pre + g.E;                        // kTile: [tok_per_chunk * K] ids
+  int32_t* pt = idt + g.tok_per_chunk * g.K;       // kTile: [tok_per_chunk * K] positions
   const int r = blockIdx.y, c = blockIdx.x;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
   const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
   const int tpw = g.tok_per_chunk / 4;
   const int tw0 = t0 + w * tpw, tw1 = min(t1, tw0 + tpw);
-  // the wave's first 64 tokens: loads issued before anything else
+  const int64_t chunk_base = ((int64_t)r * g.T + t0) * g.K;
+  const int n = (t1 - t0) * g.K;
+  // loads issued before anything else: the chunk's flat ids (kTile), or the wave's
+  // first 64 tokens
   int v0[kMaxK], pos0[kMaxK];
-  if (tw0 + lane < tw1) load_token(ids + ((int64_t)r * g.T + tw0 + lane) * g.K, g.K, vec, v0);
+  int tv[kTile ? kLmTileLd : 1];
+  if (kTile) {
+#pragma unroll
+    for (int u = 0; u < kLmTileLd; ++u)
+      if (u * 256 < n) tv[u] = ids[chunk_base + min(u * 256 + (int)threadIdx.x, n - 1)];
+  } else if (tw0 + lane < tw1) {
+    load_token(ids + ((int64_t)r * g.T + tw0 + lane) * g.K, g.K, vec, v0);
+  }
   for (int e = threadIdx.x; e < g.E; e += 256) {
     pre[e] = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) { mask[ww * g.E + e] = 0; whist[ww * g.E + e] = 0; }
   }
+  if (kTile) {
+#pragma unroll
+    for (int u = 0; u < kLmTileLd; ++u)
+      if (u * 256 + (int)threadIdx.x < n) idt[u * 256 + threadIdx.x] = tv[u];
+  }
   __syncthreads();
+  if (kTile && tw0 + lane < tw1) {
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (k < g.K) v0[k] = idt[(tw0 + lane - t0) * g.K + k];
+  }
   // pre[e] = sum of the earlier chunks' histograms: `per` threads per expert, each
   // with up to 16 independent loads in flight, combined by LDS integer atomics
   {
@@ -144,7 +208,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   const bool one = tpw <= kWave;
   // pass 1: ranks among the wave's tokens (provisional, relative to the wave).  The
   // first 64 tokens of the wave stay in registers for pass 2; later ones (only when a
-  // wave has more than 64 tokens) go through bucket_pos.
+  // wave has more than 64 tokens) go through the position tile (kTile) or bucket_pos.
   for (int tb = tw0; tb < tw1; tb += kWave) {
     const int t = tb + lane;
     const bool live = t < tw1;
@@ -154,7 +218,13 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k) v[k] = v0[k];
     } else if (live) {
-      load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+      if (kTile) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+          if (k < g.K) v[k] = idt[(t - t0) * g.K + k];
+      } else {
+        load_token(ids + ((int64_t)r * g.T + t) * g.K, g.K, vec, v);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
@@ -185,7 +255,13 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k) { v0[k] = v[k]; pos0[k] = pos[k]; }
     } else if (live) {
-      store_token(bp, g.K, vec, pos);
+      if (kTile) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+          if (k < g.K) pt[(t - t0) * g.K + k] = pos[k];
+      } else {
+        store_token(bp, g.K, vec, pos);
+      }
     }
   }
   __syncthreads();
@@ -212,6 +288,10 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
     if (tb == tw0) {
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k) { v[k] = v0[k]; pos[k] = pos0[k]; }
+    } else if (kTile) {
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < g.K) { v[k] = idt[(t - t0) * g.K + k]; pos[k] = pt[(t - t0) * g.K + k]; }
     } else {
       load_token(ids + base, g.K, vec, v);
       load_token(bucket_pos + base, g.K, vec, pos);
@@ -225,9 +305,19 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
         if (k2 < k) dup |= ok && v[k2] == v[k];
       if (ok) pos[k] += whist[w * g.E + v[k]];
     }
-    store_token(bucket_pos + base, g.K, vec, pos);
+    if (kTile) {
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < g.K) pt[(t - t0) * g.K + k] = pos[k];
+    } else {
+      store_token(bucket_pos + base, g.K, vec, pos);
+    }
   }
   if (dup) set_err(err, UEP_ERR_DUP_ID);
+  if (kTile) {          // the chunk's positions leave in one flat coalesced write
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) bucket_pos[chunk_base + i] = pt[i];
+  }
 }
 
 __global__ __launch_bounds__(kLmThreads) void lm_chunk(const int32_t* __restrict__ ids,
@@ -384,29 +474,45 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
                                       int32_t* err, void* ws, size_t ws_bytes, void* stream) {
   if (R <= 0 || T < 0 || K <= 0 || E <= 0) return UEP_EINVAL;
   if (R > 64 || K > 64 || E > kLmMaxE || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
-  if (!counts || (T > 0 && (!topk_ids || !bucket_pos))) return UEP_EINVAL;
+  if (!counts || (T > 0 && !topk_ids)) return UEP_EINVAL;
   if (!ws || ws_bytes < uep_load_matrix_workspace_size(R, T, K, E)) return UEP_EWORKSPACE;
   LmGeom g = lm_geom(R, T, K, E);
   hipStream_t s = uep_stream(stream);
   dim3 grid(g.n_chunks, R);
+  if (!bucket_pos) {          // counts only: flat histograms, then one sum per rank
+    if (T > 0) {
+      hipLaunchKernelGGL(lm_hist, grid, dim3(256), sizeof(int32_t) * E, s, topk_ids, (int32_t*)ws,
+                         err, g);
+      UEP_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)ws, counts, g);
+    UEP_CHECK_LAUNCH();
+    return UEP_OK;
+  }
   if (lm_bitmap(K, E)) {
     const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
                      (T == 0 || reinterpret_cast<uintptr_t>(bucket_pos) % 16 == 0);
     if (T > 0) {
       hipLaunchKernelGGL(lm_hist, grid, dim3(256), sizeof(int32_t) * E, s, topk_ids, (int32_t*)ws,
-                         err, g, vec);
+                         err, g);
       UEP_CHECK_LAUNCH();
     }
     const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
-    if (K <= 8)
-      hipLaunchKernelGGL(lm_rank<8>, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
-                         counts, err, g, vec);
-    else if (K <= 12)
-      hipLaunchKernelGGL(lm_rank<12>, grid, dim3(256), lds, s, topk_ids, bucket_pos,
-                         (const int32_t*)ws, counts, err, g, vec);
-    else
-      hipLaunchKernelGGL(lm_rank<16>, grid, dim3(256), lds, s, topk_ids, bucket_pos, (const int32_t*)ws,
-                         counts, err, g, vec);
+    const size_t lds_tile = lds + sizeof(int32_t) * 2 * (size_t)g.tok_per_chunk * K;
+    const bool tile = !vec && lds_tile <= kLmTileMaxLds;
+    const size_t sh = tile ? lds_tile : lds;
+    const int32_t* ch = (const int32_t*)ws;
+#define UEP_LM_RANK(KM, TL) \
+    hipLaunchKernelGGL((lm_rank<KM, TL>), grid, dim3(256), sh, s, topk_ids, bucket_pos, ch, counts, \
+                       err, g, vec)
+    if (K <= 8) {
+      if (tile) UEP_LM_RANK(8, true); else UEP_LM_RANK(8, false);
+    } else if (K <= 12) {
+      if (tile) UEP_LM_RANK(12, true); else UEP_LM_RANK(12, false);
+    } else {
+      if (tile) UEP_LM_RANK(16, true); else UEP_LM_RANK(16, false);
+    }
+#undef UEP_LM_RANK
     UEP_CHECK_LAUNCH();
     return UEP_OK;
   }

@@ -115,11 +115,17 @@ def load_matrix_workspace_size(R, T, K, E) -> int:
     return int(LIB.uep_load_matrix_workspace_size(R, T, K, E))
 
 
-def load_matrix(topk_ids, E, counts=None, bucket_pos=None, err=None, ws=None, stream=None):
+def load_matrix(topk_ids, E, counts=None, bucket_pos=None, err=None, ws=None, stream=None,
+                counts_only=False):
+    """counts [R][E] and bucket_pos [R][T][K]; with counts_only=True the positions are
+    not computed and None is returned in their place."""
     _i32(topk_ids, "topk_ids")
     R, T, K = topk_ids.shape
     counts = _new((R, E), topk_ids) if counts is None else counts
-    bucket_pos = _new((R, T, K), topk_ids) if bucket_pos is None else bucket_pos
+    if counts_only:
+        bucket_pos = None
+    elif bucket_pos is None:
+        bucket_pos = _new((R, T, K), topk_ids)
     n = load_matrix_workspace_size(R, T, K, E)
     ws = _new((max(n, 4),), topk_ids, torch.uint8) if ws is None else ws
     _check(LIB.uep_load_matrix(_p(topk_ids), R, T, K, E, _p(counts), _p(bucket_pos), _p(err),

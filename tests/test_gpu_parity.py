@@ -108,6 +108,38 @@ def test_load_matrix_k_variants(K):
     assert host(err)[0] == 0
     assert np.array_equal(host(counts), counts_o)
     assert np.array_equal(host(bp), bp_o)
+    # counts only (no positions)
+    c2, none = U.load_matrix(to_dev(ids), E, err=err, counts_only=True)
+    assert none is None and np.array_equal(host(c2), counts_o) and host(err)[0] == 0
+    # a duplicate id inside one token is flagged by the ranking pass
+    bad = ids.copy()
+    bad[1, 5, K - 1] = bad[1, 5, 0] if bad[1, 5, 0] >= 0 else 3
+    bad[1, 5, 0] = bad[1, 5, K - 1]
+    if K > 1:
+        err2 = err_word()
+        U.load_matrix(to_dev(bad), E, err=err2)
+        assert host(err2)[0] & U.ERR_DUP_ID
+
+
+@pytest.mark.parametrize("R,T,K,E", [(3, 0, 8, 16), (2, 300, 5, 2000), (5, 1000, 9, 320)])
+def test_load_matrix_counts_only(R, T, K, E):
+    """Counts without positions: an empty layer, the large-E geometry of the fallback
+    ranking kernels, and the shape of the Waterfill-extended top-k (K + 1 = 9 columns
+    over E + R pseudo-experts); ids out of range are still flagged."""
+    say("case: load matrix counts only", R, T, K, E)
+    rng = np.random.default_rng(R * 1000 + K)
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.05)
+    counts_o, _ = O.load_matrix(ids, E)
+    err = err_word()
+    counts = torch.full((R, E), -5, dtype=torch.int32, device=DEV)
+    c, bp = U.load_matrix(to_dev(ids), E, counts=counts, err=err, counts_only=True)
+    assert bp is None and host(err)[0] == 0
+    assert np.array_equal(host(c), counts_o)
+    if T:
+        bad = ids.copy()
+        bad[0, 0, 0] = E
+        U.load_matrix(to_dev(bad), E, err=err, counts_only=True)
+        assert host(err)[0] & U.ERR_ID_RANGE
 
 
 def test_plan_edge_cases():
