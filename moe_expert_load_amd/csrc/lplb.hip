@@ -14,12 +14,12 @@
 // Solver: Mehrotra predictor-corrector, fp32 iterates, one workgroup.  The normal
 // equations A D A^T dy = rhs are reduced by eliminating the (diagonal) expert rows;
 // the remaining R x R rank matrix P = (d_M + d_a) 11^T + diag(d_s) + sum over groups
-// of a weighted Laplacian of the copies' ranks is assembled and Cholesky-factored in
-// fp64 in LDS.  fp32 is not enough there: the dense M direction (d_M -> inf) swamps
-// the differential entries of copies whose optimal share is a small fraction of the
-// peak.  Diagonal entries are formed as sums of positive terms (no cancellation); a
-// pivot that lost its precision is replaced by a huge one (Cholesky-infinity), which
-// drops that direction.  Iterations stop once the duality gap is below 1e-4 of the
+// of a weighted Laplacian of the copies' ranks is assembled and factored as
+// U diag(p) U^T (LDL^T, no square roots) in fp64 in LDS.  fp32 is not enough there:
+// the dense M direction (d_M -> inf) swamps the differential entries of copies whose
+// optimal share is a small fraction of the peak.  Diagonal entries are formed as sums
+// of positive terms (no cancellation); a pivot that lost its precision is treated as
+// infinite (1/p = 1e-64, Cholesky-infinity), which drops that direction.  Iterations stop once the duality gap is below 1e-4 of the
 // objective M (or mu < 1e-9), at most `iters` of them.
 // Output: x >= 0 normalised so each group sums exactly to its count, m = the max rank
 // load of that split, and integer quotas by largest remainder on rint(x * 256).
@@ -43,6 +43,7 @@ constexpr float kBigM = 8.0f;
 constexpr float kEta = 0.99f;
 constexpr float kMuStop = 1e-9f;
 constexpr double kGapRel = 1e-4;
+constexpr int kLpPanel = 8;              // Cholesky panel width (divides 16)
 constexpr double kPivTol = 1e-13;
 constexpr int kLpMaxNV = kLpMaxN + kLpMaxR + 2;
 constexpr int kLpMaxRows = kLpMaxR + kLpMaxG;
@@ -112,7 +113,7 @@ struct LpShared {
   // normal equations (fp64)
   double d[kLpMaxNV], beta[kLpMaxG], t64[kLpMaxRows], u64[kLpMaxR];
   double P[kLpMaxR][kLpMaxR + 1];
-  double Linv[kLpMaxR], d0[kLpMaxR];
+  double Dinv[kLpMaxR], d0[kLpMaxR];
   double colbuf[2][kLpMaxR];
   // reductions
   double red[kLpThreads / kWave];
@@ -275,13 +276,13 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
     // so every substitution step is one broadcast and one FMA.  P holds U's strictly
     // lower part and zeros elsewhere, so lanes outside the triangle add 0: no
     // branches, and each pass loads its 64 entries in one burst before the chain.
-    const double linv_l = S.Linv[l];
+    const double dinv_l = S.Dinv[l];
     double u[kLpMaxR];
 #pragma unroll
     for (int q = 0; q < kLpMaxR; ++q) u[q] = S.P[l][q];
 #pragma unroll
     for (int q = 0; q < kLpMaxR; ++q) b = fma(-u[q], readlane_d(b, q), b);   // U z = r1
-    b *= linv_l * linv_l;                                                   // w = D^-1 z
+    b *= dinv_l;                                                            // w = D^-1 z
 #pragma unroll
     for (int q = 0; q < kLpMaxR; ++q) u[q] = S.P[q][l];
 #pragma unroll
@@ -302,11 +303,11 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
   __syncthreads();
 }
 
-// The hardware estimate is good to about 2^-24 relative (measured on MI355X); one
-// Newton step brings it to about 2^-47, far beyond what the fp32 iterates resolve.
-__device__ __forceinline__ double rsqrt_d(double x) {
-  const double y = __builtin_amdgcn_rsq(x);
-  return y * (1.5 - 0.5 * x * y * y);
+// The hardware reciprocal estimate is good to about 2^-24 relative; one Newton step
+// brings it to about 2^-47, far beyond what the fp32 iterates resolve.
+__device__ __forceinline__ double rcp_d(double x) {
+  const double y = __builtin_amdgcn_rcp(x);
+  return fma(y, fma(-x, y, 1.0), y);
 }
 
 __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, LpShared& S) {
@@ -350,15 +351,19 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
     S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - off;
   }
   __syncthreads();
-  // Blocked right-looking Cholesky, four panels of 16 columns.  Thread (ti, tk) keeps
-  // a 4x4 register tile of the trailing matrix: rows i = ti + 16a, columns
-  // k = tk + 16b.  For panel p: the tiles of column block p are published to LDS;
-  // wave 0 factors the 64 x 16 panel with one row per lane (pivots and column
-  // entries broadcast by readlane, no barriers) and stores U = L diag(Linv) strictly
-  // below the diagonal, zeros above, and the pivots; then every thread subtracts the
-  // panel's rank-16 product from its trailing tiles, L_ij L_kj = U_ij U_kj p_j.
-  // Eight barriers in all.  A pivot that lost its precision (p_j <= tol * original
-  // diagonal) drops its direction: its column of U is 0 and Linv = 1e-32.
+  // Blocked right-looking LDL^T (Cholesky without square roots), panels of kLpPanel
+  // columns.  Thread (ti, tk) keeps a 4x4 register tile of the trailing matrix: rows
+  // i = ti + 16a, columns k = tk + 16b.  For each panel: the tiles of the panel's
+  // columns are published to LDS; wave 0 factors the 64 x kLpPanel panel with one row
+  // per lane and stores the unit lower factor U (U_ic = a_ic / p_c strictly below the
+  // diagonal, zeros elsewhere), the pivots p_c and 1/p_c; then every thread subtracts
+  // the panel's product from the trailing entries of its tile, U_ij (U_kj p_j).  In
+  // the panel the unscaled column entries a_kc are broadcast (readlane) while the
+  // pivot's reciprocal is still being formed, so a column's dependent chain is one
+  // broadcast, the reciprocal, one multiply and one FMA.  Narrow panels keep wave 0's
+  // serial work small and hand the rest to all four waves.  A pivot that lost its
+  // precision (p_c <= tol * original diagonal) drops its direction: its column of U
+  // is 0 and 1/p_c is replaced by 1e-64.
   const int ti = threadIdx.x / 16, tk = threadIdx.x % 16;
   double* piv = S.colbuf[0];
   double A[4][4];
@@ -368,10 +373,14 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
     for (int b = 0; b < 4; ++b) A[a][b] = S.P[ti + 16 * a][tk + 16 * b];
   __syncthreads();
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb) {
-    const int c0 = 16 * pb;
+  for (int pb = 0; pb < kLpMaxR / kLpPanel; ++pb) {
+    const int c0 = kLpPanel * pb, c1 = c0 + kLpPanel;
+    const int bb = c0 / 16, k0 = c0 % 16;
+    if (tk >= k0 && tk < k0 + kLpPanel) {
 #pragma unroll
-    for (int a = pb; a < 4; ++a) S.P[ti + 16 * a][c0 + tk] = A[a][pb];
+      for (int a = 0; a < 4; ++a)
+        if (16 * a + 15 >= c0) S.P[ti + 16 * a][tk + 16 * bb] = A[a][bb];
+    }
     __syncthreads();
     if (threadIdx.x < kWave) {
       // the lane index is re-read per panel (empty asm, no instruction) so the 64
@@ -379,39 +388,52 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
       // the interior-point loop as 64 live masks
       int l = threadIdx.x;
       asm volatile("" : "+v"(l));
-      double r[16];
+      double r[kLpPanel], thr[kLpPanel];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) r[j] = S.P[l][c0 + j];
+      for (int j = 0; j < kLpPanel; ++j) {
+        r[j] = S.P[l][c0 + j];
+        thr[j] = kPivTol * S.d0[c0 + j];
+      }
+      double my_piv = 0.0, my_dinv = 0.0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < kLpPanel; ++j) {
         const int c = c0 + j;
         const double pj = readlane_d(r[j], c);
-        const bool bad = !(pj > kPivTol * S.d0[c]);
-        const double inv = bad ? 0.0 : rsqrt_d(pj);
-        if (l == c) {
-          S.Linv[c] = bad ? 1e-32 : inv;
-          piv[c] = pj;
-        }
-        const double lic = l > c ? r[j] * inv : 0.0;        // L_lc (0 on and above)
-        S.P[l][c] = lic * inv;                               // U = L Linv
+        double akc[kLpPanel];                                // a_kc of the panel's later rows
 #pragma unroll
-        for (int j2 = j + 1; j2 < 16; ++j2) r[j2] = fma(-lic, readlane_d(lic, c0 + j2), r[j2]);
+        for (int j2 = j + 1; j2 < kLpPanel; ++j2) akc[j2] = readlane_d(r[j], c0 + j2);
+        const bool bad = !(pj > thr[j]);
+        const double rc = bad ? 0.0 : rcp_d(pj);
+        if (l == c) {
+          my_piv = pj;
+          my_dinv = bad ? 1e-64 : rc;
+        }
+        const double u = l > c ? r[j] * rc : 0.0;           // U_lc (0 on and above)
+        S.P[l][c] = u;
+#pragma unroll
+        for (int j2 = j + 1; j2 < kLpPanel; ++j2) r[j2] = fma(-u, akc[j2], r[j2]);
+      }
+      if (l >= c0 && l < c1) {
+        piv[l] = my_piv;
+        S.Dinv[l] = my_dinv;
       }
     }
     __syncthreads();
-    if (pb < 3) {
+    if (c1 < kLpMaxR) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < kLpPanel; ++j) {
         const double pj = piv[c0 + j];
         double ui[4], uk[4];
 #pragma unroll
-        for (int a = pb + 1; a < 4; ++a) ui[a] = S.P[ti + 16 * a][c0 + j];
+        for (int a = 0; a < 4; ++a) ui[a] = 16 * a + 15 >= c1 ? S.P[ti + 16 * a][c0 + j] : 0.0;
 #pragma unroll
-        for (int b2 = pb + 1; b2 < 4; ++b2) uk[b2] = S.P[tk + 16 * b2][c0 + j] * pj;
+        for (int b2 = 0; b2 < 4; ++b2) uk[b2] = 16 * b2 + 15 >= c1 ? S.P[tk + 16 * b2][c0 + j] * pj : 0.0;
 #pragma unroll
-        for (int a = pb + 1; a < 4; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b2 = pb + 1; b2 < 4; ++b2) A[a][b2] = fma(-ui[a], uk[b2], A[a][b2]);
+          for (int b2 = 0; b2 < 4; ++b2)
+            if (16 * a + 15 >= c1 && 16 * b2 + 15 >= c1 && ti + 16 * a >= c1 && tk + 16 * b2 >= c1)
+              A[a][b2] = fma(-ui[a], uk[b2], A[a][b2]);
       }
     }
   }
