@@ -32,8 +32,11 @@ constexpr int kStMaxSlots = 64 * 8;
 // [r_begin, r_end) (gradients go to the main's rank), else slots of ranks in
 // [r_begin, r_end) (weights go to the slot's rank).
 struct StGroups {
+  int32_t sel_e[kStMaxSlots];                 // selected slot's expert, else -1
+  int32_t lead_cnt[kStMaxSlots];              // group size at its first slot, else 0
+  int32_t lead_of[kStMaxSlots], pos_in[kStMaxSlots];   // first slot and rank of a member
+  int32_t grp_of[kStMaxSlots];                // group index of a leading slot
   int32_t g_exp[kStMaxSlots], g_first[kStMaxSlots + 1], g_mem[kStMaxSlots];
-  int32_t lead_cnt[kStMaxSlots], grp_of[kStMaxSlots];
   int32_t n_grp;
 };
 
@@ -44,51 +47,60 @@ __device__ __forceinline__ bool st_selected(int i, int e, int S, int E_loc, int 
   return r >= r_begin && r < r_end;
 }
 
+// Every workgroup of the persistent grid builds the table at its start, so the build
+// is kept short: one coalesced read of the slot table, LDS-only comparisons, and the
+// leaders compacted in slot order by wave 0 with a ballot and a prefix sum (64 slots
+// per round), three barriers in all.
 template <bool kByHome>
 __device__ __forceinline__ void st_build_groups(const int32_t* __restrict__ slot_expert, int n_slots,
                                                 int S, int E_loc, int r_begin, int r_end,
                                                 StGroups& G) {
-  // a selected slot leads its expert's group if no earlier selected slot holds it
   for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
     const int e = slot_expert[i];
-    int cnt = 0;
-    if (st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end)) {
-      bool seen = false;
-      for (int i2 = 0; i2 < i; ++i2)
-        seen |= slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end);
-      if (!seen)
-        for (int i2 = i; i2 < n_slots; ++i2)
-          cnt += slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end);
-    }
-    G.lead_cnt[i] = cnt;
+    G.sel_e[i] = st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end) ? e : -1;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {          // serial scan over at most 512 counts
-    int ng = 0, nm = 0;
-    for (int i = 0; i < n_slots; ++i) {
-      if (G.lead_cnt[i] == 0) continue;
-      G.g_exp[ng] = slot_expert[i];
-      G.g_first[ng] = nm;
-      G.grp_of[i] = ng;
-      nm += G.lead_cnt[i];
-      ++ng;
-    }
-    G.g_first[ng] = nm;
-    G.n_grp = ng;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {   // members, in slot order
-    const int e = slot_expert[i];
-    if (!st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end)) continue;
-    int lead = -1, pos = 0;
-    for (int i2 = 0; i2 < i; ++i2)
-      if (slot_expert[i2] == e && st_selected<kByHome>(i2, e, S, E_loc, r_begin, r_end)) {
-        if (lead < 0) lead = i2;
-        ++pos;
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
+    const int e = G.sel_e[i];
+    int cnt = 0, pos = 0, first = i;
+    if (e >= 0)
+      for (int i2 = 0; i2 < n_slots; ++i2) {
+        const bool same = G.sel_e[i2] == e;
+        cnt += same;
+        if (i2 < i && same) {
+          ++pos;
+          first = min(first, i2);
+        }
       }
-    if (lead < 0) lead = i;
-    G.g_mem[G.g_first[G.grp_of[lead]] + pos] = i;
+    G.lead_cnt[i] = (e >= 0 && first == i) ? cnt : 0;
+    G.lead_of[i] = first;
+    G.pos_in[i] = pos;
   }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    int ng = 0, nm = 0;
+    for (int base = 0; base < n_slots; base += kWave) {
+      const int i = base + threadIdx.x;
+      const int cnt = i < n_slots ? G.lead_cnt[i] : 0;
+      const uint64_t lead = ballot(cnt > 0);
+      const int incl = wave_incl_scan(cnt);
+      if (cnt > 0) {
+        const int gi = ng + __popcll(lead & lanemask_lt());
+        G.grp_of[i] = gi;
+        G.g_exp[gi] = G.sel_e[i];
+        G.g_first[gi] = nm + incl - cnt;
+      }
+      ng += __popcll(lead);
+      nm += readlane(incl, kWave - 1);
+    }
+    if (threadIdx.x == 0) {
+      G.g_first[ng] = nm;
+      G.n_grp = ng;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_slots; i += kStThreads)     // members, in slot order
+    if (G.sel_e[i] >= 0) G.g_mem[G.g_first[G.grp_of[G.lead_of[i]]] + G.pos_in[i]] = i;
   __syncthreads();
 }
 
