@@ -468,6 +468,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
 
     rank_us = graph_us(torch, rank_share, reps=w.R, replays=2, indexed=True)
     plan_us = graph_us(torch, lambda s: L.plan_step(s))
+    stage_kernel_us = graph_us(torch, lambda s: L.stage(s), reps=5)
     perm_rank_us = graph_us(torch, lambda s, i: L.permute(s, i % w.R, i % w.R + 1, row_src=False),
                             reps=w.R, replays=2, indexed=True)
     L.plan_step(stream)
@@ -504,6 +505,10 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         **grad,
     }
     out["extra"]["stage_frac"] = out["extra"]["stage_gbs"] / HBM_PEAK_GBS
+    # the staging kernel alone, graph-replayed back to back (no launch latency)
+    out["extra"]["stage_kernel_us"] = stage_kernel_us
+    out["extra"]["stage_kernel_gbs"] = stage_bytes / (stage_kernel_us * 1e-6) / 1e9 if n_used else 0.0
+    out["extra"]["stage_kernel_frac"] = out["extra"]["stage_kernel_gbs"] / HBM_PEAK_GBS
     return out
 
 
