@@ -69,14 +69,17 @@ __device__ __forceinline__ void wave_argmin(int& v, int& idx) {
 
 // Wave-wide max / min of an int, uniform result: DPP butterflies inside each row of
 // 16 lanes (quad_perm xor 1, xor 2, then row_ror 4 and 8), then the four row results
-// are combined with readlane.  Every lane of the wave must be active.
+// are combined with readlane.  Every lane of the wave must be active.  These four
+// patterns give every lane a source lane in its own row, so bound_ctrl never applies;
+// the mov_dpp form lets the compiler fold each move into its max/min, one
+// v_max_i32_dpp (or v_min) per step instead of a copy, a DPP move and the max.
 template <bool kMax>
 __device__ __forceinline__ int wave_reduce_dpp(int v) {
   auto op = [](int a, int b) { return kMax ? max(a, b) : min(a, b); };
-  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false));  // row_ror:4
-  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));  // row_ror:4
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));  // row_ror:8
   const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
   const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
   return op(op(a, b), op(c, d));

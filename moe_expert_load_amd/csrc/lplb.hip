@@ -124,18 +124,20 @@ struct LpShared {
 // Wave reductions by DPP (quad_perm xor 1, xor 2, row_ror 4 and 8 leave every row of
 // 16 lanes holding its row's total; the four rows are combined from lanes 0/16/32/48),
 // then across the 4 waves through LDS.  Every lane of the workgroup must take part.
+// Every lane has a source lane in its own row under these patterns, so mov_dpp's
+// bound_ctrl never applies; the form lets the compiler fold a move into its fp32 op.
 __device__ __forceinline__ double dpp_d(double v, int ctrl_sel) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
   switch (ctrl_sel) {
-    case 0: lo = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xF, 0xF, false);
-            hi = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xF, 0xF, false); break;
-    case 1: lo = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xF, 0xF, false);
-            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xF, 0xF, false); break;
-    case 2: lo = __builtin_amdgcn_update_dpp(lo, lo, 0x124, 0xF, 0xF, false);
-            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x124, 0xF, 0xF, false); break;
-    default: lo = __builtin_amdgcn_update_dpp(lo, lo, 0x128, 0xF, 0xF, false);
-             hi = __builtin_amdgcn_update_dpp(hi, hi, 0x128, 0xF, 0xF, false); break;
+    case 0: lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+            hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true); break;
+    case 1: lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+            hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true); break;
+    case 2: lo = __builtin_amdgcn_mov_dpp(lo, 0x124, 0xF, 0xF, true);
+            hi = __builtin_amdgcn_mov_dpp(hi, 0x124, 0xF, 0xF, true); break;
+    default: lo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, true);
+             hi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, true); break;
   }
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
@@ -143,10 +145,10 @@ __device__ __forceinline__ double dpp_d(double v, int ctrl_sel) {
 __device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
   int b = __float_as_int(v);
   switch (ctrl_sel) {
-    case 0: b = __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false); break;
-    case 1: b = __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false); break;
-    case 2: b = __builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false); break;
-    default: b = __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false); break;
+    case 0: b = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true); break;
+    case 1: b = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true); break;
+    case 2: b = __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, true); break;
+    default: b = __builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true); break;
   }
   return __int_as_float(b);
 }

@@ -27,12 +27,12 @@ constexpr int kSqThreads = 256;
 constexpr int kBig = 0x7fffffff;
 constexpr int kPackBits = 25;               // loads below 2^25 fit a (load, lane) key
 
-// Unsigned wave minimum (same DPP pattern as wave_reduce_dpp).
+// Unsigned wave minimum (same DPP pattern and foldable form as wave_reduce_dpp).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));
   const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
   const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
   const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
