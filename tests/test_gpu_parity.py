@@ -576,3 +576,90 @@ def test_waterfill_zero_slack_and_fallback_cases():
     sh, wl, _, _, _ = U.waterfill(to_dev(counts), to_dev(ids), to_dev(B), 0, 0)
     assert host(wl)[0] == H_o == 43
     assert np.array_equal(host(sh), sh_o) and sh_o[0].tolist() == [3, 0]
+
+
+def test_path_in_a_captured_graph_replays():
+    """The library allocates and synchronises nothing on the path, so the whole Tiny
+    layer (load matrix, quota solve, reroute/assign, permute, staging, combine) can be
+    captured once into a graph and replayed.  Between replays the program writes new
+    routing and activations into the captured input buffers with its own eager work;
+    every replay's outputs must equal the oracle's for that input."""
+    w = W.TINY
+    say("case: path captured in a graph", w)
+    R, T, K, E, H, S = w.R, w.T, w.K, w.E, w.H, w.S
+    ids_d = torch.empty(R, T, K, dtype=torch.int32, device=DEV)
+    x_d = torch.empty(R, T, H, dtype=torch.bfloat16, device=DEV)
+    main_w = torch.empty(E, w.expert_elems, dtype=torch.int16, device=DEV)
+    slot_w = torch.zeros(R, S, w.expert_elems, dtype=torch.int16, device=DEV)
+    gate = torch.empty(R, T, K, dtype=torch.float32, device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts, bp = torch.empty(R, E, **i32), torch.empty(R, T, K, **i32)
+    lm_ws = torch.empty(max(U.load_matrix_workspace_size(R, T, K, E), 4), dtype=torch.uint8,
+                        device=DEV)
+    ipr = E // R + S
+    plan = {"slot_expert": torch.empty(R, S, **i32), "inst_expert": torch.empty(R * ipr, **i32),
+            "inst_quota": torch.empty(R * ipr, **i32), "rank_load": torch.empty(R, **i32),
+            "stats": torch.empty(4, **i32)}
+    xfer, ioff = torch.empty(R, R * ipr, **i32), torch.empty(R * ipr + 1, **i32)
+    dinst, drow = torch.empty(R, T, K, **i32), torch.empty(R, T, K, **i32)
+    rr_ws = torch.empty(max(U.reroute_workspace_size(R, E, ipr), 4), dtype=torch.uint8, device=DEV)
+    out = torch.zeros(R * T * K, H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(R, T, H, dtype=torch.bfloat16, device=DEV)
+
+    def path(s):
+        U.load_matrix(ids_d, E, counts, bp, None, lm_ws, s)
+        U.solve_quota(counts, S, w.q_min, out=plan, stream=s)
+        U.reroute_assign(counts, ids_d, bp, ipr, plan["inst_expert"], plan["inst_quota"], 0, R,
+                         xfer, ioff, dinst, drow, None, rr_ws, s)
+        U.permute(x_d, drow, out, None, 0, R, s)
+        U.stage_replica_weights(U.STAGE_WEIGHTS, R, E, S, plan["slot_expert"], w.expert_elems,
+                                main_w=main_w, slot_w=slot_w, stream=s)
+        U.combine(out, drow, gate, y, stream=s)
+
+    rng = np.random.default_rng(2024)
+
+    def new_inputs():
+        ids = random_routing(rng, R, T, K, E, empty_frac=0.05)
+        ids_d.copy_(torch.from_numpy(ids))
+        x_d.copy_(torch.from_numpy(rng.standard_normal((R, T, H)).astype(np.float32))
+                  .to(torch.bfloat16))
+        main_w.copy_(torch.from_numpy(rng.integers(-2**15, 2**15, (E, w.expert_elems),
+                                                   dtype=np.int16)))
+        g = rng.random((R, T, K)).astype(np.float32)
+        gate.copy_(torch.from_numpy(g))
+        torch.cuda.synchronize()
+        return ids, g
+
+    s = torch.cuda.Stream()
+    new_inputs()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        path(s)                                   # warm, outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        path(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ids, g = new_inputs()
+        slot_w.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o = oracle_plan(ids, E, S, w.q_min)
+        assert np.array_equal(host(counts), o["counts"]), rep
+        assert np.array_equal(host(plan["inst_quota"]), o["plan"]["inst_quota"]), rep
+        assert np.array_equal(host(drow), o["dest_row"]), rep
+        xb = host(x_d.view(torch.int16)).view(np.uint16)
+        P = int((o["dest_row"] >= 0).sum())
+        exp_out, _, _ = O.permute(xb, o["dest_row"], 0, R, P)
+        got_out = host(out.view(torch.int16)).view(np.uint16)[:P]
+        assert np.array_equal(got_out, exp_out), rep
+        se = o["plan"]["slot_expert"]
+        mw = host(main_w).view(np.uint16)
+        sw_exp = np.zeros((R, S, w.expert_elems), dtype=np.uint16)
+        O.stage_forward(se, mw, sw_exp)
+        assert np.array_equal(host(slot_w).view(np.uint16), sw_exp), rep
+        y_exp = O.combine(exp_out, o["dest_row"], g)
+        assert np.array_equal(host(y.view(torch.int16)).view(np.uint16), y_exp), rep
