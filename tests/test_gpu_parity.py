@@ -471,6 +471,42 @@ def test_grad_reduce_matches_oracle():
     assert np.array_equal(host(mg), main2) and np.array_equal(host(sg), slot2)
 
 
+def test_grad_reduce_qwen_layer_full_size():
+    """Backward reduction at the real size: the Qwen layer's plan (21 slots holding 11
+    experts), 72 MiB fp32 gradients per expert, main_grad spanning 9 GiB (offsets past
+    2^32 bytes).  Every replicated expert's main and every used slot compared whole;
+    an expert without replicas is left untouched."""
+    w = W.QWEN_LAYER
+    say("case: grad reduce full size", w)
+    ids = W.routing(w)
+    o = oracle_plan(ids, w.E, w.S, w.q_min)
+    se = o["plan"]["slot_expert"].astype(np.int32)
+    n = w.expert_elems
+    g = torch.Generator(device=DEV).manual_seed(31)
+    mg = torch.randn(w.E, n, generator=g, device=DEV)
+    sg = torch.randn(w.R, w.S, n, generator=g, device=DEV)
+    rep = sorted(set(int(e) for e in se.reshape(-1) if e >= 0))
+    idle = next(e for e in range(w.E) if e not in rep)
+    main_h = host(mg[rep])                                  # the replicated experts' mains
+    slot_h = host(sg)
+    idle_h = host(mg[idle])
+    U.stage_replica_weights(U.STAGE_GRAD_REDUCE, w.R, w.E, w.S, to_dev(se), n, main_grad=mg,
+                            slot_grad=sg)
+    torch.cuda.synchronize()
+    # the oracle on the touched rows only: replicated experts renumbered 0..len(rep)-1
+    # (the whole group is reduced, so home ranks do not filter anything)
+    remap = {e: i for i, e in enumerate(rep)}
+    se_c = np.vectorize(lambda e: remap.get(int(e), -1))(se).astype(np.int64)
+    exp_main, exp_slot = main_h.copy(), slot_h.copy()
+    O.grad_reduce(se_c, exp_main, exp_slot, w.E_loc)
+    for i, e in enumerate(rep):
+        assert np.array_equal(host(mg[e]), exp_main[i]), e
+    sg_h = host(sg)
+    assert np.array_equal(sg_h, exp_slot)
+    assert not np.signbit(sg_h[se >= 0]).any()
+    assert np.array_equal(host(mg[idle]), idle_h)
+
+
 def test_waterfill_layer_full_size():
     """DeepSeek-V3-shaped layer with Waterfill: H, S_r and every token's shared rank
     bit-exact; the fused layout (K+1 columns) through load matrix, identity quotas,
