@@ -121,6 +121,22 @@ def test_load_matrix_k_variants(K):
         assert host(err2)[0] & U.ERR_DUP_ID
 
 
+@pytest.mark.parametrize("K", [9, 13])
+def test_load_matrix_untiled_large_e(K):
+    """K % 4 != 0 with E = 1024: the LDS tiles would not fit 64 KiB next to the
+    per-expert masks, so the ranking reads each token's ids with strided loads."""
+    say("case: load matrix untiled, E = 1024, K", K)
+    rng = np.random.default_rng(90 + K)
+    R, T, E = 2, 600, 1024
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.03)
+    counts_o, bp_o = O.load_matrix(ids, E)
+    err = err_word()
+    counts, bp = U.load_matrix(to_dev(ids), E, err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(counts), counts_o)
+    assert np.array_equal(host(bp), bp_o)
+
+
 @pytest.mark.parametrize("R,T,K,E", [(3, 0, 8, 16), (2, 300, 5, 2000), (5, 1000, 9, 320)])
 def test_load_matrix_counts_only(R, T, K, E):
     """Counts without positions: an empty layer, the large-E geometry of the fallback
