@@ -152,9 +152,10 @@ uep_status uep_solve_quota(const int32_t* counts, int32_t R, int32_t E, int32_t 
  * (used with the Waterfill layout of [BLOG] section "共享专家融合作为启用机制",
  * where each rank has one shared-expert slot next to its routed experts).
  *
- *   counts      [R][E]     in
+ *   counts      [R][E]     in   R <= 64
  *   inst_expert [n_inst]   in   each expert at most once
  *   inst_quota  [n_inst]   out  total load of the instance's expert (0 if unused)
+ * Returns UEP_EINVAL for null pointers or non-positive sizes, UEP_EGEOM for R > 64.
  * ------------------------------------------------------------------------- */
 uep_status uep_identity_quota(const int32_t* counts, int32_t R, int32_t E, int32_t n_inst,
                               const int32_t* inst_expert, int32_t* inst_quota, void* stream);

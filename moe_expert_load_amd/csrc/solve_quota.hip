@@ -226,13 +226,27 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
   }
 }
 
-__global__ void identity_quota_kernel(const int32_t* __restrict__ counts, int R, int E, int n_inst,
-                                      const int32_t* __restrict__ inst_expert,
-                                      int32_t* __restrict__ inst_quota) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_inst) return;
-  const int e = inst_expert[i];
-  inst_quota[i] = (e >= 0 && e < E) ? column_sum(counts, R, E, e) : 0;
+// Four lanes per instance (a quad), each summing every fourth rank with its (at most
+// 16) loads in flight: one round trip for R <= 64; the quad adds with two DPP steps.
+__global__ __launch_bounds__(256) void identity_quota_kernel(const int32_t* __restrict__ counts,
+                                                             int R, int E, int n_inst,
+                                                             const int32_t* __restrict__ inst_expert,
+                                                             int32_t* __restrict__ inst_quota) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = t / 4, part = t % 4;
+  const int e = i < n_inst ? inst_expert[i] : -1;
+  const bool ok = e >= 0 && e < E;
+  int v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)         // clamped address, no branch: every load issues
+    v[u] = counts[(int64_t)min(part + 4 * u, R - 1) * E + (ok ? e : 0)];
+  int acc = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc += ok && part + 4 * u < R ? v[u] : 0;
+  // every lane takes part (the grid covers whole quads): quad_perm [1,0,3,2], [2,3,0,1]
+  acc += __builtin_amdgcn_mov_dpp(acc, 0xB1, 0xF, 0xF, true);
+  acc += __builtin_amdgcn_mov_dpp(acc, 0x4E, 0xF, 0xF, true);
+  if (part == 0 && i < n_inst) inst_quota[i] = acc;
 }
 
 }  // namespace uep
@@ -265,9 +279,10 @@ extern "C" uep_status uep_identity_quota(const int32_t* counts, int32_t R, int32
                                          int32_t n_inst, const int32_t* inst_expert,
                                          int32_t* inst_quota, void* stream) {
   if (R <= 0 || E <= 0 || n_inst < 0) return UEP_EINVAL;
+  if (R > 64 || n_inst >= (1 << 28)) return UEP_EGEOM;
   if (n_inst == 0) return UEP_OK;
   if (!counts || !inst_expert || !inst_quota) return UEP_EINVAL;
-  hipLaunchKernelGGL(identity_quota_kernel, dim3((n_inst + 255) / 256), dim3(256), 0,
+  hipLaunchKernelGGL(identity_quota_kernel, dim3((4 * n_inst + 255) / 256), dim3(256), 0,
                      uep_stream(stream), counts, R, E, n_inst, inst_expert, inst_quota);
   UEP_CHECK_LAUNCH();
   return UEP_OK;

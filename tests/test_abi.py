@@ -73,6 +73,7 @@ def test_host_side_calls_without_gpu(lib):
     assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3), null, null,
                            null) == 1
     assert lib.uep_lplb_prepare(null, i32(2), i32(2), i32(2), null, ctypes.c_size_t(0), null) == 1
+    assert lib.uep_identity_quota(null, i32(65), i32(130), i32(4), null, null, null) == 2
     assert lib.uep_stage_replica_weights(i32(0), i32(4), i32(8), i32(9), null, i32(0), i32(4), null,
                                          null, null, null, ctypes.c_int64(8), null) == 2
     assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2),
