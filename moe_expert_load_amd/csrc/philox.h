@@ -9,14 +9,28 @@
 
 namespace uep {
 
+// 64 x 64 -> 128-bit product from four 32 x 32 + 64 multiply-adds (v_mad_u64_u32),
+// sharing the partial products between the high and the low word.  No partial sum
+// overflows: (2^32 - 1)^2 + (2^32 - 1) < 2^64.
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t p10 = (uint64_t)a1 * b0 + (p00 >> 32);
+  const uint64_t p01 = (uint64_t)a0 * b1 + (uint32_t)p10;
+  hi = (uint64_t)a1 * b1 + (p10 >> 32) + (p01 >> 32);
+  lo = (p01 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2,
                                                      uint64_t c3, uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
-    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(M0, c0, hi0, lo0);
+    mulhilo64(M1, c2, hi1, lo1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
