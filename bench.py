@@ -306,6 +306,33 @@ def fill_reference(torch, U, nbytes=1 << 30, reps=5):
     return {"bytes_per_launch": nbytes, "avg_launch_ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
+def sequential_permute_line(torch, U, L, perm_ms, reps=5):
+    """The same uep_permute call on the layer's own x and dispatch buffers, with
+    destination rows t*K + k: the same bytes as the real permute, written as one fully
+    sequential stream.  How fast HBM takes the permute's traffic depends on where the
+    driver placed these buffers (the same kernel varies by up to a third between fresh
+    allocations), so the permute is judged against this line from the same process and
+    the same memory.  Returns its rate and the permute's fraction of it."""
+    R, T, K = L.dinst.shape
+    H = L.x.shape[2]
+    dseq = torch.arange(R * T * K, dtype=torch.int32, device=DEV).view(R, T, K)
+    rs = torch.empty(R * T * K, dtype=torch.int32, device=DEV)
+    s = torch.cuda.current_stream()
+    U.permute(L.x, dseq, L.out, rs, 0, None, s)
+    torch.cuda.synchronize()
+    t = Timer(torch, reps)
+    for _ in range(reps):
+        t.start(s)
+        U.permute(L.x, dseq, L.out, rs, 0, None, s)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del dseq, rs
+    torch.cuda.empty_cache()
+    return {"sequential_permute_gbs": permute_bytes(R * T, R * T * K, H) / (ms * 1e-3) / 1e9,
+            "permute_over_sequential": ms / perm_ms}
+
+
 def base_line(w, W, value, ms, args, dtype, extra_cfg=None):
     cfg = {"workload": w.name, "R": w.R, "E": w.E, "S": w.S, "tokens_per_rank": w.T,
            "top_k": w.K, "hidden": w.H, "q_min": w.q_min,
@@ -447,6 +474,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     stage_bytes = (n_distinct + n_used) * w.expert_elems * 2
     copy = copy_reference(torch, U)
     fill = fill_reference(torch, U)
+    seq = sequential_permute_line(torch, U, L, perm_ms)
     comb = combine_figures(torch, U, W, L)
     floor = launch_floor(torch, U)
     grad = grad_reduce_figures(torch, U, L)
@@ -500,6 +528,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
         "device_copy_gbs": copy["gbs"],
         "device_fill_gbs": fill["gbs"],
         "permute_over_fill_line": (pb / (perm_ms * 1e-3) / 1e9) / fill["gbs"],
+        **seq,
         **comb,
         **floor,
         **grad,
@@ -567,6 +596,7 @@ def bench_waterfill(args, torch, U, W, w):
     out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
                                measured_traffic(w.name))
     out["cpu_baseline"] = None
+    seq = sequential_permute_line(torch, U, L, tp.mean_ms())
     plan_us = graph_us(torch, lambda s: wf_plan(s))
     wf_us = graph_us(torch, lambda s: U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl,
                                                   L.ids, stream=s))
@@ -581,7 +611,8 @@ def bench_waterfill(args, torch, U, W, w):
     U.waterfill(counts1, ids_d, B, seed, 0, 4, sh_all, wl, sl, rl, None, want_ext=False,
                 all_ranks=True)
     shared_all = np.bincount(sh_all.cpu().numpy().reshape(-1), minlength=w.R)
-    out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "waterfill_us": wf_us,
+    out["extra"] = {**seq, "us_per_layer_rank_share": rank_us, "plan_us": plan_us,
+                    "waterfill_us": wf_us,
                     "waterline": int(wl.item()),
                     "imbalance_routed_only": float(L_r.max() / L_r.mean()),
                     "imbalance_shared_local": float((L_r + local).max() / (L_r + local).mean()),
@@ -628,6 +659,7 @@ def bench_lplb(args, torch, U, W, w):
     out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
                                measured_traffic(w.name))
     out["cpu_baseline"] = None
+    seq = sequential_permute_line(torch, U, L, tp.mean_ms(), reps=3)
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)
     plan_us = graph_us(torch, lambda s: lp_plan(s), reps=5)
@@ -668,7 +700,9 @@ def bench_lplb(args, torch, U, W, w):
         where = np.nonzero(inst == e)[0]
         for i in where:
             uni[i // ipr] += c[e] / len(where)
-    out["extra"] = {"us_per_layer_rank_share": rank_us, "plan_us": plan_us, "lplb_us": lp_us,
+    out["extra"] = {**seq, "us_per_layer_rank_share": rank_us, "plan_us": plan_us,
+                    "lplb_us": lp_us,
+                    "load_matrix_us": graph_us(torch, L.load, reps=5),
                     "lp_iterations_run": int(st[2].item()), "m": float(m.item()),
                     "max_load_uniform_split": float(uni.max()), "mean_load": float(c.sum() / w.R),
                     "sample_plan_us": sample_us, "max_load_sampled": int(load_sampled.max())}

@@ -137,6 +137,31 @@ def test_load_matrix_untiled_large_e(K):
     assert np.array_equal(host(bp), bp_o)
 
 
+@pytest.mark.parametrize("R,T,K,E", [(2, 9000, 8, 288), (2, 40000, 3, 32), (2, 9000, 13, 32),
+                                     (1, 20000, 16, 64)])
+def test_load_matrix_long_ranks(R, T, K, E):
+    """Ranks long enough that chunks grow past their base size (at most 32 chunks per
+    rank): waves rank several batches of 64 tokens, and chunks of more than 4096 ids
+    (K = 3 and 13 here) take the strided path even where a tile would fit the LDS."""
+    say("case: load matrix long ranks", R, T, K, E)
+    rng = np.random.default_rng(T + K)
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
+    counts_o, bp_o = O.load_matrix(ids, E)
+    err = err_word()
+    counts, bp = U.load_matrix(to_dev(ids), E, err=err)
+    assert host(err)[0] == 0
+    assert np.array_equal(host(counts), counts_o)
+    assert np.array_equal(host(bp), bp_o)
+    c2, _ = U.load_matrix(to_dev(ids), E, err=err, counts_only=True)
+    assert np.array_equal(host(c2), counts_o) and host(err)[0] == 0
+    bad = ids.copy()
+    bad[R - 1, T - 1, K - 1] = bad[R - 1, T - 1, 0] if bad[R - 1, T - 1, 0] >= 0 else 1
+    bad[R - 1, T - 1, 0] = bad[R - 1, T - 1, K - 1]
+    err2 = err_word()
+    U.load_matrix(to_dev(bad), E, err=err2)
+    assert host(err2)[0] & U.ERR_DUP_ID
+
+
 @pytest.mark.parametrize("R,T,K,E", [(3, 0, 8, 16), (2, 300, 5, 2000), (5, 1000, 9, 320)])
 def test_load_matrix_counts_only(R, T, K, E):
     """Counts without positions: an empty layer, the large-E geometry of the fallback
