@@ -2,9 +2,11 @@
 // "在 Gate 之后获取当前层真实负载": the exact per-expert load of this layer,
 // gathered for the whole EP group into one matrix).
 //
-// Main path (E <= 1024, K <= 16), two launches over chunks of a rank's tokens:
+// Main path (E <= 1024, K <= 16), two launches over chunks of a rank's tokens (three
+// for long ranks):
 //   lm_hist: per-chunk expert histogram with LDS integer atomics (order-free), the
 //     chunk's ids read as one flat coalesced range.
+//   lm_scan (long ranks only): each rank's chunk histograms become exclusive prefixes.
 //   lm_rank: each of the 4 waves walks its quarter of the chunk 64 tokens at a time,
 //     lane = token.  Every lane ORs its bit into a per-expert 64-bit lane mask in LDS
 //     for each of its K experts; a pair's rank among the wave's 64 tokens is then the
@@ -124,8 +126,53 @@ __global__ __launch_bounds__(256) void lm_counts(const int32_t* __restrict__ chu
   }
 }
 
-// kMaxK bounds K (8, 12 or 16): per-token arrays stay small enough for four waves per
-// SIMD, so the 1024 workgroups of a 32-rank layer fit the chip in one round.
+// Long ranks (more earlier chunks than one round of prefix loads covers): each rank's
+// chunk histograms are turned into exclusive prefixes in place, so a ranking
+// workgroup loads one row instead of summing every earlier chunk's (which reads the
+// histograms about n_chunks / 2 times over).  Four threads per expert, each over a
+// quarter of the chunks: sums, an LDS exchange of the four partial sums, then the
+// prefixes written from the re-read (now cached) counts.
+constexpr int kLmScanParts = 4;
+
+__global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist, LmGeom g) {
+  __shared__ int32_t part_sum[256];
+  const int r = blockIdx.y;
+  const int e = blockIdx.x * (256 / kLmScanParts) + threadIdx.x / kLmScanParts;
+  const int q = threadIdx.x % kLmScanParts;
+  const int span = (g.n_chunks + kLmScanParts - 1) / kLmScanParts;
+  const int c_lo = min(g.n_chunks, q * span), c_hi = min(g.n_chunks, c_lo + span);
+  int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
+  int sum = 0;
+  if (e < g.E) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 16) {
+      int acc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = ch[(int64_t)min(c0 + u, c_hi - 1) * g.E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sum += c0 + u < c_hi ? acc[u] : 0;
+    }
+  }
+  part_sum[threadIdx.x] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q2 = 0; q2 < q; ++q2) run += part_sum[threadIdx.x - q + q2];
+  if (e < g.E) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 16) {
+      int acc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = ch[(int64_t)min(c0 + u, c_hi - 1) * g.E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < c_hi) {
+          ch[(int64_t)(c0 + u) * g.E + e] = run;
+          run += acc[u];
+        }
+    }
+  }
+}
+
+// kMaxK bounds K (8, 12 or 16): per-token arrays stay small (K <= 8: six waves per
+// SIMD), so the 1024 workgroups of a 32-rank layer fit the chip in one round.
 // kTile (for K % 4 != 0, where a token's ids are not 16-byte vectors): the chunk's ids
 // come in through one flat coalesced read into an LDS tile, the lanes read their
 // tokens' ids from it, and the final positions leave through a second tile and one
@@ -138,7 +185,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
                                                int32_t* __restrict__ bucket_pos,
                                                const int32_t* __restrict__ chunk_hist,
                                                int32_t* __restrict__ counts, int32_t* err,
-                                               LmGeom g, bool vec) {
+                                               LmGeom g, bool vec, bool scanned) {
   extern __shared__ uint64_t lr_lds[];
   uint64_t* mask = lr_lds;                                             // [4][E]
   int32_t* whist = reinterpret_cast<int32_t*>(lr_lds + 4 * g.E);       // [4][E]
@@ -164,10 +211,23 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
   } else if (tw0 + lane < tw1) {
     load_token(ids + ((int64_t)r * g.T + tw0 + lane) * g.K, g.K, vec, v0);
   }
-  for (int e = threadIdx.x; e < g.E; e += 256) {
-    pre[e] = 0;
+  // scanned: chunk_hist already holds each chunk's exclusive prefix (E <= 1024 here)
+  int pv[kLmBitmapMaxE / 256];
+  if (scanned) {
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) { mask[ww * g.E + e] = 0; whist[ww * g.E + e] = 0; }
+    for (int u = 0; u < kLmBitmapMaxE / 256; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      if (e < g.E) pv[u] = ch[(int64_t)c * g.E + e];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kLmBitmapMaxE / 256; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    if (e < g.E) {
+      pre[e] = scanned ? pv[u] : 0;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) { mask[ww * g.E + e] = 0; whist[ww * g.E + e] = 0; }
+    }
   }
   if (kTile) {
 #pragma unroll
@@ -180,9 +240,9 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
     for (int k = 0; k < kMaxK; ++k)
       if (k < g.K) v0[k] = idt[(tw0 + lane - t0) * g.K + k];
   }
-  // pre[e] = sum of the earlier chunks' histograms: `per` threads per expert, each
-  // with up to 16 independent loads in flight, combined by LDS integer atomics
-  {
+  // otherwise pre[e] = sum of the earlier chunks' histograms: `per` threads per
+  // expert, each with up to 16 independent loads in flight, combined by LDS atomics
+  if (!scanned) {
     const int per = g.E >= 256 ? 1 : 256 / g.E;
     const int part = threadIdx.x % per;
     for (int e = threadIdx.x / per; e < g.E; e += 256 / per) {
@@ -497,6 +557,14 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
                          err, g);
       UEP_CHECK_LAUNCH();
     }
+    // long ranks: one in-place scan of the chunk histograms instead of every ranking
+    // workgroup summing the earlier ones (more than one round of 16 loads per thread)
+    const int per = E >= 256 ? 1 : 256 / E;
+    const bool scanned = T > 0 && g.n_chunks > 16 * per;
+    if (scanned) {
+      hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, (int32_t*)ws, g);
+      UEP_CHECK_LAUNCH();
+    }
     const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
     const size_t lds_tile = lds + sizeof(int32_t) * 2 * (size_t)g.tok_per_chunk * K;
     const bool tile = !vec && lds_tile <= kLmTileMaxLds;
@@ -504,7 +572,7 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
     const int32_t* ch = (const int32_t*)ws;
 #define UEP_LM_RANK(KM, TL) \
     hipLaunchKernelGGL((lm_rank<KM, TL>), grid, dim3(256), sh, s, topk_ids, bucket_pos, ch, counts, \
-                       err, g, vec)
+                       err, g, vec, scanned)
     if (K <= 8) {
       if (tile) UEP_LM_RANK(8, true); else UEP_LM_RANK(8, false);
     } else if (K <= 12) {

@@ -138,11 +138,12 @@ def test_load_matrix_untiled_large_e(K):
 
 
 @pytest.mark.parametrize("R,T,K,E", [(2, 9000, 8, 288), (2, 40000, 3, 32), (2, 9000, 13, 32),
-                                     (1, 20000, 16, 64)])
+                                     (1, 20000, 16, 64), (2, 6000, 9, 1024)])
 def test_load_matrix_long_ranks(R, T, K, E):
-    """Ranks long enough that chunks grow past their base size (at most 32 chunks per
-    rank): waves rank several batches of 64 tokens, and chunks of more than 4096 ids
-    (K = 3 and 13 here) take the strided path even where a tile would fit the LDS."""
+    """Ranks of many chunks.  Where the earlier chunks' histograms take more than one
+    round of loads per thread to sum (E = 288, 64 and 1024 here), they are first
+    scanned in place into exclusive prefixes; E = 1024 with K = 9 also takes the LDS
+    tiles.  The others sum the earlier chunks in the ranking kernel."""
     say("case: load matrix long ranks", R, T, K, E)
     rng = np.random.default_rng(T + K)
     ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
