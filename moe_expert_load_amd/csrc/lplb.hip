@@ -25,6 +25,7 @@
 // load of that split, and integer quotas by largest remainder on rint(x * 256).
 #include <math.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -663,57 +664,113 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
 // only instance).  Weights are the integers w_p = rint(max(x_p, 0) * 256) of the
 // quota step; the draw for slot k of global token g is word 0 of Philox4x64-10 at
 // counter (g, k, 1, 0), key (seed, layer), scaled by a 64x64->128-bit product, so
-// the choice is exact integer arithmetic.  One thread per (token, slot) pair.
+// the choice is exact integer arithmetic.
+//
+// Each workgroup first stages the small tables in LDS (expert -> instance or group,
+// the groups' running copy weights and the copies' instances), then walks quads of
+// four consecutive slots of one token (one thread per quad, grid-stride), so every
+// lookup after the id load is an LDS read and ids and results move as 16-byte
+// vectors when K % 4 == 0.
+constexpr int kLsThreads = 256;
+constexpr int kLsMaxBlocks = 2048;          // 8 workgroups per CU of a 256-CU device
+
 __device__ __forceinline__ uint64_t copy_weight(float x) {
   return (uint64_t)rintf(fmaxf(x, 0.0f) * 256.0f);
 }
 
-__global__ __launch_bounds__(256) void lplb_sample_kernel(const int32_t* __restrict__ ids,
-                                                          int64_t n_pairs, int K, int R,
-                                                          const int32_t* __restrict__ lpw,
-                                                          const float* __restrict__ x,
-                                                          uint64_t seed, uint64_t layer,
-                                                          int32_t* __restrict__ dest_inst,
-                                                          int32_t* err) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n_pairs) return;
+struct LsShared {
+  int32_t ei[kLpMaxE];                      // exp_inst: instance, -2 - group, or -1
+  uint64_t cw[kLpMaxN];                     // running weight of copies within their group
+  int32_t ci[kLpMaxN];                      // copy -> instance
+  int32_t gs[kLpMaxG + 1];                  // group -> first copy
+};
+
+__global__ __launch_bounds__(kLsThreads) void lplb_sample_kernel(const int32_t* __restrict__ ids,
+                                                                 int64_t n_tok, int K, int R,
+                                                                 const int32_t* __restrict__ lpw,
+                                                                 const float* __restrict__ x,
+                                                                 uint64_t seed, uint64_t layer,
+                                                                 int32_t* __restrict__ dest_inst,
+                                                                 int32_t* err, bool vec) {
+  __shared__ LsShared S;
+  const int qpt = (K + 3) / 4;                           // quads per token
+  const int64_t n_quad = n_tok * qpt;
   if (lpw[0] != kLpMagic || lpw[1] != R) {
-    dest_inst[j] = -1;
-    set_err(err, UEP_ERR_LP);
+    for (int64_t q = (int64_t)blockIdx.x * kLsThreads + threadIdx.x; q < n_quad;
+         q += (int64_t)gridDim.x * kLsThreads) {
+      const int64_t g = q / qpt;
+      const int k0 = (int)(q % qpt) * 4;
+      for (int k = k0; k < min(K, k0 + 4); ++k) dest_inst[g * K + k] = -1;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) set_err(err, UEP_ERR_LP);
     return;
   }
   const LpView L = lp_view(lpw);
-  const int e = ids[j];
-  int out = -1;
-  if (e >= L.E || e < -1) {
-    set_err(err, UEP_ERR_ID_RANGE);
-  } else if (e >= 0) {
-    const int ei = L.exp_inst[e];
-    if (ei >= 0) {
-      out = ei;
-    } else if (ei == -1) {
-      set_err(err, UEP_ERR_LP);
-    } else {
-      const int gi = -2 - ei;
-      const int c0 = L.grp_start[gi], c1 = L.grp_start[gi + 1];
-      uint64_t W = 0;
-      for (int c = c0; c < c1; ++c) W += copy_weight(x[c]);
-      const uint64_t u = philox4x64_10_w0((uint64_t)(j / K), (uint64_t)(j % K), 1, 0, seed, layer);
-      int pick = c0;
-      if (W == 0) {
-        pick = c0 + (int)__umul64hi(u, (uint64_t)(c1 - c0));
-      } else {
-        const uint64_t v = __umul64hi(u, W);
-        uint64_t run = 0;
-        for (int c = c0; c < c1; ++c) {
-          run += copy_weight(x[c]);
-          if (run > v) { pick = c; break; }
-        }
-      }
-      out = L.copy_inst[pick];
+  for (int e = threadIdx.x; e < L.E; e += kLsThreads) S.ei[e] = L.exp_inst[e];
+  for (int c = threadIdx.x; c < L.n; c += kLsThreads) {
+    S.cw[c] = copy_weight(x[c]);
+    S.ci[c] = L.copy_inst[c];
+  }
+  for (int g = threadIdx.x; g <= L.G; g += kLsThreads) S.gs[g] = L.grp_start[g];
+  __syncthreads();
+  for (int g = threadIdx.x; g < L.G; g += kLsThreads) {
+    uint64_t run = 0;
+    for (int c = S.gs[g]; c < S.gs[g + 1]; ++c) {
+      run += S.cw[c];
+      S.cw[c] = run;
     }
   }
-  dest_inst[j] = out;
+  __syncthreads();
+  int bad = 0;
+  for (int64_t q = (int64_t)blockIdx.x * kLsThreads + threadIdx.x; q < n_quad;
+       q += (int64_t)gridDim.x * kLsThreads) {
+    const int64_t g = q / qpt;
+    const int k0 = (int)(q % qpt) * 4;
+    const int64_t j0 = g * K + k0;
+    int e[4], out[4];
+    if (vec) {
+      const int4 v = *reinterpret_cast<const int4*>(ids + j0);
+      e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = k0 + u < K ? ids[j0 + u] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      out[u] = -1;
+      if (e[u] >= L.E || e[u] < -1) {
+        bad |= UEP_ERR_ID_RANGE;
+      } else if (e[u] >= 0) {
+        const int ei = S.ei[e[u]];
+        if (ei >= 0) {
+          out[u] = ei;
+        } else if (ei == -1) {
+          bad |= UEP_ERR_LP;
+        } else {
+          const int gi = -2 - ei;
+          const int c0 = S.gs[gi], c1 = S.gs[gi + 1];
+          const uint64_t W = S.cw[c1 - 1];
+          const uint64_t r = philox4x64_10_w0((uint64_t)g, (uint64_t)(k0 + u), 1, 0, seed, layer);
+          int pick = c0;
+          if (W == 0) {
+            pick = c0 + (int)__umul64hi(r, (uint64_t)(c1 - c0));
+          } else {
+            const uint64_t v = __umul64hi(r, W);
+            while (pick < c1 - 1 && S.cw[pick] <= v) ++pick;
+          }
+          out[u] = S.ci[pick];
+        }
+      }
+    }
+    if (vec) {
+      *reinterpret_cast<int4*>(dest_inst + j0) = make_int4(out[0], out[1], out[2], out[3]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k0 + u < K) dest_inst[j0 + u] = out[u];
+    }
+  }
+  if (bad) set_err(err, bad);
 }
 
 }  // namespace uep
@@ -821,12 +878,16 @@ extern "C" uep_status uep_lplb_sample(const int32_t* topk_ids, int32_t R, int32_
                                       void* stream) {
   if (R <= 0 || T < 0 || K <= 0) return UEP_EINVAL;
   if (R > kLpMaxR || K > 64 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
-  const int64_t n = (int64_t)R * T * K;
-  if (n == 0) return UEP_OK;
+  const int64_t n_tok = (int64_t)R * T;
+  if (n_tok == 0) return UEP_OK;
   if (!topk_ids || !lp || !x || !dest_inst) return UEP_EINVAL;
-  hipLaunchKernelGGL(lplb_sample_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     uep_stream(stream), topk_ids, n, K, R, static_cast<const int32_t*>(lp), x,
-                     seed, layer, dest_inst, err);
+  const int64_t n_quad = n_tok * ((K + 3) / 4);
+  const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(dest_inst) % 16 == 0;
+  const int64_t blocks = std::min<int64_t>((n_quad + kLsThreads - 1) / kLsThreads, kLsMaxBlocks);
+  hipLaunchKernelGGL(lplb_sample_kernel, dim3((unsigned)blocks), dim3(kLsThreads), 0,
+                     uep_stream(stream), topk_ids, n_tok, K, R, static_cast<const int32_t*>(lp), x,
+                     seed, layer, dest_inst, err, vec);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }

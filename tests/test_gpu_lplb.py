@@ -260,6 +260,54 @@ def test_lplb_sample_random(seed):
     assert np.array_equal(host(dr), dr_o)
 
 
+def test_lplb_sample_errors_and_layouts():
+    """An id out of range and an expert without an instance leave -1 on their pair and
+    raise their error bits while every other pair is drawn as usual; a structure built
+    for another R leaves every pair -1; ids and outputs that are not 16-byte aligned
+    (K % 4 == 0) take the scalar loads and stores; K = 6 has a half-empty second quad."""
+    for K in (4, 6):
+        rng = np.random.default_rng(1400 + K)
+        R, E_loc, T = 4, 3, 150
+        ids, inst, ipr, E = random_lplb_case(rng, R, E_loc, T, K, 3)
+        say(f"case: lplb sample errors and layouts R={R} E={E} T={T} K={K}")
+        counts_o, _ = O.load_matrix(ids, E)
+        # an expert with a single instance loses it; its pairs must come back -1
+        single = [e for e in range(E) if (inst == e).sum() == 1 and (ids == e).any()]
+        gone = single[0]
+        inst2 = inst.copy()
+        inst2[inst2 == gone] = -1
+        x32 = np.asarray(O.lplb(counts_o, inst, ipr)["x"], dtype=np.float32)
+        lp = U.lplb_prepare(inst2, R, E, ipr, DEV)
+        xd = to_dev(x32 if x32.size else np.zeros(1), torch.float32)
+        bad = ids.copy()
+        bad[1, 7, 2] = E                                  # out of range
+        ref_ids = np.where(bad == gone, -1, bad)
+        ref_ids[1, 7, 2] = -1
+        di_o = O.lplb_sample(ref_ids, inst2, ipr, E, x32, 5, 1)
+        n = ids.size
+        big = torch.zeros(n + 4, dtype=torch.int32, device=DEV)
+        big[1:1 + n] = to_dev(bad).view(-1)
+        out_big = torch.full((n + 4,), -9, dtype=torch.int32, device=DEV)
+        for aligned in (True, False):
+            err = err_word()
+            if aligned:
+                di = U.lplb_sample(to_dev(bad), lp, xd, 5, 1, err=err)
+            else:
+                di = U.lplb_sample(big[1:1 + n].view(R, T, K), lp, xd, 5, 1,
+                                   dest_inst=out_big[1:1 + n].view(R, T, K), err=err)
+            e = int(host(err)[0])
+            assert e & U.ERR_ID_RANGE and e & U.ERR_LP
+            assert np.array_equal(host(di), di_o)
+        ob = host(out_big)
+        assert ob[0] == -9 and (ob[1 + n:] == -9).all()
+        # a structure built for 2 ranks, used with 4
+        inst_small = np.where(inst[:2 * ipr] < 2 * E_loc, inst[:2 * ipr], -1)
+        lp2 = U.lplb_prepare(inst_small, 2, 2 * E_loc, ipr, DEV)
+        err = err_word()
+        di = U.lplb_sample(to_dev(np.where(ids < 2 * E_loc, ids, -1)), lp2, xd, 5, 1, err=err)
+        assert host(err)[0] & U.ERR_LP and (host(di) == -1).all()
+
+
 def test_lplb_sample_layer_full_size():
     """LPLB layer: the draw of three source ranks bit-exact on the oracle's split; with
     the kernel's own split, every pair lands on a copy of its expert and each copy's
