@@ -329,8 +329,9 @@ uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float*
  * is a probability distribution over its physical copies; every token routed to a
  * replicated expert draws one copy from it, and a single-copy expert keeps its only
  * instance.  Weights are the integers w_p = rint(max(x_p, 0) * 256) of uep_lplb's
- * quota step; the draw for slot k of global token g = r*T + t is word 0 u of
- * Philox4x64-10 at counter (g, k, 1, 0), key (seed, layer); v = floor(u * W / 2^64)
+ * quota step; the draw for slot k of global token g = r*T + t is word k mod 4 u of
+ * Philox4x64-10 at counter (g, k div 4, 1, 0), key (seed, layer) (one block of the
+ * generator per four slots of a token); v = floor(u * W / 2^64)
  * with W = sum w_p, and the first copy (instance order) whose running weight exceeds
  * v wins; W = 0: copy floor(u * n / 2^64) of the expert's n copies.
  * The dispatch layout then follows from uep_load_matrix on dest_inst (instances as

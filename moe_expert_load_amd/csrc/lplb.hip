@@ -662,15 +662,16 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
 // normalised per replicated expert, is a distribution over its physical copies from
 // which every token routed to that expert draws one; a single-copy expert keeps its
 // only instance).  Weights are the integers w_p = rint(max(x_p, 0) * 256) of the
-// quota step; the draw for slot k of global token g is word 0 of Philox4x64-10 at
-// counter (g, k, 1, 0), key (seed, layer), scaled by a 64x64->128-bit product, so
-// the choice is exact integer arithmetic.
+// quota step; the draw for slot k of global token g is word k mod 4 of Philox4x64-10
+// at counter (g, k div 4, 1, 0), key (seed, layer), scaled by a 64x64->128-bit
+// product, so the choice is exact integer arithmetic and one block of the generator
+// serves four slots.
 //
 // Each workgroup first stages the small tables in LDS (expert -> instance or group,
 // the groups' running copy weights and the copies' instances), then walks quads of
-// four consecutive slots of one token (one thread per quad, grid-stride), so every
-// lookup after the id load is an LDS read and ids and results move as 16-byte
-// vectors when K % 4 == 0.
+// four consecutive slots of one token (one thread per quad, grid-stride): one Philox
+// block per quad, every lookup after the id load an LDS read, and ids and results
+// moved as 16-byte vectors when K % 4 == 0.
 constexpr int kLsThreads = 256;
 constexpr int kLsMaxBlocks = 2048;          // 8 workgroups per CU of a 256-CU device
 
@@ -735,31 +736,38 @@ __global__ __launch_bounds__(kLsThreads) void lplb_sample_kernel(const int32_t* 
 #pragma unroll
       for (int u = 0; u < 4; ++u) e[u] = k0 + u < K ? ids[j0 + u] : -1;
     }
+    int grp[4];                                        // group of a slot that draws, or -1
+    bool draw = false;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       out[u] = -1;
+      grp[u] = -1;
       if (e[u] >= L.E || e[u] < -1) {
         bad |= UEP_ERR_ID_RANGE;
       } else if (e[u] >= 0) {
         const int ei = S.ei[e[u]];
-        if (ei >= 0) {
-          out[u] = ei;
-        } else if (ei == -1) {
-          bad |= UEP_ERR_LP;
+        if (ei >= 0) out[u] = ei;
+        else if (ei == -1) bad |= UEP_ERR_LP;
+        else grp[u] = -2 - ei;
+        draw |= grp[u] >= 0;
+      }
+    }
+    if (draw) {
+      uint64_t r[4];
+      philox4x64_10((uint64_t)g, (uint64_t)(k0 / 4), 1, 0, seed, layer, r);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (grp[u] < 0) continue;
+        const int c0 = S.gs[grp[u]], c1 = S.gs[grp[u] + 1];
+        const uint64_t W = S.cw[c1 - 1];
+        int pick = c0;
+        if (W == 0) {
+          pick = c0 + (int)__umul64hi(r[u], (uint64_t)(c1 - c0));
         } else {
-          const int gi = -2 - ei;
-          const int c0 = S.gs[gi], c1 = S.gs[gi + 1];
-          const uint64_t W = S.cw[c1 - 1];
-          const uint64_t r = philox4x64_10_w0((uint64_t)g, (uint64_t)(k0 + u), 1, 0, seed, layer);
-          int pick = c0;
-          if (W == 0) {
-            pick = c0 + (int)__umul64hi(r, (uint64_t)(c1 - c0));
-          } else {
-            const uint64_t v = __umul64hi(r, W);
-            while (pick < c1 - 1 && S.cw[pick] <= v) ++pick;
-          }
-          out[u] = S.ci[pick];
+          const uint64_t v = __umul64hi(r[u], W);
+          while (pick < c1 - 1 && S.cw[pick] <= v) ++pick;
         }
+        out[u] = S.ci[pick];
       }
     }
     if (vec) {

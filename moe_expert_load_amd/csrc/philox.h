@@ -1,7 +1,7 @@
 // Philox4x64-10, the counter-based generator of J. K. Salmon, M. A. Moraes, R. O. Dror
 // and D. E. Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11), section 4,
-// with the 4x64 multipliers and Weyl key increments given there.  Word 0 of the block
-// at counter (c0, c1, c2, c3) under key (k0, k1).
+// with the 4x64 multipliers and Weyl key increments given there.  The block (words
+// 0..3) at counter (c0, c1, c2, c3) under key (k0, k1).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,8 +22,8 @@ __device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t& hi, 
   lo = (p01 << 32) | (uint32_t)p00;
 }
 
-__device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2,
-                                                     uint64_t c3, uint64_t k0, uint64_t k1) {
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                              uint64_t k0, uint64_t k1, uint64_t (&w)[4]) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
@@ -39,7 +39,18 @@ __device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, u
     k0 += W0;
     k1 += W1;
   }
-  return c0;
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+}
+
+// word 0 alone (the last round's other product is dead code then)
+__device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                     uint64_t c3, uint64_t k0, uint64_t k1) {
+  uint64_t w[4];
+  philox4x64_10(c0, c1, c2, c3, k0, k1, w);
+  return w[0];
 }
 
 }  // namespace uep

@@ -234,7 +234,8 @@ def lplb_sample(topk_ids, inst_expert, inst_per_rank: int, E: int, x, seed: int,
 
     Readings: the distribution is taken on the integer weights w_p = rint(max(x_p, 0) *
     256) of the quota step (exact on both sides); the draw for slot k of global token
-    g is word 0 u of Philox4x64-10 at counter (g, k, 1, 0), key (seed, layer);
+    g is word k mod 4 u of Philox4x64-10 at counter (g, floor(k / 4), 1, 0), key
+    (seed, layer), so one block of the generator serves four slots of a token;
     v = floor(u * W / 2^64) with W = sum w_p, and the first copy (instance order) whose
     running weight exceeds v wins; with W = 0 the copy floor(u * n / 2^64) of the n
     copies.  x is indexed like lplb_structure's copies (replicated experts ascending,
@@ -254,7 +255,8 @@ def lplb_sample(topk_ids, inst_expert, inst_per_rank: int, E: int, x, seed: int,
     out = np.full((R, T, K), -1, dtype=np.int64)
     for r in (range(R) if ranks is None else ranks):
         g = np.arange(r * T, (r + 1) * T, dtype=np.uint64)
-        u = [philox4x64_10_np(g, (seed, layer), c1=k, c2=1)[:, 0] for k in range(K)]
+        blocks = [philox4x64_10_np(g, (seed, layer), c1=b, c2=1) for b in range((K + 3) // 4)]
+        u = [blocks[k // 4][:, k % 4] for k in range(K)]
         for t in range(T):
             for k in range(K):
                 e = int(ids[r, t, k])

@@ -34,8 +34,8 @@ def test_philox_matches_numpy(key):
 
 @pytest.mark.parametrize("key", [(3, 5), (MASK, 0)])
 def test_philox_full_counters_match_numpy(key):
-    """All four counter words (the LPLB draw uses (g, k, 1, 0)): numpy's Philox started
-    at counter (g - 1, w1, w2, w3) outputs the block at (g, w1, w2, w3)."""
+    """All four counter words (the LPLB draw uses (g, k div 4, 1, 0)): numpy's Philox
+    started at counter (g - 1, w1, w2, w3) outputs the block at (g, w1, w2, w3)."""
     cases = [(1, 0, 1, 0), (77, 5, 1, 0), (2 ** 40, 63, 1, 0), (9, 2 ** 63, 7, 2 ** 50)]
     for g, w1, w2, w3 in cases:
         bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
@@ -128,16 +128,20 @@ def test_waterfill_fallback_takes_the_lightest_clearly_lighter_candidate():
     assert (sh[1:] == -1).all()
 
 
-def _numpy_philox_word0(seed, layer, c0, c1=0, c2=0, c3=0):
-    """Word 0 of Philox4x64-10 at counter (c0, c1, c2, c3) from numpy's own generator,
-    which outputs the block at its counter + 1 (so it starts one below, with the borrow
-    carried through the four words)."""
+def _numpy_philox_words(seed, layer, c0, c1=0, c2=0, c3=0):
+    """Words 0..3 of Philox4x64-10 at counter (c0, c1, c2, c3) from numpy's own
+    generator, which outputs the block at its counter + 1 (so it starts one below, with
+    the borrow carried through the four words)."""
     c = (c0 | (c1 << 64) | (c2 << 128) | (c3 << 192)) - 1
     c %= 1 << 256
     start = [(c >> (64 * j)) & MASK for j in range(4)]
     bg = np.random.Philox(key=np.array([seed, layer], dtype=np.uint64),
                           counter=np.array(start, dtype=np.uint64))
-    return int(bg.random_raw())
+    return [int(bg.random_raw()) for _ in range(4)]
+
+
+def _numpy_philox_word0(seed, layer, c0, c1=0, c2=0, c3=0):
+    return _numpy_philox_words(seed, layer, c0, c1, c2, c3)[0]
 
 
 @pytest.mark.parametrize("shift,all_ranks", [(4, False), (0, False), (2, False), (4, True)])
@@ -423,20 +427,32 @@ def test_lplb_sample_zero_weights_uniform_and_single_copies():
 
 
 def test_lplb_sample_draw_is_the_published_generator():
-    """Every pair recomputed from numpy's own Philox4x64-10 at counter (g, k, 1, 0), key
-    (seed, layer): expert 0's copies (instances 0, 5, 11) carry weights 256, 512, 1280
-    and expert 5's (instances 2, 7) weight 0 each, so expert 5 takes the uniform branch,
-    copy floor(u * 2 / 2^64)."""
+    """Every pair recomputed from numpy's own Philox4x64-10: slot k of token g takes word
+    k mod 4 of the block at counter (g, k div 4, 1, 0), key (seed, layer).  Tokens have
+    six slots, so both blocks of a token and words 0..3 are used: expert 0's copies
+    (instances 0, 5, 11) carry weights 256, 512, 1280 and sit in slot 1 (block 0, word
+    1) or slot 4 (block 1, word 0); expert 5's (instances 2, 7) weigh 0 each, so it
+    takes the uniform branch, copy floor(u * 2 / 2^64), from slot 3 (block 0, word 3)
+    or slot 5 (block 1, word 1); single-copy experts fill the other slots."""
     inst, ipr = _two_copy_table()
     x = np.array([1.0, 2.0, 5.0, 0.0, 0.0], dtype=np.float32)
     R, T, seed, layer = 4, 6, 123, 9
-    ids = np.zeros((R, T, 2), dtype=np.int64)
-    ids[:, :, 1] = 5
+    ids = np.zeros((R, T, 6), dtype=np.int64)
+    ids[:, :3, :] = [3, 0, 4, 5, 6, 1]     # expert 0 in slot 1, expert 5 in slot 3
+    ids[:, 3:, :] = [3, 6, 4, 1, 0, 5]     # expert 0 in slot 4, expert 5 in slot 5
     out = O.lplb_sample(ids, inst, ipr, 8, x, seed=seed, layer=layer)
+    single = {1: 1, 3: 4, 4: 6, 6: 9}      # expert -> its only instance
     for r in range(R):
         for t in range(T):
             g = r * T + t
-            v = (_numpy_philox_word0(seed, layer, g, 0, 1) * 2048) >> 64
-            assert out[r, t, 0] == (0 if v < 256 else (5 if v < 768 else 11))
-            u = _numpy_philox_word0(seed, layer, g, 1, 1)
-            assert out[r, t, 1] == (2, 7)[(u * 2) >> 64]
+            words = _numpy_philox_words(seed, layer, g, 0, 1) + \
+                _numpy_philox_words(seed, layer, g, 1, 1)
+            for k in range(6):
+                e = int(ids[r, t, k])
+                if e == 0:
+                    v = (words[k] * 2048) >> 64
+                    assert out[r, t, k] == (0 if v < 256 else (5 if v < 768 else 11))
+                elif e == 5:
+                    assert out[r, t, k] == (2, 7)[(words[k] * 2) >> 64]
+                else:
+                    assert out[r, t, k] == single[e]
