@@ -316,6 +316,10 @@ uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
  *   m          [1]        out  max rank load of that split
  *   inst_quota [I]        out  integer quotas for every instance
  *   stats      [4]        out  optional: {n_replicated, n_copies, iterations run, 0}
+ *   err                   out  optional; UEP_ERR_LP: an expert with load but no instance
+ *                              or a column sum of 2^27 or more (the solve still runs), or
+ *                              `lp` not a structure from uep_lplb_prepare (then nothing
+ *                              else is written)
  * ------------------------------------------------------------------------- */
 size_t uep_lplb_struct_size(int32_t R, int32_t E, int32_t inst_per_rank);
 uep_status uep_lplb_prepare(const int32_t* inst_expert_host, int32_t R, int32_t E,
@@ -342,8 +346,9 @@ uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float*
  *   lp                    in   device structure from uep_lplb_prepare (same R)
  *   x         [n_copies]  in   per-copy split (uep_lplb's x, same copy order)
  *   dest_inst [R][T][K]   out  physical instance of every pair
- *   err                   optional: UEP_ERR_ID_RANGE, UEP_ERR_LP (no instance, or
- *                         a structure that is not one for R ranks)
+ *   err                   optional: UEP_ERR_ID_RANGE, UEP_ERR_LP (an expert with no
+ *                         instance; or `lp` not a structure from uep_lplb_prepare for R
+ *                         ranks, and then every pair is -1)
  * ------------------------------------------------------------------------- */
 uep_status uep_lplb_sample(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
                            const void* lp, const float* x, uint64_t seed, uint64_t layer,

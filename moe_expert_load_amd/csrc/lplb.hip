@@ -451,6 +451,14 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ stats,
                                                           int32_t* err) {
   __shared__ LpShared S;                    // static LDS: no dynamic-base lookups
+  // a buffer that is not a structure from uep_lplb_prepare (or sizes beyond the LDS
+  // tables) is refused whole: nothing but the error word is written
+  if (lpw[0] != kLpMagic || lpw[1] < 1 || lpw[1] > kLpMaxR || lpw[2] < 1 || lpw[2] > kLpMaxE ||
+      lpw[3] < 1 || lpw[4] != lpw[1] * lpw[3] || lpw[4] > kLpMaxI || lpw[5] < 0 ||
+      lpw[5] > kLpMaxG || lpw[6] < 0 || lpw[6] > kLpMaxN || lpw[7] < 0) {
+    if (threadIdx.x == 0) set_err(err, UEP_ERR_LP);
+    return;
+  }
   const LpView L = lp_view(lpw);
   const int R = L.R, E = L.E, G = L.G, n = L.n, nv = n + R + 2;
   const int tid = threadIdx.x;
@@ -696,7 +704,9 @@ __global__ __launch_bounds__(kLsThreads) void lplb_sample_kernel(const int32_t* 
   __shared__ LsShared S;
   const int qpt = (K + 3) / 4;                           // quads per token
   const int64_t n_quad = n_tok * qpt;
-  if (lpw[0] != kLpMagic || lpw[1] != R) {
+  // a structure for other ranks, or sizes beyond the LDS tables, is refused whole
+  if (lpw[0] != kLpMagic || lpw[1] != R || lpw[2] < 1 || lpw[2] > kLpMaxE || lpw[5] < 0 ||
+      lpw[5] > kLpMaxG || lpw[6] < 0 || lpw[6] > kLpMaxN) {
     for (int64_t q = (int64_t)blockIdx.x * kLsThreads + threadIdx.x; q < n_quad;
          q += (int64_t)gridDim.x * kLsThreads) {
       const int64_t g = q / qpt;

@@ -308,6 +308,33 @@ def test_lplb_sample_errors_and_layouts():
         assert host(err)[0] & U.ERR_LP and (host(di) == -1).all()
 
 
+def test_lplb_refuses_a_foreign_structure():
+    """A buffer that is not a structure from uep_lplb_prepare (all zeros, or a real one
+    with its copy count overwritten beyond the LDS tables) is refused by both kernels:
+    the solve writes nothing but UEP_ERR_LP, the draw leaves every pair -1."""
+    rng = np.random.default_rng(1500)
+    ids, inst, ipr, E = random_lplb_case(rng, 4, 2, 50, 3, 2)
+    R = 4
+    say("case: lplb foreign structure")
+    good = U.lplb_prepare(inst, R, E, ipr, DEV)
+    bad_n = good.clone()
+    bad_n.view(torch.int32)[6] = 1 << 20                   # n_copies beyond the tables
+    for lp in (torch.zeros_like(good), bad_n):
+        err = err_word()
+        x = torch.full((8,), -3.0, dtype=torch.float32, device=DEV)
+        m = torch.full((1,), -3.0, dtype=torch.float32, device=DEV)
+        q = torch.full((len(inst),), -3, dtype=torch.int32, device=DEV)
+        st = torch.full((4,), -3, dtype=torch.int32, device=DEV)
+        counts = to_dev(O.load_matrix(ids, E)[0])
+        U.lplb(counts, lp, 8, len(inst), iters=30, x=x, m=m, inst_quota=q, stats=st, err=err)
+        assert host(err)[0] == U.ERR_LP
+        assert (host(x) == -3.0).all() and host(m)[0] == -3.0
+        assert (host(q) == -3).all() and (host(st) == -3).all()
+        err = err_word()
+        di = U.lplb_sample(to_dev(ids), lp, x, 1, 2, err=err)
+        assert host(err)[0] == U.ERR_LP and (host(di) == -1).all()
+
+
 def test_lplb_sample_layer_full_size():
     """LPLB layer: the draw of three source ranks bit-exact on the oracle's split; with
     the kernel's own split, every pair lands on a copy of its expert and each copy's
