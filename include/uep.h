@@ -248,7 +248,8 @@ uep_status uep_combine(const uint16_t* out, const int32_t* dest_row, const float
  *                                 main_grad[e] = ((main_grad[e] + g_r1) + g_r2) + ...
  *                                 in fp32 round-to-nearest-even, then those slot
  *                                 gradients are set to +0.0
- *   slot_expert [R][S]                       in   from uep_solve_quota
+ *   slot_expert [R][S]                       in   from uep_solve_quota; entries outside
+ *                                                 [0, E) are empty slots (skipped)
  *   main_w  [E][expert_elems] bf16, slot_w [R][S][expert_elems] bf16   (WEIGHTS)
  *   main_grad [E][expert_elems] f32, slot_grad [R][S][expert_elems] f32 (GRAD_REDUCE)
  *   expert_elems % 8 == 0; unused pointers of the other mode may be NULL.

@@ -41,8 +41,9 @@ struct StGroups {
 };
 
 template <bool kByHome>
-__device__ __forceinline__ bool st_selected(int i, int e, int S, int E_loc, int r_begin, int r_end) {
-  if (e < 0) return false;
+__device__ __forceinline__ bool st_selected(int i, int e, int S, int E_loc, int n_exp,
+                                            int r_begin, int r_end) {
+  if (e < 0 || e >= n_exp) return false;        // empty, or not an expert: skipped
   const int r = kByHome ? e / E_loc : i / S;
   return r >= r_begin && r < r_end;
 }
@@ -55,9 +56,10 @@ template <bool kByHome>
 __device__ __forceinline__ void st_build_groups(const int32_t* __restrict__ slot_expert, int n_slots,
                                                 int S, int E_loc, int r_begin, int r_end,
                                                 StGroups& G) {
+  const int n_exp = n_slots / S * E_loc;           // R ranks x E_loc mains
   for (int i = threadIdx.x; i < n_slots; i += kStThreads) {
     const int e = slot_expert[i];
-    G.sel_e[i] = st_selected<kByHome>(i, e, S, E_loc, r_begin, r_end) ? e : -1;
+    G.sel_e[i] = st_selected<kByHome>(i, e, S, E_loc, n_exp, r_begin, r_end) ? e : -1;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < n_slots; i += kStThreads) {

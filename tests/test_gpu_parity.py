@@ -486,6 +486,22 @@ def test_stage_weights_matches_oracle():
                                 r_begin=r0, r_end=r1)
         O.stage_forward(se, main, slot, r0, r1)
         assert np.array_equal(host(slot_d).view(np.uint16), slot), (r0, r1)
+    # entries outside [0, E) are empty slots in both modes: skipped, never dereferenced
+    se_bad = se.copy()
+    se_bad[4, 0], se_bad[4, 1], se_bad[0, 0] = E, 1 << 30, -7
+    slot = rng.integers(0, 1 << 16, (R, S, n), dtype=np.uint16)
+    slot_d = to_dev(slot.view(np.int16), torch.int16)
+    U.stage_replica_weights(U.STAGE_WEIGHTS, R, E, S, to_dev(se_bad), n,
+                            main_w=to_dev(main.view(np.int16), torch.int16), slot_w=slot_d)
+    O.stage_forward(np.where((se_bad >= 0) & (se_bad < E), se_bad, -1), main, slot, 0, R)
+    assert np.array_equal(host(slot_d).view(np.uint16), slot)
+    mg_h = rng.standard_normal((E, n)).astype(np.float32)
+    sg_h = rng.standard_normal((R, S, n)).astype(np.float32)
+    mg, sg = to_dev(mg_h, torch.float32), to_dev(sg_h, torch.float32)
+    U.stage_replica_weights(U.STAGE_GRAD_REDUCE, R, E, S, to_dev(se_bad), n, main_grad=mg,
+                            slot_grad=sg)
+    O.grad_reduce(np.where((se_bad >= 0) & (se_bad < E), se_bad, -1), mg_h, sg_h, E // R)
+    assert np.array_equal(host(mg), mg_h) and np.array_equal(host(sg), sg_h)
 
 
 def test_grad_reduce_matches_oracle():
