@@ -94,6 +94,37 @@ def test_random_small_plans(seed):
     compare_plan(g, o, S)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_random_plans_wide(seed):
+    """Random geometries across the supported range: R up to 64, E up to 2048 (every
+    fifth seed above 1024, the fallback ranking kernels), top-k up to 16, up to 4 slots
+    per rank, up to 3000 tokens per rank, empty slots; the plan and the permute of
+    random 16-bit rows (every row and row_src entry) bit-exact."""
+    rng = np.random.default_rng(5000 + seed)
+    R = int(rng.integers(1, 65))
+    E_loc = int(rng.integers(1, 17)) if seed % 5 else int(rng.integers(17, 33))
+    E = R * E_loc
+    K = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(0, 3001))
+    S = int(rng.integers(0, 5))
+    q_min = int(rng.integers(0, 400))
+    H = 8 * int(rng.integers(1, 9))
+    say(f"case: wide random plan seed={seed} R={R} E={E} K={K} T={T} S={S} q_min={q_min} H={H}")
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.03 * (seed % 3))
+    o = oracle_plan(ids, E, S, q_min)
+    g = plan_on_gpu(U, to_dev(ids), E, S, q_min)
+    compare_plan(g, o, S)
+    xh = rng.integers(0, 1 << 16, (R, T, H), dtype=np.uint16)
+    P = int(o["counts"].sum())
+    out = torch.zeros(P, H, dtype=torch.int16, device=DEV)
+    row_src = torch.full((P,), -7, dtype=torch.int32, device=DEV)
+    U.permute(to_dev(xh.view(np.int16), torch.int16), g["dest_row"], out, row_src)
+    eo, es, ew = O.permute(xh, o["dest_row"], 0, R, P)
+    assert ew.all()
+    assert np.array_equal(host(out).view(np.uint16), eo)
+    assert np.array_equal(host(row_src), es)
+
+
 @pytest.mark.parametrize("K", [3, 7, 8, 9, 12, 13, 16])
 def test_load_matrix_k_variants(K):
     """Every register-size variant of the ranking kernel (K <= 8, <= 12, <= 16) at its
@@ -640,6 +671,30 @@ def test_waterfill_random_small(seed):
                                           local_pref_shift=shift, all_ranks=mode)
         assert host(wl)[0] == H_o and np.array_equal(host(sl), S_o)
         assert np.array_equal(host(sh), sh_o)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_waterfill_random_wide(seed):
+    """Waterfill over the supported range: R up to 64, up to 8 experts per rank, top-k
+    up to 16, up to 1500 tokens per rank, local preference shifts 0..8, both candidate
+    modes; waterline, slacks and every token's shared rank bit-exact."""
+    rng = np.random.default_rng(900 + seed)
+    R = int(rng.integers(2, 65))
+    E = R * int(rng.integers(1, 9))
+    K = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 1501))
+    shift = int(rng.integers(0, 9))
+    mode = bool(seed % 2)
+    say(f"case: waterfill wide seed={seed} R={R} E={E} K={K} T={T} shift={shift} all={mode}")
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
+    B = rng.integers(0, T + 1, R).astype(np.int32)
+    counts_o, _ = O.load_matrix(ids, E)
+    sh_o, H_o, S_o, L_o = O.waterfill(counts_o, ids, B, 777 + seed, 5, shift, all_ranks=mode)
+    sh, wl, sl, rl, ext = U.waterfill(to_dev(counts_o), to_dev(ids), to_dev(B), 777 + seed, 5,
+                                      local_pref_shift=shift, all_ranks=mode)
+    assert host(wl)[0] == H_o and np.array_equal(host(sl), S_o)
+    assert np.array_equal(host(rl), L_o)
+    assert np.array_equal(host(sh), sh_o)
 
 
 def test_waterfill_zero_slack_and_fallback_cases():
