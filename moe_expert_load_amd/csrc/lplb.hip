@@ -212,20 +212,24 @@ __device__ __forceinline__ void blk_min2(float& x, float& y, LpShared& S) {
   y = ty;
 }
 
-// out[R+G] = A * vec
-__device__ __forceinline__ void lp_Av(const float* vec, float* out, int n, int R, int G, LpShared& S) {
-  const float Ma = vec[n + R] + vec[n + R + 1];
+// out[i] = fin(i, (A * vec)_i) for i < R + G, with vec(j) the j-th element (read from
+// LDS or formed on the fly).  Thread i writes out[i] only: a caller that next touches
+// out[i] in thread i needs no barrier in between.
+template <class Vec, class Fin>
+__device__ __forceinline__ void lp_Av(Vec vec, Fin fin, float* out, int n, int R, int G,
+                                      LpShared& S) {
+  const float Ma = vec(n + R) + vec(n + R + 1);
   for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
     float acc;
     if (i < R) {
-      acc = Ma - vec[n + i];
-      for (int k = S.rank_start[i]; k < S.rank_start[i + 1]; ++k) acc -= vec[S.rank_copy[k]];
+      acc = Ma - vec(n + i);
+      for (int k = S.rank_start[i]; k < S.rank_start[i + 1]; ++k) acc -= vec(S.rank_copy[k]);
     } else {
       const int g = i - R;
       acc = 0.0f;
-      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += vec[p];
+      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += vec(p);
     }
-    out[i] = acc;
+    out[i] = fin(i, acc);
   }
 }
 
@@ -527,14 +531,14 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     for (int i = tid; i < nv; i += kLpThreads) S.z[i] = fmaxf(lp_cost(i, n, R) - S.tv[i], 0.0f) + 1.0f;
     __syncthreads();
 
+    // Barriers below separate only accesses across threads: a loop over i that reads
+    // what the same thread wrote at index i in the step before needs none.
+    const auto plus_rb = [&](int i, float a) { return a + S.rb[i]; };
     for (int it = 0; it < iters; ++it) {
-      // residuals and complementarity
-      lp_Av(S.v, S.rb, n, R, G, S);
-      __syncthreads();
-      for (int i = tid; i < R + G; i += kLpThreads)
-        S.rb[i] = (i < R ? S.f[i] : S.hh[i - R]) - S.rb[i];
+      // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
+      lp_Av([&](int j) { return S.v[j]; },
+            [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, S);
       lp_ATy(S.y, S.tv, n, R, G, S);
-      __syncthreads();
       double cz = 0.0;
       for (int i = tid; i < nv; i += kLpThreads) {
         S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
@@ -547,21 +551,15 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
       if (!(mu >= kMuStop) || gap <= kGapRel * fmax(1.0, (double)S.v[n + R])) break;
       ++run;
       lp_factor(n, R, G, L, S);
-      // predictor: rhs = rb + A (v + D rc)
-      for (int i = tid; i < nv; i += kLpThreads) S.tv[i] = S.v[i] + (float)(S.d[i] * S.rc[i]);
-      __syncthreads();
-      lp_Av(S.tv, S.rhs, n, R, G, S);
-      __syncthreads();
-      for (int i = tid; i < R + G; i += kLpThreads) S.rhs[i] += S.rb[i];
+      // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
+      lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
       __syncthreads();
       lp_solve(n, R, G, S);
       lp_ATy(S.dy, S.tv, n, R, G, S);
-      __syncthreads();
       for (int i = tid; i < nv; i += kLpThreads) {
         S.dz[i] = S.rc[i] - S.tv[i];
         S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
       }
-      __syncthreads();
       float ap, ad;
       lp_steps(nv, S, ap, ad);
       double ca = 0.0;
@@ -577,19 +575,15 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
         S.tv[i] = (float)(S.d[i] * S.rc[i]) - rmu / S.z[i];
       }
       __syncthreads();
-      lp_Av(S.tv, S.rhs, n, R, G, S);
-      __syncthreads();
-      for (int i = tid; i < R + G; i += kLpThreads) S.rhs[i] += S.rb[i];
+      lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, S);
       __syncthreads();
       lp_solve(n, R, G, S);
       lp_ATy(S.dy, S.tv, n, R, G, S);
-      __syncthreads();
       for (int i = tid; i < nv; i += kLpThreads) {
         const float rmu = S.dv[i];
         S.dz[i] = S.rc[i] - S.tv[i];
         S.dv[i] = rmu / S.z[i] - (float)(S.d[i] * S.dz[i]);
       }
-      __syncthreads();
       float ap2, ad2;
       lp_steps(nv, S, ap2, ad2);
       for (int i = tid; i < nv; i += kLpThreads) {
