@@ -308,6 +308,27 @@ def test_lplb_sample_errors_and_layouts():
         assert host(err)[0] & U.ERR_LP and (host(di) == -1).all()
 
 
+def test_lplb_sample_zero_weight_copy_ahead():
+    """R = 4, E = 8 (two mains per rank), expert 0 on instances 0, 5 and 11 with weights
+    (0, 1, 0): W = 1, every draw has v = 0 and must take instance 5, never the
+    zero-weight copy ahead of it; the oracle agrees pair by pair."""
+    say("case: lplb sample zero-weight copy ahead")
+    ipr = 3
+    inst = np.full(4 * ipr, -1, dtype=np.int32)
+    for r in range(4):
+        inst[r * ipr:r * ipr + 2] = [2 * r, 2 * r + 1]
+    inst[1 * ipr + 2] = 0
+    inst[3 * ipr + 2] = 0
+    inst[0 * ipr + 2] = 5
+    x = np.array([0.0, 1.0 / 256.0, 0.0, 1.0, 1.0], dtype=np.float32)
+    ids = np.zeros((4, 300, 1), dtype=np.int32)
+    lp = U.lplb_prepare(inst, 4, 8, ipr, DEV)
+    err = err_word()
+    di = host(U.lplb_sample(to_dev(ids), lp, to_dev(x, torch.float32), 3, 1, err=err))
+    assert host(err)[0] == 0 and (di == 5).all()
+    assert np.array_equal(di, O.lplb_sample(ids, inst, ipr, 8, x, seed=3, layer=1))
+
+
 def test_lplb_refuses_a_foreign_structure():
     """A buffer that is not a structure from uep_lplb_prepare (all zeros, or a real one
     with its copy count overwritten beyond the LDS tables) is refused by both kernels:

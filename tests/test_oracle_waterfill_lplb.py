@@ -426,6 +426,18 @@ def test_lplb_sample_zero_weights_uniform_and_single_copies():
     assert (np.abs(got - n * p) <= 4 * np.sqrt(n * p * (1 - p)) + 1).all()
 
 
+def test_lplb_sample_zero_weight_copy_ahead_is_never_drawn():
+    """Weights (0, 1, 0) over expert 0's copies (instances 0, 5, 11): W = 1, so every
+    draw has v = 0, and the first copy whose running weight exceeds 0 is instance 5; a
+    zero-weight copy ahead of it (or after it) is never taken."""
+    inst, ipr = _two_copy_table()
+    x = np.array([0.0, 1.0 / 256.0, 0.0, 1.0, 1.0], dtype=np.float32)
+    R, T = 4, 500
+    ids = np.zeros((R, T, 1), dtype=np.int64)
+    out = O.lplb_sample(ids, inst, ipr, 8, x, seed=3, layer=1)
+    assert (out == 5).all()
+
+
 def test_lplb_sample_draw_is_the_published_generator():
     """Every pair recomputed from numpy's own Philox4x64-10: slot k of token g takes word
     k mod 4 of the block at counter (g, k div 4, 1, 0), key (seed, layer).  Tokens have
