@@ -61,7 +61,8 @@ enum {
   UEP_ERR_INST_DUP = 8,     /* two instances of one expert on one rank */
   UEP_ERR_BAD_QUOTA = 16,   /* negative quota, or quota on an unused instance */
   UEP_ERR_COVER = 32,       /* a bucket position not covered by the transfer plan */
-  UEP_ERR_LP = 64           /* LPLB: an expert with load but no instance */
+  UEP_ERR_LP = 64,          /* LPLB: an expert with load but no instance */
+  UEP_ERR_ROW_RANGE = 128   /* a dest_row entry outside [-1, out_rows) */
 };
 
 /* Library version string and a static text for a status code (host). */
@@ -198,14 +199,17 @@ uep_status uep_reroute_assign(const int32_t* counts, const int32_t* topk_ids,
  * Each source row is read once and written to each of its K rows.
  *
  *   x        [R][T][H] bf16 bits  in   activations (H % 8 == 0, rows 16-byte aligned)
- *   dest_row [R][T][K]            in   from uep_reroute_assign
+ *   dest_row [R][T][K]            in   from uep_reroute_assign (-1: no row)
  *   r_begin, r_end                     only sources in [r_begin, r_end) are moved
- *   out      [P][H] bf16 bits     out  P = number of routed pairs (max dest_row + 1)
- *   row_src  [P]                  out  optional; (r*T + t)*K + k of the pair in each row
+ *   out      [out_rows][H] bf16   out  dispatch buffer, out_rows >= the routed pairs
+ *                                      (inst_offset[I] of uep_reroute_assign)
+ *   row_src  [out_rows]           out  optional; (r*T + t)*K + k of the pair in each row
+ *   err                           out  optional; UEP_ERR_ROW_RANGE: a dest_row entry
+ *                                      outside [-1, out_rows), that pair is not moved
  * ------------------------------------------------------------------------- */
 uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, int32_t T,
                        int32_t K, int32_t H, int32_t r_begin, int32_t r_end, uint16_t* out,
-                       int32_t* row_src, void* stream);
+                       int64_t out_rows, int32_t* row_src, int32_t* err, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * uep_combine -- expert outputs from the dispatch buffer back to token order.
@@ -218,17 +222,20 @@ uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, in
  * each product and addition rounded to nearest even in fp32, k ascending from +0.0,
  * no fused multiply-add, then nearest-even rounding to bf16 (a NaN stays a NaN).
  *
- *   out      [P][H] bf16 bits     in   dispatch buffer (layout of uep_permute's out),
+ *   out      [out_rows][H] bf16   in   dispatch buffer (layout of uep_permute's out),
  *                                      16-byte aligned
  *   dest_row [R][T][K]            in   from uep_reroute_assign
  *   gate_w   [R][T][K] fp32       in   combine weights
  *   r_begin, r_end                     only tokens of ranks in [r_begin, r_end) are written
  *   y        [R][T][H] bf16 bits  out  16-byte aligned; other ranks' rows are untouched
+ *   err                           out  optional; UEP_ERR_ROW_RANGE: a dest_row entry
+ *                                      outside [-1, out_rows), taken as no row
  * Returns UEP_EINVAL / UEP_EGEOM like uep_permute.
  * ------------------------------------------------------------------------- */
-uep_status uep_combine(const uint16_t* out, const int32_t* dest_row, const float* gate_w,
-                       int32_t R, int32_t T, int32_t K, int32_t H, int32_t r_begin,
-                       int32_t r_end, uint16_t* y, void* stream);
+uep_status uep_combine(const uint16_t* out, int64_t out_rows, const int32_t* dest_row,
+                       const float* gate_w, int32_t R, int32_t T, int32_t K, int32_t H,
+                       int32_t r_begin, int32_t r_end, uint16_t* y, int32_t* err,
+                       void* stream);
 
 /* ------------------------------------------------------------------------- *
  * uep_stage_replica_weights -- redundant-slot weight staging / gradient reduction.

@@ -35,14 +35,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __restrict__ y_disp,
                                                              const int32_t* __restrict__ dest_row,
                                                              const float* __restrict__ gate_w,
-                                                             u32x4* __restrict__ y, int64_t g0,
-                                                             int64_t g1, int K, int nvec) {
+                                                             u32x4* __restrict__ y,
+                                                             int64_t out_rows, int64_t g0,
+                                                             int64_t g1, int K, int nvec,
+                                                             int32_t* err) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x % kWave;
   const int64_t b = xcd_block(blockIdx.x, gridDim.x);
   const int64_t g = g0 + b * kCbTokPerBlock + threadIdx.x / kWave;
   if (g >= g1) return;
-  const int d_mine = lane < K ? dest_row[g * K + lane] : -1;
+  const int d_mine = checked_row(lane < K ? dest_row[g * K + lane] : -1, out_rows, err);
   const int w_mine = lane < K ? __float_as_int(gate_w[g * K + lane]) : 0;
   for (int v0 = 0; v0 < nvec; v0 += kCbVec * kWave) {
     float acc[kCbVec * 8];
@@ -101,10 +103,11 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
 
 using namespace uep;
 
-extern "C" uep_status uep_combine(const uint16_t* y_disp, const int32_t* dest_row,
-                                  const float* gate_w, int32_t R, int32_t T, int32_t K, int32_t H,
-                                  int32_t r_begin, int32_t r_end, uint16_t* y, void* stream) {
-  if (R <= 0 || T < 0 || K <= 0 || H <= 0) return UEP_EINVAL;
+extern "C" uep_status uep_combine(const uint16_t* y_disp, int64_t out_rows,
+                                  const int32_t* dest_row, const float* gate_w, int32_t R,
+                                  int32_t T, int32_t K, int32_t H, int32_t r_begin, int32_t r_end,
+                                  uint16_t* y, int32_t* err, void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || H <= 0 || out_rows < 0) return UEP_EINVAL;
   if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
   if (K > 64 || H % 8 != 0 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
   const int64_t g0 = (int64_t)r_begin * T, g1 = (int64_t)r_end * T;
@@ -115,7 +118,7 @@ extern "C" uep_status uep_combine(const uint16_t* y_disp, const int32_t* dest_ro
   const int64_t blocks = (g1 - g0 + kCbTokPerBlock - 1) / kCbTokPerBlock;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(kCbThreads), 0,
                      uep_stream(stream), reinterpret_cast<const u32x4*>(y_disp), dest_row, gate_w,
-                     reinterpret_cast<u32x4*>(y), g0, g1, K, H / 8);
+                     reinterpret_cast<u32x4*>(y), out_rows, g0, g1, K, H / 8, err);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
 }

@@ -121,6 +121,16 @@ __device__ __forceinline__ void set_err(int32_t* err, int bits) {
   if (err) atomicOr(err, bits);
 }
 
+// A dispatch row taken from device data: rows outside [-1, out_rows) become -1 (no
+// row) and raise UEP_ERR_ROW_RANGE once per wave.  Every lane of the wave calls it.
+__device__ __forceinline__ int checked_row(int d, int64_t out_rows, int32_t* err) {
+  const bool bad = d < -1 || d >= out_rows;
+  const uint64_t m = ballot(bad);
+  if (m && (threadIdx.x % kWave) == (unsigned)(__ffsll((unsigned long long)m) - 1))
+    set_err(err, UEP_ERR_ROW_RANGE);
+  return bad ? -1 : d;
+}
+
 }  // namespace uep
 
 // Host-side helpers.

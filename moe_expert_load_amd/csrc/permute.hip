@@ -27,13 +27,14 @@ constexpr int kVec = 8;   // 16-byte vectors per lane per slice (8 KiB per wave)
 template <bool kNT>
 __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ dest_row,
-                                                             u32x4* __restrict__ out, int64_t g0,
-                                                             int64_t g1, int K, int nvec) {
+                                                             u32x4* __restrict__ out, int64_t out_rows,
+                                                             int64_t g0, int64_t g1, int K, int nvec,
+                                                             int32_t* err) {
   const int lane = threadIdx.x % kWave;
   const int64_t b = xcd_block(blockIdx.x, gridDim.x);
   const int64_t g = g0 + b * kPmTokPerBlock + threadIdx.x / kWave;
   if (g >= g1) return;
-  const int d_mine = lane < K ? dest_row[g * K + lane] : -1;
+  const int d_mine = checked_row(lane < K ? dest_row[g * K + lane] : -1, out_rows, err);
   const u32x4* src = x + g * nvec;
   for (int v0 = 0; v0 < nvec; v0 += kVec * kWave) {
     u32x4 buf[kVec];
@@ -58,15 +59,17 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
   }
 }
 
-// row_src[dest_row[j]] = j for the pairs j in [j0, j1), one thread per pair.
+// row_src[dest_row[j]] = j for the pairs j in [j0, j1), one thread per pair (rows
+// outside the buffer were flagged by the permute and are skipped here).
 __global__ __launch_bounds__(kPmThreads) void row_src_kernel(const int32_t* __restrict__ dest_row,
                                                              int32_t* __restrict__ row_src,
-                                                             int64_t j0, int64_t j1, int swizzle) {
+                                                             int64_t out_rows, int64_t j0,
+                                                             int64_t j1, int swizzle) {
   const int64_t b = swizzle ? xcd_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t j = j0 + b * kPmThreads + threadIdx.x;
   if (j >= j1) return;
   const int32_t d = dest_row[j];
-  if (d >= 0) row_src[d] = (int32_t)j;
+  if (d >= 0 && d < out_rows) row_src[d] = (int32_t)j;
 }
 
 }  // namespace uep
@@ -75,8 +78,9 @@ using namespace uep;
 
 extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, int32_t R, int32_t T,
                                   int32_t K, int32_t H, int32_t r_begin, int32_t r_end,
-                                  uint16_t* out, int32_t* row_src, void* stream) {
-  if (R <= 0 || T < 0 || K <= 0 || H <= 0) return UEP_EINVAL;
+                                  uint16_t* out, int64_t out_rows, int32_t* row_src, int32_t* err,
+                                  void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || H <= 0 || out_rows < 0) return UEP_EINVAL;
   if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
   if (K > 64 || H % 8 != 0 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
   const int64_t g0 = (int64_t)r_begin * T, g1 = (int64_t)r_end * T;
@@ -93,9 +97,11 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
   u32x4* ov = reinterpret_cast<u32x4*>(out);
   hipStream_t s = uep_stream(stream);
   if (nt)
-    hipLaunchKernelGGL(permute_kernel<true>, grid, block, 0, s, xv, dest_row, ov, g0, g1, K, H / 8);
+    hipLaunchKernelGGL(permute_kernel<true>, grid, block, 0, s, xv, dest_row, ov, out_rows, g0, g1,
+                       K, H / 8, err);
   else
-    hipLaunchKernelGGL(permute_kernel<false>, grid, block, 0, s, xv, dest_row, ov, g0, g1, K, H / 8);
+    hipLaunchKernelGGL(permute_kernel<false>, grid, block, 0, s, xv, dest_row, ov, out_rows, g0, g1,
+                       K, H / 8, err);
   UEP_CHECK_LAUNCH();
   if (row_src) {
     const int64_t j0 = g0 * K, j1 = g1 * K;
@@ -103,8 +109,8 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
     // The XCD map helps once the scatter spans many blocks (measured: whole
     // Qwen-layer group faster, one rank's share slower).
     const int swizzle = rblocks >= 4096;
-    hipLaunchKernelGGL(row_src_kernel, dim3((unsigned)rblocks), block, 0, s, dest_row, row_src, j0,
-                       j1, swizzle);
+    hipLaunchKernelGGL(row_src_kernel, dim3((unsigned)rblocks), block, 0, s, dest_row, row_src,
+                       out_rows, j0, j1, swizzle);
     UEP_CHECK_LAUNCH();
   }
   return UEP_OK;

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libuep.so")
 
 OK, EINVAL, EGEOM, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 ERR_ID_RANGE, ERR_DUP_ID, ERR_QUOTA_SUM, ERR_INST_DUP = 1, 2, 4, 8
-ERR_BAD_QUOTA, ERR_COVER, ERR_LP = 16, 32, 64
+ERR_BAD_QUOTA, ERR_COVER, ERR_LP, ERR_ROW_RANGE = 16, 32, 64, 128
 STAGE_WEIGHTS, STAGE_GRAD_REDUCE = 0, 1
 
 _P = ctypes.c_void_p
@@ -42,8 +42,8 @@ SIGNATURES = {
     "uep_reroute_workspace_size": (_SZ, [_I, _I, _I]),
     "uep_reroute_assign": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
-    "uep_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P, _P, _P]),
+    "uep_combine": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "uep_stage_replica_weights": (_I, [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
     "uep_waterfill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U64, _U64, _I, _I, _P, _P, _P, _P, _P,
                            _P]),
@@ -186,21 +186,32 @@ def reroute_assign(counts, topk_ids, bucket_pos, inst_per_rank, inst_expert, ins
     return xfer, inst_offset, dest_inst, dest_row
 
 
-def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None):
-    """x [R][T][H] bf16 (or 16-bit) tensor; out [P][H] of the same dtype."""
+def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None, err=None):
+    """x [R][T][H] bf16 (or 16-bit) tensor; out [P][H] of the same dtype (P rows bound
+    the dispatch rows: an entry of dest_row outside [-1, P) is skipped and flagged)."""
     R, T, H = x.shape
+    _i32(dest_row, "dest_row")
     K = dest_row.shape[2]
     r_end = R if r_end is None else r_end
     if x.element_size() != 2 or out.element_size() != 2:
         raise TypeError("x and out must hold 16-bit elements")
-    _check(LIB.uep_permute(_p(x), _p(dest_row), R, T, K, H, r_begin, r_end, _p(out),
-                           _p(row_src), _s(stream)), "uep_permute")
+    if tuple(dest_row.shape) != (R, T, K) or out.dim() != 2 or out.shape[1] != H:
+        raise TypeError("dest_row must be [R][T][K] and out [P][H] for x [R][T][H]")
+    if row_src is not None:
+        _i32(row_src, "row_src")
+        if row_src.numel() != out.shape[0]:
+            raise TypeError("row_src must have one entry per row of out")
+    _check(LIB.uep_permute(_p(x), _p(dest_row), R, T, K, H, r_begin, r_end, _p(out), out.shape[0],
+                           _p(row_src), _p(err), _s(stream)), "uep_permute")
     return out, row_src
 
 
-def combine(out, dest_row, gate_w, y, r_begin=0, r_end=None, stream=None):
+def combine(out, dest_row, gate_w, y, r_begin=0, r_end=None, stream=None, err=None):
     """out [P][H] 16-bit dispatch buffer; dest_row [R][T][K] int32; gate_w [R][T][K]
     float32; y [R][T][H] 16-bit (rows of ranks in [r_begin, r_end) are written)."""
+    _i32(dest_row, "dest_row")
+    if out.dim() != 2 or dest_row.dim() != 3:
+        raise TypeError("out must be [P][H] and dest_row [R][T][K]")
     R, T, K = dest_row.shape
     H = out.shape[1]
     r_end = R if r_end is None else r_end
@@ -210,8 +221,8 @@ def combine(out, dest_row, gate_w, y, r_begin=0, r_end=None, stream=None):
         raise TypeError("gate_w must be float32 [R][T][K]")
     if tuple(y.shape) != (R, T, H):
         raise TypeError("y must be [R][T][H]")
-    _check(LIB.uep_combine(_p(out), _p(dest_row), _p(gate_w), R, T, K, H, r_begin, r_end, _p(y),
-                           _s(stream)), "uep_combine")
+    _check(LIB.uep_combine(_p(out), out.shape[0], _p(dest_row), _p(gate_w), R, T, K, H, r_begin,
+                           r_end, _p(y), _p(err), _s(stream)), "uep_combine")
     return y
 
 

@@ -68,21 +68,25 @@ def test_host_side_calls_without_gpu(lib):
                                ctypes.c_size_t(0), null) == 2
     assert lib.uep_solve_quota(null, i32(3), i32(7), i32(1), i32(1), null, null, null, null, null,
                                null) == 2
-    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2), null, null,
-                           null) == 2
-    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3), null, null,
-                           null) == 1
+    i64 = ctypes.c_int64
+    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2), null,
+                           i64(16), null, null, null) == 2
+    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3), null,
+                           i64(16), null, null, null) == 1
+    assert lib.uep_permute(null, null, i32(2), i32(4), i32(2), i32(16), i32(0), i32(2), null,
+                           i64(-1), null, null, null) == 1
     assert lib.uep_lplb_prepare(null, i32(2), i32(2), i32(2), null, ctypes.c_size_t(0), null) == 1
     assert lib.uep_identity_quota(null, i32(65), i32(130), i32(4), null, null, null) == 2
     assert lib.uep_stage_replica_weights(i32(0), i32(4), i32(8), i32(9), null, i32(0), i32(4), null,
                                          null, null, null, ctypes.c_int64(8), null) == 2
-    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(12), i32(0), i32(2),
-                           null, null) == 2
-    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(16), i32(1), i32(3),
-                           null, null) == 1
-    assert lib.uep_combine(null, null, null, i32(2), i32(4), i32(2), i32(16), i32(0), i32(2),
-                           null, null) == 1
-    i64 = ctypes.c_int64
+    assert lib.uep_combine(null, i64(16), null, null, i32(2), i32(4), i32(2), i32(12), i32(0),
+                           i32(2), null, null, null) == 2
+    assert lib.uep_combine(null, i64(16), null, null, i32(2), i32(4), i32(2), i32(16), i32(1),
+                           i32(3), null, null, null) == 1
+    assert lib.uep_combine(null, i64(16), null, null, i32(2), i32(4), i32(2), i32(16), i32(0),
+                           i32(2), null, null, null) == 1
+    assert lib.uep_combine(null, i64(-1), null, null, i32(2), i32(4), i32(2), i32(16), i32(0),
+                           i32(2), null, null, null) == 1
     assert lib.uep_device_copy(null, null, i64(0), null) == 0
     assert lib.uep_device_copy(null, null, i64(-16), null) == 1
     assert lib.uep_device_copy(null, null, i64(32), null) == 1
@@ -114,7 +118,8 @@ int main(void) {
   /* geometry errors are answered on the host, before any device work */
   if (uep_load_matrix(NULL, 0, 1, 1, 4, NULL, NULL, NULL, NULL, 0, NULL) != UEP_EINVAL) return 3;
   if (uep_load_matrix(NULL, 65, 1, 1, 4, NULL, NULL, NULL, NULL, 0, NULL) != UEP_EGEOM) return 4;
-  if (uep_permute(NULL, NULL, 2, 4, 2, 12, 0, 2, NULL, NULL, NULL) != UEP_EGEOM) return 5;
+  if (uep_permute(NULL, NULL, 2, 4, 2, 12, 0, 2, NULL, 16, NULL, NULL, NULL) != UEP_EGEOM) return 5;
+  if (UEP_ERR_ROW_RANGE != 128) return 6;
   printf("%%d functions, %%s\n", (int)(sizeof table / sizeof table[0]), v);
   return 0;
 }

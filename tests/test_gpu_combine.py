@@ -75,6 +75,42 @@ def test_combine_rank_range_and_noops():
     assert (bits(y) == 0).all()
 
 
+def test_permute_and_combine_bound_rows_by_the_buffer():
+    """dest_row entries outside [-1, P) (P = rows of the dispatch buffer: one at P, one
+    far beyond, one below -1) are skipped by the permute, row_src and the combine and
+    raise UEP_ERR_ROW_RANGE; every other row matches the oracle run on the same table
+    with those entries empty.  Rows past P in a larger allocation stay untouched."""
+    say("case: permute / combine row bounds")
+    R, T, K, E, H = 4, 60, 3, 8, 264
+    dr, y_disp, w = random_case(11, R, T, K, E, H, 0.0)
+    P = y_disp.shape[0]
+    bad = dr.copy()
+    bad[0, 3, 1], bad[2, 7, 0], bad[3, 59, 2] = P, 1 << 30, -5
+    ok = np.where((bad >= -1) & (bad < P), bad, -1)
+    rng = np.random.default_rng(12)
+    xh = rng.integers(0, 1 << 16, (R, T, H), dtype=np.uint16)
+    x = to_dev(xh.view(np.int16), torch.int16)
+    big = torch.full((P + 5, H), 7, dtype=torch.int16, device=DEV)
+    rs_big = torch.full((P + 5,), -7, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    U.permute(x, to_dev(bad), big[:P], rs_big[:P], err=err)
+    eo, es, ew = O.permute(xh, ok, 0, R, P)
+    got = host(big).view(np.uint16)
+    assert host(err)[0] == U.ERR_ROW_RANGE
+    assert np.array_equal(got[:P][ew], eo[ew]) and (got[:P][~ew] == 7).all()
+    assert (got[P:] == 7).all() and (host(rs_big)[P:] == -7).all()
+    assert np.array_equal(host(rs_big)[:P][ew], es[ew])
+    y = torch.full((R, T, H), 77, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    U.combine(y_disp, to_dev(bad), to_dev(w, torch.float32), y, err=err)
+    assert host(err)[0] == U.ERR_ROW_RANGE
+    assert np.array_equal(bits(y), O.combine(bits(y_disp), ok, w))
+    # the valid table raises nothing
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    U.combine(y_disp, to_dev(dr), to_dev(w, torch.float32), y, err=err)
+    assert host(err)[0] == 0
+
+
 def test_combine_summation_order_hand_case():
     """Terms 1, 2^-8, 0.75*2^-24, 0.75*2^-24: summed in ascending k in fp32 the small
     terms are lost and the bf16 tie rounds to even (0x3F80); the reversed slot order
