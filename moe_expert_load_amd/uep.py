@@ -110,6 +110,18 @@ def _new(shape, like: torch.Tensor, dtype=torch.int32) -> torch.Tensor:
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def _buf(t: Optional[torch.Tensor], n: int, name: str, dtype=torch.int32):
+    """A caller's buffer for the library to read or write: contiguous, of `dtype` (any
+    16-bit type for torch.int16), with at least n elements, since the kernels index it
+    by the geometry alone.  None stays None."""
+    if t is None:
+        return None
+    ok_type = t.element_size() == 2 if dtype == torch.int16 else t.dtype == dtype
+    if not ok_type or not t.is_contiguous() or t.numel() < n:
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor of at least {n} elements")
+    return t
+
+
 # ---------------------------------------------------------------------------
 def load_matrix_workspace_size(R, T, K, E) -> int:
     return int(LIB.uep_load_matrix_workspace_size(R, T, K, E))
@@ -121,11 +133,14 @@ def load_matrix(topk_ids, E, counts=None, bucket_pos=None, err=None, ws=None, st
     not computed and None is returned in their place."""
     _i32(topk_ids, "topk_ids")
     R, T, K = topk_ids.shape
-    counts = _new((R, E), topk_ids) if counts is None else counts
+    counts = _new((R, E), topk_ids) if counts is None else _buf(counts, R * E, "counts")
     if counts_only:
         bucket_pos = None
     elif bucket_pos is None:
         bucket_pos = _new((R, T, K), topk_ids)
+    else:
+        _buf(bucket_pos, R * T * K, "bucket_pos")
+    _buf(err, 1, "err")
     n = load_matrix_workspace_size(R, T, K, E)
     ws = _new((max(n, 4),), topk_ids, torch.uint8) if ws is None else ws
     _check(LIB.uep_load_matrix(_p(topk_ids), R, T, K, E, _p(counts), _p(bucket_pos), _p(err),
@@ -144,6 +159,10 @@ def solve_quota(counts, S, q_min, out=None, stream=None):
     inst_quota = o.get("inst_quota", _new((R * ipr,), counts))
     rank_load = o.get("rank_load", _new((R,), counts))
     stats = o.get("stats", _new((4,), counts))
+    for name, t, n in (("slot_expert", slot_expert, R * S), ("inst_expert", inst_expert, R * ipr),
+                       ("inst_quota", inst_quota, R * ipr), ("rank_load", rank_load, R),
+                       ("stats", stats, 4)):
+        _buf(t, n, name)
     _check(LIB.uep_solve_quota(_p(counts), R, E, S, q_min, _p(slot_expert), _p(inst_expert),
                                _p(inst_quota), _p(rank_load), _p(stats), _s(stream)),
            "uep_solve_quota")
@@ -153,9 +172,11 @@ def solve_quota(counts, S, q_min, out=None, stream=None):
 
 
 def identity_quota(counts, inst_expert, inst_quota=None, stream=None):
+    _i32(counts, "counts")
     R, E = counts.shape
+    _i32(inst_expert, "inst_expert")
     n = inst_expert.numel()
-    inst_quota = _new((n,), counts) if inst_quota is None else inst_quota
+    inst_quota = _new((n,), counts) if inst_quota is None else _buf(inst_quota, n, "inst_quota")
     _check(LIB.uep_identity_quota(_p(counts), R, E, n, _p(inst_expert), _p(inst_quota),
                                   _s(stream)), "uep_identity_quota")
     return inst_quota
@@ -168,14 +189,23 @@ def reroute_workspace_size(R, E, inst_per_rank) -> int:
 def reroute_assign(counts, topk_ids, bucket_pos, inst_per_rank, inst_expert, inst_quota,
                    r_begin=0, r_end=None, xfer=None, inst_offset=None, dest_inst=None,
                    dest_row=None, err=None, ws=None, stream=None):
+    _i32(counts, "counts")
+    _i32(topk_ids, "topk_ids")
     R, E = counts.shape
     _, T, K = topk_ids.shape
     r_end = R if r_end is None else r_end
     I = R * inst_per_rank
-    xfer = _new((R, I), counts) if xfer is None else xfer
-    inst_offset = _new((I + 1,), counts) if inst_offset is None else inst_offset
-    dest_inst = _new((R, T, K), counts) if dest_inst is None else dest_inst
-    dest_row = _new((R, T, K), counts) if dest_row is None else dest_row
+    _buf(bucket_pos, R * T * K, "bucket_pos")
+    _buf(inst_expert, I, "inst_expert")
+    _buf(inst_quota, I, "inst_quota")
+    _buf(err, 1, "err")
+    xfer = _new((R, I), counts) if xfer is None else _buf(xfer, R * I, "xfer")
+    inst_offset = _new((I + 1,), counts) if inst_offset is None else _buf(inst_offset, I + 1,
+                                                                           "inst_offset")
+    dest_inst = _new((R, T, K), counts) if dest_inst is None else _buf(dest_inst, R * T * K,
+                                                                       "dest_inst")
+    dest_row = _new((R, T, K), counts) if dest_row is None else _buf(dest_row, R * T * K,
+                                                                     "dest_row")
     n = reroute_workspace_size(R, E, inst_per_rank)
     ws = _new((max(n, 4),), counts, torch.uint8) if ws is None else ws
     _check(LIB.uep_reroute_assign(_p(counts), _p(topk_ids), _p(bucket_pos), R, T, K, E,
@@ -248,6 +278,12 @@ def device_fill(dst, value=0, stream=None):
 def stage_replica_weights(mode, R, E, S, slot_expert, expert_elems, main_w=None, slot_w=None,
                           main_grad=None, slot_grad=None, r_begin=0, r_end=None, stream=None):
     r_end = R if r_end is None else r_end
+    n = int(expert_elems)
+    _buf(slot_expert, R * S, "slot_expert")
+    _buf(main_w, E * n, "main_w", torch.int16)
+    _buf(slot_w, R * S * n, "slot_w", torch.int16)
+    _buf(main_grad, E * n, "main_grad", torch.float32)
+    _buf(slot_grad, R * S * n, "slot_grad", torch.float32)
     _check(LIB.uep_stage_replica_weights(mode, R, E, S, _p(slot_expert), r_begin, r_end,
                                          _p(main_w), _p(slot_w), _p(main_grad), _p(slot_grad),
                                          int(expert_elems), _s(stream)),
@@ -257,14 +293,20 @@ def stage_replica_weights(mode, R, E, S, slot_expert, expert_elems, main_w=None,
 def waterfill(counts, topk_ids, batch_size, seed, layer, local_pref_shift=4, shared_rank=None,
               waterline=None, slack=None, rank_load=None, ext_topk=None, want_ext=True,
               stream=None, all_ranks=False):
+    _i32(counts, "counts")
+    _i32(topk_ids, "topk_ids")
     R, E = counts.shape
     _, T, K = topk_ids.shape
-    shared_rank = _new((R, T), counts) if shared_rank is None else shared_rank
-    waterline = _new((1,), counts) if waterline is None else waterline
-    slack = _new((R,), counts) if slack is None else slack
-    rank_load = _new((R,), counts) if rank_load is None else rank_load
+    _buf(batch_size, R, "batch_size")
+    shared_rank = _new((R, T), counts) if shared_rank is None else _buf(shared_rank, R * T,
+                                                                       "shared_rank")
+    waterline = _new((1,), counts) if waterline is None else _buf(waterline, 1, "waterline")
+    slack = _new((R,), counts) if slack is None else _buf(slack, R, "slack")
+    rank_load = _new((R,), counts) if rank_load is None else _buf(rank_load, R, "rank_load")
     if ext_topk is None and want_ext:
         ext_topk = _new((R, T, K + 1), counts)
+    else:
+        _buf(ext_topk, R * T * (K + 1), "ext_topk")
     _check(LIB.uep_waterfill(_p(counts), _p(topk_ids), _p(batch_size), R, T, K, E,
                              ctypes.c_uint64(seed & (2 ** 64 - 1)),
                              ctypes.c_uint64(layer & (2 ** 64 - 1)), local_pref_shift,
@@ -290,10 +332,17 @@ def lplb_prepare(inst_expert_host, R, E, inst_per_rank, device, stream=None) -> 
 
 def lplb(counts, lp, n_copies, n_inst, iters=30, x=None, m=None, inst_quota=None, stats=None,
          err=None, stream=None):
-    x = torch.empty((max(n_copies, 1),), dtype=torch.float32, device=counts.device) if x is None else x
-    m = torch.empty((1,), dtype=torch.float32, device=counts.device) if m is None else m
-    inst_quota = _new((n_inst,), counts) if inst_quota is None else inst_quota
-    stats = _new((4,), counts) if stats is None else stats
+    _i32(counts, "counts")
+    if lp.numel() * lp.element_size() < lplb_struct_size(counts.shape[0], counts.shape[1], 1):
+        raise TypeError("lp is smaller than any LP structure for these counts")
+    x = torch.empty((max(n_copies, 1),), dtype=torch.float32, device=counts.device) if x is None \
+        else _buf(x, max(n_copies, 1), "x", torch.float32)
+    m = torch.empty((1,), dtype=torch.float32, device=counts.device) if m is None \
+        else _buf(m, 1, "m", torch.float32)
+    inst_quota = _new((n_inst,), counts) if inst_quota is None else _buf(inst_quota, n_inst,
+                                                                         "inst_quota")
+    stats = _new((4,), counts) if stats is None else _buf(stats, 4, "stats")
+    _buf(err, 1, "err")
     _check(LIB.uep_lplb(_p(counts), _p(lp), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
                         _p(err), _s(stream)), "uep_lplb")
     return x[:n_copies], m, inst_quota, stats
@@ -305,7 +354,9 @@ def lplb_sample(topk_ids, lp, x, seed, layer, dest_inst=None, err=None, stream=N
     R, T, K = topk_ids.shape
     if x.dtype != torch.float32:
         raise TypeError("x must be float32")
-    dest_inst = _new((R, T, K), topk_ids) if dest_inst is None else dest_inst
+    dest_inst = _new((R, T, K), topk_ids) if dest_inst is None else _buf(dest_inst, R * T * K,
+                                                                         "dest_inst")
+    _buf(err, 1, "err")
     _check(LIB.uep_lplb_sample(_p(topk_ids), R, T, K, _p(lp), _p(x),
                                ctypes.c_uint64(seed & (2 ** 64 - 1)),
                                ctypes.c_uint64(layer & (2 ** 64 - 1)), _p(dest_inst), _p(err),

@@ -419,6 +419,27 @@ def test_host_argument_errors():
         U.load_matrix(torch.zeros(2, 4, 2, dtype=torch.int32), 8)
     with pytest.raises(TypeError):
         U.load_matrix(torch.zeros(2, 4, 4, dtype=torch.int32, device=DEV)[:, :, ::2], 8)
+    # caller buffers smaller than the geometry, or of the wrong type, are refused too
+    ids = to_dev(np.zeros((2, 4, 2)))
+    with pytest.raises(TypeError, match="counts"):
+        U.load_matrix(ids, 8, counts=torch.zeros(15, dtype=torch.int32, device=DEV))
+    with pytest.raises(TypeError, match="bucket_pos"):
+        U.load_matrix(ids, 8, bucket_pos=torch.zeros(2, 4, 1, dtype=torch.int32, device=DEV))
+    counts, bp = U.load_matrix(ids, 8)
+    with pytest.raises(TypeError, match="dest_row"):
+        U.reroute_assign(counts, ids, bp, 5, torch.zeros(10, dtype=torch.int32, device=DEV),
+                         torch.zeros(10, dtype=torch.int32, device=DEV),
+                         dest_row=torch.zeros(15, dtype=torch.int32, device=DEV))
+    with pytest.raises(TypeError, match="slot_w"):
+        U.stage_replica_weights(U.STAGE_WEIGHTS, 2, 8, 1, torch.zeros(2, 1, dtype=torch.int32,
+                                                                        device=DEV), 64,
+                                main_w=torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV),
+                                slot_w=torch.zeros(2, 63, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(TypeError, match="main_grad"):
+        U.stage_replica_weights(U.STAGE_GRAD_REDUCE, 2, 8, 1, torch.zeros(2, 1, dtype=torch.int32,
+                                                                            device=DEV), 64,
+                                main_grad=torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV),
+                                slot_grad=torch.zeros(2, 64, dtype=torch.float32, device=DEV))
 
 
 @pytest.mark.parametrize("nbytes", [16, 16 * 4096, 16 * (3 * 4096 + 17)])
