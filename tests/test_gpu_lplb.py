@@ -122,6 +122,42 @@ def test_lplb_random(seed):
     check_lplb(counts.astype(np.int32), inst, ipr)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_lplb_random_multi_slot(seed):
+    """Layers with 1-3 redundant slots per rank, so an expert can have up to four copies
+    (larger groups, more rank pairs per group): M within the bound of the fp64 simplex
+    optimum, the split summing to each count, largest-remainder quotas."""
+    rng = np.random.default_rng(3000 + seed)
+    R = int(rng.choice([4, 8, 13, 16, 32, 48, 64]))
+    E_loc = int(rng.integers(1, 5))
+    S2 = int(rng.integers(1, 4))
+    E, ipr = R * E_loc, E_loc + S2
+    inst = np.full(R * ipr, -1, dtype=np.int32)
+    for r in range(R):
+        inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+    free = [S2] * R
+    n_copies, n_groups = 0, 0
+    target = int(rng.integers(0, R * S2 + 1))
+    placed = 0
+    for e in rng.permutation(E):
+        if placed >= target or n_groups >= 120:
+            break
+        k = int(rng.integers(1, 4))
+        ranks = [int(r) for r in rng.permutation(R) if r != e // E_loc and free[r] > 0][:k]
+        if not ranks or n_copies + 1 + len(ranks) > 240:
+            continue
+        for r in ranks:
+            inst[r * ipr + E_loc + (S2 - free[r])] = e
+            free[r] -= 1
+        placed += len(ranks)
+        n_copies += 1 + len(ranks)
+        n_groups += 1
+    counts = rng.multinomial(int(rng.integers(1, 2_000_000)),
+                             rng.dirichlet(np.full(E, rng.choice([0.1, 0.3, 1.0]))), size=R)
+    say(f"case: lplb multi-slot seed={seed} R={R} E={E} S={S2} groups={n_groups} copies={n_copies}")
+    check_lplb(counts.astype(np.int32), inst, ipr)
+
+
 def test_lplb_special_cases():
     say("case: lplb special cases")
     # red0: no replicas -> M* = max fixed load, quotas = loads
