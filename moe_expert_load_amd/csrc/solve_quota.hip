@@ -15,9 +15,14 @@
 // non-zero quota, quota descending then id ascending.  For a donor e: open a replica
 // in the lowest free slot of the least loaded rank t (L_t < T*, a free slot, no copy
 // of e), moving min(q_e, L_h - T*, T* - L_t) if that is >= q_min.  The first donor
-// that can move ends the step; none -> stop.  Every move empties the donor main,
-// brings h down to T* or brings t up to T*, so a placed replica never takes more
-// tokens later and there is no "add to an existing replica" case.
+// that can move ends the step.  None -> a relay (the article's other kind of step,
+// an update of the quota distribution): for the donors of h in the same order, among
+// ranks x != h with a free slot, no copy of e and L_x >= T* (least loaded first, lowest
+// index on ties), x's first main f (quota descending, id ascending) whose least loaded
+// replica holder y has L_y < T* and frees enough room: d2 = min(q_f, T* - L_y) moves
+// from x's main to y's replica, and e opens on x with d = min(q_e, L_h - T*,
+// T* - (L_x - d2)) if L_x - d2 < T* and d >= q_min.  No relay -> stop.  No rank ever
+// rises above T*, and every step opens a replica (at most R*S steps).
 #include "common.h"
 
 namespace uep {
@@ -66,10 +71,89 @@ __device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delt
   st.free_slots -= 1;
 }
 
+// Relay step for the stuck heaviest rank h (see the rule above).  by[] (E entries of
+// LDS) receives, per expert, the least loaded (load << 6 | rank) of its replica
+// holders below T*.  A main f of x qualifies when it frees room on x (L_x - d2 < T*)
+// and that room, T* - (L_x - d2), is at least q_min; given a donor whose quota and
+// h's excess are both >= q_min, this does not depend on the donor, so every lane picks
+// its first qualifying main once, and each donor costs one wave minimum over the
+// candidate ranks (kPacked: loads below 2^25, one 32-bit DPP minimum).
+template <int kS, bool kPacked>
+__device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
+                         int E, int E_loc, int S, int q_min, int t_star, int h, int Lh,
+                         int& n_rep) {
+  for (int e = lane; e < E; e += kWave) by[e] = ~0ull;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (active && st.L < t_star) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+      if (s < S && st.sl_e[s] >= 0)
+        atomicMin((unsigned long long*)&by[st.sl_e[s]], ((uint64_t)st.L << 6) | (uint64_t)lane);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // this lane as the relay rank x: its first qualifying main (quota descending, id ascending)
+  int bf = -1, bq = 0, by_l = 0, bd2 = 0, room = 0;
+  if (active && lane != h && st.free_slots > 0 && st.L >= t_star) {
+    for (int j0 = 0; j0 < E_loc; j0 += 8) {
+      int qf[8];
+      uint64_t key[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {        // the batch's loads first, then the choice
+        const int f = lane * E_loc + min(j0 + u, E_loc - 1);
+        qf[u] = q_main[f];
+        key[u] = by[f];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= E_loc || qf[u] <= bq || key[u] == ~0ull) continue;
+        const int d2 = min(qf[u], t_star - (int)(key[u] >> 6));
+        if (st.L - d2 >= t_star || t_star - (st.L - d2) < q_min) continue;
+        bf = lane * E_loc + j0 + u; bq = qf[u]; by_l = (int)(key[u] & 63u); bd2 = d2;
+        room = t_star - (st.L - d2);
+      }
+    }
+  }
+  const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
+  bool tried = false;
+  for (;;) {
+    // donors of h in donor order: largest untried main quota, lowest expert id on ties
+    const int qd = wave_max((lane < E_loc && qj > 0 && !tried) ? qj : 0);
+    if (qd <= 0) return false;
+    const int jd = first_lane(lane < E_loc && qj == qd && !tried);
+    const int e = h * E_loc + jd;
+    const bool cand = bf >= 0 && qd >= q_min && Lh - t_star >= q_min && slot_of<kS>(st, S, e) < 0;
+    int x = -1;
+    if (kPacked) {
+      const uint32_t k = wave_min_u32(cand ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
+      if (k != 0xFFFFFFFFu) x = (int)(k & 63u);
+    } else {
+      const int Lx = wave_min(cand ? st.L : kBig);
+      if (Lx != kBig) x = first_lane(cand && st.L == Lx);
+    }
+    if (x >= 0) {
+      const int f = readlane(bf, x), y = readlane(by_l, x), d2 = readlane(bd2, x);
+      const int d = min(qd, min(Lh - t_star, readlane(room, x)));
+      if (lane == y) {
+#pragma unroll
+        for (int s = 0; s < kS; ++s)
+          if (s < S && st.sl_e[s] == f) st.sl_q[s] += d2;
+        st.L += d2;
+      }
+      if (lane == x) { open_slot<kS>(st, S, e, d); st.L += d - d2; }
+      if (lane == h) st.L -= d;
+      if (lane == 0) { q_main[e] -= d; q_main[f] -= d2; }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      ++n_rep;
+      return true;
+    }
+    if (lane == jd) tried = true;
+  }
+}
+
 // The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
 // reduction give value and lowest lane together.
 template <int kS>
-__device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
+__device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
                                               int R, int E_loc, int S, int q_min, int t_star,
                                               int& steps, int& n_rep, int& stuck) {
   for (;;) {
@@ -80,7 +164,9 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     const int over = Lh - t_star;
     const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
     bool tried = false, moved = false;
-    for (;;) {
+    // no rank below T* with a free slot: no donor can move directly, go to the relay
+    const bool any_recv = ballot(active && lane != h && st.L < t_star && st.free_slots > 0) != 0;
+    for (; any_recv;) {
       // next donor: largest untried main quota on h, lowest expert id on ties
       const int kd = wave_max((lane < E_loc && qj > 0 && !tried) ? (qj << 6) | (63 - lane) : -1);
       if (kd < 0) break;
@@ -104,6 +190,9 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       }
       if (lane == jd) tried = true;
     }
+    if (!moved)
+      moved = sq_relay<kS, true>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
+                                 h, Lh, n_rep);
     if (!moved) { stuck = 1; break; }
     ++steps;
   }
@@ -111,7 +200,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
 
 // The same rule for any load below 2^31: value reductions, then ballots.
 template <int kS>
-__device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
+__device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
                                             int R, int E_loc, int S, int q_min, int t_star,
                                             int& steps, int& n_rep, int& stuck) {
   for (;;) {
@@ -121,7 +210,8 @@ __device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, int
     const int over = Lh - t_star;
     const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
     bool tried = false, moved = false;
-    for (;;) {
+    const bool any_recv = ballot(active && lane != h && st.L < t_star && st.free_slots > 0) != 0;
+    for (; any_recv;) {
       const int dk = (lane < E_loc && qj > 0 && !tried) ? qj : -1;
       const int qd = wave_max(dk);
       if (qd <= 0) break;
@@ -144,6 +234,9 @@ __device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, int
       }
       if (lane == jd) tried = true;
     }
+    if (!moved)
+      moved = sq_relay<kS, false>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
+                                  h, Lh, n_rep);
     if (!moved) { stuck = 1; break; }
     ++steps;
   }
@@ -155,7 +248,9 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
     int32_t* __restrict__ slot_expert, int32_t* __restrict__ inst_expert,
     int32_t* __restrict__ inst_quota, int32_t* __restrict__ rank_load,
     int32_t* __restrict__ stats) {
-  extern __shared__ int32_t sq_lds[];       // [E] main quotas, starting at the expert loads
+  extern __shared__ uint64_t sq_lds64[];    // [E] relay table, then [E] main quotas
+  uint64_t* by = sq_lds64;
+  int32_t* sq_lds = reinterpret_cast<int32_t*>(sq_lds64 + E);
   const int tid = threadIdx.x;
   const int E_loc = E / R;
   for (int e = tid; e < E; e += kSqThreads) sq_lds[e] = 0;
@@ -198,9 +293,9 @@ __global__ __launch_bounds__(kSqThreads) void solve_quota_kernel(
 
   int steps = 0, n_rep = 0, stuck = 0;
   if (total < (1 << kPackBits))
-    search_packed<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+    search_packed<kS>(st, q_main, by, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
   else
-    search_wide<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+    search_wide<kS>(st, q_main, by, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
 
   const int ipr = E_loc + S;
   for (int i = lane; i < R * E_loc; i += kWave) {
@@ -261,7 +356,7 @@ extern "C" uep_status uep_solve_quota(const int32_t* counts, int32_t R, int32_t 
   if (R > 64 || E > 4096 || E % R != 0 || S > kSqMaxS || E / R > 64) return UEP_EGEOM;
   if (!counts || !inst_expert || !inst_quota || !rank_load || !stats || (S > 0 && !slot_expert))
     return UEP_EINVAL;
-  const size_t lds = sizeof(int32_t) * E;
+  const size_t lds = (sizeof(uint64_t) + sizeof(int32_t)) * E;
   hipStream_t st = uep_stream(stream);
 #define UEP_SQ_LAUNCH(KS)                                                                     \
   hipLaunchKernelGGL(solve_quota_kernel<KS>, dim3(1), dim3(kSqThreads), lds, st, counts, R, E, \

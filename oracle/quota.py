@@ -25,14 +25,23 @@ The article does not print the search.  Reading used here ("fill to the waterlin
       d = min(q_main[e], L_h - T*, T* - L_t); only if d >= q_min put e into t's
       lowest free slot with quota d; the first donor that can move applies its move
       and the step ends.
-      if no donor of h can move, stop (the peak cannot fall further).
+      if no donor of h can move, try a relay (below); if none applies, stop.
 
-Donors only fall to T* and receivers only rise to T*, so every step exhausts a main,
-brings a donor down to T* or fills a receiver up to T*: at most E + 2R steps.  The
-same fact means a replica, once placed, never receives more: its expert's main is
-empty, or its home rank sits at T* (never again the heaviest above T*), or the
-replica's rank sits at T* (never again a receiver).  So "adding to an existing
-replica" never arises, and every move opens a new replica.
+    relay (the article's other kind of step, an update of the quota distribution):
+      for the donors e of h in the same order: among ranks x != h with a free slot, no
+      instance of e and L_x >= T* (so no receiver by themselves), least loaded first
+      (lowest index on ties), and for each x its mains f with a non-zero quota in donor
+      order, take the least loaded rank y holding a replica of f with L_y < T* (lowest
+      index on ties);  d2 = min(q_main[f], T* - L_y);  if L_x - d2 < T* and
+      d = min(q_main[e], L_h - T*, T* - (L_x - d2)) >= q_min: move d2 of f from x's
+      main to y's replica and open e in x's lowest free slot with quota d.  The first
+      (e, x, f) that qualifies is the step.
+
+No rank is ever pushed above T* and h's excess falls by d > 0 every step, so the
+search ends; every step opens one replica, so there are at most R*S steps.  Without
+relays a replica never receives more (its expert's main is empty, or its home rank
+or its own rank sits at T*); a relay is the one move that adds to an existing
+replica.
 Home of expert e: rank e // (E/R) (contiguous EP blocks).  Physical instance ids:
 i = r*(E_loc+S) + j; j < E_loc is the main of expert r*E_loc + j, j >= E_loc is slot j-E_loc.
 
@@ -46,6 +55,42 @@ import numpy as np
 
 def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
+
+
+def _relay(h, mains, L, q_main, slot_e, slot_q, free, t_star, q_min, E_loc, R, S) -> bool:
+    """One relay step for the stuck heaviest rank h (see the module docstring): frees
+    room on a rank x at or above T* by topping up an existing replica of one of x's
+    mains on a rank y below T*, then opens a replica of h's donor on x."""
+    for e in mains:
+        xs = sorted((L[x], x) for x in range(R)
+                    if x != h and free[x] > 0 and e not in slot_e[x] and L[x] >= t_star)
+        for Lx, x in xs:
+            fs = [f for f in range(x * E_loc, (x + 1) * E_loc) if q_main[f] > 0]
+            fs.sort(key=lambda f: (-q_main[f], f))
+            for f in fs:
+                ys = [(L[y], y) for y in range(R) if L[y] < t_star and f in slot_e[y]]
+                if not ys:
+                    continue
+                Ly, y = min(ys)
+                d2 = min(q_main[f], t_star - Ly)
+                if Lx - d2 >= t_star:
+                    continue
+                d = min(q_main[e], L[h] - t_star, t_star - (Lx - d2))
+                if d < q_min:
+                    continue
+                slot_q[y][slot_e[y].index(f)] += d2
+                q_main[f] -= d2
+                L[x] -= d2
+                L[y] += d2
+                s = S - free[x]
+                slot_e[x][s] = e
+                slot_q[x][s] = d
+                free[x] -= 1
+                q_main[e] -= d
+                L[h] -= d
+                L[x] += d
+                return True
+    return False
 
 
 def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
@@ -87,6 +132,8 @@ def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
                     L[t] += d
                     moved = True
                     break
+        if not moved:
+            moved = _relay(h, mains, L, q_main, slot_e, slot_q, free, t_star, q_min, E_loc, R, S)
         if not moved:
             stuck = True
             break

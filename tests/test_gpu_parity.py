@@ -582,8 +582,8 @@ def test_grad_reduce_matches_oracle():
 
 
 def test_grad_reduce_qwen_layer_full_size():
-    """Backward reduction at the real size: the Qwen layer's plan (21 slots holding 11
-    experts), 72 MiB fp32 gradients per expert, main_grad spanning 9 GiB (offsets past
+    """Backward reduction at the real size: the Qwen layer's plan (every used slot and
+    replicated expert), 72 MiB fp32 gradients per expert, main_grad spanning 9 GiB (offsets past
     2^32 bytes).  Every replicated expert's main and every used slot compared whole;
     an expert without replicas is left untouched."""
     w = W.QWEN_LAYER
