@@ -7,8 +7,8 @@
 // order); the search is one wave64, lane r = rank r: L_r, free slots and the rank's
 // slot table live in registers, per-expert main quotas in LDS.  A step is a few DPP
 // wave reductions (argmax over ranks, argmax over donors, argmin over receivers), so
-// the whole solve is a strictly sequential loop of at most E + 2R steps with no
-// barrier other than the wave itself.
+// the whole solve is a strictly sequential loop, one replica per step (at most R*S
+// steps), with no barrier other than the wave itself.
 //
 // Step rule ("fill to the waterline", T* = ceil(sum_e c_e / R)): h = most loaded
 // rank (lowest index on ties); stop if L_h <= T*.  Donors are h's mains with a

@@ -104,7 +104,8 @@ def _check_plan_invariants(counts, S, q_min, plan):
     # post-plan rank loads are the instance quotas summed per rank
     rl = np.array([iq[r * ipr:(r + 1) * ipr].sum() for r in range(R)])
     assert np.array_equal(rl, plan["rank_load"])
-    assert plan["n_steps"] <= E + 2 * R
+    # every step, plain or relay, opens exactly one replica
+    assert plan["n_steps"] == plan["n_replicas"] <= R * S
     L0 = np.array([c[r * E_loc:(r + 1) * E_loc].sum() for r in range(R)])
     assert rl.max() <= L0.max()
     # ranks that received load never pass the waterline
