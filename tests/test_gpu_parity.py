@@ -290,6 +290,27 @@ def test_solve_quota_large_loads(total):
 
 
 QUOTA_RULE_CASES = golden("quota_rule_cases.json")["cases"]
+# cases whose T* is exact, so scaling every load and q_min scales the whole hand result
+RELAY_SCALABLE = [c for c in QUOTA_RULE_CASES
+                  if sum(c["c"]) % c["R"] == 0 and c["n_steps"] > 1 and not c["stuck"]]
+
+
+@pytest.mark.parametrize("case", RELAY_SCALABLE, ids=[c["name"] for c in RELAY_SCALABLE])
+def test_solve_quota_relays_above_the_packed_limit(case):
+    """The hand-worked cases with relays, every load and q_min times 2^23 so the total
+    passes 2^25 and the solver takes its wide (unpacked) search: the plan is the hand
+    result scaled (T* is exact in these cases, so every step scales)."""
+    say("case: solve_quota relay, scaled", case["name"])
+    f = 1 << 23
+    counts = np.zeros((case["R"], case["E"]), dtype=np.int64)
+    counts[0] = np.array(case["c"]) * f
+    assert counts.sum() >= 1 << 25
+    g = U.solve_quota(to_dev(counts), case["S"], case["q_min"] * f)
+    assert host(g["slot_expert"]).tolist() == case["slot_expert"]
+    assert (host(g["inst_quota"]) == np.array(case["inst_quota"]) * f).all()
+    assert (host(g["rank_load"]) == np.array(case["rank_load"]) * f).all()
+    assert host(g["stats"]).tolist() == [case["n_replicas"], case["n_steps"], case["t_star"] * f,
+                                         int(case["stuck"])]
 
 
 @pytest.mark.parametrize("case", QUOTA_RULE_CASES, ids=[c["name"] for c in QUOTA_RULE_CASES])
