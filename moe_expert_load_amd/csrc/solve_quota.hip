@@ -82,6 +82,7 @@ template <int kS, bool kPacked>
 __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
                          int E, int E_loc, int S, int q_min, int t_star, int h, int Lh,
                          int& n_rep) {
+  if (Lh - t_star < q_min) return false;
   for (int e = lane; e < E; e += kWave) by[e] = ~0ull;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (active && st.L < t_star) {
@@ -113,15 +114,17 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane
       }
     }
   }
+  if (ballot(bf >= 0) == 0) return false;
   const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
   bool tried = false;
   for (;;) {
-    // donors of h in donor order: largest untried main quota, lowest expert id on ties
+    // donors of h in donor order: largest untried main quota, lowest expert id on ties;
+    // the quotas only fall from here, so one below q_min ends the relay
     const int qd = wave_max((lane < E_loc && qj > 0 && !tried) ? qj : 0);
-    if (qd <= 0) return false;
+    if (qd <= 0 || qd < q_min) return false;
     const int jd = first_lane(lane < E_loc && qj == qd && !tried);
     const int e = h * E_loc + jd;
-    const bool cand = bf >= 0 && qd >= q_min && Lh - t_star >= q_min && slot_of<kS>(st, S, e) < 0;
+    const bool cand = bf >= 0 && slot_of<kS>(st, S, e) < 0;
     int x = -1;
     if (kPacked) {
       const uint32_t k = wave_min_u32(cand ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
@@ -162,14 +165,17 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, u
     if (Lh <= t_star) break;
     const int h = 63 - (kh & 63);
     const int over = Lh - t_star;
+    // every move, plain or relay, is at most the excess: below q_min nothing can move
+    if (over < q_min) { stuck = 1; break; }
     const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
     bool tried = false, moved = false;
     // no rank below T* with a free slot: no donor can move directly, go to the relay
     const bool any_recv = ballot(active && lane != h && st.L < t_star && st.free_slots > 0) != 0;
     for (; any_recv;) {
-      // next donor: largest untried main quota on h, lowest expert id on ties
+      // next donor: largest untried main quota on h, lowest expert id on ties; the
+      // quotas only fall from here, so one below q_min ends the scan
       const int kd = wave_max((lane < E_loc && qj > 0 && !tried) ? (qj << 6) | (63 - lane) : -1);
-      if (kd < 0) break;
+      if (kd < 0 || (kd >> 6) < q_min) break;
       const int qd = kd >> 6, jd = 63 - (kd & 63);
       const int e = h * E_loc + jd;
       const bool c2 = active && lane != h && st.L < t_star && st.free_slots > 0 &&
@@ -208,13 +214,14 @@ __device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, uin
     if (Lh <= t_star) break;
     const int h = first_lane(active && st.L == Lh);
     const int over = Lh - t_star;
+    if (over < q_min) { stuck = 1; break; }
     const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
     bool tried = false, moved = false;
     const bool any_recv = ballot(active && lane != h && st.L < t_star && st.free_slots > 0) != 0;
     for (; any_recv;) {
       const int dk = (lane < E_loc && qj > 0 && !tried) ? qj : -1;
       const int qd = wave_max(dk);
-      if (qd <= 0) break;
+      if (qd <= 0 || qd < q_min) break;
       const int jd = first_lane(dk == qd);
       const int e = h * E_loc + jd;
       const bool c2 = active && lane != h && st.free_slots > 0 && st.L < t_star &&
