@@ -132,7 +132,8 @@ QUOTA_RULE_CASES = golden("quota_rule_cases.json")["cases"]
 @pytest.mark.parametrize("case", QUOTA_RULE_CASES, ids=[c["name"] for c in QUOTA_RULE_CASES])
 def test_quota_tie_and_order_rules_by_hand(case):
     """Hand-worked plans that each hinge on one rule: rank ties, donor ties, the strict
-    'below T*' receiver test with q_min = 0, and the slot fill order."""
+    'below T*' receiver test with q_min = 0, the slot fill order, a move of exactly
+    q_min, and the relay's order and amounts."""
     counts = np.zeros((case["R"], case["E"]), dtype=np.int64)
     counts[0] = case["c"]
     plan = O.solve_quota(counts, case["S"], case["q_min"])
