@@ -77,7 +77,9 @@ __device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delt
 // and that room, T* - (L_x - d2), is at least q_min; given a donor whose quota and
 // h's excess are both >= q_min, this does not depend on the donor, so every lane picks
 // its first qualifying main once, and each donor costs one wave minimum over the
-// candidate ranks (kPacked: loads below 2^25, one 32-bit DPP minimum).
+// candidate ranks (kPacked: loads below 2^25, one 32-bit DPP minimum).  It fails at
+// once when h's excess is below q_min or no lane has a qualifying main, since every
+// donor would then fail.
 template <int kS, bool kPacked>
 __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
                          int E, int E_loc, int S, int q_min, int t_star, int h, int Lh,
