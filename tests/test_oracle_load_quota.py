@@ -113,6 +113,22 @@ def _check_plan_invariants(counts, S, q_min, plan):
     for r in range(R):
         if rl[r] > L0[r]:
             assert rl[r] <= t_star
+    # the stop: balanced, or the heaviest rank (lowest index on ties) is above T* and
+    # none of its mains can open a replica of at least q_min on a rank below T*
+    if not plan["stuck"]:
+        assert rl.max() <= t_star
+    else:
+        h = int(np.argmax(rl))
+        assert rl[h] > t_star
+        for e in range(h * E_loc, (h + 1) * E_loc):
+            q_e = int(iq[h * ipr + e - h * E_loc])
+            if q_e == 0:
+                continue
+            for t in range(R):
+                slots = ie[t * ipr + E_loc:(t + 1) * ipr]
+                if t == h or rl[t] >= t_star or (slots < 0).sum() == 0 or e in slots:
+                    continue
+                assert min(q_e, rl[h] - t_star, t_star - rl[t]) < q_min
 
 
 def test_quota_hand_example():
