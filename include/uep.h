@@ -129,10 +129,22 @@ uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_t T, int32_
  * no logical expert twice on one rank, and a new replica gets at least q_min
  * tokens.  Section "共享冗余 slot 管理动态专家副本": mains never move.
  * Every caller with the same counts gets the same plan (deterministic, ties to
- * the lowest index).  Search ("fill to the waterline", T* = ceil(sum c / R)):
- * the most loaded rank donates from its mains (quota descending) to an existing
- * replica under T*, else to a new replica on the least loaded rank with a free
- * slot if that move is >= q_min; donors fall to T*, receivers rise to T*.
+ * the lowest index).  Search ("fill to the waterline", T* = ceil(sum c / R),
+ * every step opens one replica, so at most R*S steps):
+ *   1. h = the most loaded rank; stop if L_h <= T*, or if L_h - T* < q_min.
+ *   2. Plain step: h's mains with quota left, quota descending (id ascending on
+ *      ties), each tried in turn: a new replica in the lowest free slot of the
+ *      least loaded rank t with L_t < T*, a free slot and no copy of the expert,
+ *      taking d = min(q_main, L_h - T*, T* - L_t) if d >= q_min.
+ *   3. Relay, when no main of h can move (the quota-distribution update): for h's
+ *      mains in the same order, the lowest-index rank x != h with L_x >= T*, a free
+ *      slot and no copy of the donor e, one of whose mains f (quota left) has a
+ *      replica on a rank y with L_y < T*.  d2 = min(q_f, T* - L_y) moves from f's
+ *      main to y's replica, then e opens on x with d = min(q_e, L_h - T*,
+ *      T* - (L_x - d2)) if d >= q_min.  Such an x sits exactly at T* and has one
+ *      such (f, y) only (a lemma of the search), so no further order applies.
+ *   4. Neither moves: stop (stats[3] = 1).
+ * No rank ever rises above T*; h's excess falls every step.
  *
  *   counts      [R][E]           in   load matrix (E % R == 0, E_loc = E / R)
  *   S, q_min                          redundant slots per rank (0..8), minimum quota

@@ -16,13 +16,21 @@
 // in the lowest free slot of the least loaded rank t (L_t < T*, a free slot, no copy
 // of e), moving min(q_e, L_h - T*, T* - L_t) if that is >= q_min.  The first donor
 // that can move ends the step.  None -> a relay (the article's other kind of step,
-// an update of the quota distribution): for the donors of h in the same order, among
-// ranks x != h with a free slot, no copy of e and L_x >= T* (least loaded first, lowest
-// index on ties), x's first main f (quota descending, id ascending) whose least loaded
-// replica holder y has L_y < T* and frees enough room: d2 = min(q_f, T* - L_y) moves
-// from x's main to y's replica, and e opens on x with d = min(q_e, L_h - T*,
-// T* - (L_x - d2)) if L_x - d2 < T* and d >= q_min.  No relay -> stop.  No rank ever
-// rises above T*, and every step opens a replica (at most R*S steps).
+// an update of the quota distribution): for the donors of h in the same order, the
+// first rank x != h (lowest index) with a free slot, no copy of e and L_x >= T* one of
+// whose mains f (quota left) has a replica on a rank y with L_y < T*: d2 =
+// min(q_f, T* - L_y) moves from x's main to y's replica, and e opens on x with
+// d = min(q_e, L_h - T*, T* - (L_x - d2)) if d >= q_min.  No relay -> stop.  No rank
+// ever rises above T*, and every step opens a replica (at most R*S steps).
+//
+// Relay lemma (proved by induction over the steps): a main with quota left has at
+// most one replica holder below T*, and a rank that has such a main is at exactly
+// T* and holds no replica.  A rank above T* has only ever donated; a replica stays
+// below T* with quota left on its main only when the donor came down to exactly T*
+// in that step, which happens once per rank; a relay uses that pair up.  So a
+// qualifying relay rank has a single (f, y), and the order of its mains, the choice
+// among holders of f and the load order among relay ranks decide nothing: the relay
+// below takes the one pair it finds and the lowest qualifying index.
 #include "common.h"
 
 namespace uep {
@@ -72,15 +80,15 @@ __device__ __forceinline__ void open_slot(SqLane<kS>& st, int S, int e, int delt
 }
 
 // Relay step for the stuck heaviest rank h (see the rule above).  by[] (E entries of
-// LDS) receives, per expert, the least loaded (load << 6 | rank) of its replica
-// holders below T*.  A main f of x qualifies when it frees room on x (L_x - d2 < T*)
-// and that room, T* - (L_x - d2), is at least q_min; given a donor whose quota and
-// h's excess are both >= q_min, this does not depend on the donor, so every lane picks
-// its first qualifying main once, and each donor costs one wave minimum over the
-// candidate ranks (kPacked: loads below 2^25, one 32-bit DPP minimum).  It fails at
-// once when h's excess is below q_min or no lane has a qualifying main, since every
-// donor would then fail.
-template <int kS, bool kPacked>
+// LDS) receives, per expert, (load << 6 | rank) of a replica holder below T*: by the
+// relay lemma a main with quota left has at most one, so the entries read below have
+// a single writer (entries of emptied mains may have several and are never read).
+// A rank x qualifies when it has that pair and the room it frees, T* - (L_x - d2), is
+// at least q_min; given a donor whose quota and h's excess are both >= q_min, this
+// does not depend on the donor, so every lane finds its pair once, and each donor
+// costs one ballot over the candidate ranks.  It fails at once when h's excess is
+// below q_min or no lane qualifies, since every donor would then fail.
+template <int kS>
 __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane, bool active,
                          int E, int E_loc, int S, int q_min, int t_star, int h, int Lh,
                          int& n_rep) {
@@ -90,28 +98,27 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane
   if (active && st.L < t_star) {
 #pragma unroll
     for (int s = 0; s < kS; ++s)
-      if (s < S && st.sl_e[s] >= 0)
-        atomicMin((unsigned long long*)&by[st.sl_e[s]], ((uint64_t)st.L << 6) | (uint64_t)lane);
+      if (s < S && st.sl_e[s] >= 0) by[st.sl_e[s]] = ((uint64_t)st.L << 6) | (uint64_t)lane;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  // this lane as the relay rank x: its first qualifying main (quota descending, id ascending)
-  int bf = -1, bq = 0, by_l = 0, bd2 = 0, room = 0;
+  // this lane as the relay rank x: its main with quota left and a holder below T*
+  int bf = -1, by_l = 0, bd2 = 0, room = 0;
   if (active && lane != h && st.free_slots > 0 && st.L >= t_star) {
     for (int j0 = 0; j0 < E_loc; j0 += 8) {
       int qf[8];
       uint64_t key[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {        // the batch's loads first, then the choice
+      for (int u = 0; u < 8; ++u) {        // the batch's loads first, then the test
         const int f = lane * E_loc + min(j0 + u, E_loc - 1);
         qf[u] = q_main[f];
         key[u] = by[f];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (j0 + u >= E_loc || qf[u] <= bq || key[u] == ~0ull) continue;
+        if (j0 + u >= E_loc || qf[u] <= 0 || key[u] == ~0ull) continue;
         const int d2 = min(qf[u], t_star - (int)(key[u] >> 6));
-        if (st.L - d2 >= t_star || t_star - (st.L - d2) < q_min) continue;
-        bf = lane * E_loc + j0 + u; bq = qf[u]; by_l = (int)(key[u] & 63u); bd2 = d2;
+        if (t_star - (st.L - d2) < q_min) continue;
+        bf = lane * E_loc + j0 + u; by_l = (int)(key[u] & 63u); bd2 = d2;
         room = t_star - (st.L - d2);
       }
     }
@@ -126,15 +133,7 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, uint64_t* by, int lane
     if (qd <= 0 || qd < q_min) return false;
     const int jd = first_lane(lane < E_loc && qj == qd && !tried);
     const int e = h * E_loc + jd;
-    const bool cand = bf >= 0 && slot_of<kS>(st, S, e) < 0;
-    int x = -1;
-    if (kPacked) {
-      const uint32_t k = wave_min_u32(cand ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
-      if (k != 0xFFFFFFFFu) x = (int)(k & 63u);
-    } else {
-      const int Lx = wave_min(cand ? st.L : kBig);
-      if (Lx != kBig) x = first_lane(cand && st.L == Lx);
-    }
+    const int x = first_lane(bf >= 0 && slot_of<kS>(st, S, e) < 0);
     if (x >= 0) {
       const int f = readlane(bf, x), y = readlane(by_l, x), d2 = readlane(bd2, x);
       const int d = min(qd, min(Lh - t_star, readlane(room, x)));
@@ -199,7 +198,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, u
       if (lane == jd) tried = true;
     }
     if (!moved)
-      moved = sq_relay<kS, true>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
+      moved = sq_relay<kS>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
                                  h, Lh, n_rep);
     if (!moved) { stuck = 1; break; }
     ++steps;
@@ -244,7 +243,7 @@ __device__ __forceinline__ void search_wide(SqLane<kS>& st, int32_t* q_main, uin
       if (lane == jd) tried = true;
     }
     if (!moved)
-      moved = sq_relay<kS, false>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
+      moved = sq_relay<kS>(st, q_main, by, lane, active, R * E_loc, E_loc, S, q_min, t_star,
                                   h, Lh, n_rep);
     if (!moved) { stuck = 1; break; }
     ++steps;

@@ -28,20 +28,33 @@ The article does not print the search.  Reading used here ("fill to the waterlin
       if no donor of h can move, try a relay (below); if none applies, stop.
 
     relay (the article's other kind of step, an update of the quota distribution):
-      for the donors e of h in the same order: among ranks x != h with a free slot, no
-      instance of e and L_x >= T* (so no receiver by themselves), least loaded first
-      (lowest index on ties), and for each x its mains f with a non-zero quota in donor
-      order, take the least loaded rank y holding a replica of f with L_y < T* (lowest
-      index on ties);  d2 = min(q_main[f], T* - L_y);  if L_x - d2 < T* and
-      d = min(q_main[e], L_h - T*, T* - (L_x - d2)) >= q_min: move d2 of f from x's
-      main to y's replica and open e in x's lowest free slot with quota d.  The first
-      (e, x, f) that qualifies is the step.
+      for the donors e of h in the same order, and the ranks x != h with a free slot, no
+      instance of e and L_x >= T* (so no receiver by themselves) in ascending index: x
+      qualifies when one of its mains f with a non-zero quota has a replica on a rank y
+      with L_y < T*;  d2 = min(q_main[f], T* - L_y);  d = min(q_main[e], L_h - T*,
+      T* - (L_x - d2));  if d >= q_min, move d2 of f from x's main to y's replica and
+      open e in x's lowest free slot with quota d.  The first (e, x) that qualifies is
+      the step.
 
 No rank is ever pushed above T* and h's excess falls by d > 0 every step, so the
-search ends; every step opens one replica, so there are at most R*S steps.  Without
-relays a replica never receives more (its expert's main is empty, or its home rank
-or its own rank sits at T*); a relay is the one move that adds to an existing
-replica.
+search ends; every step opens one replica, so there are at most R*S steps.
+
+Relay lemma.  Call (f, y) a live pair when f's main has quota left and y < T* holds
+a replica of f.  A rank above T* has only ever donated (ranks at or below T* never
+rise above it), so it holds no replica.  A plain step leaves its receiver below T*
+with quota left on the donor only when the donor h comes down to exactly T*; a relay
+that opens e on x does the same only when h reaches T*.  So each rank gains a live
+pair at most once, at the moment it reaches T* from above, and at that moment it
+holds nothing.  A relay uses up the pair it takes (y reaches T* or f's main empties),
+and its rank x, which needs a live pair of its own to qualify, is therefore exactly
+at T*, holds no replica and has exactly one live pair; after the relay x holds only
+e, whose pair is the donor's own.  Hence, by induction over the steps: every live
+pair is the one its home rank gained on reaching T*, each rank has at most one, and
+every qualifying relay rank sits at T* with a single (f, y).  The order of x's mains,
+the choice among holders of f, the load order among relay ranks and a test that x
+ends below T* therefore never decide anything; the search below states them not at
+all and checks the lemma each time a relay rank qualifies.
+
 Home of expert e: rank e // (E/R) (contiguous EP blocks).  Physical instance ids:
 i = r*(E_loc+S) + j; j < E_loc is the main of expert r*E_loc + j, j >= E_loc is slot j-E_loc.
 
@@ -59,37 +72,35 @@ def _ceil_div(a: int, b: int) -> int:
 
 def _relay(h, mains, L, q_main, slot_e, slot_q, free, t_star, q_min, E_loc, R, S) -> bool:
     """One relay step for the stuck heaviest rank h (see the module docstring): frees
-    room on a rank x at or above T* by topping up an existing replica of one of x's
-    mains on a rank y below T*, then opens a replica of h's donor on x."""
+    room on a rank x at T* by topping up the replica of one of x's mains on a rank y
+    below T*, then opens a replica of h's donor on x."""
     for e in mains:
-        xs = sorted((L[x], x) for x in range(R)
-                    if x != h and free[x] > 0 and e not in slot_e[x] and L[x] >= t_star)
-        for Lx, x in xs:
-            fs = [f for f in range(x * E_loc, (x + 1) * E_loc) if q_main[f] > 0]
-            fs.sort(key=lambda f: (-q_main[f], f))
-            for f in fs:
-                ys = [(L[y], y) for y in range(R) if L[y] < t_star and f in slot_e[y]]
-                if not ys:
-                    continue
-                Ly, y = min(ys)
-                d2 = min(q_main[f], t_star - Ly)
-                if Lx - d2 >= t_star:
-                    continue
-                d = min(q_main[e], L[h] - t_star, t_star - (Lx - d2))
-                if d < q_min:
-                    continue
-                slot_q[y][slot_e[y].index(f)] += d2
-                q_main[f] -= d2
-                L[x] -= d2
-                L[y] += d2
-                s = S - free[x]
-                slot_e[x][s] = e
-                slot_q[x][s] = d
-                free[x] -= 1
-                q_main[e] -= d
-                L[h] -= d
-                L[x] += d
-                return True
+        for x in range(R):
+            if x == h or free[x] == 0 or e in slot_e[x] or L[x] < t_star:
+                continue
+            pairs = [(f, y) for f in range(x * E_loc, (x + 1) * E_loc) if q_main[f] > 0
+                     for y in range(R) if L[y] < t_star and f in slot_e[y]]
+            if not pairs:
+                continue
+            if len(pairs) != 1 or L[x] != t_star:
+                raise RuntimeError(f"relay lemma violated at rank {x}: L = {L[x]}, T* = {t_star}, "
+                                   f"live pairs {pairs}")
+            f, y = pairs[0]
+            d2 = min(q_main[f], t_star - L[y])
+            d = min(q_main[e], L[h] - t_star, t_star - (L[x] - d2))
+            if d < q_min:
+                continue
+            slot_q[y][slot_e[y].index(f)] += d2
+            q_main[f] -= d2
+            L[y] += d2
+            s = S - free[x]
+            slot_e[x][s] = e
+            slot_q[x][s] = d
+            free[x] -= 1
+            q_main[e] -= d
+            L[h] -= d
+            L[x] += d - d2
+            return True
     return False
 
 
@@ -107,6 +118,7 @@ def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
     slot_q = [[0] * S for _ in range(R)]
     free = [S] * R
     steps = 0
+    relays = 0
     stuck = False
     while True:
         h = max(range(R), key=lambda r: (L[r], -r))     # max load, lowest index on ties
@@ -134,6 +146,7 @@ def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
                     break
         if not moved:
             moved = _relay(h, mains, L, q_main, slot_e, slot_q, free, t_star, q_min, E_loc, R, S)
+            relays += int(moved)
         if not moved:
             stuck = True
             break
@@ -158,6 +171,7 @@ def solve_quota(counts: np.ndarray, S: int, q_min: int) -> dict:
         "rank_load": np.array(L, dtype=np.int64),
         "n_replicas": n_rep,
         "n_steps": steps,
+        "n_relays": relays,
         "t_star": t_star,
         "stuck": stuck,
         "inst_per_rank": ipr,

@@ -215,6 +215,33 @@ def test_quota_invariants_random(seed):
     _check_plan_invariants(counts, S, q_min, plan)
 
 
+def test_quota_relay_lemma_random():
+    """The relay lemma (oracle/quota.py docstring) on many small random instances with one
+    to four slots per rank: the oracle raises if a qualifying relay rank is not exactly at
+    T* or has more than one main with a replica holder below T*.  Relays must actually
+    occur here, or the check would be empty."""
+    rng = np.random.default_rng(2024)
+    relays = 0
+    for _ in range(4000):
+        R = int(rng.integers(2, 10))
+        E_loc = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 5))
+        mode = int(rng.integers(0, 3))
+        if mode == 0:
+            c = rng.integers(0, 20, R * E_loc)
+        elif mode == 1:
+            c = (rng.pareto(1.0, R * E_loc) * 5).astype(np.int64)
+        else:
+            c = rng.integers(0, 3, R * E_loc) * rng.integers(0, 30, R * E_loc)
+        counts = np.zeros((R, R * E_loc), dtype=np.int64)
+        counts[0] = c
+        q_min = int(rng.choice([0, 1, 2, 3]))
+        plan = O.solve_quota(counts, S, q_min)
+        relays += plan["n_relays"]
+        assert plan["n_relays"] <= plan["n_steps"] == plan["n_replicas"]
+    assert relays > 500
+
+
 def test_quota_invariants_qwen_layer():
     w = W.QWEN_LAYER
     counts, _ = O.load_matrix(W.routing(w), w.E)
