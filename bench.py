@@ -33,6 +33,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# The CPU leg times the oracle on one thread: pin every BLAS / OpenMP pool before numpy
+# (or torch) loads one.  The GPU legs do no host compute that these pools would serve.
+for _var in ("OMP_NUM_THREADS", "MKL_NUM_THREADS", "OPENBLAS_NUM_THREADS", "BLIS_NUM_THREADS",
+             "NUMEXPR_NUM_THREADS"):
+    os.environ.setdefault(_var, "1")
+
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
@@ -167,8 +173,8 @@ def permute_bytes(N, P, H):
     return N * H * 2 + P * H * 2 + P * 4
 
 
-PERMUTE_CALL = "permute_kernel<false> + row_src_kernel (one uep_permute call)"
-PERMUTE_CALL_NT = "permute_kernel<true> + row_src_kernel (one uep_permute call)"
+PERMUTE_CALL = ("prefetch_kernel + permute_kernel per chunk of at most 224 MiB of source rows, "
+                "then row_src_kernel (one uep_permute call)")
 PERMUTE_SOURCES = ("moe_expert_load_amd/csrc/permute.hip", "moe_expert_load_amd/csrc/common.h")
 
 
@@ -388,55 +394,199 @@ def combine_figures(torch, U, W, L, reps=5):
 
 # ----------------------------------------------------------------------------- CPU leg
 def host_cpu():
-    """CPU model name and logical CPU count of this host."""
+    """CPU model name (lscpu's, else /proc/cpuinfo's), logical CPUs, and the threads the
+    numpy / BLAS / OpenMP pools of this process actually hold."""
+    import subprocess
     model = "unknown"
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
         pass
-    return model, os.cpu_count()
+    if model == "unknown":
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in pools] + [1])
+    except ImportError:
+        pools = []
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "pool_threads": threads,
+            "pools": sorted({p.get("internal_api", "?") for p in pools})}
 
 
-def cpu_baseline(w, ids, x_host, passes=5):
-    """The oracle as it stands, single process: the whole step of the layer (load
-    matrix, quota solve, reroute, assignment, permute of every rank, staging of every
-    used slot), repeated `passes` times; value = tokens per second of the mean pass."""
+def _one_thread(fn):
+    """Run a CPU leg with every BLAS / OpenMP pool limited to one thread (threadpoolctl),
+    on top of the environment pins set before numpy loaded."""
+    def run(*a, **k):
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            return fn(*a, **k)
+        with threadpool_limits(limits=1):
+            return fn(*a, **k)
+    run.__doc__ = fn.__doc__
+    return run
+
+
+def _median_s(fn, runs=3):
+    """Median wall-clock seconds of `runs` calls of fn (its last result kept in fn.last)."""
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn.last = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def _cpu_line(value, per_step_s, sample, host):
+    return {"value": value, "unit": "tokens/s", "cores": host["pool_threads"], "kind": "oracle",
+            "sample": sample, "per_step_ms_median": {k: v * 1e3 for k, v in per_step_s.items()},
+            "host": host}
+
+
+@_one_thread
+def cpu_baseline_layer(w, ids, x_host, runs=3):
+    """The oracle as it stands, one thread, on the Qwen layer: each step of the path
+    (load matrix, quota solve, reroute + assignment, whole-group permute, staging of every
+    used slot, backward gradient reduction of the plan) timed `runs` times, median.  value
+    = tokens per second of the forward step (load matrix + solve + reroute/assign +
+    permute + staging), the GPU step's content."""
     import oracle as O
     n = w.expert_elems
-    mw = np.zeros((w.E, n), dtype=np.uint16)
-    sw = np.zeros((w.R, w.S, n), dtype=np.uint16)
-    t_plan = t_perm = t_stage = 0.0
-    for _ in range(passes):
-        t0 = time.perf_counter()
-        counts, bp = O.load_matrix(ids, w.E)
-        plan = O.solve_quota(counts, w.S, w.q_min)
-        X, io, so = O.reroute(counts, plan["inst_expert"], plan["inst_quota"],
-                              plan["inst_per_rank"])
-        _, dr = O.assign(ids, bp, X, plan["inst_expert"], plan["inst_per_rank"], io, so)
-        t1 = time.perf_counter()
-        out = O.permute(x_host, dr, 0, w.R, w.P)
-        del out
-        t2 = time.perf_counter()
-        O.stage_forward(plan["slot_expert"], mw, sw)
-        t3 = time.perf_counter()
-        t_plan += t1 - t0
-        t_perm += t2 - t1
-        t_stage += t3 - t2
-    total = (t_plan + t_perm + t_stage) / passes
-    model, ncpu = host_cpu()
-    used = int((plan["slot_expert"] >= 0).sum())
-    return {
-        "value": w.N / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": (f"the whole layer step {passes} times ({t_plan + t_perm + t_stage:.1f} s of CPU "
-                   f"work): plan {t_plan / passes:.2f} s, permute of all {w.R} ranks "
-                   f"{t_perm / passes:.2f} s, staging of all {used} used slots "
-                   f"{t_stage / passes:.2f} s per pass; Python+numpy, one thread"),
-        "host": {"cpu_model": model, "logical_cpus": ncpu},
-    }
+    host = host_cpu()
+    t = {}
+    f = lambda: O.load_matrix(ids, w.E)                              # noqa: E731
+    t["load_matrix"] = _median_s(f, runs)
+    counts, bp = f.last
+    f = lambda: O.solve_quota(counts, w.S, w.q_min)                  # noqa: E731
+    t["solve_quota"] = _median_s(f, runs)
+    plan = f.last
+    ie, ipr = plan["inst_expert"], plan["inst_per_rank"]
+
+    def rr():
+        X, io, so = O.reroute(counts, ie, plan["inst_quota"], ipr)
+        return O.assign(ids, bp, X, ie, ipr, io, so)[1]
+    t["reroute_assign"] = _median_s(rr, runs)
+    dr = rr.last
+    f = lambda: O.permute(x_host, dr, 0, w.R, w.P)[1]                 # noqa: E731
+    t["permute"] = _median_s(f, runs)
+    se = plan["slot_expert"]
+    rep = sorted(set(int(e) for e in se.reshape(-1) if e >= 0))
+    # staging and the reduction on the touched expert rows only (the others are never read)
+    remap = {e: i for i, e in enumerate(rep)}
+    se_c = np.vectorize(lambda e: remap.get(int(e), -1))(se).astype(np.int64)
+    rng = np.random.default_rng(5)
+    main_w = rng.integers(0, 1 << 16, (len(rep), n), dtype=np.uint16)
+    slot_w = np.zeros((w.R, w.S, n), dtype=np.uint16)
+    t["stage_forward"] = _median_s(lambda: O.stage_forward(se_c, main_w, slot_w), runs)
+    del main_w, slot_w
+    main_g = rng.standard_normal((len(rep), n), dtype=np.float32)
+    slot_g = rng.standard_normal((w.R, w.S, n), dtype=np.float32)
+    t["grad_reduce"] = _median_s(lambda: O.grad_reduce(se_c, main_g, slot_g, w.E_loc), runs)
+    del main_g, slot_g
+    fwd = sum(t[k] for k in ("load_matrix", "solve_quota", "reroute_assign", "permute",
+                             "stage_forward"))
+    sample = (f"each step of the whole layer {runs} times, median: the forward step (plan, "
+              f"permute of all {w.R} ranks, staging of all {int((se >= 0).sum())} used slots) "
+              f"{fwd:.2f} s, the backward reduction {t['grad_reduce']:.2f} s; Python+numpy, "
+              f"BLAS/OpenMP pinned to one thread")
+    return _cpu_line(w.N / fwd, t, sample, host)
+
+
+@_one_thread
+def cpu_baseline_waterfill(w, ids, x_host, inst, ipr, seed, runs=3):
+    """The oracle, one thread, on the DeepSeek-V3 Waterfill layer: routed loads, Waterfill,
+    the fused (K+1)-column layout's load matrix, identity quotas, reroute + assignment, and
+    the whole group's permute (31.5 GiB of dispatch rows, produced in blocks of 131072
+    rows from the oracle's row map, each block's time summed), median of `runs`."""
+    import oracle as O
+    host = host_cpu()
+    t = {}
+    B = np.full(w.R, w.T, dtype=np.int32)
+    f = lambda: O.load_matrix(ids, w.E)[0]                           # noqa: E731
+    t["load_matrix_routed"] = _median_s(f, runs)
+    counts = f.last
+    f = lambda: O.waterfill(counts, ids, B, seed, 0)                  # noqa: E731
+    t["waterfill"] = _median_s(f, runs)
+    ext = O.extend_topk(ids, f.last[0], w.E)
+    E2 = w.E + w.R
+    f = lambda: O.load_matrix(ext, E2)                                # noqa: E731
+    t["load_matrix_fused"] = _median_s(f, runs)
+    c2, bp2 = f.last
+    f = lambda: O.identity_quota(c2, inst)                            # noqa: E731
+    t["identity_quota"] = _median_s(f, runs)
+    q = f.last
+
+    def rr():
+        X, io, so = O.reroute(c2, inst, q, ipr)
+        return O.assign(ext, bp2, X, inst, ipr, io, so)[1]
+    t["reroute_assign"] = _median_s(rr, runs)
+    dr = rr.last
+    P = int(c2.sum())
+    K2 = w.K + 1
+
+    def perm():
+        src = O.row_sources(dr, P)
+        for a in range(0, P, 1 << 17):
+            O.rows_of(x_host, src, K2, a, min(P, a + (1 << 17)))
+    t["permute"] = _median_s(perm, runs)
+    total = sum(t.values())
+    sample = (f"each step of the whole layer {runs} times, median ({total:.2f} s per pass): plan "
+              f"{total - t['permute']:.2f} s, permute of all {w.R} ranks into the fused layout "
+              f"{t['permute']:.2f} s; Python+numpy, BLAS/OpenMP pinned to one thread")
+    return _cpu_line(w.N / total, t, sample, host)
+
+
+@_one_thread
+def cpu_baseline_lplb(w, ids, x_host, inst, ipr, rank_sample=4, runs=3):
+    """The oracle, one thread, on the LPLB layer: load matrix, the fp64 simplex and
+    largest-remainder quotas, reroute + assignment on those quotas, and the permute of
+    `rank_sample` of the R source ranks (their rows produced in blocks from the oracle's
+    row map), scaled by R / rank_sample for the whole group; median of `runs`."""
+    import oracle as O
+    host = host_cpu()
+    t = {}
+    f = lambda: O.load_matrix(ids, w.E)                               # noqa: E731
+    t["load_matrix"] = _median_s(f, runs)
+    counts, bp = f.last
+    f = lambda: O.lplb(counts, inst, ipr)                             # noqa: E731
+    t["lplb_simplex"] = _median_s(f, runs)
+    q = f.last["inst_quota"]
+
+    def rr():
+        X, io, so = O.reroute(counts, inst, q, ipr)
+        return O.assign(ids, bp, X, inst, ipr, io, so)[1]
+    t["reroute_assign"] = _median_s(rr, runs)
+    dr = rr.last
+    sub = np.full_like(dr, -1)
+    sub[:rank_sample] = dr[:rank_sample]
+
+    def perm():
+        src = O.row_sources(sub, w.P)
+        rows = np.nonzero(src >= 0)[0]
+        for a in range(0, rows.size, 1 << 17):
+            blk = rows[a:a + (1 << 17)]
+            O.rows_of(x_host, src[blk], w.K, 0, blk.size)
+    t_sample = _median_s(perm, runs)
+    t["permute"] = t_sample * w.R / rank_sample
+    total = sum(t.values())
+    sample = (f"each step {runs} times, median: plan {total - t['permute']:.2f} s for the whole "
+              f"layer, permute of {rank_sample} of {w.R} source ranks {t_sample:.2f} s, scaled x"
+              f"{w.R // rank_sample} to the group ({t['permute']:.2f} s); Python+numpy, "
+              f"BLAS/OpenMP pinned to one thread")
+    return _cpu_line(w.N / total, t, sample, host)
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -511,8 +661,12 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     if with_cpu:
         log("cpu baseline (oracle) ...")
         x_host = L.x.view(torch.int16).cpu().numpy().view(np.uint16)
-        cpu = cpu_baseline(w, ids, x_host)
+        cpu = cpu_baseline_layer(w, ids, x_host)
+        del x_host
     out["cpu_baseline"] = cpu
+    gpu_steps = {"load_matrix": graph_us(torch, L.load), "solve_quota": graph_us(torch, L.solve),
+                 "reroute_assign": graph_us(torch, L.reroute), "permute": perm_ms * 1e3,
+                 "stage_forward": stage_kernel_us, "grad_reduce": grad["grad_reduce_ms"] * 1e3}
     rank_bytes = permute_bytes(w.T, w.T * w.K, w.H) - w.T * w.K * 4
     out["extra"] = {
         "us_per_layer_rank_share": rank_us,
@@ -538,6 +692,9 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     out["extra"]["stage_kernel_us"] = stage_kernel_us
     out["extra"]["stage_kernel_gbs"] = stage_bytes / (stage_kernel_us * 1e-6) / 1e9 if n_used else 0.0
     out["extra"]["stage_kernel_frac"] = out["extra"]["stage_kernel_gbs"] / HBM_PEAK_GBS
+    out["extra"]["steps_gpu_us_vs_oracle_ms"] = {
+        k: {"gpu_us": v, "oracle_ms": cpu["per_step_ms_median"][k] if cpu else None}
+        for k, v in gpu_steps.items()}
     return out
 
 
@@ -593,9 +750,14 @@ def bench_waterfill(args, torch, U, W, w):
     pb = permute_bytes(N, L.P, w.H)
     out = base_line(w, W, N / (ms * 1e-3), ms, args, "int32",
                     {"top_k_fused": K2, "shared_slot_per_rank": 1})
-    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
+    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL,
                                measured_traffic(w.name))
     out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        x_host = L.x.view(torch.int16).cpu().numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline_waterfill(w, ids, x_host, inst, ipr, seed)
+        del x_host
     seq = sequential_permute_line(torch, U, L, tp.mean_ms())
     plan_us = graph_us(torch, lambda s: wf_plan(s))
     wf_us = graph_us(torch, lambda s: U.waterfill(counts1, ids_d, B, seed, 0, 4, sh, wl, sl, rl,
@@ -656,9 +818,14 @@ def bench_lplb(args, torch, U, W, w):
     pb = permute_bytes(w.N, w.P, w.H)
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"static_replicas": w.n_static_replicas, "lp_iters": args.lp_iters})
-    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL_NT,
+    out["roofline"] = roofline(pb, tp.mean_ms(), PERMUTE_CALL,
                                measured_traffic(w.name))
     out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        x_host = L.x.view(torch.int16).cpu().numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline_lplb(w, ids, x_host, inst, ipr)
+        del x_host
     seq = sequential_permute_line(torch, U, L, tp.mean_ms(), reps=3)
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)
@@ -820,6 +987,31 @@ def _csv(directory, suffix):
         return list(csv.DictReader(f))
 
 
+def _permute_calls(rows, name_key, order_key, whole_rs_blocks, blocks_of):
+    """Group the launches of whole-group uep_permute calls: each call is a run of
+    consecutive prefetch_kernel / permute_kernel launches closed by a row_src_kernel
+    launch over every pair (whole_rs_blocks workgroups).  Returns a list of lists of
+    rows, one list per call, in launch order."""
+    calls, run = [], []
+    for r in sorted(rows, key=lambda r: int(r[order_key])):
+        name = r[name_key]
+        if "prefetch_kernel" in name or "uep::permute_kernel" in name:
+            run.append(r)
+        elif "row_src_kernel" in name and blocks_of(r) == whole_rs_blocks and run:
+            calls.append(run + [r])
+            run = []
+        else:
+            run = []
+    return calls
+
+
+# the default bench's warm-up and timed steps (main()'s defaults)
+_DEFAULT_WARMUP, _DEFAULT_STEPS = 3, 20
+# (workload, pairs) of the whole-group permute calls the summaries look for
+_TRACE_WORKLOADS = (("qwen3_235b_layer", 32 * 8192 * 8), ("dsv3_waterfill", 64 * 4096 * 9),
+                    ("lplb_layer", 64 * 16384 * 8), ("tiny", 4 * 512 * 2))
+
+
 def trace_summary(directory):
     """Markdown table of a rocprofv3 --kernel-trace --stats CSV run: rocprofv3's own
     per-name statistics, then the trace split by (kernel, workgroup count), since one
@@ -849,6 +1041,35 @@ def trace_summary(directory):
         d = np.array(d, dtype=np.float64) / 1e3
         print(f"| {k} | {b} x {wg} | {len(d)} | {d.mean():.2f} | {np.median(d):.2f} | "
               f"{d.min():.2f} | {d.max():.2f} |")
+
+    def blocks_of(r):
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+
+    uep_rows = [r for r in trace if "uep::" in r["Kernel_Name"]]
+    for workload, P in _TRACE_WORKLOADS:
+        calls = _permute_calls(uep_rows, "Kernel_Name", "Start_Timestamp", (P + 255) // 256,
+                               blocks_of)
+        if not calls:
+            continue
+        busy = np.array([sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in c)
+                         for c in calls], dtype=np.float64) / 1e3
+        span = np.array([int(c[-1]["End_Timestamp"]) - int(c[0]["Start_Timestamp"]) for c in calls],
+                        dtype=np.float64) / 1e3
+        print(f"\nwhole-group uep_permute calls ({workload}, {P} pairs): {len(calls)} calls of "
+              f"{len(calls[0])} launches; kernel time per call avg {busy.mean():.2f} us "
+              f"(median {np.median(busy):.2f}); first start to last end avg {span.mean():.2f} us "
+              f"(median {np.median(span):.2f})")
+        w0, n = _DEFAULT_WARMUP, _DEFAULT_STEPS
+        if len(calls) >= w0 + n:
+            b, sp = busy[w0:w0 + n], span[w0:w0 + n]
+            print(f"- calls {w0 + 1}-{w0 + n} (the default bench's {n} timed steps, after {w0} "
+                  f"warm-up steps): kernel time per call avg {b.mean():.2f} us, first start to "
+                  f"last end avg {sp.mean():.2f} us")
+        if len(calls) > w0 + n:
+            b = busy[w0 + n:]
+            print(f"- calls {w0 + n + 1}-{len(calls)} (later calls of the same run, e.g. the "
+                  f"sequential-row reference line): kernel time per call avg {b.mean():.2f} us")
 
 
 def pmc_summary(fetch_dir, write_dir, workload="qwen3_235b_layer"):
@@ -881,15 +1102,31 @@ def pmc_summary(fetch_dir, write_dir, workload="qwen3_235b_layer"):
         fw = write.get(k, float("nan"))
         print(f"| {k[0]} | {k[1]} | {fetch[k]:.1f} | {fw:.1f} | {fetch[k] * f_fetch / 1024:.1f} | "
               f"{fw * f_write / 1024:.1f} |")
-    pk = [k for k in fetch if "permute_kernel" in k[0] and k[1] == (w.N + 3) // 4]
-    rk = [k for k in fetch if "row_src_kernel" in k[0] and k[1] == (w.P + 255) // 256]
-    kib = sum(fetch[k] * f_fetch + write[k] * f_write for k in pk + rk)
+    P = w.N * (w.K + 1) if w.shared_expert else w.P
+
+    def per_call(rows, counter):
+        rows = [r for r in rows if r["Counter_Name"] == counter and "uep::" in r["Kernel_Name"]]
+        order = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Correlation_Id"
+        calls = _permute_calls(rows, "Kernel_Name", order, (P + 255) // 256,
+                               lambda r: int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1))
+        sums = [sum(float(r["Counter_Value"]) for r in c) for c in calls]
+        return float(np.median(sums)), len(calls), len(calls[0]) if calls else 0
+
+    f_kib, nf, lf = per_call(_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    w_kib, nw, lw = per_call(_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    kib = f_kib * f_fetch + w_kib * f_write
     traffic = int(round(kib * 1024))
-    alg = permute_bytes(w.N, w.P, w.H)
+    H = w.H
+    N = w.N
+    alg = N * H * 2 + P * H * 2 + P * 4
     print(f"\ncalibration (uep_device_copy, 1 GiB read + 1 GiB written): FETCH_SIZE x {f_fetch:.5f}, "
           f"WRITE_SIZE x {f_write:.5f}\n")
+    print(f"whole-group uep_permute calls: {nf} in the FETCH_SIZE run, {nw} in the WRITE_SIZE run, "
+          f"{lf} launches each (prefetch and permute per chunk, then row_src); per call "
+          f"(median): FETCH_SIZE {f_kib:.1f} KiB -> {f_kib * f_fetch / 1024:.1f} MiB read, "
+          f"WRITE_SIZE {w_kib:.1f} KiB -> {w_kib * f_write / 1024:.1f} MiB written\n")
     print(f"- workload = {workload}")
-    print(f"- kernels = {', '.join(f'{k[0]} ({k[1]} workgroups)' for k in pk + rk)}")
+    print(f"- kernels = {PERMUTE_CALL}")
     print(f"- algorithmic_bytes_per_launch = {alg}")
     print(f"- traffic_bytes_per_launch = {traffic}")
     print(f"- traffic_over_algorithmic = {traffic / alg:.4f}")
@@ -922,8 +1159,6 @@ def main():
         print("bench.py measures one GPU only: the EP group is simulated as virtual ranks on a "
               "single device, so --gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
-
     import torch
     from moe_expert_load_amd import uep as U
     from moe_expert_load_amd import workload as W

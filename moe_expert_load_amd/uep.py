@@ -10,6 +10,7 @@ not built: there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from typing import Optional
 
@@ -319,45 +320,82 @@ def lplb_struct_size(R, E, inst_per_rank) -> int:
     return int(LIB.uep_lplb_struct_size(R, E, inst_per_rank))
 
 
-def lplb_prepare(inst_expert_host, R, E, inst_per_rank, device, stream=None) -> torch.Tensor:
+@dataclasses.dataclass(frozen=True)
+class LPStruct:
+    """An LP structure from uep_lplb_prepare: the device buffer plus the host's own
+    record of its sizes (ranks, experts, instances per rank, instances, replicated
+    experts G and their copies n), which the calls below check every caller buffer
+    against before a kernel sees it."""
+
+    buf: torch.Tensor
+    R: int
+    E: int
+    inst_per_rank: int
+    I: int
+    G: int
+    n: int
+
+
+def lplb_prepare(inst_expert_host, R, E, inst_per_rank, device, stream=None) -> LPStruct:
     """Offline: build the LP structure from a host instance table into a device buffer."""
     import numpy as np
     ie = np.ascontiguousarray(np.asarray(inst_expert_host, dtype=np.int32))
+    if ie.size != R * inst_per_rank:
+        raise TypeError(f"inst_expert must have R * inst_per_rank = {R * inst_per_rank} entries")
     n = lplb_struct_size(R, E, inst_per_rank)
     buf = torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
     _check(LIB.uep_lplb_prepare(ie.ctypes.data_as(ctypes.c_void_p), R, E, inst_per_rank,
                                 _p(buf), buf.numel(), _s(stream)), "uep_lplb_prepare")
-    return buf
+    copies = np.bincount(ie[(ie >= 0) & (ie < E)], minlength=E)
+    rep = copies >= 2
+    return LPStruct(buf, R, E, inst_per_rank, R * inst_per_rank, int(rep.sum()),
+                    int(copies[rep].sum()))
 
 
-def lplb(counts, lp, n_copies, n_inst, iters=30, x=None, m=None, inst_quota=None, stats=None,
-         err=None, stream=None):
+def _lp(lp) -> LPStruct:
+    if not isinstance(lp, LPStruct):
+        raise TypeError("lp must be the LPStruct that lplb_prepare returned")
+    return lp
+
+
+def lplb(counts, lp, n_copies=None, n_inst=None, iters=30, x=None, m=None, inst_quota=None,
+         stats=None, err=None, stream=None):
+    """The LP split for one batch.  n_copies and n_inst, when given, must equal the
+    structure's own counts; every buffer is checked against the structure."""
+    lp = _lp(lp)
     _i32(counts, "counts")
-    if lp.numel() * lp.element_size() < lplb_struct_size(counts.shape[0], counts.shape[1], 1):
-        raise TypeError("lp is smaller than any LP structure for these counts")
-    x = torch.empty((max(n_copies, 1),), dtype=torch.float32, device=counts.device) if x is None \
-        else _buf(x, max(n_copies, 1), "x", torch.float32)
+    if tuple(counts.shape) != (lp.R, lp.E):
+        raise TypeError(f"counts must be [{lp.R}][{lp.E}] for this LP structure, got "
+                        f"{list(counts.shape)}")
+    if n_copies is not None and n_copies != lp.n:
+        raise TypeError(f"n_copies {n_copies} != the structure's {lp.n} copies")
+    if n_inst is not None and n_inst != lp.I:
+        raise TypeError(f"n_inst {n_inst} != the structure's {lp.I} instances")
+    x = torch.empty((max(lp.n, 1),), dtype=torch.float32, device=counts.device) if x is None \
+        else _buf(x, max(lp.n, 1), "x", torch.float32)
     m = torch.empty((1,), dtype=torch.float32, device=counts.device) if m is None \
         else _buf(m, 1, "m", torch.float32)
-    inst_quota = _new((n_inst,), counts) if inst_quota is None else _buf(inst_quota, n_inst,
-                                                                         "inst_quota")
+    inst_quota = _new((lp.I,), counts) if inst_quota is None else _buf(inst_quota, lp.I,
+                                                                        "inst_quota")
     stats = _new((4,), counts) if stats is None else _buf(stats, 4, "stats")
     _buf(err, 1, "err")
-    _check(LIB.uep_lplb(_p(counts), _p(lp), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
+    _check(LIB.uep_lplb(_p(counts), _p(lp.buf), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
                         _p(err), _s(stream)), "uep_lplb")
-    return x[:n_copies], m, inst_quota, stats
+    return x[:lp.n], m, inst_quota, stats
 
 
 def lplb_sample(topk_ids, lp, x, seed, layer, dest_inst=None, err=None, stream=None):
     """Per-token copy draw from LPLB's split: dest_inst [R][T][K] int32."""
+    lp = _lp(lp)
     _i32(topk_ids, "topk_ids")
     R, T, K = topk_ids.shape
-    if x.dtype != torch.float32:
-        raise TypeError("x must be float32")
+    if R != lp.R:
+        raise TypeError(f"topk_ids has {R} ranks, the LP structure {lp.R}")
+    _buf(x, lp.n, "x", torch.float32)
     dest_inst = _new((R, T, K), topk_ids) if dest_inst is None else _buf(dest_inst, R * T * K,
                                                                          "dest_inst")
     _buf(err, 1, "err")
-    _check(LIB.uep_lplb_sample(_p(topk_ids), R, T, K, _p(lp), _p(x),
+    _check(LIB.uep_lplb_sample(_p(topk_ids), R, T, K, _p(lp.buf), _p(x),
                                ctypes.c_uint64(seed & (2 ** 64 - 1)),
                                ctypes.c_uint64(layer & (2 ** 64 - 1)), _p(dest_inst), _p(err),
                                _s(stream)), "uep_lplb_sample")

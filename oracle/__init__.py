@@ -29,7 +29,7 @@ Parity status of each function (what pins it) is listed in the module headers.
 from .load_matrix import load_matrix, OracleInputError
 from .quota import solve_quota
 from .reroute import reroute, assign, identity_quota
-from .permute import permute, permute_rows
+from .permute import permute, permute_rows, row_sources, rows_of
 from .combine import combine, combine_f32, combine_tokens, f32_to_bf16_bits, bf16_bits_to_f32
 from .stage import stage_forward, grad_reduce
 from .philox import philox4x64_10, philox4x64_10_np
@@ -38,7 +38,7 @@ from .lplb import lplb_structure, lplb_lp, simplex, hamilton_quotas, lplb, lplb_
 
 __all__ = [
     "load_matrix", "OracleInputError", "solve_quota", "reroute", "assign", "identity_quota",
-    "permute", "permute_rows", "combine", "combine_f32", "combine_tokens", "f32_to_bf16_bits",
+    "permute", "permute_rows", "row_sources", "rows_of", "combine", "combine_f32", "combine_tokens", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "stage_forward", "grad_reduce", "philox4x64_10", "philox4x64_10_np",
     "waterfill", "extend_topk", "lplb_structure", "lplb_lp", "simplex", "hamilton_quotas", "lplb",
     "lplb_sample",

@@ -37,6 +37,36 @@ def permute(x_bits: np.ndarray, dest_row: np.ndarray, r_begin: int, r_end: int, 
     return out, row_src, written
 
 
+def row_sources(dest_row: np.ndarray, n_rows: int) -> np.ndarray:
+    """row_src of the whole buffer: for every dispatch row, the flat pair index
+    j = (r*T + t)*K + k that targets it, -1 where no pair does.  The content of row d
+    is then x[row_src[d] // K] (the token of that pair): the permute's definition with
+    the row loop turned around, for full-size checks chunked over rows."""
+    flat = np.asarray(dest_row).reshape(-1)
+    pairs = np.nonzero(flat >= 0)[0]
+    rows = flat[pairs]
+    if rows.size and (rows.max() >= n_rows or np.bincount(rows, minlength=n_rows).max() > 1):
+        raise ValueError("a pair targets a row outside the buffer, or two pairs one row")
+    src = np.full(n_rows, -1, dtype=np.int64)
+    src[rows] = pairs
+    return src
+
+
+def rows_of(x_bits: np.ndarray, row_src: np.ndarray, K: int, a: int, b: int) -> np.ndarray:
+    """Content of dispatch rows [a, b) given row_sources' map: row d is the activation
+    row of the token of pair row_src[d] (rows no pair targets stay zero).  The permute
+    written over output rows, so a buffer too large to hold can be produced block by
+    block."""
+    x = np.asarray(x_bits)
+    H = x.shape[-1]
+    flat = x.reshape(-1, H)
+    src = np.asarray(row_src[a:b])
+    out = np.zeros((b - a, H), dtype=x.dtype)
+    live = src >= 0
+    out[live] = flat[src[live] // K]
+    return out
+
+
 def permute_rows(x_bits: np.ndarray, dest_row: np.ndarray, rows: np.ndarray) -> tuple:
     """Expected content of selected dispatch rows only (for full-size sampled checks).
 

@@ -45,3 +45,35 @@ def random_routing(rng, R, T, K, E, p=None, empty_frac=0.0):
     if empty_frac:
         ids[rng.random(ids.shape) < empty_frac] = -1
     return ids
+
+
+def compare_dispatch_rows(x, out, dest_row_oracle, chunk_rows=1 << 18):
+    """Every row of a dispatch buffer against the oracle's definition of the permute:
+    row d holds x[row_src[d] // K] bit for bit, row_src being the oracle's inverse of its
+    own dest_row (oracle.row_sources).  The expected rows are gathered from x on the
+    device chunk by chunk (so buffers of 100+ GiB are compared whole) and compared
+    element by element with torch.equal.  Rows no pair targets must be all zero bits
+    (callers pass a zeroed buffer when such rows exist).  Returns the oracle's row_src."""
+    import oracle as O
+    P, H = out.shape
+    K = dest_row_oracle.shape[-1]
+    src = O.row_sources(dest_row_oracle, P)
+    xf = x.reshape(-1, H).view(torch.int16)
+    of = out.view(torch.int16)
+    for a in range(0, P, chunk_rows):
+        b = min(P, a + chunk_rows)
+        s = src[a:b]
+        live = s >= 0
+        if live.all():
+            exp = xf.index_select(0, torch.from_numpy(s // K).to(DEV))
+            assert torch.equal(of[a:b], exp), f"dispatch rows [{a}, {b}) differ"
+        else:
+            idx = np.nonzero(live)[0]
+            if idx.size:
+                exp = xf.index_select(0, torch.from_numpy(s[idx] // K).to(DEV))
+                got = of[a:b].index_select(0, torch.from_numpy(idx).to(DEV))
+                assert torch.equal(got, exp), f"dispatch rows in [{a}, {b}) differ"
+            dead = np.nonzero(~live)[0]
+            got0 = of[a:b].index_select(0, torch.from_numpy(dead).to(DEV))
+            assert int(torch.count_nonzero(got0)) == 0, f"untargeted rows in [{a}, {b}) written"
+    return src

@@ -34,6 +34,18 @@ def test_header_declares_the_path():
         assert n in names
 
 
+def test_solve_quota_comment_states_the_search_the_kernel_runs():
+    """The header's account of uep_solve_quota describes the search as built: plain
+    steps, then relays, then the stop; the 'top up an existing replica' branch the
+    search no longer has is not described."""
+    text = open(HEADER).read()
+    block = text[text.index("uep_solve_quota -- "):text.index("uep_status uep_solve_quota(")]
+    flat = " ".join(re.sub(r"(?m)^\s*\* ?", " ", block).split())
+    assert "Relay" in flat and "Plain step" in flat and "stop" in flat
+    assert "d2 = min(q_f, T* - L_y)" in flat
+    assert "existing replica under T*" not in flat and "top up" not in flat.lower()
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
@@ -147,3 +159,34 @@ def test_header_compiles_and_links_from_c_and_cpp(lib, tmp_path, compiler, std, 
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.startswith(f"{len(names)} functions")
+
+
+def test_lplb_binding_checks_buffers_against_the_structure(lib):
+    """The LPLB calls check counts, x, inst_quota and topk_ids against the structure's
+    own sizes before any kernel could index them (host tensors here: each check must
+    fire before a device pointer is taken)."""
+    import torch
+    from moe_expert_load_amd import uep as U
+    lp = U.LPStruct(buf=torch.zeros(64, dtype=torch.uint8), R=4, E=8, inst_per_rank=3, I=12,
+                    G=2, n=4)
+    counts = torch.zeros(4, 8, dtype=torch.int32)
+    with pytest.raises(TypeError, match="counts must be"):
+        U.lplb(torch.zeros(4, 9, dtype=torch.int32), lp)
+    with pytest.raises(TypeError, match="n_copies"):
+        U.lplb(counts, lp, n_copies=5)
+    with pytest.raises(TypeError, match="n_inst"):
+        U.lplb(counts, lp, n_inst=11)
+    with pytest.raises(TypeError, match="x must be"):
+        U.lplb(counts, lp, x=torch.zeros(3, dtype=torch.float32))
+    with pytest.raises(TypeError, match="inst_quota must be"):
+        U.lplb(counts, lp, x=torch.zeros(4, dtype=torch.float32), m=torch.zeros(1),
+               inst_quota=torch.zeros(11, dtype=torch.int32))
+    with pytest.raises(TypeError, match="LPStruct"):
+        U.lplb(counts, lp.buf)
+    ids = torch.zeros(5, 2, 2, dtype=torch.int32)
+    with pytest.raises(TypeError, match="ranks"):
+        U.lplb_sample(ids, lp, torch.zeros(4, dtype=torch.float32), 1, 1)
+    with pytest.raises(TypeError, match="x must be"):
+        U.lplb_sample(ids[:4], lp, torch.zeros(3, dtype=torch.float32), 1, 1)
+    with pytest.raises(TypeError, match="inst_expert must have"):
+        U.lplb_prepare([0, 1, -1], 4, 8, 3, "cpu")

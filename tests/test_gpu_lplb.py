@@ -9,6 +9,8 @@ the quotas is then checked bit-exact against the oracle on the oracle's own quot
 by its properties on the kernel's quotas.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -19,7 +21,7 @@ if not torch.cuda.is_available():
 import oracle as O                                       # noqa: E402
 from moe_expert_load_amd import uep as U                 # noqa: E402
 from moe_expert_load_amd import workload as W            # noqa: E402
-from tests.gpu_helpers import DEV, to_dev, host, err_word, say  # noqa: E402
+from tests.gpu_helpers import DEV, to_dev, host, err_word, say, compare_dispatch_rows  # noqa: E402
 from tests.test_oracle_reroute_permute import (check_reroute_properties,  # noqa: E402
                                                check_assign_properties)
 
@@ -186,7 +188,10 @@ def test_lplb_special_cases():
 
 
 def test_lplb_layer_full_size():
-    """LPLB-shaped layer: R = 64, 256 experts + 32 static replicas, 16384 tokens per rank."""
+    """LPLB-shaped layer: R = 64, 256 experts + 32 static replicas, 16384 tokens per rank.
+    M against the simplex optimum; reroute/assign on the oracle's quotas bit-exact and the
+    whole group's permute on that plan compared on every one of its 8,388,608 rows;
+    reroute on the kernel's own quotas by its properties."""
     w = W.LPLB_LAYER
     say("case: lplb layer full size", w)
     ids = W.routing(w)
@@ -208,6 +213,17 @@ def test_lplb_layer_full_size():
     assert host(err)[0] == 0
     assert np.array_equal(host(xfer), X_o) and np.array_equal(host(ioff), io_o)
     assert np.array_equal(host(di), di_o) and np.array_equal(host(dr), dr_o)
+    # permute of the whole group (hidden 7168, 112 GiB) on that plan: every row compared
+    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
+    x_act = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV, dtype=torch.bfloat16)
+    out = torch.empty(w.P, w.H, dtype=torch.bfloat16, device=DEV)
+    row_src = torch.empty(w.P, dtype=torch.int32, device=DEV)
+    U.permute(x_act, dr, out, row_src)
+    torch.cuda.synchronize()
+    src_o = compare_dispatch_rows(x_act, out, dr_o)
+    assert np.array_equal(host(row_src), src_o)
+    del out, row_src, x_act
+    torch.cuda.empty_cache()
     # reroute/assign on the kernel's own quotas: properties
     xfer, ioff, di, dr = U.reroute_assign(counts, ids_d, bp, ipr, inst_d, to_dev(q), err=err)
     assert host(err)[0] == 0
@@ -215,21 +231,6 @@ def test_lplb_layer_full_size():
     check_reroute_properties(counts_o, inst, q, ipr, Xg)
     drh = host(dr)
     assert np.array_equal(np.sort(drh.reshape(-1)), np.arange(w.P))
-    # permute of the whole group (hidden 7168), sampled rows
-    gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
-    x_act = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV, dtype=torch.bfloat16)
-    out = torch.empty(w.P, w.H, dtype=torch.bfloat16, device=DEV)
-    U.permute(x_act, dr, out)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([rng.integers(0, w.P, 3000), [0, w.P - 1]]))
-    flat = drh.reshape(-1)
-    pos = np.empty(w.P, dtype=np.int64)
-    pos[flat] = np.arange(w.P)
-    tok = torch.from_numpy(pos[rows] // w.K).to(DEV)
-    exp = host(x_act.view(w.R * w.T, w.H).view(torch.int16)[tok])
-    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)])
-    assert np.array_equal(got, exp)
 
 
 # ---------------------------------------------------------------- per-token copy draw
@@ -336,11 +337,15 @@ def test_lplb_sample_errors_and_layouts():
             assert np.array_equal(host(di), di_o)
         ob = host(out_big)
         assert ob[0] == -9 and (ob[1 + n:] == -9).all()
-        # a structure built for 2 ranks, used with 4
+        # a structure built for 2 ranks, used with 4: the binding refuses it on the host;
+        # with its record claiming 4 ranks, the kernel refuses the buffer itself
         inst_small = np.where(inst[:2 * ipr] < 2 * E_loc, inst[:2 * ipr], -1)
         lp2 = U.lplb_prepare(inst_small, 2, 2 * E_loc, ipr, DEV)
+        ids_small = to_dev(np.where(ids < 2 * E_loc, ids, -1))
+        with pytest.raises(TypeError):
+            U.lplb_sample(ids_small, lp2, xd, 5, 1)
         err = err_word()
-        di = U.lplb_sample(to_dev(np.where(ids < 2 * E_loc, ids, -1)), lp2, xd, 5, 1, err=err)
+        di = U.lplb_sample(ids_small, dataclasses.replace(lp2, R=R), xd, 5, 1, err=err)
         assert host(err)[0] & U.ERR_LP and (host(di) == -1).all()
 
 
@@ -374,16 +379,17 @@ def test_lplb_refuses_a_foreign_structure():
     R = 4
     say("case: lplb foreign structure")
     good = U.lplb_prepare(inst, R, E, ipr, DEV)
-    bad_n = good.clone()
+    bad_n = good.buf.clone()
     bad_n.view(torch.int32)[6] = 1 << 20                   # n_copies beyond the tables
-    for lp in (torch.zeros_like(good), bad_n):
+    for buf in (torch.zeros_like(good.buf), bad_n):
+        lp = dataclasses.replace(good, buf=buf)
         err = err_word()
         x = torch.full((8,), -3.0, dtype=torch.float32, device=DEV)
         m = torch.full((1,), -3.0, dtype=torch.float32, device=DEV)
         q = torch.full((len(inst),), -3, dtype=torch.int32, device=DEV)
         st = torch.full((4,), -3, dtype=torch.int32, device=DEV)
         counts = to_dev(O.load_matrix(ids, E)[0])
-        U.lplb(counts, lp, 8, len(inst), iters=30, x=x, m=m, inst_quota=q, stats=st, err=err)
+        U.lplb(counts, lp, iters=30, x=x, m=m, inst_quota=q, stats=st, err=err)
         assert host(err)[0] == U.ERR_LP
         assert (host(x) == -3.0).all() and host(m)[0] == -3.0
         assert (host(q) == -3).all() and (host(st) == -3).all()

@@ -15,7 +15,7 @@ import oracle as O                                       # noqa: E402
 from moe_expert_load_amd import uep as U                 # noqa: E402
 from moe_expert_load_amd import workload as W            # noqa: E402
 from tests.gpu_helpers import (DEV, to_dev, host, err_word, say, plan_on_gpu,  # noqa: E402
-                               random_routing)
+                               random_routing, compare_dispatch_rows)
 from tests.conftest import golden                        # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -490,8 +490,9 @@ def test_device_fill(nbytes):
 
 
 def test_qwen_layer_full_size():
-    """Qwen3-235B-shaped layer: plan bit-exact at full size; permute of one rank's share
-    compared whole, the whole-group permute on sampled rows; staging of 3 slots."""
+    """Qwen3-235B-shaped layer: plan bit-exact at full size; the whole-group permute
+    compared on every one of its 2,097,152 dispatch rows (16 GiB) and row_src whole; one
+    rank's share compared whole; staging of every used slot against the oracle."""
     w = W.QWEN_LAYER
     say("case: qwen layer full size", w)
     ids = W.routing(w)
@@ -506,38 +507,31 @@ def test_qwen_layer_full_size():
     row_src = torch.empty(P, dtype=torch.int32, device=DEV)
     U.permute(x, g["dest_row"], out, row_src)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([rng.integers(0, P, 4000), [0, P - 1]]))
-    xh = host(x.view(torch.int16)).view(np.uint16)
-    exp, src = O.permute_rows(xh, o["dest_row"], rows)
-    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)]).view(np.uint16)
-    assert np.array_equal(got, exp)
-    assert np.array_equal(host(row_src)[rows], src)
-    assert np.array_equal(np.sort(host(row_src)), np.arange(P))       # every row written once
+    src_o = compare_dispatch_rows(x, out, o["dest_row"])
+    assert np.array_equal(host(row_src), src_o)
+    del out
     # one rank's share, compared in full
     r = 5
     out_r = torch.zeros(P, w.H, dtype=torch.bfloat16, device=DEV)
     U.permute(x, g["dest_row"], out_r, None, r_begin=r, r_end=r + 1)
+    xh = host(x.view(torch.int16)).view(np.uint16)
     rows_r = np.sort(o["dest_row"][r].reshape(-1))
     exp_r, _ = O.permute_rows(xh, o["dest_row"], rows_r)
     got_r = host(out_r.view(torch.int16)[torch.from_numpy(rows_r).to(DEV)]).view(np.uint16)
     assert np.array_equal(got_r, exp_r)
-    del out, out_r
-    # staging: forward weights and the fp32 gradient reduction
+    del out_r
+    # staging: every used slot (and every unused one) against the oracle's copy
     plan = o["plan"]
     n = w.expert_elems
     main_w = torch.randint(-32768, 32767, (w.E, n), dtype=torch.int16, device=DEV)
     slot_w = torch.zeros(w.R, w.S, n, dtype=torch.int16, device=DEV)
     U.stage_replica_weights(U.STAGE_WEIGHTS, w.R, w.E, w.S, g["plan"]["slot_expert"].contiguous(),
                             n, main_w=main_w, slot_w=slot_w)
-    se = plan["slot_expert"]
-    used = [(r_, s_) for r_ in range(w.R) for s_ in range(w.S) if se[r_, s_] >= 0]
-    for (r_, s_) in used[:3]:
-        assert torch.equal(slot_w[r_, s_], main_w[int(se[r_, s_])])
-    for r_ in range(w.R):
-        for s_ in range(w.S):
-            if se[r_, s_] < 0:
-                assert int((slot_w[r_, s_] != 0).sum()) == 0
+    main_h = host(main_w).view(np.uint16)          # 4.5 GiB: experts past 2^32 bytes included
+    slot_o = np.zeros((w.R, w.S, n), dtype=np.uint16)
+    O.stage_forward(plan["slot_expert"], main_h, slot_o)
+    assert np.array_equal(host(slot_w).view(np.uint16), slot_o)
+    say(f"staged slots compared: {int((plan['slot_expert'] >= 0).sum())} of {w.R * w.S}")
     del main_w, slot_w
 
 
@@ -641,7 +635,8 @@ def test_grad_reduce_qwen_layer_full_size():
 def test_waterfill_layer_full_size():
     """DeepSeek-V3-shaped layer with Waterfill: H, S_r and every token's shared rank
     bit-exact; the fused layout (K+1 columns) through load matrix, identity quotas,
-    reroute and assignment bit-exact; permute sampled."""
+    reroute and assignment bit-exact; the whole group's permute compared on every row,
+    and one rank's share with every other row left untouched."""
     w = W.DSV3_WATERFILL
     say("case: waterfill full size", w)
     ids = W.routing(w)
@@ -682,18 +677,25 @@ def test_waterfill_layer_full_size():
     assert np.array_equal(host(q), q_o)
     assert np.array_equal(host(xfer), X_o) and np.array_equal(host(ioff), io_o)
     assert np.array_equal(host(di), di_o) and np.array_equal(host(dr), dr_o)
-    # permute one rank's share of the fused layout (K+1 rows per token)
+    # the whole group's permute of the fused layout (K+1 rows per token, 31.5 GiB):
+    # every dispatch row compared, and row_src whole
     P = int(c2_o.sum())
     gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
     x = torch.randn(w.R, w.T, w.H, generator=gen, device=DEV).to(torch.bfloat16)
-    out = torch.zeros(P, w.H, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(P, w.H, dtype=torch.bfloat16, device=DEV)
+    row_src = torch.empty(P, dtype=torch.int32, device=DEV)
+    U.permute(x, dr, out, row_src)
+    torch.cuda.synchronize()
+    src_o = compare_dispatch_rows(x, out, dr_o)
+    assert np.array_equal(host(row_src), src_o)
+    # one rank's share into a zeroed buffer: its rows exactly, nothing else written
+    out.zero_()
     r = 9
     U.permute(x, dr, out, None, r_begin=r, r_end=r + 1)
-    rows = np.sort(dr_o[r].reshape(-1))[::37]
-    xh = host(x.view(torch.int16)).view(np.uint16)
-    exp, _ = O.permute_rows(xh, dr_o, rows)
-    got = host(out.view(torch.int16)[torch.from_numpy(rows).to(DEV)]).view(np.uint16)
-    assert np.array_equal(got, exp)
+    torch.cuda.synchronize()
+    dr_r = np.full_like(dr_o, -1)
+    dr_r[r] = dr_o[r]
+    compare_dispatch_rows(x, out, dr_r)
 
 
 @pytest.mark.parametrize("seed", range(4))

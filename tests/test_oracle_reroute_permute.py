@@ -165,6 +165,23 @@ def test_permute_matches_fancy_index():
     bad[0, 1, 0] = bad[0, 0, 0]
     with pytest.raises(ValueError):
         O.permute(x, bad, 0, w.R, w.P)
+    # the row-order inverse used by full-size checks: the same map as the pair loop's,
+    # and the same rows block by block
+    assert np.array_equal(O.row_sources(dr, w.P), row_src)
+    assert np.array_equal(np.concatenate([O.rows_of(x, row_src, w.K, a, min(w.P, a + 1000))
+                                          for a in range(0, w.P, 1000)]), out)
+    assert np.array_equal(O.rows_of(x, rs1, w.K, 0, w.P), out1)
+    with pytest.raises(ValueError):
+        O.row_sources(bad, w.P)
+    with pytest.raises(ValueError):
+        O.row_sources(dr, w.P - 1)
+
+
+def test_row_sources_hand_example():
+    """One rank, two tokens, top-2, an empty slot, a buffer of four rows: pair 0 -> row 2,
+    pair 1 empty, pair 2 -> row 0, pair 3 -> row 1; row 3 is targeted by no pair."""
+    dr = np.array([[[2, -1], [0, 1]]])
+    assert O.row_sources(dr, 4).tolist() == [2, 3, 0, -1]
 
 
 def test_slot_memory_arithmetic():
