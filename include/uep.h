@@ -122,6 +122,22 @@ uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_t T, int32_
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * uep_load_matrix_noalloc -- uep_load_matrix without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, outputs and errors as
+ * uep_load_matrix minus ws / ws_bytes; the chunk histograms live in an 8 MiB array the
+ * library holds on each GPU it runs on, until the process ends.  Geometries whose
+ * uep_load_matrix_workspace_size() exceeds 8 MiB return UEP_EWORKSPACE (the layers
+ * here need 0.5-5 MiB).  All calls on one GPU share that array: calls that overlap on
+ * one GPU (several streams or host threads) race and must be ordered by the caller.
+ * Allocates and frees nothing; the first call on a device looks up the array's device
+ * address once (UEP_EHIP if that fails).
+ * ------------------------------------------------------------------------- */
+uep_status uep_load_matrix_noalloc(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                                   int32_t E, int32_t* counts, int32_t* bucket_pos,
+                                   int32_t* err, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_solve_quota -- joint replica placement and quota solve.
  * [UEP] section "Quota 同时决定专家副本与 token 分流": a quota is the token load an
  * expert instance receives after rerouting; each search step may instantiate a

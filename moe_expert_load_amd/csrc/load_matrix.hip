@@ -17,6 +17,8 @@
 //   (match-any), lm_fix adds the earlier chunks' counts.
 // Counts only (no bucket_pos): lm_hist, then lm_counts sums each rank's chunks.
 // Pairs of one expert are ranked in token order: ids are distinct inside a token.
+#include <mutex>
+
 #include "common.h"
 
 namespace uep {
@@ -593,4 +595,49 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
                      (const int32_t*)ws, counts, err, g);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
+}
+
+// ---------------------------------------------------------------------------------
+// uep_load_matrix_noalloc: the same call with its chunk histograms in a library-owned
+// device array instead of a caller workspace, for callers that cannot allocate.
+//
+// `scratch` is a file-scope device array: each GPU the library runs on holds its own
+// copy until the process ends.  Its device address is looked up once per device, with
+// that device current, on the first call there (hipGetSymbolAddress); the host-side
+// name of the array is only a stand-in and is never handed to a kernel.  Every call on
+// one GPU shares that GPU's array, so calls that overlap on one GPU (two streams, or
+// two host threads) race on it.  The kernels write every histogram they read before
+// reading it, so nothing needs clearing between calls.
+namespace uep {
+constexpr size_t kLmScratchBytes = 8u << 20;
+constexpr int kLmMaxDevices = 64;
+}  // namespace uep
+
+static __device__ __align__(256) int32_t scratch[uep::kLmScratchBytes / sizeof(int32_t)];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[uep::kLmMaxDevices] = {};
+}  // namespace
+
+extern "C" uep_status uep_load_matrix_noalloc(const int32_t* topk_ids, int32_t R, int32_t T,
+                                              int32_t K, int32_t E, int32_t* counts,
+                                              int32_t* bucket_pos, int32_t* err, void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || E <= 0) return UEP_EINVAL;
+  const size_t need = uep_load_matrix_workspace_size(R, T, K, E);
+  if (need > kLmScratchBytes) return UEP_EWORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kLmMaxDevices) return UEP_EHIP;
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return UEP_EHIP;
+      g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return uep_load_matrix(topk_ids, R, T, K, E, counts, bucket_pos, err, ptr, kLmScratchBytes,
+                         stream);
 }

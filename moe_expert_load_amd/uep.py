@@ -38,6 +38,7 @@ SIGNATURES = {
     "uep_device_fill": (_I, [_P, _I64, ctypes.c_uint32, _P]),
     "uep_load_matrix_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "uep_load_matrix": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "uep_load_matrix_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "uep_solve_quota": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "uep_identity_quota": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "uep_reroute_workspace_size": (_SZ, [_I, _I, _I]),
@@ -147,6 +148,25 @@ def load_matrix(topk_ids, E, counts=None, bucket_pos=None, err=None, ws=None, st
     _check(LIB.uep_load_matrix(_p(topk_ids), R, T, K, E, _p(counts), _p(bucket_pos), _p(err),
                                _p(ws), ws.numel() * ws.element_size(), _s(stream)),
            "uep_load_matrix")
+    return counts, bucket_pos
+
+
+def load_matrix_noalloc(topk_ids, E, counts=None, bucket_pos=None, err=None, stream=None,
+                        counts_only=False):
+    """uep_load_matrix_noalloc: as load_matrix, with the library's own per-device scratch
+    instead of a workspace (pass counts / bucket_pos to allocate nothing here either)."""
+    _i32(topk_ids, "topk_ids")
+    R, T, K = topk_ids.shape
+    counts = _new((R, E), topk_ids) if counts is None else _buf(counts, R * E, "counts")
+    if counts_only:
+        bucket_pos = None
+    elif bucket_pos is None:
+        bucket_pos = _new((R, T, K), topk_ids)
+    else:
+        _buf(bucket_pos, R * T * K, "bucket_pos")
+    _buf(err, 1, "err")
+    _check(LIB.uep_load_matrix_noalloc(_p(topk_ids), R, T, K, E, _p(counts), _p(bucket_pos),
+                                       _p(err), _s(stream)), "uep_load_matrix_noalloc")
     return counts, bucket_pos
 
 
