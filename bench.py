@@ -589,6 +589,58 @@ def cpu_baseline_lplb(w, ids, x_host, inst, ipr, rank_sample=4, runs=3):
     return _cpu_line(w.N / total, t, sample, host)
 
 
+@_one_thread
+def cpu_baseline_sweep(w, routings, layers=(0, 1, 2, 3), runs=1):
+    """The oracle, one thread, on a sample of the sweep's layers: forward (load matrix,
+    solve, reroute + assignment, whole-group permute, staging of the layer's slots into
+    one shared slot set) and backward (staging again, gradient reduction) per layer;
+    per-layer medians and the 94-layer sum scaled from the sample."""
+    import oracle as O
+    host = host_cpu()
+    n = w.expert_elems
+    rng = np.random.default_rng(9)
+    x_host = rng.integers(0, 1 << 16, (w.R, w.T, w.H), dtype=np.uint16)
+    slot_w = np.zeros((w.R, w.S, n), dtype=np.uint16)
+    slot_g = np.zeros((w.R, w.S, n), dtype=np.float32)
+    fwd, bwd, cached = [], [], []
+    for l in layers:
+        t0 = time.perf_counter()
+        ids = routings[l]
+        counts, bp = O.load_matrix(ids, w.E)
+        plan = O.solve_quota(counts, w.S, w.q_min)
+        ie, ipr = plan["inst_expert"], plan["inst_per_rank"]
+        X, io, so = O.reroute(counts, ie, plan["inst_quota"], ipr)
+        _, dr = O.assign(ids, bp, X, ie, ipr, io, so)
+        O.permute(x_host, dr, 0, w.R, w.P)
+        se = plan["slot_expert"]
+        rep = sorted(set(int(e) for e in se.reshape(-1) if e >= 0))
+        remap = {e: i for i, e in enumerate(rep)}
+        se_c = np.vectorize(lambda e: remap.get(int(e), -1))(se).astype(np.int64)
+        main_w = rng.integers(0, 1 << 16, (len(rep), n), dtype=np.uint16)
+        t1 = time.perf_counter()
+        O.stage_forward(se_c, main_w, slot_w)
+        fwd.append(time.perf_counter() - t1 + (t1 - t0))
+        cached.append((se_c, main_w, len(rep)))
+    for se_c, main_w, nrep in reversed(cached):
+        main_g = rng.standard_normal((nrep, n), dtype=np.float32)
+        slot_g[se_c >= 0] = 1.0
+        t0 = time.perf_counter()
+        O.stage_forward(se_c, main_w, slot_w)
+        O.grad_reduce(se_c, main_g, slot_g, w.E_loc)
+        bwd.append(time.perf_counter() - t0)
+    f, b = np.array(fwd), np.array(bwd)
+    per_layer = float(np.median(f + b[::-1]))
+    total = (f.sum() + b.sum()) * w.layers / len(layers)
+    t = {"fwd_layer_p50": float(np.median(f)), "fwd_layer_max": float(f.max()),
+         "bwd_layer_p50": float(np.median(b)), "bwd_layer_max": float(b.max()),
+         "sweep_scaled_from_sample": total}
+    sample = (f"layers {list(layers)} of {w.layers}, forward in order then backward in reverse "
+              f"through one shared slot set, once each: forward {f.sum():.2f} s, backward "
+              f"{b.sum():.2f} s; the {w.layers}-layer sum scaled from the sample is {total:.1f} s; "
+              f"Python+numpy, BLAS/OpenMP pinned to one thread")
+    return _cpu_line(w.N * w.layers / total, t, sample, host), per_layer
+
+
 # ----------------------------------------------------------------------------- workloads
 def bench_layer(args, torch, U, W, w, with_cpu):
     """UltraEP layer: plan + staging + whole-group permute."""
@@ -923,6 +975,9 @@ def bench_sweep(args, torch, U, W, w):
                     {"layers": w.layers, "weight_sets_cycled": pool, "zipf_s": "0.8+0.6U per layer"})
     out["roofline"] = None
     out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"], _ = cpu_baseline_sweep(w, routings)
     out["extra"] = {"fwd_us_sum": float(f.sum() / args.steps), "fwd_us_p50": float(np.percentile(f, 50)),
                     "fwd_us_p99": float(np.percentile(f, 99)),
                     "bwd_us_sum": float(b.sum() / args.steps), "bwd_us_p50": float(np.percentile(b, 50)),
