@@ -128,6 +128,8 @@ class Layer:
         self.drow = torch.empty(R, T, K, **i32)
         self.rr_ws = torch.empty(max(U.reroute_workspace_size(R, E, self.ipr), 4),
                                  dtype=torch.uint8, device=DEV)
+        self.plan_ws = torch.empty(max(U.plan_workspace_size(R, T, K, E, max(w.S, 0)), 4),
+                                   dtype=torch.uint8, device=DEV)
         gen = torch.Generator(device=DEV).manual_seed(W.tensor_seed(w, 0, 0))
         self.x = torch.randn(R, T, H, generator=gen, device=DEV, dtype=torch.bfloat16)
         self.P = R * T * K
@@ -162,6 +164,16 @@ class Layer:
                        r_begin, r_end, s)
 
     def plan_step(self, s, r_begin=0, r_end=None):
+        """The layer's plan in one uep_plan call (the solve overlapped with the ranking)."""
+        out = {"counts": self.counts, "bucket_pos": self.bp, "xfer": self.xfer,
+               "inst_offset": self.ioff, "dest_inst": self.dinst, "dest_row": self.drow,
+               **{k: self.plan[k] for k in ("slot_expert", "inst_expert", "inst_quota",
+                                            "rank_load", "stats")}}
+        self.U.plan(self.ids, self.E, self.w.S, self.w.q_min, r_begin, r_end, out, None,
+                    self.plan_ws, s)
+
+    def plan_separate(self, s, r_begin=0, r_end=None):
+        """The same plan as three calls: load matrix, quota solve, reroute/assignment."""
         self.load(s)
         self.solve(s)
         self.reroute(s, r_begin, r_end)
@@ -698,6 +710,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
 
     rank_us = graph_us(torch, rank_share, reps=w.R, replays=2, indexed=True)
     plan_us = graph_us(torch, lambda s: L.plan_step(s))
+    plan_sep_us = graph_us(torch, lambda s: L.plan_separate(s))
     stage_kernel_us = graph_us(torch, lambda s: L.stage(s), reps=5)
     perm_rank_us = graph_us(torch, lambda s, i: L.permute(s, i % w.R, i % w.R + 1, row_src=False),
                             reps=w.R, replays=2, indexed=True)
@@ -723,6 +736,7 @@ def bench_layer(args, torch, U, W, w, with_cpu):
     out["extra"] = {
         "us_per_layer_rank_share": rank_us,
         "plan_us": plan_us,
+        "plan_three_calls_us": plan_sep_us,
         "permute_rank_us": perm_rank_us,
         "permute_rank_gbs": rank_bytes / (perm_rank_us * 1e-6) / 1e9,
         "stage_ms": stage_ms,

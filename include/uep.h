@@ -221,6 +221,26 @@ uep_status uep_reroute_assign(const int32_t* counts, const int32_t* topk_ids,
                               void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * uep_plan -- uep_load_matrix, uep_solve_quota and uep_reroute_assign of one layer in
+ * one call ([UEP] sections "在 Gate 之后获取当前层真实负载" and "Quota 同时决定专家副本与
+ * token 分流": the solve sits on the forward critical path between the Gate and the
+ * dispatch).  Outputs and errors are those of the three calls, bit for bit; the solve
+ * runs on the finished load matrix concurrently with the bucket-position ranking,
+ * which it does not need.  Arguments are the union of the three calls' (S, q_min as
+ * uep_solve_quota; r_begin / r_end restrict the assignment as in uep_reroute_assign;
+ * inst_per_rank = E / R + S); ws is one workspace of uep_plan_workspace_size() bytes.
+ * Geometries off the ranking fast path (E > 1024 or K > 16) run the three calls in
+ * sequence.
+ * ------------------------------------------------------------------------- */
+size_t uep_plan_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E, int32_t S);
+uep_status uep_plan(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K, int32_t E,
+                    int32_t S, int32_t q_min, int32_t r_begin, int32_t r_end, int32_t* counts,
+                    int32_t* bucket_pos, int32_t* slot_expert, int32_t* inst_expert,
+                    int32_t* inst_quota, int32_t* rank_load, int32_t* stats, int32_t* xfer,
+                    int32_t* inst_offset, int32_t* dest_inst, int32_t* dest_row, int32_t* err,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_permute -- scatter token activations into the per-instance dispatch buffer.
  * [UEP] section "流式通信算子加速动态权重分发": once replica weights are in place,
  * token dispatch follows the reroute plan; this is its on-device permutation.

@@ -17,9 +17,11 @@
 //   (match-any), lm_fix adds the earlier chunks' counts.
 // Counts only (no bucket_pos): lm_hist, then lm_counts sums each rank's chunks.
 // Pairs of one expert are ranked in token order: ids are distinct inside a token.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
+#include "solve_quota.h"
 
 namespace uep {
 
@@ -182,19 +184,20 @@ __global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist,
 constexpr int kLmTileLd = 16;                          // flat loads per thread: 4096 ids
 constexpr size_t kLmTileMaxLds = 64 * 1024;            // tiles only while the LDS fits 64 KiB
 
+// The ranking of chunk c of rank r by one 256-thread workgroup (lr_lds: the dynamic LDS
+// the launch sizes); counts may be NULL when the load matrix is already written.
 template <int kMaxK, bool kTile>
-__global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
-                                               int32_t* __restrict__ bucket_pos,
-                                               const int32_t* __restrict__ chunk_hist,
-                                               int32_t* __restrict__ counts, int32_t* err,
-                                               LmGeom g, bool vec, bool scanned) {
-  extern __shared__ uint64_t lr_lds[];
+__device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
+                                             int32_t* __restrict__ bucket_pos,
+                                             const int32_t* __restrict__ chunk_hist,
+                                             int32_t* __restrict__ counts, int32_t* err,
+                                             const LmGeom& g, bool vec, bool scanned, int c,
+                                             int r, uint64_t* lr_lds) {
   uint64_t* mask = lr_lds;                                             // [4][E]
   int32_t* whist = reinterpret_cast<int32_t*>(lr_lds + 4 * g.E);       // [4][E]
   int32_t* pre = whist + 4 * g.E;                                      // [E]
   int32_t* idt = pre + g.E;                        // kTile: [tok_per_chunk * K] ids
   int32_t* pt = idt + g.tok_per_chunk * g.K;       // kTile: [tok_per_chunk * K] positions
-  const int r = blockIdx.y, c = blockIdx.x;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
   const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
       whist[ww * g.E + e] = run;
       run += x;
     }
-    if (c == g.n_chunks - 1) counts[(int64_t)r * g.E + e] = run;
+    if (counts && c == g.n_chunks - 1) counts[(int64_t)r * g.E + e] = run;
   }
   __syncthreads();
   // pass 2: final positions, and the check for an expert twice in one token
@@ -380,6 +383,39 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += 256) bucket_pos[chunk_base + i] = pt[i];
   }
+}
+
+template <int kMaxK, bool kTile>
+__global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
+                                               int32_t* __restrict__ bucket_pos,
+                                               const int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts, int32_t* err,
+                                               LmGeom g, bool vec, bool scanned) {
+  extern __shared__ uint64_t lr_lds[];
+  lm_rank_body<kMaxK, kTile>(ids, bucket_pos, chunk_hist, counts, err, g, vec, scanned,
+                             blockIdx.x, blockIdx.y, lr_lds);
+}
+
+// Fused plan launch: block 0 runs the quota solve on the load matrix that the launch
+// before it finished (the solve needs the counts only), while blocks 1.. rank the
+// chunks as lm_rank does.  The solve is one workgroup's dependent chain, several times
+// longer than the ranking, so the ranking costs the plan no time of its own.
+template <int kMaxK, bool kTile, int kS>
+__global__ __launch_bounds__(256) void plan_rank_solve(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ bucket_pos,
+    const int32_t* __restrict__ chunk_hist, int32_t* err, LmGeom g, bool vec, bool scanned,
+    const int32_t* __restrict__ counts, int S, int q_min, int32_t* __restrict__ slot_expert,
+    int32_t* __restrict__ inst_expert, int32_t* __restrict__ inst_quota,
+    int32_t* __restrict__ rank_load, int32_t* __restrict__ stats) {
+  extern __shared__ uint64_t pl_lds[];
+  if (blockIdx.x == 0) {
+    solve_body<kS>(counts, g.R, g.E, S, q_min, slot_expert, inst_expert, inst_quota, rank_load,
+                   stats, reinterpret_cast<int32_t*>(pl_lds));
+    return;
+  }
+  const int b = (int)blockIdx.x - 1;
+  lm_rank_body<kMaxK, kTile>(ids, bucket_pos, chunk_hist, nullptr, err, g, vec, scanned,
+                             b % g.n_chunks, b / g.n_chunks, pl_lds);
 }
 
 __global__ __launch_bounds__(kLmThreads) void lm_chunk(const int32_t* __restrict__ ids,
@@ -595,6 +631,102 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
                      (const int32_t*)ws, counts, err, g);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
+}
+
+// ---------------------------------------------------------------------------------
+// uep_plan: uep_load_matrix, uep_solve_quota and uep_reroute_assign in one call, with
+// the solve overlapped with the ranking.  Launches: lm_hist, lm_counts (the load
+// matrix), lm_scan for long ranks, plan_rank_solve (solve || ranking), then the
+// reroute and assignment of uep_reroute_assign.  Geometries off the ranking fast path
+// (E > 1024 or K > 16) run the three calls one after the other instead.
+static size_t plan_align(size_t b) { return (b + 255) / 256 * 256; }
+
+extern "C" size_t uep_plan_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E, int32_t S) {
+  if (R <= 0 || T < 0 || K <= 0 || E <= 0 || S < 0 || E % R != 0) return 0;
+  return plan_align(uep_load_matrix_workspace_size(R, T, K, E)) +
+         uep_reroute_workspace_size(R, E, E / R + S);
+}
+
+extern "C" uep_status uep_plan(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                               int32_t E, int32_t S, int32_t q_min, int32_t r_begin,
+                               int32_t r_end, int32_t* counts, int32_t* bucket_pos,
+                               int32_t* slot_expert, int32_t* inst_expert, int32_t* inst_quota,
+                               int32_t* rank_load, int32_t* stats, int32_t* xfer,
+                               int32_t* inst_offset, int32_t* dest_inst, int32_t* dest_row,
+                               int32_t* err, void* ws, size_t ws_bytes, void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || E <= 0 || S < 0 || q_min < 0) return UEP_EINVAL;
+  if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
+  if (R > 64 || K > 64 || E > 4096 || E % R != 0 || E / R > 64 || S > kSqMaxS ||
+      (int64_t)R * T * K >= (1ll << 31))
+    return UEP_EGEOM;
+  // every check of the three calls, before anything is enqueued
+  if (!counts || !inst_expert || !inst_quota || !rank_load || !stats || !xfer || !inst_offset ||
+      (S > 0 && !slot_expert) || (T > 0 && (!topk_ids || !bucket_pos)) ||
+      (T > 0 && r_end > r_begin && (!dest_inst || !dest_row)))
+    return UEP_EINVAL;
+  if ((int64_t)R * (E / R + S) > (1 << 20)) return UEP_EGEOM;
+  if (!ws || ws_bytes < uep_plan_workspace_size(R, T, K, E, S)) return UEP_EWORKSPACE;
+  const size_t lm_bytes = plan_align(uep_load_matrix_workspace_size(R, T, K, E));
+  void* rr_ws = static_cast<char*>(ws) + lm_bytes;
+  const size_t rr_bytes = ws_bytes - lm_bytes;
+  const int ipr = E / R + S;
+  if (!lm_bitmap(K, E) || T == 0) {
+    uep_status st = uep_load_matrix(topk_ids, R, T, K, E, counts, bucket_pos, err, ws, lm_bytes,
+                                    stream);
+    if (st == UEP_OK)
+      st = uep_solve_quota(counts, R, E, S, q_min, slot_expert, inst_expert, inst_quota,
+                           rank_load, stats, stream);
+    if (st == UEP_OK)
+      st = uep_reroute_assign(counts, topk_ids, bucket_pos, R, T, K, E, ipr, inst_expert,
+                              inst_quota, r_begin, r_end, xfer, inst_offset, dest_inst, dest_row,
+                              err, rr_ws, rr_bytes, stream);
+    return st;
+  }
+  LmGeom g = lm_geom(R, T, K, E);
+  hipStream_t s = uep_stream(stream);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(lm_hist, dim3(g.n_chunks, R), dim3(256), sizeof(int32_t) * E, s, topk_ids,
+                     hist, err, g);
+  UEP_CHECK_LAUNCH();
+  hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
+  UEP_CHECK_LAUNCH();
+  const int per = E >= 256 ? 1 : 256 / E;
+  const bool scanned = g.n_chunks > 16 * per;
+  if (scanned) {
+    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, g);
+    UEP_CHECK_LAUNCH();
+  }
+  const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(bucket_pos) % 16 == 0;
+  const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
+  const size_t lds_tile = lds + sizeof(int32_t) * 2 * (size_t)g.tok_per_chunk * K;
+  const bool tile = !vec && lds_tile <= kLmTileMaxLds;
+  const size_t sh = std::max(tile ? lds_tile : lds, sizeof(int32_t) * (size_t)E);
+  const dim3 grid(1 + g.n_chunks * R);
+#define UEP_PLAN_FUSED(KM, TL, KS)                                                              \
+  hipLaunchKernelGGL((plan_rank_solve<KM, TL, KS>), grid, dim3(256), sh, s, topk_ids, bucket_pos, \
+                     (const int32_t*)hist, err, g, vec, scanned, (const int32_t*)counts, S, q_min, \
+                     slot_expert, inst_expert, inst_quota, rank_load, stats)
+#define UEP_PLAN_S(KM, TL)                        \
+  do {                                            \
+    if (S <= 1) UEP_PLAN_FUSED(KM, TL, 1);        \
+    else if (S <= 2) UEP_PLAN_FUSED(KM, TL, 2);   \
+    else if (S <= 4) UEP_PLAN_FUSED(KM, TL, 4);   \
+    else UEP_PLAN_FUSED(KM, TL, 8);               \
+  } while (0)
+  if (K <= 8) {
+    if (tile) UEP_PLAN_S(8, true); else UEP_PLAN_S(8, false);
+  } else if (K <= 12) {
+    if (tile) UEP_PLAN_S(12, true); else UEP_PLAN_S(12, false);
+  } else {
+    if (tile) UEP_PLAN_S(16, true); else UEP_PLAN_S(16, false);
+  }
+#undef UEP_PLAN_S
+#undef UEP_PLAN_FUSED
+  UEP_CHECK_LAUNCH();
+  return uep_reroute_assign(counts, topk_ids, bucket_pos, R, T, K, E, ipr, inst_expert, inst_quota,
+                            r_begin, r_end, xfer, inst_offset, dest_inst, dest_row, err, rr_ws,
+                            rr_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------

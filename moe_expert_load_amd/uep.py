@@ -44,6 +44,9 @@ SIGNATURES = {
     "uep_reroute_workspace_size": (_SZ, [_I, _I, _I]),
     "uep_reroute_assign": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "uep_plan_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "uep_plan": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                      _P, _P, _P, _SZ, _P]),
     "uep_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P, _P, _P]),
     "uep_combine": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "uep_stage_replica_weights": (_I, [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
@@ -235,6 +238,40 @@ def reroute_assign(counts, topk_ids, bucket_pos, inst_per_rank, inst_expert, ins
                                   _p(err), _p(ws), ws.numel() * ws.element_size(), _s(stream)),
            "uep_reroute_assign")
     return xfer, inst_offset, dest_inst, dest_row
+
+
+def plan_workspace_size(R, T, K, E, S) -> int:
+    return int(LIB.uep_plan_workspace_size(R, T, K, E, S))
+
+
+def plan(topk_ids, E, S, q_min, r_begin=0, r_end=None, out=None, err=None, ws=None, stream=None):
+    """uep_plan: load matrix, quota solve and reroute/assignment in one call.  `out` may
+    hold preallocated buffers under the keys below; returns that dict."""
+    _i32(topk_ids, "topk_ids")
+    R, T, K = topk_ids.shape
+    r_end = R if r_end is None else r_end
+    ipr = E // R + S
+    I = R * ipr
+    shapes = {"counts": (R, E), "bucket_pos": (R, T, K), "slot_expert": (R, max(S, 1)),
+              "inst_expert": (I,), "inst_quota": (I,), "rank_load": (R,), "stats": (4,),
+              "xfer": (R, I), "inst_offset": (I + 1,), "dest_inst": (R, T, K),
+              "dest_row": (R, T, K)}
+    o = {} if out is None else dict(out)
+    for k, shp in shapes.items():
+        n = 1
+        for d in shp:
+            n *= d
+        o[k] = _new(shp, topk_ids) if o.get(k) is None else _buf(o[k], n, k)
+    _buf(err, 1, "err")
+    need = plan_workspace_size(R, T, K, E, S)
+    ws = _new((max(need, 4),), topk_ids, torch.uint8) if ws is None else ws
+    _check(LIB.uep_plan(_p(topk_ids), R, T, K, E, S, q_min, r_begin, r_end, _p(o["counts"]),
+                        _p(o["bucket_pos"]), _p(o["slot_expert"]), _p(o["inst_expert"]),
+                        _p(o["inst_quota"]), _p(o["rank_load"]), _p(o["stats"]), _p(o["xfer"]),
+                        _p(o["inst_offset"]), _p(o["dest_inst"]), _p(o["dest_row"]), _p(err),
+                        _p(ws), ws.numel() * ws.element_size(), _s(stream)), "uep_plan")
+    o["inst_per_rank"] = ipr
+    return o
 
 
 def permute(x, dest_row, out, row_src=None, r_begin=0, r_end=None, stream=None, err=None):

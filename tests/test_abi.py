@@ -111,6 +111,21 @@ def test_host_side_calls_without_gpu(lib):
     assert lib.uep_device_fill(null, i64(32), u32(7), null) == 1
     assert lib.uep_device_fill(fake_a, i64(24), u32(7), null) == 2
     assert lib.uep_device_fill(ctypes.c_void_p(4100), i64(32), u32(7), null) == 2
+    # the fused plan: workspace = load matrix + reroute workspaces; host checks first
+    lib.uep_plan_workspace_size.restype = ctypes.c_size_t
+    wp = lib.uep_plan_workspace_size(32, 8192, 8, 128, 1)
+    assert wp >= big + lib.uep_reroute_workspace_size(32, 128, 5)
+    assert lib.uep_plan_workspace_size(3, 16, 2, 7, 1) == 0             # E % R != 0
+    plan_args = [null] * 12 + [null, ctypes.c_size_t(0), null]      # 12 outputs + err, ws
+    assert lib.uep_plan(null, i32(3), i32(16), i32(2), i32(7), i32(1), i32(1), i32(0), i32(3),
+                        *plan_args) == 2
+    assert lib.uep_plan(null, i32(4), i32(16), i32(2), i32(8), i32(1), i32(1), i32(0), i32(5),
+                        *plan_args) == 1
+    assert lib.uep_plan(null, i32(4), i32(16), i32(2), i32(8), i32(1), i32(1), i32(0), i32(4),
+                        *plan_args) == 1
+    fake = ctypes.c_void_p(4096)
+    assert lib.uep_plan(fake, i32(4), i32(16), i32(2), i32(8), i32(1), i32(1), i32(0), i32(4),
+                        *([fake] * 12), fake, ctypes.c_size_t(16), null) == 3
 
 
 C_PROGRAM = r"""

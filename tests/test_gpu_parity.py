@@ -856,3 +856,53 @@ def test_path_in_a_captured_graph_replays():
         assert np.array_equal(host(slot_w).view(np.uint16), sw_exp), rep
         y_exp = O.combine(exp_out, o["dest_row"], g)
         assert np.array_equal(host(y.view(torch.int16)).view(np.uint16), y_exp), rep
+
+
+# (R, T, K, E, S, q_min): every slot-count instantiation of the fused launch, the three
+# top-k bounds with and without the LDS tile (K % 4), long ranks whose chunk
+# histograms are scanned in place, the large-E path that runs the calls in sequence,
+# one rank, and an empty layer
+FUSED_PLAN_GEOMS = [(4, 512, 2, 8, 1, 32), (8, 700, 8, 64, 2, 20), (16, 3000, 6, 128, 4, 50),
+                    (5, 1000, 10, 40, 8, 5), (6, 800, 12, 48, 2, 3), (7, 900, 14, 70, 3, 0),
+                    (4, 600, 16, 64, 1, 2), (4, 4500, 8, 256, 2, 10), (32, 300, 16, 2048, 1, 1),
+                    (1, 100, 4, 16, 2, 1), (4, 0, 2, 8, 1, 1)]
+
+
+@pytest.mark.parametrize("geom", FUSED_PLAN_GEOMS, ids=[str(g) for g in FUSED_PLAN_GEOMS])
+def test_plan_fused_matches_the_separate_calls_and_the_oracle(geom):
+    """uep_plan (load matrix, solve overlapped with the ranking, reroute/assignment in
+    one call) gives the oracle's plan bit for bit, and the same bits as the three
+    separate calls; with a rank range it assigns exactly that range."""
+    R, T, K, E, S, q_min = geom
+    rng = np.random.default_rng(sum(geom) * 7 + 1)
+    say(f"case: fused plan R={R} T={T} K={K} E={E} S={S} q_min={q_min}")
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
+    o = oracle_plan(ids, E, S, q_min)
+    ids_d = to_dev(ids)
+    err = err_word()
+    f = U.plan(ids_d, E, S, q_min, err=err)
+    compare_plan({**f, "plan": f, "err": err}, o, S)
+    g = plan_on_gpu(U, ids_d, E, S, q_min)
+    for k in ("counts", "bucket_pos", "xfer", "inst_offset", "dest_inst", "dest_row"):
+        assert torch.equal(f[k], g[k]), k
+    for k in ("inst_expert", "inst_quota", "rank_load", "stats"):
+        assert torch.equal(f[k], g["plan"][k]), k
+    if R > 1 and T > 0:
+        r0 = R // 2
+        keep = {k: torch.full_like(f[k], -7) for k in ("dest_inst", "dest_row")}
+        f2 = U.plan(ids_d, E, S, q_min, r_begin=r0, r_end=r0 + 1, out=keep)
+        dr, di = host(f2["dest_row"]), host(f2["dest_inst"])
+        assert np.array_equal(dr[r0], o["dest_row"][r0]) and np.array_equal(di[r0], o["dest_inst"][r0])
+        others = np.arange(R) != r0
+        assert (dr[others] == -7).all() and (di[others] == -7).all()
+
+
+def test_plan_fused_qwen_layer_full_size():
+    """The fused plan at the Qwen3-235B layer's size, against the oracle."""
+    w = W.QWEN_LAYER
+    say("case: fused plan, qwen layer full size", w)
+    ids = W.routing(w)
+    o = oracle_plan(ids, w.E, w.S, w.q_min)
+    err = err_word()
+    f = U.plan(to_dev(ids), w.E, w.S, w.q_min, err=err)
+    compare_plan({**f, "plan": f, "err": err}, o, w.S)
