@@ -39,7 +39,8 @@ constexpr int kLpMaxG = 128;
 constexpr int kLpMaxN = 256;
 constexpr int kLpMaxE = 4096;
 constexpr int kLpMaxI = 64 * 40;
-constexpr int kLpMagic = 0x4C50424C;
+constexpr int kLpMagic = 0x4C50424D;             // structure layout 2: with lane groups
+constexpr int kLpLanes = 256;                     // lane slots of the block path (one workgroup)
 constexpr float kBigM = 8.0f;
 constexpr float kEta = 0.99f;
 constexpr float kMuStop = 1e-9f;
@@ -59,17 +60,24 @@ constexpr int kLpMaxRows = kLpMaxR + kLpMaxG;
 // (ent_p[k] on r, ent_q[k] on r') for k in [ent_start[e], ent_start[e+1]).
 // exp_inst[e]: instance of a single-copy expert, -2 - g for replicated group g, -1 none
 // inst_copy[i]: copy index of instance i, or -1
+// then: blk | lane_rank[256] | rank_lane[R]
+// blk (0, 8 or 16): the lane-group size of the block solve, 0 for the dense one.  The
+// rank matrix couples two ranks only when a replicated expert has copies on both, so
+// its off-diagonal part splits into connected components; with every component at
+// most blk ranks, the components are packed into 256 / blk groups of blk lanes
+// (first fit, largest first), lane_rank[l] is the rank of lane l (-1: padding) and
+// rank_lane[r] its lane.
 struct LpView {
-  int R, E, ipr, I, G, n, n_ent;
+  int R, E, ipr, I, G, n, n_ent, blk;
   const int32_t *grp_expert, *grp_start, *copy_inst, *copy_rank, *copy_group;
   const int32_t *rank_start, *rank_copy, *exp_inst, *inst_expert, *inst_copy;
-  const int32_t *ent_rr, *ent_start, *ent_p, *ent_q;
+  const int32_t *ent_rr, *ent_start, *ent_p, *ent_q, *lane_rank, *rank_lane;
 };
 
 __host__ __device__ inline size_t lp_words(int R, int E, int I, int G, int n, int n_ent,
                                            int n_pair) {
   return 8 + (size_t)G + (G + 1) + 3 * (size_t)n + (R + 1) + n + E + 2 * (size_t)I +
-         (size_t)n_ent + (n_ent + 1) + 2 * (size_t)n_pair;
+         (size_t)n_ent + (n_ent + 1) + 2 * (size_t)n_pair + 1 + kLpLanes + R;
 }
 
 __device__ inline LpView lp_view(const int32_t* w) {
@@ -90,7 +98,10 @@ __device__ inline LpView lp_view(const int32_t* w) {
   v.ent_start = p; p += v.n_ent + 1;
   const int n_pair = v.ent_start[v.n_ent];
   v.ent_p = p; p += n_pair;
-  v.ent_q = p;
+  v.ent_q = p; p += n_pair;
+  v.blk = *p; p += 1;
+  v.lane_rank = p; p += kLpLanes;
+  v.rank_lane = p;
   return v;
 }
 
@@ -317,7 +328,9 @@ __device__ __forceinline__ double rcp_d(double x) {
   return fma(y, fma(-x, y, 1.0), y);
 }
 
-__device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, LpShared& S) {
+// d = v / z (the diagonal of the normal equations), each group's beta = sum of its
+// copies' d, and the dense coefficient delta = d_M + d_a of the rank matrix's 11^T term.
+__device__ __forceinline__ double lp_scaling(int n, int R, int G, LpShared& S) {
   const int nv = n + R + 2;
   for (int i = threadIdx.x; i < nv; i += kLpThreads) S.d[i] = (double)S.v[i] / (double)S.z[i];
   __syncthreads();
@@ -326,7 +339,37 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
     for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) b += S.d[p];
     S.beta[g] = b;
   }
-  const double delta = S.d[n + R] + S.d[n + R + 1];
+  return S.d[n + R] + S.d[n + R + 1];
+}
+
+// rank r's diagonal entry of the rank matrix without the dense term: its slack's d plus,
+// for each copy p on r, d_p * (the other copies of p's group) / beta, a sum of positive
+// terms (no cancellation)
+__device__ __forceinline__ double lp_rank_diag(int n, int r, const LpShared& S) {
+  double diag = S.d[n + r];
+  for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+    const int p = S.rank_copy[k], g = S.copy_group[p];
+    double others = 0.0;
+    for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
+      if (q != p) others += S.d[q];
+    diag += S.d[p] * (others / S.beta[g]);
+  }
+  return diag;
+}
+
+// an off-diagonal entry of the rank matrix without the dense term is -off: the copy
+// pairs of one group that touch both ranks
+__device__ __forceinline__ double lp_entry_off(int e, const LpView& L, const LpShared& S) {
+  double off = 0.0;
+  for (int k = L.ent_start[e]; k < L.ent_start[e + 1]; ++k) {
+    const int p = L.ent_p[k], q = L.ent_q[k];
+    off += S.d[p] * (S.d[q] / S.beta[S.copy_group[p]]);
+  }
+  return off;
+}
+
+__device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, LpShared& S) {
+  const double delta = lp_scaling(n, R, G, S);
   // every entry starts at the dense M/a term; the matrix is padded to 64 x 64 with
   // identity rows and columns beyond R so the factorization has no bounds tests
   for (int idx = threadIdx.x; idx < kLpMaxR * kLpMaxR; idx += kLpThreads) {
@@ -337,26 +380,13 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
   __syncthreads();
   // diagonal: slack term plus each copy's d_p * (other copies of its group) / beta
   for (int r = threadIdx.x; r < R; r += kLpThreads) {
-    double diag = delta + S.d[n + r];
-    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-      const int p = S.rank_copy[k], g = S.copy_group[p];
-      double others = 0.0;
-      for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
-        if (q != p) others += S.d[q];
-      diag += S.d[p] * (others / S.beta[g]);
-    }
+    const double diag = delta + lp_rank_diag(n, r, S);
     S.P[r][r] = diag;
     S.d0[r] = diag;
   }
   // off-diagonal entries touched by copies of one group on both ranks
-  for (int e = threadIdx.x; e < L.n_ent; e += kLpThreads) {
-    double off = 0.0;
-    for (int k = L.ent_start[e]; k < L.ent_start[e + 1]; ++k) {
-      const int p = L.ent_p[k], q = L.ent_q[k];
-      off += S.d[p] * (S.d[q] / S.beta[S.copy_group[p]]);
-    }
-    S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - off;
-  }
+  for (int e = threadIdx.x; e < L.n_ent; e += kLpThreads)
+    S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - lp_entry_off(e, L, S);
   __syncthreads();
   // Blocked right-looking LDL^T (Cholesky without square roots), panels of kLpPanel
   // columns.  Thread (ti, tk) keeps a 4x4 register tile of the trailing matrix: rows
@@ -447,6 +477,214 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
   }
 }
 
+// ---- block solve of the rank matrix P = B + delta 11^T ---------------------------
+// B (P without its dense term) is block diagonal over the components of the rank
+// coupling graph, packed into groups of kBlk lanes (lane_rank).  Every group factors
+// its block as U diag(p) U^T in registers, one row per lane, the rows broadcast within
+// the group by shuffles; all groups at once.  A solve is then one forward and one
+// backward substitution per group and the rank-one correction of Sherman-Morrison:
+// P^-1 b = v - w (delta 1^T v) / (1 + delta 1^T w), v = B^-1 b, w = B^-1 1, both fp64.
+// Pivots that lost their precision are dropped as in the dense factorization.
+__device__ __forceinline__ double shfl_d(double v, int src) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __shfl((int)(uint32_t)u, src, kWave);
+  const int hi = __shfl((int)(uint32_t)(u >> 32), src, kWave);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+template <int kBlk>
+struct LpBlk {
+  double r[kBlk];        // the lane's row of its block; after factoring, U's strict lower part
+  double dinv, w;        // 1 / pivot (1e-64 for a dropped pivot), and (B^-1 1) on this lane
+  double s1, delta;      // sum of B^-1 1 over the ranks, and delta = d_M + d_a
+  int a, base, rank;     // row in the group, the group's first lane, the rank (-1: padding)
+};
+
+// x = B_g^-1 b on the lane's group (U's columns read back from LDS for the backward pass)
+template <int kBlk>
+__device__ __forceinline__ double lpb_subst(const LpBlk<kBlk>& B, double b, const double* ust) {
+  double z = b;
+#pragma unroll
+  for (int j = 0; j < kBlk; ++j) {                      // U z = b
+    const double zj = shfl_d(z, B.base + j);
+    if (B.a > j) z = fma(-B.r[j], zj, z);
+  }
+  z *= B.dinv;
+  double uc[kBlk];
+#pragma unroll
+  for (int j = 0; j < kBlk; ++j) uc[j] = ust[(B.base + j) * kBlk + B.a];
+#pragma unroll
+  for (int j = kBlk - 1; j >= 0; --j) {                 // U^T x = D^-1 z
+    const double xj = shfl_d(z, B.base + j);
+    if (B.a < j) z = fma(-uc[j], xj, z);
+  }
+  return z;
+}
+
+template <int kBlk>
+__device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, const LpView& L,
+                                           LpShared& S) {
+  B.delta = lp_scaling(n, R, G, S);
+  double* ust = &S.P[0][0];                 // kLpLanes rows of kBlk entries
+  const int t = threadIdx.x;
+  __syncthreads();                          // beta and d complete
+#pragma unroll
+  for (int b = 0; b < kBlk; ++b) ust[t * kBlk + b] = 0.0;
+  ust[t * kBlk + B.a] = B.rank >= 0 ? lp_rank_diag(n, B.rank, S) : 1.0;
+  __syncthreads();
+  for (int e = t; e < L.n_ent; e += kLpThreads) {
+    const double off = -lp_entry_off(e, L, S);
+    const int l1 = L.rank_lane[L.ent_rr[e] / kLpMaxR], l2 = L.rank_lane[L.ent_rr[e] % kLpMaxR];
+    ust[l1 * kBlk + l2 % kBlk] = off;
+    ust[l2 * kBlk + l1 % kBlk] = off;
+  }
+  __syncthreads();
+  double d0 = 0.0;
+#pragma unroll
+  for (int b = 0; b < kBlk; ++b) {
+    B.r[b] = ust[t * kBlk + b];
+    if (b == B.a) d0 = B.r[b];
+  }
+  B.dinv = 0.0;
+#pragma unroll
+  for (int j = 0; j < kBlk; ++j) {
+    const double pj = shfl_d(B.r[j], B.base + j);
+    const double thr = kPivTol * shfl_d(d0, B.base + j);
+    double ajb[kBlk];
+#pragma unroll
+    for (int b = j + 1; b < kBlk; ++b) ajb[b] = shfl_d(B.r[b], B.base + j);
+    const bool bad = !(pj > thr);
+    const double rc = bad ? 0.0 : rcp_d(pj);
+    if (B.a == j) B.dinv = bad ? 1e-64 : rc;
+    if (B.a > j) {
+      const double u = B.r[j] * rc;
+      B.r[j] = u;
+#pragma unroll
+      for (int b = j + 1; b < kBlk; ++b) B.r[b] = fma(-u, ajb[b], B.r[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kBlk; ++b) ust[t * kBlk + b] = b < B.a ? B.r[b] : 0.0;
+  __syncthreads();
+  B.w = lpb_subst<kBlk>(B, B.rank >= 0 ? 1.0 : 0.0, ust);
+  B.s1 = blk_sum(B.rank >= 0 ? B.w : 0.0, S);
+}
+
+// dy = (A D A^T)^{-1} rhs with the block factors (the group rows as in lp_solve)
+template <int kBlk>
+__device__ __forceinline__ void lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G, LpShared& S) {
+  for (int g = threadIdx.x; g < G; g += kLpThreads) S.t64[g] = (double)S.rhs[R + g] / S.beta[g];
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += kLpThreads) {
+    double acc = S.rhs[r];
+    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+      const int p = S.rank_copy[k];
+      acc += S.d[p] * S.t64[S.copy_group[p]];
+    }
+    S.u64[r] = acc;
+  }
+  __syncthreads();
+  const double v = lpb_subst<kBlk>(B, B.rank >= 0 ? S.u64[B.rank] : 0.0, &S.P[0][0]);
+  const double sv = blk_sum(B.rank >= 0 ? v : 0.0, S);
+  const double y = v - B.w * (B.delta * sv / (1.0 + B.delta * B.s1));
+  if (B.rank >= 0) S.u64[B.rank] = y;
+  __syncthreads();
+  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
+    if (i < R) {
+      S.dy[i] = (float)S.u64[i];
+    } else {
+      const int g = i - R;
+      double acc = S.rhs[i];
+      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
+      S.dy[i] = (float)(acc / S.beta[g]);
+    }
+  }
+  __syncthreads();
+}
+
+// The interior-point loop: Mehrotra predictor-corrector from the starting point in S,
+// at most `iters` steps; kBlk = 0 factors the rank matrix densely, kBlk = 8 or 16 uses
+// the block solve over lane groups of that size.  Returns the number of steps run.
+template <int kBlk>
+__device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpView& L,
+                                      LpShared& S) {
+  const int nv = n + R + 2;
+  const int tid = threadIdx.x;
+  int run = 0;
+  LpBlk<(kBlk > 0 ? kBlk : 1)> B;
+  if constexpr (kBlk > 0) {
+    B.a = tid % kBlk;
+    B.base = tid - B.a;
+    B.rank = L.lane_rank[tid];
+  }
+  // Barriers below separate only accesses across threads: a loop over i that reads
+  // what the same thread wrote at index i in the step before needs none.
+  const auto plus_rb = [&](int i, float a) { return a + S.rb[i]; };
+  for (int it = 0; it < iters; ++it) {
+    // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
+    lp_Av([&](int j) { return S.v[j]; },
+          [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, S);
+    lp_ATy(S.y, S.tv, n, R, G, S);
+    double cz = 0.0;
+    for (int i = tid; i < nv; i += kLpThreads) {
+      S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
+      cz += (double)(S.v[i] * S.z[i]);
+    }
+    const double gap = blk_sum(cz, S);
+    const float mu = (float)(gap / nv);
+    // stop once the duality gap, which bounds the objective error of a feasible
+    // iterate, is below kGapRel of the objective (fp32 iterates gain nothing beyond)
+    if (!(mu >= kMuStop) || gap <= kGapRel * fmax(1.0, (double)S.v[n + R])) break;
+    ++run;
+    if constexpr (kBlk > 0) lpb_factor<kBlk>(B, n, R, G, L, S);
+    else lp_factor(n, R, G, L, S);
+    // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
+    lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
+    __syncthreads();
+    if constexpr (kBlk > 0) lpb_solve<kBlk>(B, n, R, G, S);
+    else lp_solve(n, R, G, S);
+    lp_ATy(S.dy, S.tv, n, R, G, S);
+    for (int i = tid; i < nv; i += kLpThreads) {
+      S.dz[i] = S.rc[i] - S.tv[i];
+      S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
+    }
+    float ap, ad;
+    lp_steps(nv, S, ap, ad);
+    double ca = 0.0;
+    for (int i = tid; i < nv; i += kLpThreads)
+      ca += (double)((S.v[i] + ap * S.dv[i]) * (S.z[i] + ad * S.dz[i]));
+    const float mu_aff = (float)(blk_sum(ca, S) / nv);
+    const float ratio = mu_aff / mu;
+    const float sg = ratio * ratio * ratio;
+    // corrector: rmu = sg mu - v z - dv dz ; rhs = rb + A (D rc - rmu / z)
+    for (int i = tid; i < nv; i += kLpThreads) {
+      const float rmu = sg * mu - S.v[i] * S.z[i] - S.dv[i] * S.dz[i];
+      S.dv[i] = rmu;                       // keep rmu in dv until the new direction
+      S.tv[i] = (float)(S.d[i] * S.rc[i]) - rmu / S.z[i];
+    }
+    __syncthreads();
+    lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, S);
+    __syncthreads();
+    if constexpr (kBlk > 0) lpb_solve<kBlk>(B, n, R, G, S);
+    else lp_solve(n, R, G, S);
+    lp_ATy(S.dy, S.tv, n, R, G, S);
+    for (int i = tid; i < nv; i += kLpThreads) {
+      const float rmu = S.dv[i];
+      S.dz[i] = S.rc[i] - S.tv[i];
+      S.dv[i] = rmu / S.z[i] - (float)(S.d[i] * S.dz[i]);
+    }
+    float ap2, ad2;
+    lp_steps(nv, S, ap2, ad2);
+    for (int i = tid; i < nv; i += kLpThreads) {
+      S.v[i] += kEta * ap2 * S.dv[i];
+      S.z[i] += kEta * ad2 * S.dz[i];
+    }
+    for (int i = tid; i < R + G; i += kLpThreads) S.y[i] += kEta * ad2 * S.dy[i];
+    __syncthreads();
+  }
+  return run;
+}
+
 __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ lpw,
                                                           int iters, float* __restrict__ x_out,
@@ -464,6 +702,10 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     return;
   }
   const LpView L = lp_view(lpw);
+  if (L.blk != 0 && L.blk != 8 && L.blk != 16) {
+    if (threadIdx.x == 0) set_err(err, UEP_ERR_LP);
+    return;
+  }
   const int R = L.R, E = L.E, G = L.G, n = L.n, nv = n + R + 2;
   const int tid = threadIdx.x;
 
@@ -531,68 +773,9 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     for (int i = tid; i < nv; i += kLpThreads) S.z[i] = fmaxf(lp_cost(i, n, R) - S.tv[i], 0.0f) + 1.0f;
     __syncthreads();
 
-    // Barriers below separate only accesses across threads: a loop over i that reads
-    // what the same thread wrote at index i in the step before needs none.
-    const auto plus_rb = [&](int i, float a) { return a + S.rb[i]; };
-    for (int it = 0; it < iters; ++it) {
-      // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
-      lp_Av([&](int j) { return S.v[j]; },
-            [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, S);
-      lp_ATy(S.y, S.tv, n, R, G, S);
-      double cz = 0.0;
-      for (int i = tid; i < nv; i += kLpThreads) {
-        S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
-        cz += (double)(S.v[i] * S.z[i]);
-      }
-      const double gap = blk_sum(cz, S);
-      const float mu = (float)(gap / nv);
-      // stop once the duality gap, which bounds the objective error of a feasible
-      // iterate, is below kGapRel of the objective (fp32 iterates gain nothing beyond)
-      if (!(mu >= kMuStop) || gap <= kGapRel * fmax(1.0, (double)S.v[n + R])) break;
-      ++run;
-      lp_factor(n, R, G, L, S);
-      // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
-      lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
-      __syncthreads();
-      lp_solve(n, R, G, S);
-      lp_ATy(S.dy, S.tv, n, R, G, S);
-      for (int i = tid; i < nv; i += kLpThreads) {
-        S.dz[i] = S.rc[i] - S.tv[i];
-        S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
-      }
-      float ap, ad;
-      lp_steps(nv, S, ap, ad);
-      double ca = 0.0;
-      for (int i = tid; i < nv; i += kLpThreads)
-        ca += (double)((S.v[i] + ap * S.dv[i]) * (S.z[i] + ad * S.dz[i]));
-      const float mu_aff = (float)(blk_sum(ca, S) / nv);
-      const float ratio = mu_aff / mu;
-      const float sg = ratio * ratio * ratio;
-      // corrector: rmu = sg mu - v z - dv dz ; rhs = rb + A (D rc - rmu / z)
-      for (int i = tid; i < nv; i += kLpThreads) {
-        const float rmu = sg * mu - S.v[i] * S.z[i] - S.dv[i] * S.dz[i];
-        S.dv[i] = rmu;                       // keep rmu in dv until the new direction
-        S.tv[i] = (float)(S.d[i] * S.rc[i]) - rmu / S.z[i];
-      }
-      __syncthreads();
-      lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, S);
-      __syncthreads();
-      lp_solve(n, R, G, S);
-      lp_ATy(S.dy, S.tv, n, R, G, S);
-      for (int i = tid; i < nv; i += kLpThreads) {
-        const float rmu = S.dv[i];
-        S.dz[i] = S.rc[i] - S.tv[i];
-        S.dv[i] = rmu / S.z[i] - (float)(S.d[i] * S.dz[i]);
-      }
-      float ap2, ad2;
-      lp_steps(nv, S, ap2, ad2);
-      for (int i = tid; i < nv; i += kLpThreads) {
-        S.v[i] += kEta * ap2 * S.dv[i];
-        S.z[i] += kEta * ad2 * S.dz[i];
-      }
-      for (int i = tid; i < R + G; i += kLpThreads) S.y[i] += kEta * ad2 * S.dy[i];
-      __syncthreads();
-    }
+    if (L.blk == 8) run = lp_ipm<8>(iters, n, R, G, L, S);
+    else if (L.blk == 16) run = lp_ipm<16>(iters, n, R, G, L, S);
+    else run = lp_ipm<0>(iters, n, R, G, L, S);
   }
 
   // split: clip, scale back, normalise every group to its count
@@ -854,6 +1037,48 @@ extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
     std::vector<int> fill(rank_start.begin(), rank_start.end() - 1);
     for (int p = 0; p < n; ++p) rank_copy[fill[copy_rank[p]]++] = p;
   }
+  // components of the rank coupling graph, packed into lane groups for the block solve
+  std::vector<int> parent(R);
+  for (int r = 0; r < R; ++r) parent[r] = r;
+  auto find = [&](int a) {
+    while (parent[a] != a) a = parent[a] = parent[parent[a]];
+    return a;
+  };
+  for (int g = 0; g < G; ++g)
+    for (int p = grp_start[g] + 1; p < grp_start[g + 1]; ++p)
+      parent[find(copy_rank[p])] = find(copy_rank[grp_start[g]]);
+  std::vector<std::vector<int>> comps;
+  {
+    std::vector<int> comp_of(R, -1);
+    for (int r = 0; r < R; ++r) {
+      const int root = find(r);
+      if (comp_of[root] < 0) { comp_of[root] = (int)comps.size(); comps.emplace_back(); }
+      comps[comp_of[root]].push_back(r);
+    }
+  }
+  size_t biggest = 0;
+  for (auto& c : comps) biggest = std::max(biggest, c.size());
+  int blk = biggest <= 8 ? 8 : (biggest <= 16 ? 16 : 0);
+  std::vector<int> lane_rank(kLpLanes, -1), rank_lane(R, -1);
+  if (blk > 0) {
+    std::vector<int> order(comps.size());
+    for (size_t c = 0; c < comps.size(); ++c) order[c] = (int)c;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return comps[a].size() > comps[b].size(); });
+    const int n_bins = kLpLanes / blk;
+    std::vector<int> fill(n_bins, 0);
+    for (int c : order) {
+      int b = 0;
+      while (b < n_bins && fill[b] + (int)comps[c].size() > blk) ++b;
+      if (b == n_bins) { blk = 0; break; }
+      for (int r : comps[c]) {
+        const int l = b * blk + fill[b]++;
+        lane_rank[l] = r;
+        rank_lane[r] = l;
+      }
+    }
+    if (blk == 0) std::fill(lane_rank.begin(), lane_rank.end(), -1);
+  }
   const size_t words = lp_words(R, E, I, G, n, n_ent, n_pair);
   if (lp_bytes < words * sizeof(int32_t)) return UEP_EWORKSPACE;
   std::vector<int32_t> w(words, 0);
@@ -866,6 +1091,8 @@ extern "C" uep_status uep_lplb_prepare(const int32_t* ie, int32_t R, int32_t E,
   for (int i = 0; i < I; ++i) w[o++] = ie[i];
   put(inst_copy);
   put(ent_rr); put(ent_start); put(ent_p); put(ent_q);
+  w[o++] = blk;
+  put(lane_rank); put(rank_lane);
   hipStream_t s = uep_stream(stream);
   if (hipMemcpyAsync(lp, w.data(), w.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) !=
       hipSuccess)
