@@ -371,7 +371,8 @@ uep_status uep_waterfill(const int32_t* counts, const int32_t* topk_ids,
  *                              then instance id), normalised to sum to each count
  *   m          [1]        out  max rank load of that split
  *   inst_quota [I]        out  integer quotas for every instance
- *   stats      [4]        out  optional: {n_replicated, n_copies, iterations run, 0}
+ *   stats      [4]        out  optional: {n_replicated, n_copies, iterations run, solve:
+ *                              8 or 16 = block solve with lane groups of that size, 0 = dense}
  *   err                   out  optional; UEP_ERR_LP: an expert with load but no instance
  *                              or a column sum of 2^27 or more (the solve still runs), or
  *                              `lp` not a structure from uep_lplb_prepare (then nothing

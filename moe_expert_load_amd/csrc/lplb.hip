@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     stats[0] = G;
     stats[1] = n;
     stats[2] = run;
-    stats[3] = 0;
+    stats[3] = L.blk;
   }
 }
 

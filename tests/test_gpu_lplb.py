@@ -439,3 +439,33 @@ def test_lplb_sample_layer_full_size():
         got = np.array([(di == i).sum() for i in insts])
         sigma = np.sqrt(tot * p * (1 - p))
         assert (np.abs(got - tot * p) <= 5 * sigma + 1).all()
+
+
+def test_lplb_block_and_dense_solves():
+    """The rank matrix is solved block by block when every component of the rank coupling
+    graph has at most 16 ranks (lane groups of 8 or 16), densely otherwise: the LPLB
+    layer's placement (components of at most 8 ranks), a chain of 12 ranks (groups of
+    16) and a ring over all 64 ranks (dense) all reach the simplex optimum within the
+    bound, and each reports the solve it took."""
+    w = W.LPLB_LAYER
+    R, E_loc = w.R, w.E_loc
+    ipr = E_loc + 1
+    ids = W.routing(w)
+    counts = O.load_matrix(ids, w.E)[0].astype(np.int32)
+
+    def mains():
+        inst = np.full(R * ipr, -1, dtype=np.int32)
+        for r in range(R):
+            inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+        return inst
+    chain = mains()
+    for r in range(11):                       # ranks 0..11 linked: one 12-rank component
+        chain[(r + 1) * ipr + E_loc] = r * E_loc
+    ring = mains()
+    for r in range(R):                        # every rank linked to the next: one component
+        ring[((r + 1) % R) * ipr + E_loc] = r * E_loc
+    for name, inst, path in (("lplb placement", W.static_replica_placement(w), 8),
+                             ("12-rank chain", chain, 16), ("64-rank ring", ring, 0)):
+        say(f"case: lplb solve path, {name}")
+        res, x, m, q, st = check_lplb(counts, inst, ipr)
+        assert st[3] == path, (name, st)
