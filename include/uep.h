@@ -32,7 +32,8 @@
  *     own synchronisation.  Outputs are unspecified when a bit is set.
  *   - Calls are stateless and re-entrant.  Calls that overlap on one stream-less
  *     set of buffers race like any other kernels writing the same memory.
- *   - Limits: R <= 64, E <= 4096, K <= 64, R*T*K < 2^31, total load < 2^31.
+ *   - Limits: R <= 64, E <= 4096, K <= 64, R*T*K < 2^31, total load < 2^31,
+ *     hidden size H <= 2^29 for the row moves (a row is one store span).
  */
 #ifndef UEP_H
 #define UEP_H

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
         }
       }
     }
-    u32x4* dst = y + g * nvec;
+    const span_t dst = span_of(y + g * nvec, (int64_t)nvec * 16);
 #pragma unroll
     for (int u = 0; u < kCbVec; ++u) {
       const int v = v0 + u * kWave + lane;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           o[c] = f32_to_bf16(acc[u * 8 + 2 * c]) | (f32_to_bf16(acc[u * 8 + 2 * c + 1]) << 16);
-        dst[v] = o;
+        stream_store(o, dst, v * 16);
       }
     }
   }
@@ -109,7 +109,8 @@ extern "C" uep_status uep_combine(const uint16_t* y_disp, int64_t out_rows,
                                   uint16_t* y, int32_t* err, void* stream) {
   if (R <= 0 || T < 0 || K <= 0 || H <= 0 || out_rows < 0) return UEP_EINVAL;
   if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
-  if (K > 64 || H % 8 != 0 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
+  if (K > 64 || H % 8 != 0 || H > (1 << 29) || (int64_t)R * T * K >= (1ll << 31))
+    return UEP_EGEOM;
   const int64_t g0 = (int64_t)r_begin * T, g1 = (int64_t)r_end * T;
   if (g1 == g0) return UEP_OK;
   if (!y_disp || !dest_row || !gate_w || !y) return UEP_EINVAL;

@@ -15,8 +15,8 @@
 // therefore moved in chunks of at most kChunkBytes of source rows, below the 256 MB
 // last-level cache: a read-only pass (prefetch_kernel, plain loads, which fill that
 // cache) pulls the chunk in, then the permute of the chunk reads it back with
-// non-temporal loads and writes with non-temporal stores, which go to HBM without
-// allocating in that cache and so leave the chunk in place.  HBM thus sees a short
+// non-temporal loads and writes with streaming stores (nt sc1), which go to HBM
+// without allocating in that cache and so leave the chunk in place.  HBM thus sees a short
 // read-only phase, then a write-only phase, per chunk; the launch boundary between
 // them keeps the phases apart (the same two phases in one launch, ordered by block
 // id, overlapped and ran slower).  Measured on MI355X against one plain launch:
@@ -80,11 +80,11 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
     for (int k = 0; k < K; ++k) {
       const int d = readlane(d_mine, k);
       if (d < 0) continue;
-      u32x4* dst = out + (int64_t)d * nvec;
+      const span_t dst = span_of(out + (int64_t)d * nvec, (int64_t)nvec * 16);
 #pragma unroll
       for (int u = 0; u < kVec; ++u) {
         const int v = v0 + u * kWave + lane;
-        if (v < nvec) __builtin_nontemporal_store(buf[u], dst + v);
+        if (v < nvec) stream_store(buf[u], dst, v * 16);
       }
     }
   }
@@ -113,7 +113,8 @@ extern "C" uep_status uep_permute(const uint16_t* x, const int32_t* dest_row, in
                                   void* stream) {
   if (R <= 0 || T < 0 || K <= 0 || H <= 0 || out_rows < 0) return UEP_EINVAL;
   if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
-  if (K > 64 || H % 8 != 0 || (int64_t)R * T * K >= (1ll << 31)) return UEP_EGEOM;
+  if (K > 64 || H % 8 != 0 || H > (1 << 29) || (int64_t)R * T * K >= (1ll << 31))
+    return UEP_EGEOM;
   const int64_t g0 = (int64_t)r_begin * T, g1 = (int64_t)r_end * T;
   if (g1 == g0) return UEP_OK;
   if (!x || !dest_row || !out) return UEP_EINVAL;

@@ -10,8 +10,11 @@
 // list in LDS (no host round trip: the plan stays on the device): the selected slots
 // grouped by expert.  It then walks tasks = (expert group) x tile with a grid stride.  A tile is 256 threads x
 // kStVec 16-byte vectors = 16 KiB of bf16 weights (or fp32 gradients); all loads of
-// a tile are issued before its stores.  Tile size, grid (16 workgroups per CU) and
-// plain (temporal) loads and stores were picked by measurement on MI355X.
+// a tile are issued before its stores.  Tile size, grid (16 workgroups per CU) and the
+// cache policy were picked by measurement on MI355X: the weight copy streams its slot
+// stores (nt sc1); the gradient reduction keeps plain stores for the main gradient it
+// has just read and non-temporal ones for the cleared replicas (streaming both ran
+// 25 % slower).
 //
 // GRAD_REDUCE keeps the article's order fixed: for every element the main's
 // gradient is added to the replicas' gradients one at a time in ascending rank
@@ -125,12 +128,13 @@ __global__ __launch_bounds__(kStThreads) void stage_weights_kernel(
       const int64_t v = v0 + k * kStThreads + threadIdx.x;
       if (v < nvec) buf[k] = src[v];
     }
+    const int64_t span = min((int64_t)kStTileVec, nvec - v0) * 16;
     for (int m = G.g_first[gi]; m < G.g_first[gi + 1]; ++m) {
-      u32x4* dst = slot_w + (int64_t)G.g_mem[m] * nvec;
+      const span_t dst = span_of(slot_w + (int64_t)G.g_mem[m] * nvec + v0, span);
 #pragma unroll
       for (int k = 0; k < kStVec; ++k) {
         const int64_t v = v0 + k * kStThreads + threadIdx.x;
-        if (v < nvec) dst[v] = buf[k];
+        if (v < nvec) stream_store(buf[k], dst, (k * kStThreads + threadIdx.x) * 16);
       }
     }
   }
