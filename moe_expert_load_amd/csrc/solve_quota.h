@@ -145,25 +145,194 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
   }
 }
 
+// Relay on the register keys of the fast search below (the rule of sq_relay; lanes as
+// there).  By the relay lemma a qualifying relay rank holds no replica, so it never
+// holds h's first donor and the first donor always finds x; should no qualifying rank
+// be free of that donor all the same, the general relay decides (returns -1).  The
+// quota of x's pair main f is read from x's own keys, every update is a select, and the
+// two changed quotas are written to LDS as well.  Returns 1 for a move, 0 for none.
+template <int kS, int kQ>
+__device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int32_t* q_main, int (&kq)[kQ],
+                                             int& dkey, int lane, bool active, int E_loc, int S,
+                                             int q_min, int t_star, int h, int Lh, int& n_rep) {
+  if (Lh - t_star < q_min) return 0;
+  // this lane as the relay rank x: its recorded pair, if still live
+  const int Ly = shfl(st.L, st.pf >= 0 ? st.py : lane);
+  const int jf = st.pf - lane * E_loc;      // the pair's main among the lane's own mains
+  int kf = -1;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) kf = j == jf ? kq[j] : kf;
+  const int qf = kf >= 0 ? kf >> 6 : 0;
+  const int d2 = min(qf, t_star - Ly);
+  const bool cand = active && lane != h && st.free_slots > 0 && st.L >= t_star && st.pf >= 0 &&
+                    Ly < t_star && qf > 0 && t_star - (st.L - d2) >= q_min;
+  if (ballot(cand) == 0) return 0;
+  const int kd = readlane(dkey, h);         // h's first donor
+  if (kd < 0 || (kd >> 6) < q_min) return 0;
+  const int qd = kd >> 6, jd = 63 - (kd & 63);
+  const int e = h * E_loc + jd;
+  const int x = first_lane(cand && slot_of<kS>(st, S, e) < 0);
+  if (x < 0) return -1;
+  const int f = readlane(st.pf, x), y = readlane(st.py, x), d2x = readlane(d2, x);
+  const int jfx = readlane(jf, x), qfx = readlane(qf, x);
+  const int d = min(qd, min(Lh - t_star, t_star - (readlane(st.L, x) - d2x)));
+  const bool is_y = lane == y, is_x = lane == x, is_h = lane == h;
+  const int slot = S - st.free_slots;
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    const bool here = is_x && s == slot;
+    st.sl_q[s] += (is_y && s < S && st.sl_e[s] == f) ? d2x : 0;
+    st.sl_e[s] = here ? e : st.sl_e[s];
+    st.sl_q[s] = here ? d : st.sl_q[s];
+  }
+  st.free_slots -= is_x ? 1 : 0;
+  st.L += is_y ? d2x : (is_x ? d - d2x : (is_h ? -d : 0));
+  // h down to T* with x left below it and quota left on e: h's pair; x's pair is used up
+  const bool rec = is_h && d == Lh - t_star && d < d2x && qd - d > 0;
+  st.pf = rec ? e : (is_x ? -1 : st.pf);
+  st.py = rec ? x : st.py;
+  const int ke = qd - d > 0 ? ((qd - d) << 6) | (63 - jd) : -1;
+  const int kfn = qfx - d2x > 0 ? ((qfx - d2x) << 6) | (63 - jfx) : -1;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) kq[j] = (is_h && j == jd) ? ke : ((is_x && j == jfx) ? kfn : kq[j]);
+  int k = kq[0];
+#pragma unroll
+  for (int j = 1; j < kQ; ++j) k = max(k, kq[j]);
+  dkey = k;
+  if (lane == 0) { q_main[e] = qd - d; q_main[f] = qfx - d2x; }
+  ++n_rep;
+  return 1;
+}
+
+// Wave max / min with every lane active, result uniform: DPP within each row of 16
+// lanes, then gfx950's row swaps (permlane16_swap pairs rows 0-1 and 2-3 of its two
+// operands, permlane32_swap the two halves), so the last steps stay in VALU and one
+// readfirstlane ends it.
+__device__ __forceinline__ int wave_max_sw(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));   // row_ror:4
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));   // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_amdgcn_readfirstlane(max((int)b[0], (int)b[1]));
+}
+__device__ __forceinline__ uint32_t wave_min_u32_sw(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)min((uint32_t)b[0], (uint32_t)b[1]));
+}
+
 // The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
 // reduction give value and lowest lane together.
-template <int kS>
+//
+// Fast steps (kQ > 0, E_loc <= kQ): lane r also holds, in registers, the donor key of
+// each of its mains j, (q_j << 6 | 63 - j) if q_j > 0 else -1, and their maximum (the
+// rank's first donor: largest quota, lowest index on ties), so h's first donor is one
+// readlane.  The lightest possible receiver (L < T*, a free slot; such a rank is never
+// h) depends neither on h nor on the donor, so its reduction runs beside h's.  A plain
+// step is then decided without a scan: if that receiver holds no copy of the first
+// donor, it is the rule's receiver for that donor and the move min(q, L_h - T*, T* - L_t)
+// is at least q_min.  These steps run in an inner loop of their own whose per-lane
+// updates are all selects: one wave runs the whole chain, and a taken branch costs it
+// more than the work it would skip.  Any other step leaves that loop.  If the
+// receiver's room or the first donor's quota is below q_min, no donor can move at all
+// (every receiver has at most that room, every donor at most that quota) and the step
+// is a relay.  Only when that receiver holds a copy of the first donor does the step
+// scan the donors, on the quotas in LDS (kept current by every step), and reload the
+// keys after.
+template <int kS, int kQ>
 __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
                                               int R, int E_loc, int S, int q_min, int t_star,
                                               int& steps, int& n_rep, int& stuck) {
+  constexpr int kQn = kQ > 0 ? kQ : 1;
+  int kq[kQn];                       // donor key of each own main (fast steps only)
+  int dkey = -1;                     // max of kq
+  auto key_max = [&]() {
+    int k = kq[0];
+#pragma unroll
+    for (int j = 1; j < kQn; ++j) k = max(k, kq[j]);
+    return k;
+  };
+  auto load_q = [&]() {              // clamped addresses: every read issues, no branch
+    const int r = min(lane, R - 1);
+#pragma unroll
+    for (int j = 0; j < kQn; ++j) {
+      const int v = q_main[r * E_loc + min(j, E_loc - 1)];
+      kq[j] = (active && j < E_loc && v > 0) ? (v << 6) | (63 - j) : -1;
+    }
+    dkey = key_max();
+  };
+  if (kQ > 0) load_q();
   for (;;) {
-    const int kh = wave_max(active ? (st.L << 6) | (63 - lane) : -1);
-    const int Lh = kh >> 6;
+    int Lh, h, Lt, tgt;
+    uint32_t kr;
+    for (;;) {
+      const int kh = wave_max_sw(active ? (st.L << 6) | (63 - lane) : -1);
+      kr = wave_min_u32_sw(active && st.L < t_star && st.free_slots > 0
+                               ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
+      Lh = kh >> 6;
+      h = 63 - (kh & 63);
+      Lt = (int)(kr >> 6);
+      tgt = (int)(kr & 63u);
+      if (kQ == 0 || Lh <= t_star) break;
+      const int over = Lh - t_star;
+      const int kd = readlane(dkey, h);
+      const int qd = kd >> 6, jd = 63 - (kd & 63);
+      const int e = h * E_loc + jd;
+      const uint64_t hold = ballot(slot_of<kS>(st, S, e) >= 0);
+      if (over < q_min || kr == 0xFFFFFFFFu || kd < 0 || qd < q_min || t_star - Lt < q_min ||
+          ((hold >> tgt) & 1ull))
+        break;
+      const int delta = min(qd, min(over, t_star - Lt));
+      const bool is_t = lane == tgt, is_h = lane == h;
+      const int slot = S - st.free_slots;
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const bool here = is_t && s == slot;
+        st.sl_e[s] = here ? e : st.sl_e[s];
+        st.sl_q[s] = here ? delta : st.sl_q[s];
+      }
+      st.free_slots -= is_t ? 1 : 0;
+      st.L += is_t ? delta : (is_h ? -delta : 0);
+      // h down to T* with the receiver left below it and quota left on e: h's pair
+      const bool rec = is_h && delta == over && Lt + delta < t_star && qd - delta > 0;
+      st.pf = rec ? e : st.pf;
+      st.py = rec ? tgt : st.py;
+      const int left = qd - delta;
+      const int knew = left > 0 ? (left << 6) | (63 - jd) : -1;
+#pragma unroll
+      for (int j = 0; j < kQn; ++j) kq[j] = (is_h && j == jd) ? knew : kq[j];
+      dkey = key_max();
+      if (lane == 0) q_main[e] = left;
+      ++n_rep;
+      ++steps;
+    }
     if (Lh <= t_star) break;
-    const int h = 63 - (kh & 63);
     const int over = Lh - t_star;
     // every move, plain or relay, is at most the excess: below q_min nothing can move
     if (over < q_min) { stuck = 1; break; }
-    const int qj = lane < E_loc ? q_main[h * E_loc + lane] : 0;
-    bool tried = false, moved = false;
     // no rank below T* with a free slot: no donor can move directly, go to the relay
-    const bool any_recv = ballot(active && lane != h && st.L < t_star && st.free_slots > 0) != 0;
-    for (; any_recv;) {
+    bool plain = kr != 0xFFFFFFFFu;
+    if (kQ > 0) {
+      const int kd = readlane(dkey, h);
+      if (kd < 0 || (kd >> 6) < q_min || t_star - Lt < q_min) plain = false;
+      if (!plain) {
+        const int rk = sq_relay_keys<kS, kQn>(st, q_main, kq, dkey, lane, active, E_loc, S, q_min,
+                                              t_star, h, Lh, n_rep);
+        if (rk == 0) { stuck = 1; break; }
+        if (rk > 0) { ++steps; continue; }
+      }
+    }
+    const int qj = plain && lane < E_loc ? q_main[h * E_loc + lane] : 0;
+    bool tried = false, moved = false;
+    for (; plain;) {
       // next donor: largest untried main quota on h, lowest expert id on ties; the
       // quotas only fall from here, so one below q_min ends the scan
       const int kd = wave_max((lane < E_loc && qj > 0 && !tried) ? (qj << 6) | (63 - lane) : -1);
@@ -174,15 +343,15 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
                       slot_of<kS>(st, S, e) < 0;
       const uint32_t km = wave_min_u32(c2 ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
       if (km != 0xFFFFFFFFu) {
-        const int tgt = (int)(km & 63u);
-        const int Lt = (int)(km >> 6);
-        const int delta = min(qd, min(over, t_star - Lt));
+        const int tgt2 = (int)(km & 63u);
+        const int Lt2 = (int)(km >> 6);
+        const int delta = min(qd, min(over, t_star - Lt2));
         if (delta >= q_min) {                         // open a new replica
-          if (lane == tgt) { open_slot<kS>(st, S, e, delta); st.L += delta; }
+          if (lane == tgt2) { open_slot<kS>(st, S, e, delta); st.L += delta; }
           if (lane == h) {
             st.L -= delta;
             // h down to T* with the receiver left below it and quota left on e
-            if (delta == over && Lt + delta < t_star && qd - delta > 0) { st.pf = e; st.py = tgt; }
+            if (delta == over && Lt2 + delta < t_star && qd - delta > 0) { st.pf = e; st.py = tgt2; }
           }
           if (lane == 0) q_main[e] = qd - delta;
           ++n_rep;
@@ -195,6 +364,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     if (!moved)
       moved = sq_relay<kS>(st, q_main, lane, active, E_loc, S, q_min, t_star, h, Lh, n_rep);
     if (!moved) { stuck = 1; break; }
+    if (kQ > 0) load_q();
     ++steps;
   }
 }
@@ -299,8 +469,12 @@ __device__ __forceinline__ void solve_body(const int32_t* __restrict__ counts, i
   const int t_star = (total + R - 1) / R;
 
   int steps = 0, n_rep = 0, stuck = 0;
-  if (total < (1 << kPackBits))
-    search_packed<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+  if (total < (1 << kPackBits) && E_loc <= 4)
+    search_packed<kS, 4>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+  else if (total < (1 << kPackBits) && E_loc <= 8)
+    search_packed<kS, 8>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+  else if (total < (1 << kPackBits))
+    search_packed<kS, 0>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
   else
     search_wide<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
 

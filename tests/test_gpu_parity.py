@@ -329,6 +329,40 @@ def test_solve_quota_tie_and_order_rules(case):
                                          int(case["stuck"])]
 
 
+def test_solve_quota_random_many():
+    """The solver alone on 500 random load matrices: 1 to 64 ranks, E/R from 1 to 24 (the
+    register-key search for E/R up to 4 and up to 8, the LDS search above), 0 to 8 slots
+    per rank, heavy-tailed expert loads that make relays and replicas on ranks that
+    already hold one, q_min 0 or up to a third of the mean rank load: plan and stats
+    equal the oracle's in every case."""
+    rng = np.random.default_rng(77)
+    relays = {}
+    for i in range(500):
+        R = int(rng.integers(1, 65))
+        u = rng.random()
+        E_loc = int(rng.integers(1, 5)) if u < 0.4 else (int(rng.integers(5, 9)) if u < 0.7
+                                                          else int(rng.integers(9, 25)))
+        E = R * E_loc
+        S = min(int(rng.integers(0, 9)), 256 // R)
+        total = int(rng.integers(R, 40000 * R))
+        we = rng.pareto(float(rng.uniform(0.3, 2.5)), E) + 1e-3
+        wr = rng.uniform(0.5, 1.5, R)
+        p = (wr[:, None] * we[None, :]).ravel()
+        counts = rng.multinomial(total, p / p.sum()).reshape(R, E).astype(np.int32)
+        q_min = 0 if rng.random() < 0.25 else int(rng.integers(0, max(1, total // (R * 3))))
+        o = O.solve_quota(counts, S, q_min)
+        g = U.solve_quota(to_dev(counts), S, q_min)
+        case = f"case {i}: R={R} E={E} S={S} q_min={q_min} total={total}"
+        for key in ("slot_expert", "inst_expert", "inst_quota", "rank_load"):
+            assert np.array_equal(host(g[key]), o[key]), (case, key)
+        assert host(g["stats"]).tolist() == [o["n_replicas"], o["n_steps"], o["t_star"],
+                                             int(o["stuck"])], case
+        form = "E/R<=4" if E_loc <= 4 else ("E/R<=8" if E_loc <= 8 else "E/R>8")
+        relays[form] = relays.get(form, 0) + o["n_relays"]
+    say("relays by search form:", relays)
+    assert min(relays.values()) >= 20
+
+
 def test_plan_already_balanced_and_max_k():
     """A layer already at the waterline gets the identity plan in zero steps; K = 64,
     the largest top-k the library takes, through the ballot-ranking path."""
