@@ -149,10 +149,11 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
 // there).  By the relay lemma a qualifying relay rank holds no replica, so it never
 // holds h's first donor and the first donor always finds x; should no qualifying rank
 // be free of that donor all the same, the general relay decides (returns -1).  The
-// quota of x's pair main f is read from x's own keys, every update is a select, and the
-// two changed quotas are written to LDS as well.  Returns 1 for a move, 0 for none.
+// quota of x's pair main f is read from x's own keys and every update is a select on
+// the registers only (the caller writes the quotas to LDS when it needs them there).
+// Returns 1 for a move, 0 for none.
 template <int kS, int kQ>
-__device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int32_t* q_main, int (&kq)[kQ],
+__device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
                                              int& dkey, int lane, bool active, int E_loc, int S,
                                              int q_min, int t_star, int h, int Lh, int& n_rep) {
   if (Lh - t_star < q_min) return 0;
@@ -193,40 +194,42 @@ __device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int32_t* q_main, in
   st.py = rec ? x : st.py;
   const int ke = qd - d > 0 ? ((qd - d) << 6) | (63 - jd) : -1;
   const int kfn = qfx - d2x > 0 ? ((qfx - d2x) << 6) | (63 - jfx) : -1;
+  const int sel = is_h ? jd : (is_x ? jfx : -1);
+  const int knew = is_h ? ke : kfn;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) kq[j] = (is_h && j == jd) ? ke : ((is_x && j == jfx) ? kfn : kq[j]);
+  for (int j = 0; j < kQ; ++j) kq[j] = sel == j ? knew : kq[j];
   int k = kq[0];
 #pragma unroll
   for (int j = 1; j < kQ; ++j) k = max(k, kq[j]);
   dkey = k;
-  if (lane == 0) { q_main[e] = qd - d; q_main[f] = qfx - d2x; }
   ++n_rep;
   return 1;
 }
 
-// Wave max / min with every lane active, result uniform: DPP within each row of 16
-// lanes, then gfx950's row swaps (permlane16_swap pairs rows 0-1 and 2-3 of its two
-// operands, permlane32_swap the two halves), so the last steps stay in VALU and one
-// readfirstlane ends it.
-__device__ __forceinline__ int wave_max_sw(int v) {
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));   // row_ror:4
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));   // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = max((int)a[0], (int)a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __builtin_amdgcn_readfirstlane(max((int)b[0], (int)b[1]));
-}
-__device__ __forceinline__ uint32_t wave_min_u32_sw(uint32_t v) {
-  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
-  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
-  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));
-  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = min((uint32_t)a[0], (uint32_t)a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)min((uint32_t)b[0], (uint32_t)b[1]));
+// The two reductions of a search step at once, every lane active, results uniform:
+// max of kh and unsigned min of kr.  DPP within each row of 16 lanes, then gfx950's row
+// swaps (permlane16_swap pairs rows 0-1 and 2-3 of its operands, permlane32_swap the
+// halves), so the last steps stay in VALU and one readfirstlane ends each; the two
+// chains are interleaved so neither waits on its own DPP hazards.
+__device__ __forceinline__ void wave_max_min_sw(int& kh, uint32_t& kr) {
+  int a = kh;
+  uint32_t b = kr;
+  a = max(a, __builtin_amdgcn_mov_dpp(a, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+  b = min(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, true));
+  a = max(a, __builtin_amdgcn_mov_dpp(a, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+  b = min(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xF, 0xF, true));
+  a = max(a, __builtin_amdgcn_mov_dpp(a, 0x124, 0xF, 0xF, true));   // row_ror:4
+  b = min(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x124, 0xF, 0xF, true));
+  a = max(a, __builtin_amdgcn_mov_dpp(a, 0x128, 0xF, 0xF, true));   // row_ror:8
+  b = min(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x128, 0xF, 0xF, true));
+  const auto a16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  const auto b16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  a = max((int)a16[0], (int)a16[1]);
+  b = min((uint32_t)b16[0], (uint32_t)b16[1]);
+  const auto a32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const auto b32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  kh = __builtin_amdgcn_readfirstlane(max((int)a32[0], (int)a32[1]));
+  kr = (uint32_t)__builtin_amdgcn_readfirstlane((int)min((uint32_t)b32[0], (uint32_t)b32[1]));
 }
 
 // The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
@@ -238,15 +241,16 @@ __device__ __forceinline__ uint32_t wave_min_u32_sw(uint32_t v) {
 // readlane.  The lightest possible receiver (L < T*, a free slot; such a rank is never
 // h) depends neither on h nor on the donor, so its reduction runs beside h's.  A plain
 // step is then decided without a scan: if that receiver holds no copy of the first
-// donor, it is the rule's receiver for that donor and the move min(q, L_h - T*, T* - L_t)
-// is at least q_min.  These steps run in an inner loop of their own whose per-lane
-// updates are all selects: one wave runs the whole chain, and a taken branch costs it
-// more than the work it would skip.  Any other step leaves that loop.  If the
-// receiver's room or the first donor's quota is below q_min, no donor can move at all
-// (every receiver has at most that room, every donor at most that quota) and the step
-// is a relay.  Only when that receiver holds a copy of the first donor does the step
-// scan the donors, on the quotas in LDS (kept current by every step), and reload the
-// keys after.
+// donor, it is the rule's receiver for that donor, and it moves
+// delta = min(q, L_h - T*, T* - L_t) if that is at least q_min (no first donor gives
+// q = -1, no receiver a negative room: both fail that test).  Every per-lane update is a
+// select: one wave runs the whole chain, and a taken branch costs it more than the work
+// it would skip.  If the receiver's room or the first donor's quota is below q_min, no
+// donor can move at all (every receiver has at most that room, every donor at most that
+// quota) and the step is a relay, also on the keys.  Only when that receiver holds a
+// copy of the first donor (or the lemma's premise failed) does the step take the donor
+// scan or the general relay, on the quotas written back to LDS, and reload the keys
+// after.  The quotas are written back to LDS at the end for the outputs.
 template <int kS, int kQ>
 __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
                                               int R, int E_loc, int S, int q_min, int t_star,
@@ -269,53 +273,56 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     }
     dkey = key_max();
   };
+  auto store_q = [&]() {
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < kQn; ++j)
+        if (j < E_loc) q_main[lane * E_loc + j] = kq[j] >= 0 ? kq[j] >> 6 : 0;
+    }
+  };
   if (kQ > 0) load_q();
   for (;;) {
-    int Lh, h, Lt, tgt;
-    uint32_t kr;
-    for (;;) {
-      const int kh = wave_max_sw(active ? (st.L << 6) | (63 - lane) : -1);
-      kr = wave_min_u32_sw(active && st.L < t_star && st.free_slots > 0
-                               ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu);
-      Lh = kh >> 6;
-      h = 63 - (kh & 63);
-      Lt = (int)(kr >> 6);
-      tgt = (int)(kr & 63u);
-      if (kQ == 0 || Lh <= t_star) break;
-      const int over = Lh - t_star;
+    int kh = active ? (st.L << 6) | (63 - lane) : -1;
+    uint32_t kr = active && st.L < t_star && st.free_slots > 0
+                      ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+    wave_max_min_sw(kh, kr);
+    const int Lh = kh >> 6;
+    if (Lh <= t_star) break;
+    const int h = 63 - (kh & 63);
+    const int over = Lh - t_star;
+    const int Lt = (int)(kr >> 6), tgt = (int)(kr & 63u);
+    if (kQ > 0) {
       const int kd = readlane(dkey, h);
       const int qd = kd >> 6, jd = 63 - (kd & 63);
       const int e = h * E_loc + jd;
-      const uint64_t hold = ballot(slot_of<kS>(st, S, e) >= 0);
-      if (over < q_min || kr == 0xFFFFFFFFu || kd < 0 || qd < q_min || t_star - Lt < q_min ||
-          ((hold >> tgt) & 1ull))
-        break;
       const int delta = min(qd, min(over, t_star - Lt));
-      const bool is_t = lane == tgt, is_h = lane == h;
-      const int slot = S - st.free_slots;
+      const uint64_t hold = ballot(slot_of<kS>(st, S, e) >= 0);
+      if (delta >= q_min && ((hold >> tgt) & 1ull) == 0) {
+        const bool is_t = lane == tgt, is_h = lane == h;
+        const int slot = S - st.free_slots;
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const bool here = is_t && s == slot;
-        st.sl_e[s] = here ? e : st.sl_e[s];
-        st.sl_q[s] = here ? delta : st.sl_q[s];
+        for (int s = 0; s < kS; ++s) {
+          const bool here = is_t && s == slot;
+          st.sl_e[s] = here ? e : st.sl_e[s];
+          st.sl_q[s] = here ? delta : st.sl_q[s];
+        }
+        st.free_slots -= is_t ? 1 : 0;
+        st.L += is_t ? delta : (is_h ? -delta : 0);
+        // h down to T* with the receiver left below it and quota left on e: h's pair
+        const bool rec = is_h && delta == over && Lt + delta < t_star && qd - delta > 0;
+        st.pf = rec ? e : st.pf;
+        st.py = rec ? tgt : st.py;
+        const int left = qd - delta;
+        const int knew = left > 0 ? (left << 6) | (63 - jd) : -1;
+        const int sel = is_h ? jd : -1;
+#pragma unroll
+        for (int j = 0; j < kQn; ++j) kq[j] = sel == j ? knew : kq[j];
+        dkey = key_max();
+        ++n_rep;
+        ++steps;
+        continue;
       }
-      st.free_slots -= is_t ? 1 : 0;
-      st.L += is_t ? delta : (is_h ? -delta : 0);
-      // h down to T* with the receiver left below it and quota left on e: h's pair
-      const bool rec = is_h && delta == over && Lt + delta < t_star && qd - delta > 0;
-      st.pf = rec ? e : st.pf;
-      st.py = rec ? tgt : st.py;
-      const int left = qd - delta;
-      const int knew = left > 0 ? (left << 6) | (63 - jd) : -1;
-#pragma unroll
-      for (int j = 0; j < kQn; ++j) kq[j] = (is_h && j == jd) ? knew : kq[j];
-      dkey = key_max();
-      if (lane == 0) q_main[e] = left;
-      ++n_rep;
-      ++steps;
     }
-    if (Lh <= t_star) break;
-    const int over = Lh - t_star;
     // every move, plain or relay, is at most the excess: below q_min nothing can move
     if (over < q_min) { stuck = 1; break; }
     // no rank below T* with a free slot: no donor can move directly, go to the relay
@@ -324,11 +331,12 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       const int kd = readlane(dkey, h);
       if (kd < 0 || (kd >> 6) < q_min || t_star - Lt < q_min) plain = false;
       if (!plain) {
-        const int rk = sq_relay_keys<kS, kQn>(st, q_main, kq, dkey, lane, active, E_loc, S, q_min,
-                                              t_star, h, Lh, n_rep);
+        const int rk = sq_relay_keys<kS, kQn>(st, kq, dkey, lane, active, E_loc, S, q_min, t_star,
+                                              h, Lh, n_rep);
         if (rk == 0) { stuck = 1; break; }
         if (rk > 0) { ++steps; continue; }
       }
+      store_q();
     }
     const int qj = plain && lane < E_loc ? q_main[h * E_loc + lane] : 0;
     bool tried = false, moved = false;
@@ -367,6 +375,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     if (kQ > 0) load_q();
     ++steps;
   }
+  if (kQ > 0) store_q();
 }
 
 // The same rule for any load below 2^31: value reductions, then ballots.
