@@ -24,6 +24,8 @@ struct RrGeom {
   int R, T, K, E, ipr, I, seg_cap;
 };
 
+constexpr int kRrPre = 4;   // instance quotas per lane loaded up front (256 instances)
+
 __device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) {
   return max(0, min(a1, b1) - max(a0, b0));
 }
@@ -50,22 +52,41 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   if (e >= E) return;
 
   const bool active = lane < R;
-  int my_i = -1, dup = 0;
-  if (active)
-    for (int j = 0; j < g.ipr; ++j)
-      if (inst_expert[lane * g.ipr + j] == e) {
-        if (my_i < 0) my_i = lane * g.ipr + j; else dup = 1;
+  // Every load is issued before any is used: the expert's column of the load matrix,
+  // this lane's row of the instance table (its experts and quotas: the lane's own
+  // instance of e and that instance's quota come from it), and the first kRrPre x 64
+  // quotas for the row offsets.  The expert's work is then one memory round trip deep.
+  const int C = active ? counts[(int64_t)lane * E + e] : 0;
+  int qpre[kRrPre];
+#pragma unroll
+  for (int u = 0; u < kRrPre; ++u) {
+    const int i = u * kWave + lane;
+    qpre[u] = i < I ? inst_quota[i] : 0;
+  }
+  int my_i = -1, dup = 0, q = 0;
+  if (active) {
+#pragma unroll 8
+    for (int j = 0; j < g.ipr; ++j) {
+      const int ie = inst_expert[lane * g.ipr + j];
+      const int iq = inst_quota[lane * g.ipr + j];
+      if (ie == e) {
+        if (my_i < 0) { my_i = lane * g.ipr + j; q = iq; } else dup = 1;
       }
+    }
+  }
   if (dup) set_err(err, UEP_ERR_INST_DUP);
 
   // exclusive prefix of all quotas: first row of my instance (expert 0 writes the array)
   int running = 0, my_off = 0, negq = 0;
-  for (int base = 0; base < I; base += kWave) {
+  for (int base = 0, u = 0; base < I; base += kWave, ++u) {
     const int i = base + lane;
-    const int q = i < I ? inst_quota[i] : 0;
-    negq |= q < 0;
-    const int incl = wave_incl_scan(q);
-    const int excl = incl - q;
+    int qi = 0;
+#pragma unroll
+    for (int w = 0; w < kRrPre; ++w) qi = w == u ? qpre[w] : qi;
+    if (u >= kRrPre) qi = i < I ? inst_quota[i] : 0;
+    negq |= qi < 0;
+    const int incl = wave_incl_scan(qi);
+    const int excl = incl - qi;
     if (e == 0 && i < I) inst_offset[i] = running + excl;
     const int src = min(max(my_i - base, 0), kWave - 1);
     const int v = shfl(excl, src);
@@ -75,8 +96,6 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   if (e == 0 && lane == 0) inst_offset[I] = running;
   if (e == 0 && negq) set_err(err, UEP_ERR_BAD_QUOTA);
 
-  const int C = active ? counts[(int64_t)lane * E + e] : 0;
-  const int q = my_i >= 0 ? inst_quota[my_i] : 0;
   const int xl = min(C, q);                 // local pass
   const int D = C - xl, Q = q - xl;
   const int d_incl = wave_incl_scan(D), q_incl = wave_incl_scan(Q);
@@ -165,6 +184,7 @@ __global__ __launch_bounds__(256) void rr_assign_flat(const int32_t* __restrict_
 
 constexpr int kRaThreads = 256;
 constexpr size_t kRaMaxLds = 60 * 1024;               // staged segment table limit
+constexpr int kRaBase = 4;                            // list bases per thread held in registers
 
 // One workgroup = 256 * kPer consecutive pairs of one source rank r.  The rank's
 // segment lists (every expert's) are first copied into LDS, compacted by an
@@ -216,9 +236,13 @@ __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restric
     }
   }
 
-  // 2. segment counts of rank r: thread t owns experts [t*m, t*m + m)
+  // 2. segment counts and list bases of rank r, loaded together: thread t owns experts
+  //    [t*m, t*m + m); the bases of its first kRaBase experts stay in registers
   const int m = (g.E + kRaThreads - 1) / kRaThreads;
   const int ea = min(g.E, tid * m), eb = min(g.E, ea + m);
+  int base_[kRaBase];
+#pragma unroll
+  for (int u = 0; u < kRaBase; ++u) base_[u] = ea + u < eb ? seg_base[(int64_t)r * g.E + ea + u] : 0;
   int mine = 0;
   for (int e = ea; e < eb; ++e) {
     const int n = seg_cnt[(int64_t)r * g.E + e];
@@ -239,7 +263,10 @@ __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restric
       lcnt[e] = n;
     }
     loff[e] = run;
-    const int sb = seg_base[(int64_t)r * g.E + e];
+    int sb = 0;
+#pragma unroll
+    for (int u = 0; u < kRaBase; ++u) sb = e - ea == u ? base_[u] : sb;
+    if (e - ea >= kRaBase) sb = seg_base[(int64_t)r * g.E + e];
     for (int k = 0; k < n; ++k) lsegs[run + k] = segs[sb + k];
     run += n;
   }
