@@ -10,12 +10,13 @@
 //   (ascending instance) with two wave scans, and every owner lane writes its
 //   column of the transfer matrix X as interval overlaps.  Every source lane then
 //   emits its segments {first bucket position, instance, row base, length}:
-//   local first, then remote instances in ascending id.  Lanes exchange values only
-//   by readlane (no LDS, no barrier).  Blocks beyond E zero the columns of unused
-//   instances.
-// rr_assign: a workgroup takes 2048 pairs of one rank, stages that rank's segments in
-//   LDS, and gives every pair its instance and dispatch row by a short backwards scan
-//   over its (rank, expert) segments.
+//   local first, then remote instances in ascending id, into the expert's list, and
+//   the first two of them also into a dense (rank, expert) table.  Lanes exchange
+//   values only by readlane (no LDS, no barrier).  Blocks beyond E zero the columns of
+//   unused instances.
+// rr_assign: one thread per 4 or 8 pairs of one rank; each pair reads its (rank,
+//   expert) entry of the dense table (32 bytes) and finds its segment there, or, for
+//   the rare pair past a (rank, expert)'s second segment, in the expert's list.
 #include "common.h"
 
 namespace uep {
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
                                                 int32_t* __restrict__ xfer,
                                                 int32_t* __restrict__ inst_offset,
                                                 int32_t* __restrict__ seg_base,
-                                                int32_t* __restrict__ seg_cnt,
+                                                int4* __restrict__ seg_inline,
                                                 int4* __restrict__ segs, int32_t* err, RrGeom g) {
   const int e = blockIdx.x, lane = threadIdx.x;
   const int R = g.R, I = g.I, E = g.E;
@@ -128,10 +129,21 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   if (lane == 0 && n_tot > g.seg_cap) set_err(err, UEP_ERR_COVER);
   const bool fits = n_tot <= g.seg_cap;
   int k = e * g.seg_cap + (n_incl - n);
+  // A segment goes to the expert's list, and the lane's first two also to its entry of
+  // the dense (rank, expert) table.  The first segment starts at bucket position 0, so
+  // its table record holds the segment count in that field instead.
+  int4* inl = seg_inline + ((int64_t)lane * E + e) * 2;
+  int idx = 0;
+  auto emit = [&](int4 sg) {
+    segs[k++] = sg;
+    if (idx == 0) inl[0] = make_int4(n, sg.y, sg.z, sg.w);
+    else if (idx == 1) inl[1] = sg;
+    ++idx;
+  };
   if (active) {
     seg_base[(int64_t)lane * E + e] = k;
-    seg_cnt[(int64_t)lane * E + e] = fits ? n : 0;
-    if (fits && xl > 0) segs[k++] = make_int4(0, my_i, my_off + overlap(0, d_lo, q_lo, q_lo + Q), xl);
+    if (!fits || n == 0) inl[0] = make_int4(0, -1, 0, 0);
+    if (fits && xl > 0) emit(make_int4(0, my_i, my_off + overlap(0, d_lo, q_lo, q_lo + Q), xl));
   }
   for (uint64_t m = owners; m; m &= m - 1) {
     const int o = __ffsll((unsigned long long)m) - 1;
@@ -142,78 +154,40 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
       if (hi > lo) {
         const int b0 = xl + (lo - d_lo);
         const int before = overlap(0, d_lo, oql, oqh) + (o < lane ? oxl : 0);
-        segs[k++] = make_int4(b0, oi, ooff + before - b0, hi - lo);
+        emit(make_int4(b0, oi, ooff + before - b0, hi - lo));
       }
     }
   }
 }
 
-// Fallback for geometries whose segment table does not fit in LDS: one thread per
-// pair, the (rank, expert) list walked backwards in global memory.
-__global__ __launch_bounds__(256) void rr_assign_flat(const int32_t* __restrict__ ids,
-                                                      const int32_t* __restrict__ bucket_pos,
-                                                      const int32_t* __restrict__ seg_base,
-                                                      const int32_t* __restrict__ seg_cnt,
-                                                      const int4* __restrict__ segs,
-                                                      int32_t* __restrict__ dest_inst,
-                                                      int32_t* __restrict__ dest_row, int32_t* err,
-                                                      int64_t j0, int64_t j1, RrGeom g) {
-  const int64_t j = j0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= j1) return;
-  const int e = ids[j], b = bucket_pos[j];
-  const int r = (int)(j / ((int64_t)g.T * g.K));
-  int di = -1, dr = -1;
-  if (e >= 0 && e < g.E) {
-    const int sb = seg_base[(int64_t)r * g.E + e];
-    int k = seg_cnt[(int64_t)r * g.E + e] - 1;
-    int4 sg = make_int4(0, -1, 0, 0);
-    for (; k >= 0; --k) {
-      sg = segs[sb + k];
-      if (sg.x <= b) break;
-    }
-    if (k >= 0 && b < sg.x + sg.w) {
-      di = sg.y;
-      dr = sg.z + b;
-    } else {
-      set_err(err, UEP_ERR_COVER);
-    }
-  }
-  dest_inst[j] = di;
-  dest_row[j] = dr;
-}
-
 constexpr int kRaThreads = 256;
-constexpr size_t kRaMaxLds = 60 * 1024;               // staged segment table limit
-constexpr int kRaBase = 4;                            // list bases per thread held in registers
+constexpr size_t kRaMaxLds = 32 * 1024;   // rank's table row staged in LDS up to this size
 
-// One workgroup = 256 * kPer consecutive pairs of one source rank r.  The rank's
-// segment lists (every expert's) are first copied into LDS, compacted by an
-// exclusive scan of their lengths: each instance receives r's tokens of one expert
-// only, so the rank has at most I segments.  The pairs' ids and bucket positions are
-// loaded before that staging; each pair then walks its (r, expert) list backwards in
-// LDS to the segment holding its bucket position.
-template <bool kVec4, int kPer>
+// A workgroup takes 256 * kPer consecutive pairs of one source rank r.  The pairs' ids
+// and bucket positions are loaded (16-byte vectors when kVec4) together with rank r's
+// row of the dense table, which kLds stages in LDS with one coalesced copy (E x 32
+// bytes); without kLds each pair gathers its entry from global memory.  An entry holds
+// the (r, expert)'s first two segments, with the segment count in the first.  A bucket
+// position in neither is looked up backwards in the expert's list (only a (rank,
+// expert) with more than two segments has one there).
+template <bool kVec4, int kPer, bool kLds>
 __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restrict__ ids,
                                                         const int32_t* __restrict__ bucket_pos,
                                                         const int32_t* __restrict__ seg_base,
-                                                        const int32_t* __restrict__ seg_cnt,
+                                                        const int4* __restrict__ seg_inline,
                                                         const int4* __restrict__ segs,
                                                         int32_t* __restrict__ dest_inst,
                                                         int32_t* __restrict__ dest_row, int32_t* err,
                                                         int r_begin, RrGeom g) {
-  extern __shared__ int4 ra_lds[];
-  int4* lsegs = ra_lds;                                          // [I]
-  int32_t* loff = reinterpret_cast<int32_t*>(ra_lds + g.I);      // [E]
-  int32_t* lcnt = loff + g.E;                                    // [E]
-  __shared__ int32_t wave_tot[kRaThreads / kWave];
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  extern __shared__ int4 ra_tab[];            // [E][2] when kLds
+  const int tid = threadIdx.x;
   const int r = r_begin + blockIdx.y;
   const int64_t n_pairs = (int64_t)g.T * g.K;
   const int64_t p0 = (int64_t)blockIdx.x * kRaThreads * kPer;
   const int64_t p1 = min(n_pairs, p0 + kRaThreads * kPer);
   const int64_t rbase = (int64_t)r * n_pairs;
 
-  // 1. this thread's pairs (issued first; consumed after the staging)
+  // 1. this thread's pairs
   int e_[kPer], b_[kPer];
   if (kVec4) {
 #pragma unroll
@@ -236,43 +210,22 @@ __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restric
     }
   }
 
-  // 2. segment counts and list bases of rank r, loaded together: thread t owns experts
-  //    [t*m, t*m + m); the bases of its first kRaBase experts stay in registers
-  const int m = (g.E + kRaThreads - 1) / kRaThreads;
-  const int ea = min(g.E, tid * m), eb = min(g.E, ea + m);
-  int base_[kRaBase];
-#pragma unroll
-  for (int u = 0; u < kRaBase; ++u) base_[u] = ea + u < eb ? seg_base[(int64_t)r * g.E + ea + u] : 0;
-  int mine = 0;
-  for (int e = ea; e < eb; ++e) {
-    const int n = seg_cnt[(int64_t)r * g.E + e];
-    lcnt[e] = n;
-    mine += n;
+  // 2. every pair's table entry: rank r's row staged in LDS, or gathered per pair
+  const int4* row = seg_inline + (int64_t)r * g.E * 2;
+  if (kLds) {
+    for (int i = tid; i < 2 * g.E; i += kRaThreads) ra_tab[i] = row[i];
+    __syncthreads();
   }
-  const int incl = wave_incl_scan(mine);
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  int run = incl - mine;
-  for (int ww = 0; ww < w; ++ww) run += wave_tot[ww];
-  // 3. copy the lists into LDS, compacted
-  for (int e = ea; e < eb; ++e) {
-    int n = lcnt[e];
-    if (run + n > g.I) {                    // cannot happen for a consistent plan
-      set_err(err, UEP_ERR_COVER);
-      n = max(0, g.I - run);
-      lcnt[e] = n;
-    }
-    loff[e] = run;
-    int sb = 0;
+  int4 s0[kPer], s1[kPer];
 #pragma unroll
-    for (int u = 0; u < kRaBase; ++u) sb = e - ea == u ? base_[u] : sb;
-    if (e - ea >= kRaBase) sb = seg_base[(int64_t)r * g.E + e];
-    for (int k = 0; k < n; ++k) lsegs[run + k] = segs[sb + k];
-    run += n;
+  for (int it = 0; it < kPer; ++it) {
+    const int e = e_[it] >= 0 && e_[it] < g.E ? e_[it] : 0;
+    const int4* t = kLds ? ra_tab + 2 * e : row + 2 * e;
+    s0[it] = t[0];
+    s1[it] = t[1];
   }
-  __syncthreads();
 
-  // 4. look the pairs up
+  // 3. resolve
   int di_[kPer], dr_[kPer];
   int bad = 0;
 #pragma unroll
@@ -281,23 +234,31 @@ __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restric
     di_[it] = -1;
     dr_[it] = -1;
     if (e < 0 || e >= g.E) continue;
-    const int o = loff[e];
-    int k = lcnt[e] - 1;
-    int4 sg = make_int4(0, -1, 0, 0);
-    for (; k >= 0; --k) {
-      sg = lsegs[o + k];
-      if (sg.x <= b) break;
+    const int cnt = s0[it].x;
+    if (cnt >= 1 && b >= 0 && b < s0[it].w) {
+      di_[it] = s0[it].y;
+      dr_[it] = s0[it].z + b;
+    } else if (cnt >= 2 && b >= s1[it].x && b < s1[it].x + s1[it].w) {
+      di_[it] = s1[it].y;
+      dr_[it] = s1[it].z + b;
+    } else if (cnt > 2) {
+      const int sb = seg_base[(int64_t)r * g.E + e];
+      for (int k = cnt - 1; k >= 2; --k) {
+        const int4 sg = segs[sb + k];
+        if (sg.x <= b) {
+          if (b < sg.x + sg.w) {
+            di_[it] = sg.y;
+            dr_[it] = sg.z + b;
+          }
+          break;
+        }
+      }
     }
-    if (k >= 0 && b < sg.x + sg.w) {
-      di_[it] = sg.y;
-      dr_[it] = sg.z + b;
-    } else {
-      bad = 1;
-    }
+    if (di_[it] < 0) bad = 1;
   }
   if (bad) set_err(err, UEP_ERR_COVER);
 
-  // 5. store
+  // 4. store
   if (kVec4) {
 #pragma unroll
     for (int it = 0; it < kPer / 4; ++it) {
@@ -321,12 +282,14 @@ __global__ __launch_bounds__(kRaThreads) void rr_assign(const int32_t* __restric
   }
 }
 
-static void rr_ws_layout(int R, int E, size_t* off_cnt, size_t* off_segs, size_t* total,
+// Workspace: the list bases [R][E] (int32), the dense table [R][E][2] (int4), then each
+// expert's segment list (seg_cap int4 entries).
+static void rr_ws_layout(int R, int E, size_t* off_inline, size_t* off_segs, size_t* total,
                          int* seg_cap) {
   *seg_cap = 3 * R + 1;
   const size_t a = sizeof(int32_t) * (size_t)R * E;
-  *off_cnt = a;
-  *off_segs = (2 * a + 15) / 16 * 16;
+  *off_inline = (a + 15) / 16 * 16;
+  *off_segs = *off_inline + 2 * sizeof(int4) * (size_t)R * E;
   *total = *off_segs + sizeof(int4) * (size_t)E * (*seg_cap);
 }
 
@@ -358,19 +321,19 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
   if (!counts || !inst_expert || !inst_quota || !xfer || !inst_offset) return UEP_EINVAL;
   const bool pairs = r_end > r_begin && T > 0;
   if (pairs && (!topk_ids || !bucket_pos || !dest_inst || !dest_row)) return UEP_EINVAL;
-  size_t off_cnt, off_segs, total;
+  size_t off_inline, off_segs, total;
   int cap;
-  rr_ws_layout(R, E, &off_cnt, &off_segs, &total, &cap);
+  rr_ws_layout(R, E, &off_inline, &off_segs, &total, &cap);
   if (!ws || ws_bytes < total) return UEP_EWORKSPACE;
   RrGeom g{R, T, K, E, inst_per_rank, R * inst_per_rank, cap};
   char* w = static_cast<char*>(ws);
   int32_t* seg_base = reinterpret_cast<int32_t*>(w);
-  int32_t* seg_cnt = reinterpret_cast<int32_t*>(w + off_cnt);
+  int4* seg_inline = reinterpret_cast<int4*>(w + off_inline);
   int4* segs = reinterpret_cast<int4*>(w + off_segs);
   hipStream_t s = uep_stream(stream);
   const int blocks = E > g.I ? E : g.I;
   hipLaunchKernelGGL(rr_expert, dim3(blocks), dim3(64), 0, s, counts, inst_expert, inst_quota,
-                     xfer, inst_offset, seg_base, seg_cnt, segs, err, g);
+                     xfer, inst_offset, seg_base, seg_inline, segs, err, g);
   UEP_CHECK_LAUNCH();
   if (pairs) {
     const bool vec = ((int64_t)T * K) % 4 == 0 &&
@@ -382,25 +345,24 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
     const int per = pairs_all >= 512ll * kRaThreads * 8 ? 8 : 4;
     const int64_t chunks = ((int64_t)T * K + kRaThreads * per - 1) / (kRaThreads * per);
     const dim3 grid((unsigned)chunks, (unsigned)(r_end - r_begin));
-    const size_t lds = sizeof(int4) * (size_t)g.I + 2 * sizeof(int32_t) * (size_t)E;
-    if (lds > kRaMaxLds) {
-      const int64_t j0 = (int64_t)r_begin * T * K, j1 = (int64_t)r_end * T * K;
-      hipLaunchKernelGGL(rr_assign_flat, dim3((unsigned)((j1 - j0 + 255) / 256)), dim3(256), 0, s,
-                         topk_ids, bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err,
-                         j0, j1, g);
-    } else if (vec && per == 8) {
-      hipLaunchKernelGGL((rr_assign<true, 8>), grid, dim3(kRaThreads), lds, s, topk_ids,
-                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
-    } else if (vec) {
-      hipLaunchKernelGGL((rr_assign<true, 4>), grid, dim3(kRaThreads), lds, s, topk_ids,
-                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
-    } else if (per == 8) {
-      hipLaunchKernelGGL((rr_assign<false, 8>), grid, dim3(kRaThreads), lds, s, topk_ids,
-                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
-    } else {
-      hipLaunchKernelGGL((rr_assign<false, 4>), grid, dim3(kRaThreads), lds, s, topk_ids,
-                         bucket_pos, seg_base, seg_cnt, segs, dest_inst, dest_row, err, r_begin, g);
-    }
+    // rank r's table row in LDS when it is small enough for several workgroups per CU
+    const size_t tab = 2 * sizeof(int4) * (size_t)E;
+    const bool lds = tab <= kRaMaxLds;
+#define UEP_RA(V, P, L)                                                                          \
+  hipLaunchKernelGGL((rr_assign<V, P, L>), grid, dim3(kRaThreads), L ? tab : 0, s, topk_ids,     \
+                     bucket_pos, (const int32_t*)seg_base, (const int4*)seg_inline,             \
+                     (const int4*)segs, dest_inst, dest_row, err, r_begin, g)
+#define UEP_RA_L(V, P)                   \
+  do {                                   \
+    if (lds) UEP_RA(V, P, true);         \
+    else UEP_RA(V, P, false);            \
+  } while (0)
+    if (vec && per == 8) UEP_RA_L(true, 8);
+    else if (vec) UEP_RA_L(true, 4);
+    else if (per == 8) UEP_RA_L(false, 8);
+    else UEP_RA_L(false, 4);
+#undef UEP_RA_L
+#undef UEP_RA
     UEP_CHECK_LAUNCH();
   }
   return UEP_OK;
