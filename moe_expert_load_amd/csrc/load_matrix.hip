@@ -110,23 +110,29 @@ __global__ __launch_bounds__(256) void lm_hist(const int32_t* __restrict__ ids,
   for (int e = tid; e < g.E; e += 256) ch[e] = lh_lds[e];
 }
 
-// Counts only: counts[r][e] = sum of rank r's chunk histograms (one workgroup per rank,
-// up to 16 loads in flight per thread).
+// Counts only: counts[r][e] = sum of rank r's chunk histograms (one workgroup per rank).
+// When E < 256, tpe adjacent threads share an expert, each over every tpe-th chunk
+// (so all 256 threads load, up to 16 loads in flight each), and add their sums with
+// lane exchanges.
 __global__ __launch_bounds__(256) void lm_counts(const int32_t* __restrict__ chunk_hist,
                                                  int32_t* __restrict__ counts, LmGeom g) {
   const int r = blockIdx.x;
   const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
-  for (int e = threadIdx.x; e < g.E; e += 256) {
+  const int tpe = g.E >= 256 ? 1 : g.E >= 128 ? 2 : g.E >= 64 ? 4 : g.E >= 32 ? 8 : 16;
+  const int part = threadIdx.x % tpe;
+  for (int e = threadIdx.x / tpe; e < g.E; e += 256 / tpe) {
     int s = 0;
     if (g.T > 0)
-      for (int c0 = 0; c0 < g.n_chunks; c0 += 16) {
+      for (int c0 = part; c0 < g.n_chunks; c0 += 16 * tpe) {
         int acc[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] = ch[(int64_t)min(c0 + u, g.n_chunks - 1) * g.E + e];
+        for (int u = 0; u < 16; ++u)
+          acc[u] = ch[(int64_t)min(c0 + u * tpe, g.n_chunks - 1) * g.E + e];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) s += c0 + u < g.n_chunks ? acc[u] : 0;
+        for (int u = 0; u < 16; ++u) s += c0 + u * tpe < g.n_chunks ? acc[u] : 0;
       }
-    counts[(int64_t)r * g.E + e] = s;
+    for (int o = 1; o < tpe; o <<= 1) s += __shfl_xor(s, o, kWave);
+    if (part == 0) counts[(int64_t)r * g.E + e] = s;
   }
 }
 

@@ -42,15 +42,21 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
   const int e = blockIdx.x, lane = threadIdx.x;
   const int R = g.R, I = g.I, E = g.E;
 
-  if (e < I) {                              // column of an unused instance, checks of the table
+  // block e also clears X's column e when instance e is unused, and checks its table
+  // entry; an expert's block does this after its own work, whose loads go first
+  auto unused_column = [&]() {
+    if (e >= I) return;
     const int ie = inst_expert[e];
     if (ie < 0) {
       for (int s = lane; s < R; s += kWave) xfer[(int64_t)s * I + e] = 0;
       if (lane == 0 && inst_quota[e] != 0) set_err(err, UEP_ERR_BAD_QUOTA);
     }
     if (lane == 0 && (ie >= E || ie < -1)) set_err(err, UEP_ERR_BAD_QUOTA);
+  };
+  if (e >= E) {
+    unused_column();
+    return;
   }
-  if (e >= E) return;
 
   const bool active = lane < R;
   // Every load is issued before any is used: the expert's column of the load matrix,
@@ -158,6 +164,7 @@ __global__ __launch_bounds__(64) void rr_expert(const int32_t* __restrict__ coun
       }
     }
   }
+  unused_column();
 }
 
 constexpr int kRaThreads = 256;
