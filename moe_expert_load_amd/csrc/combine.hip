@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
 #pragma clang fp contract(off)
   const int lane = threadIdx.x % kWave;
   const int64_t b = xcd_block(blockIdx.x, gridDim.x);
-  const int64_t g = g0 + b * kCbTokPerBlock + threadIdx.x / kWave;
+  // the wave's token, uniform (readfirstlane), so the row spans below live in SGPRs
+  const int64_t g = g0 + b * kCbTokPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (g >= g1) return;
   const int d_mine = checked_row(lane < K ? dest_row[g * K + lane] : -1, out_rows, err);
   const int w_mine = lane < K ? __float_as_int(gate_w[g * K + lane]) : 0;
@@ -59,13 +60,10 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
         const int k = k0 + q;
         dq[q] = k < K ? readlane(d_mine, k) : -1;
         wq[q] = k < K ? __int_as_float(readlane(w_mine, k)) : 0.0f;
-        if (dq[q] >= 0) {
-          const u32x4* src = y_disp + (int64_t)dq[q] * nvec;
+        if (dq[q] >= 0) {          // a span per row: vectors past its end read as zero
+          const span_t src = span_of(y_disp + (int64_t)dq[q] * nvec, (int64_t)nvec * 16);
 #pragma unroll
-          for (int u = 0; u < kCbVec; ++u) {
-            const int v = v0 + u * kWave + lane;
-            if (v < nvec) buf[q][u] = __builtin_nontemporal_load(src + v);
-          }
+          for (int u = 0; u < kCbVec; ++u) buf[q][u] = stream_load(src, (v0 + u * kWave + lane) * 16);
         }
       }
 #pragma unroll
@@ -86,15 +84,12 @@ __global__ __launch_bounds__(kCbThreads) void combine_kernel(const u32x4* __rest
     }
     const span_t dst = span_of(y + g * nvec, (int64_t)nvec * 16);
 #pragma unroll
-    for (int u = 0; u < kCbVec; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v < nvec) {
-        u32x4 o;
+    for (int u = 0; u < kCbVec; ++u) {           // past the row's end: not written
+      u32x4 o;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          o[c] = f32_to_bf16(acc[u * 8 + 2 * c]) | (f32_to_bf16(acc[u * 8 + 2 * c + 1]) << 16);
-        stream_store(o, dst, v * 16);
-      }
+      for (int c = 0; c < 4; ++c)
+        o[c] = f32_to_bf16(acc[u * 8 + 2 * c]) | (f32_to_bf16(acc[u * 8 + 2 * c + 1]) << 16);
+      stream_store(o, dst, (v0 + u * kWave + lane) * 16);
     }
   }
 }

@@ -66,26 +66,23 @@ __global__ __launch_bounds__(kPmThreads) void permute_kernel(const u32x4* __rest
                                                              int32_t* err) {
   const int lane = threadIdx.x % kWave;
   const int64_t b = xcd_block(blockIdx.x, gridDim.x);
-  const int64_t g = g0 + b * kPmTokPerBlock + threadIdx.x / kWave;
+  // the wave's token, uniform (readfirstlane), so the row spans below live in SGPRs
+  const int64_t g = g0 + b * kPmTokPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (g >= g1) return;
   const int d_mine = checked_row(lane < K ? dest_row[g * K + lane] : -1, out_rows, err);
-  const u32x4* src = x + g * nvec;
+  // source and destination rows as buffer spans: a vector past the row's end reads as
+  // zero and is not written, so no lane needs a guard
+  const span_t src = span_of(x + g * nvec, (int64_t)nvec * 16);
   for (int v0 = 0; v0 < nvec; v0 += kVec * kWave) {
     u32x4 buf[kVec];
 #pragma unroll
-    for (int u = 0; u < kVec; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v < nvec) buf[u] = __builtin_nontemporal_load(src + v);
-    }
+    for (int u = 0; u < kVec; ++u) buf[u] = stream_load(src, (v0 + u * kWave + lane) * 16);
     for (int k = 0; k < K; ++k) {
       const int d = readlane(d_mine, k);
       if (d < 0) continue;
       const span_t dst = span_of(out + (int64_t)d * nvec, (int64_t)nvec * 16);
 #pragma unroll
-      for (int u = 0; u < kVec; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (v < nvec) stream_store(buf[u], dst, v * 16);
-      }
+      for (int u = 0; u < kVec; ++u) stream_store(buf[u], dst, (v0 + u * kWave + lane) * 16);
     }
   }
 }
