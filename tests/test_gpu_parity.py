@@ -329,6 +329,29 @@ def test_solve_quota_tie_and_order_rules(case):
                                          int(case["stuck"])]
 
 
+@pytest.mark.parametrize("seed", [185, 94, 62, 279, 69, 102, 90, 37])
+def test_plan_many_segments_per_rank_expert(seed):
+    """One dominant expert replicated over most ranks (2-5 slots per rank), so a rank's
+    tokens of it split over three to five instances: the assignment resolves those past
+    its dense table's first two segments by walking the expert's list.  The seeds were
+    picked with the oracle for the most such (rank, expert) pairs; whole plan bit-exact."""
+    rng = np.random.default_rng(9000 + seed)
+    R = int(rng.integers(4, 17))
+    E = R * int(rng.integers(1, 4))
+    K = int(rng.integers(1, min(E, 4) + 1))
+    T = int(rng.integers(100, 600))
+    S = int(rng.integers(2, 6))
+    q_min = int(rng.integers(0, 20))
+    p = rng.dirichlet(np.full(E, 0.1))
+    p[int(rng.integers(E))] += 3.0 * rng.random()
+    ids = random_routing(rng, R, T, K, E, p=p / p.sum())
+    say(f"case: many segments seed={seed} R={R} E={E} K={K} T={T} S={S} q_min={q_min}")
+    o = oracle_plan(ids, E, S, q_min)
+    inst = [np.nonzero(np.asarray(o["plan"]["inst_expert"]) == e)[0] for e in range(E)]
+    assert max((o["xfer"][:, i] > 0).sum(axis=1).max() for i in inst if len(i)) >= 3
+    compare_plan(plan_on_gpu(U, to_dev(ids), E, S, q_min), o, S)
+
+
 def test_solve_quota_random_many():
     """The solver alone on 500 random load matrices: 1 to 64 ranks, E/R from 1 to 24 (the
     register-key search for E/R up to 4 and up to 8, the LDS search above), 0 to 8 slots
