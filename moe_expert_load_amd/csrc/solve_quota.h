@@ -145,6 +145,44 @@ __device__ bool sq_relay(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
   }
 }
 
+// Donor key of main j with quota q: (q << 6 | 63 - j) when q > 0, else ~j.  The keys of
+// one rank are distinct, order its mains by quota descending then index ascending, and
+// 63 - (key & 63) gives j back in both forms; key >> 6 is q, or -1 when q is 0.  The
+// fast search keeps each rank's keys sorted in that order, so the first donor is the
+// first key.
+__device__ __forceinline__ int donor_key(int q, int j) { return q > 0 ? (q << 6) | (63 - j) : ~j; }
+
+__device__ __forceinline__ int key_main(int k) { return 63 - (k & 63); }
+
+// Odd-even transposition sort, descending (kQ rounds sort kQ keys).
+template <int kQ>
+__device__ __forceinline__ void sort_keys(int (&k)[kQ]) {
+#pragma unroll
+  for (int r = 0; r < kQ; ++r)
+#pragma unroll
+    for (int j = r & 1; j + 1 < kQ; j += 2) {
+      const int a = max(k[j], k[j + 1]), b = min(k[j], k[j + 1]);
+      k[j] = a;
+      k[j + 1] = b;
+    }
+}
+
+// Sorted keys with the first one replaced by x <= k[0]: entry j of the merge of
+// k[1..kQ-1] with x is the median of k[j], k[j + 1] and x (the last is min(k[kQ-1], x)).
+// With x = k[0] the keys stay as they are, so every lane runs it.
+__device__ __forceinline__ int med3_i32(int a, int b, int c) {
+  int r;
+  asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <int kQ>
+__device__ __forceinline__ void replace_first_key(int (&k)[kQ], int x) {
+#pragma unroll
+  for (int j = 0; j + 1 < kQ; ++j) k[j] = med3_i32(k[j], k[j + 1], x);
+  k[kQ - 1] = min(k[kQ - 1], x);
+}
+
 // Relay on the register keys of the fast search below (the rule of sq_relay; lanes as
 // there).  By the relay lemma a qualifying relay rank holds no replica, so it never
 // holds h's first donor and the first donor always finds x; should no qualifying rank
@@ -162,7 +200,7 @@ __device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
   const int jf = st.pf - lane * E_loc;      // the pair's main among the lane's own mains
   int kf = -1;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) kf = j == jf ? kq[j] : kf;
+  for (int j = 0; j < kQ; ++j) kf = key_main(kq[j]) == jf ? kq[j] : kf;
   const int qf = kf >= 0 ? kf >> 6 : 0;
   const int d2 = min(qf, t_star - Ly);
   const bool cand = active && lane != h && st.free_slots > 0 && st.L >= t_star && st.pf >= 0 &&
@@ -192,16 +230,14 @@ __device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
   const bool rec = is_h && d == Lh - t_star && d < d2x && qd - d > 0;
   st.pf = rec ? e : (is_x ? -1 : st.pf);
   st.py = rec ? x : st.py;
-  const int ke = qd - d > 0 ? ((qd - d) << 6) | (63 - jd) : -1;
-  const int kfn = qfx - d2x > 0 ? ((qfx - d2x) << 6) | (63 - jfx) : -1;
+  const int ke = donor_key(qd - d, jd);
+  const int kfn = donor_key(qfx - d2x, jfx);
   const int sel = is_h ? jd : (is_x ? jfx : -1);
   const int knew = is_h ? ke : kfn;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) kq[j] = sel == j ? knew : kq[j];
-  int k = kq[0];
-#pragma unroll
-  for (int j = 1; j < kQ; ++j) k = max(k, kq[j]);
-  dkey = k;
+  for (int j = 0; j < kQ; ++j) kq[j] = key_main(kq[j]) == sel ? knew : kq[j];
+  sort_keys<kQ>(kq);
+  dkey = kq[0];
   ++n_rep;
   return 1;
 }
@@ -211,6 +247,9 @@ __device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
 // swaps (permlane16_swap pairs rows 0-1 and 2-3 of its operands, permlane32_swap the
 // halves), so the last steps stay in VALU and one readfirstlane ends each; the two
 // chains are interleaved so neither waits on its own DPP hazards.
+// kHalf (R <= 32: lanes 32..63 hold no rank): the halves need no exchange, and lane 0
+// already holds both results after the row swap.
+template <bool kHalf>
 __device__ __forceinline__ void wave_max_min_sw(int& kh, uint32_t& kr) {
   int a = kh;
   uint32_t b = kr;
@@ -226,6 +265,11 @@ __device__ __forceinline__ void wave_max_min_sw(int& kh, uint32_t& kr) {
   const auto b16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
   a = max((int)a16[0], (int)a16[1]);
   b = min((uint32_t)b16[0], (uint32_t)b16[1]);
+  if (kHalf) {
+    kh = __builtin_amdgcn_readfirstlane(a);
+    kr = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+    return;
+  }
   const auto a32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
   const auto b32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
   kh = __builtin_amdgcn_readfirstlane(max((int)a32[0], (int)a32[1]));
@@ -251,33 +295,30 @@ __device__ __forceinline__ void wave_max_min_sw(int& kh, uint32_t& kr) {
 // copy of the first donor (or the lemma's premise failed) does the step take the donor
 // scan or the general relay, on the quotas written back to LDS, and reload the keys
 // after.  The quotas are written back to LDS at the end for the outputs.
-template <int kS, int kQ>
+template <int kS, int kQ, bool kHalf>
 __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, int lane, bool active,
                                               int R, int E_loc, int S, int q_min, int t_star,
                                               int& steps, int& n_rep, int& stuck) {
   constexpr int kQn = kQ > 0 ? kQ : 1;
-  int kq[kQn];                       // donor key of each own main (fast steps only)
-  int dkey = -1;                     // max of kq
-  auto key_max = [&]() {
-    int k = kq[0];
-#pragma unroll
-    for (int j = 1; j < kQn; ++j) k = max(k, kq[j]);
-    return k;
-  };
+  int kq[kQn];                       // donor keys of the own mains, sorted (fast steps only)
+  int dkey = -1;                     // kq[0], the rank's first donor
   auto load_q = [&]() {              // clamped addresses: every read issues, no branch
     const int r = min(lane, R - 1);
 #pragma unroll
     for (int j = 0; j < kQn; ++j) {
       const int v = q_main[r * E_loc + min(j, E_loc - 1)];
-      kq[j] = (active && j < E_loc && v > 0) ? (v << 6) | (63 - j) : -1;
+      kq[j] = donor_key(active && j < E_loc ? v : 0, j);
     }
-    dkey = key_max();
+    sort_keys<kQn>(kq);
+    dkey = kq[0];
   };
   auto store_q = [&]() {
     if (active) {
 #pragma unroll
-      for (int j = 0; j < kQn; ++j)
-        if (j < E_loc) q_main[lane * E_loc + j] = kq[j] >= 0 ? kq[j] >> 6 : 0;
+      for (int j = 0; j < kQn; ++j) {
+        const int jj = key_main(kq[j]);
+        if (jj < E_loc) q_main[lane * E_loc + jj] = kq[j] >= 0 ? kq[j] >> 6 : 0;
+      }
     }
   };
   if (kQ > 0) load_q();
@@ -285,7 +326,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     int kh = active ? (st.L << 6) | (63 - lane) : -1;
     uint32_t kr = active && st.L < t_star && st.free_slots > 0
                       ? ((uint32_t)st.L << 6) | (uint32_t)lane : 0xFFFFFFFFu;
-    wave_max_min_sw(kh, kr);
+    wave_max_min_sw<kHalf>(kh, kr);
     const int Lh = kh >> 6;
     if (Lh <= t_star) break;
     const int h = 63 - (kh & 63);
@@ -295,29 +336,41 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       const int kd = readlane(dkey, h);
       const int qd = kd >> 6, jd = 63 - (kd & 63);
       const int e = h * E_loc + jd;
-      const int delta = min(qd, min(over, t_star - Lt));
-      const uint64_t hold = ballot(slot_of<kS>(st, S, e) >= 0);
-      if (delta >= q_min && ((hold >> tgt) & 1ull) == 0) {
-        const bool is_t = lane == tgt, is_h = lane == h;
-        const int slot = S - st.free_slots;
+      const int room = min(qd, t_star - Lt);
+      const int delta = min(over, room);
+      // does the receiver hold a copy of e?  Not with one slot per rank: its only slot is
+      // free, and e's main is on h.  (Slots past S hold -1, never an expert.)
+      bool held = false;
+      if (kS > 1) {
+        bool any = false;
 #pragma unroll
-        for (int s = 0; s < kS; ++s) {
-          const bool here = is_t && s == slot;
-          st.sl_e[s] = here ? e : st.sl_e[s];
-          st.sl_q[s] = here ? delta : st.sl_q[s];
+        for (int s = 0; s < kS; ++s) any |= st.sl_e[s] == e;
+        held = ((ballot(any) >> tgt) & 1ull) != 0;
+      }
+      if (delta >= q_min && !held) {
+        const bool is_t = lane == tgt, is_h = lane == h;
+        if (kS == 1) {          // the receiver's only slot is free
+          st.sl_e[0] = is_t ? e : st.sl_e[0];
+          st.sl_q[0] = is_t ? delta : st.sl_q[0];
+        } else {
+          const int slot = S - st.free_slots;
+#pragma unroll
+          for (int s = 0; s < kS; ++s) {
+            const bool here = is_t && s == slot;
+            st.sl_e[s] = here ? e : st.sl_e[s];
+            st.sl_q[s] = here ? delta : st.sl_q[s];
+          }
         }
         st.free_slots -= is_t ? 1 : 0;
-        st.L += is_t ? delta : (is_h ? -delta : 0);
-        // h down to T* with the receiver left below it and quota left on e: h's pair
-        const bool rec = is_h && delta == over && Lt + delta < t_star && qd - delta > 0;
+        st.L = is_t ? Lt + delta : (is_h ? Lh - delta : st.L);
+        // h down to T* (delta = over) with the receiver left below it and quota left on
+        // e (delta below both the room and the quota): h's pair
+        const bool rec = is_h && over < room;
         st.pf = rec ? e : st.pf;
         st.py = rec ? tgt : st.py;
-        const int left = qd - delta;
-        const int knew = left > 0 ? (left << 6) | (63 - jd) : -1;
-        const int sel = is_h ? jd : -1;
-#pragma unroll
-        for (int j = 0; j < kQn; ++j) kq[j] = sel == j ? knew : kq[j];
-        dkey = key_max();
+        // h's first donor (its first key) gets the quota left, the other lanes keep theirs
+        replace_first_key<kQn>(kq, is_h ? donor_key(qd - delta, jd) : kq[0]);
+        dkey = kq[0];
         ++n_rep;
         ++steps;
         continue;
@@ -478,12 +531,17 @@ __device__ __forceinline__ void solve_body(const int32_t* __restrict__ counts, i
   const int t_star = (total + R - 1) / R;
 
   int steps = 0, n_rep = 0, stuck = 0;
-  if (total < (1 << kPackBits) && E_loc <= 4)
-    search_packed<kS, 4>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+#define UEP_SQ_PACKED(KQ, HALF) \
+  search_packed<kS, KQ, HALF>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck)
+  if (total < (1 << kPackBits) && E_loc <= 4 && R <= 32)
+    UEP_SQ_PACKED(4, true);
+  else if (total < (1 << kPackBits) && E_loc <= 4)
+    UEP_SQ_PACKED(4, false);
   else if (total < (1 << kPackBits) && E_loc <= 8)
-    search_packed<kS, 8>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+    UEP_SQ_PACKED(8, false);
   else if (total < (1 << kPackBits))
-    search_packed<kS, 0>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
+    UEP_SQ_PACKED(0, false);
+#undef UEP_SQ_PACKED
   else
     search_wide<kS>(st, q_main, lane, active, R, E_loc, S, q_min, t_star, steps, n_rep, stuck);
 
