@@ -183,18 +183,35 @@ __device__ __forceinline__ void replace_first_key(int (&k)[kQ], int x) {
   k[kQ - 1] = min(k[kQ - 1], x);
 }
 
+// One pass of compare-exchanges down the keys: puts back in order a sorted set of keys
+// in which one key has decreased.
+template <int kQ>
+__device__ __forceinline__ void sink_key(int (&k)[kQ]) {
+#pragma unroll
+  for (int j = 0; j + 1 < kQ; ++j) {
+    const int a = max(k[j], k[j + 1]), b = min(k[j], k[j + 1]);
+    k[j] = a;
+    k[j + 1] = b;
+  }
+}
+
 // Relay on the register keys of the fast search below (the rule of sq_relay; lanes as
-// there).  By the relay lemma a qualifying relay rank holds no replica, so it never
-// holds h's first donor and the first donor always finds x; should no qualifying rank
-// be free of that donor all the same, the general relay decides (returns -1).  The
-// quota of x's pair main f is read from x's own keys and every update is a select on
-// the registers only (the caller writes the quotas to LDS when it needs them there).
+// there).  kd is h's first donor key; the caller has checked h's excess against q_min.
+// By the relay lemma a qualifying relay rank holds no replica, so it never holds h's
+// first donor and the first donor always finds x; should no qualifying rank be free of
+// that donor all the same, the general relay decides (returns -1).  Each lane reads the
+// quota of its own pair main f from its keys, and every update is a select on the
+// registers only (the caller writes the quotas to LDS when it needs them there).
 // Returns 1 for a move, 0 for none.
 template <int kS, int kQ>
-__device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
-                                             int& dkey, int lane, bool active, int E_loc, int S,
-                                             int q_min, int t_star, int h, int Lh, int& n_rep) {
-  if (Lh - t_star < q_min) return 0;
+__device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ], int lane,
+                                             bool active, int E_loc, int S,
+                                             int q_min, int t_star, int h, int Lh, int kd,
+                                             int& n_rep) {
+  // no donor of at least q_min on h: nothing can move
+  if (kd < 0 || (kd >> 6) < q_min) return 0;
+  const int qd = kd >> 6, jd = key_main(kd);
+  const int e = h * E_loc + jd;
   // this lane as the relay rank x: its recorded pair, if still live
   const int Ly = shfl(st.L, st.pf >= 0 ? st.py : lane);
   const int jf = st.pf - lane * E_loc;      // the pair's main among the lane's own mains
@@ -205,39 +222,52 @@ __device__ __forceinline__ int sq_relay_keys(SqLane<kS>& st, int (&kq)[kQ],
   const int d2 = min(qf, t_star - Ly);
   const bool cand = active && lane != h && st.free_slots > 0 && st.L >= t_star && st.pf >= 0 &&
                     Ly < t_star && qf > 0 && t_star - (st.L - d2) >= q_min;
-  if (ballot(cand) == 0) return 0;
-  const int kd = readlane(dkey, h);         // h's first donor
-  if (kd < 0 || (kd >> 6) < q_min) return 0;
-  const int qd = kd >> 6, jd = 63 - (kd & 63);
-  const int e = h * E_loc + jd;
-  const int x = first_lane(cand && slot_of<kS>(st, S, e) < 0);
-  if (x < 0) return -1;
-  const int f = readlane(st.pf, x), y = readlane(st.py, x), d2x = readlane(d2, x);
-  const int jfx = readlane(jf, x), qfx = readlane(qf, x);
-  const int d = min(qd, min(Lh - t_star, t_star - (readlane(st.L, x) - d2x)));
-  const bool is_y = lane == y, is_x = lane == x, is_h = lane == h;
-  const int slot = S - st.free_slots;
+  bool copy = false;
 #pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    const bool here = is_x && s == slot;
-    st.sl_q[s] += (is_y && s < S && st.sl_e[s] == f) ? d2x : 0;
-    st.sl_e[s] = here ? e : st.sl_e[s];
-    st.sl_q[s] = here ? d : st.sl_q[s];
+  for (int s = 0; s < kS; ++s) copy |= st.sl_e[s] == e;
+  const uint64_t any = ballot(cand), free_of_e = ballot(cand && !copy);
+  if (free_of_e == 0) return any ? -1 : 0;
+  const int x = __ffsll((unsigned long long)free_of_e) - 1;
+  const int f = readlane(st.pf, x), y = readlane(st.py, x), d2x = readlane(d2, x);
+  const int Lx = readlane(st.L, x), Lyx = readlane(Ly, x);
+  const int d = min(qd, min(Lh - t_star, t_star - (Lx - d2x)));
+  const bool is_y = lane == y, is_x = lane == x, is_h = lane == h;
+  if (kS == 1) {            // x's only slot is free
+    st.sl_q[0] = is_x ? d : ((is_y && st.sl_e[0] == f) ? st.sl_q[0] + d2x : st.sl_q[0]);
+    st.sl_e[0] = is_x ? e : st.sl_e[0];
+  } else {
+    const int slot = S - st.free_slots;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const bool here = is_x && s == slot;
+      st.sl_q[s] += (is_y && s < S && st.sl_e[s] == f) ? d2x : 0;
+      st.sl_e[s] = here ? e : st.sl_e[s];
+      st.sl_q[s] = here ? d : st.sl_q[s];
+    }
   }
   st.free_slots -= is_x ? 1 : 0;
-  st.L += is_y ? d2x : (is_x ? d - d2x : (is_h ? -d : 0));
+  // the three new loads are uniform; one select each (the lanes differ)
+  const int nLy = Lyx + d2x, nLx = Lx + d - d2x, nLh = Lh - d;
+  int L = st.L;
+  L = is_h ? nLh : L;
+  L = is_x ? nLx : L;
+  L = is_y ? nLy : L;
+  st.L = L;
   // h down to T* with x left below it and quota left on e: h's pair; x's pair is used up
   const bool rec = is_h && d == Lh - t_star && d < d2x && qd - d > 0;
   st.pf = rec ? e : (is_x ? -1 : st.pf);
   st.py = rec ? x : st.py;
-  const int ke = donor_key(qd - d, jd);
-  const int kfn = donor_key(qfx - d2x, jfx);
-  const int sel = is_h ? jd : (is_x ? jfx : -1);
-  const int knew = is_h ? ke : kfn;
+  // h's first donor and x's pair main lose quota: each lane changes at most one key,
+  // which only falls, so one pass down puts the keys back in order
+  const int ke = donor_key(qd - d, jd);                 // uniform
+  const int kfn = donor_key(qf - d2, jf);               // this lane's, used on x
+  int old = kf, knew = kf;                              // other lanes: no change
+  old = is_h ? kq[0] : old;
+  knew = is_h ? ke : knew;
+  knew = is_x ? kfn : knew;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) kq[j] = key_main(kq[j]) == sel ? knew : kq[j];
-  sort_keys<kQ>(kq);
-  dkey = kq[0];
+  for (int j = 0; j < kQ; ++j) kq[j] = kq[j] == old ? knew : kq[j];
+  sink_key<kQ>(kq);
   ++n_rep;
   return 1;
 }
@@ -300,8 +330,9 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
                                               int R, int E_loc, int S, int q_min, int t_star,
                                               int& steps, int& n_rep, int& stuck) {
   constexpr int kQn = kQ > 0 ? kQ : 1;
-  int kq[kQn];                       // donor keys of the own mains, sorted (fast steps only)
-  int dkey = -1;                     // kq[0], the rank's first donor
+  int kq[kQn];                       // donor keys of the own mains, sorted (fast steps only);
+                                     // kq[0] is the rank's first donor
+  int nrep = 0;                      // replicas opened = steps taken (every step opens one)
   auto load_q = [&]() {              // clamped addresses: every read issues, no branch
     const int r = min(lane, R - 1);
 #pragma unroll
@@ -310,7 +341,6 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       kq[j] = donor_key(active && j < E_loc ? v : 0, j);
     }
     sort_keys<kQn>(kq);
-    dkey = kq[0];
   };
   auto store_q = [&]() {
     if (active) {
@@ -333,7 +363,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     const int over = Lh - t_star;
     const int Lt = (int)(kr >> 6), tgt = (int)(kr & 63u);
     if (kQ > 0) {
-      const int kd = readlane(dkey, h);
+      const int kd = readlane(kq[0], h);
       const int qd = kd >> 6, jd = 63 - (kd & 63);
       const int e = h * E_loc + jd;
       const int room = min(qd, t_star - Lt);
@@ -347,7 +377,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
         for (int s = 0; s < kS; ++s) any |= st.sl_e[s] == e;
         held = ((ballot(any) >> tgt) & 1ull) != 0;
       }
-      if (delta >= q_min && !held) {
+      if (__builtin_expect(delta >= q_min && !held, 1)) {
         const bool is_t = lane == tgt, is_h = lane == h;
         if (kS == 1) {          // the receiver's only slot is free
           st.sl_e[0] = is_t ? e : st.sl_e[0];
@@ -370,9 +400,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
         st.py = rec ? tgt : st.py;
         // h's first donor (its first key) gets the quota left, the other lanes keep theirs
         replace_first_key<kQn>(kq, is_h ? donor_key(qd - delta, jd) : kq[0]);
-        dkey = kq[0];
-        ++n_rep;
-        ++steps;
+        ++nrep;
         continue;
       }
     }
@@ -381,13 +409,13 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
     // no rank below T* with a free slot: no donor can move directly, go to the relay
     bool plain = kr != 0xFFFFFFFFu;
     if (kQ > 0) {
-      const int kd = readlane(dkey, h);
+      const int kd = readlane(kq[0], h);
       if (kd < 0 || (kd >> 6) < q_min || t_star - Lt < q_min) plain = false;
       if (!plain) {
-        const int rk = sq_relay_keys<kS, kQn>(st, kq, dkey, lane, active, E_loc, S, q_min, t_star,
-                                              h, Lh, n_rep);
+        const int rk = sq_relay_keys<kS, kQn>(st, kq, lane, active, E_loc, S, q_min, t_star,
+                                              h, Lh, kd, nrep);
         if (rk == 0) { stuck = 1; break; }
-        if (rk > 0) { ++steps; continue; }
+        if (rk > 0) continue;
       }
       store_q();
     }
@@ -415,7 +443,7 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
             if (delta == over && Lt2 + delta < t_star && qd - delta > 0) { st.pf = e; st.py = tgt2; }
           }
           if (lane == 0) q_main[e] = qd - delta;
-          ++n_rep;
+          ++nrep;
           moved = true;
           break;
         }
@@ -423,12 +451,13 @@ __device__ __forceinline__ void search_packed(SqLane<kS>& st, int32_t* q_main, i
       if (lane == jd) tried = true;
     }
     if (!moved)
-      moved = sq_relay<kS>(st, q_main, lane, active, E_loc, S, q_min, t_star, h, Lh, n_rep);
+      moved = sq_relay<kS>(st, q_main, lane, active, E_loc, S, q_min, t_star, h, Lh, nrep);
     if (!moved) { stuck = 1; break; }
     if (kQ > 0) load_q();
-    ++steps;
   }
   if (kQ > 0) store_q();
+  n_rep += nrep;
+  steps += nrep;
 }
 
 // The same rule for any load below 2^31: value reductions, then ballots.
