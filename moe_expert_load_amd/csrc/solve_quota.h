@@ -309,10 +309,11 @@ __device__ __forceinline__ void wave_max_min_sw(int& kh, uint32_t& kr) {
 // The search with packed keys (every load < 2^25): (load << 6 | lane) makes one
 // reduction give value and lowest lane together.
 //
-// Fast steps (kQ > 0, E_loc <= kQ): lane r also holds, in registers, the donor key of
-// each of its mains j, (q_j << 6 | 63 - j) if q_j > 0 else -1, and their maximum (the
-// rank's first donor: largest quota, lowest index on ties), so h's first donor is one
-// readlane.  The lightest possible receiver (L < T*, a free slot; such a rank is never
+// Fast steps (kQ > 0, E_loc <= kQ): lane r also holds, in registers, the donor keys of
+// its mains (donor_key), sorted, so the first is the rank's first donor (largest quota,
+// lowest index on ties) and h's first donor is one readlane; a step changes one key of
+// h, its first, which only falls, and one median per key puts it back in order.  On
+// R <= 32 ranks the reductions stay in the lower half of the wave.  The lightest possible receiver (L < T*, a free slot; such a rank is never
 // h) depends neither on h nor on the donor, so its reduction runs beside h's.  A plain
 // step is then decided without a scan: if that receiver holds no copy of the first
 // donor, it is the rule's receiver for that donor, and it moves
