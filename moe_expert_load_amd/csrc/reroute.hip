@@ -14,7 +14,7 @@
 //   the first two of them also into a dense (rank, expert) table.  Lanes exchange
 //   values only by readlane (no LDS, no barrier).  Blocks beyond E zero the columns of
 //   unused instances.
-// rr_assign: one thread per 4 or 8 pairs of one rank; each pair reads its (rank,
+// rr_assign: one thread per 4 pairs of one rank; each pair reads its (rank,
 //   expert) entry of the dense table (32 bytes) and finds its segment there, or, for
 //   the rare pair past a (rank, expert)'s second segment, in the expert's list.
 #include "common.h"
@@ -347,9 +347,10 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
                      ((reinterpret_cast<uintptr_t>(topk_ids) | reinterpret_cast<uintptr_t>(bucket_pos) |
                        reinterpret_cast<uintptr_t>(dest_inst) | reinterpret_cast<uintptr_t>(dest_row)) %
                       16) == 0;
-    // 8 pairs per thread when that still gives >= 512 workgroups, else 4
-    const int64_t pairs_all = (int64_t)T * K * (r_end - r_begin);
-    const int per = pairs_all >= 512ll * kRaThreads * 8 ? 8 : 4;
+    // 4 pairs per thread: more, smaller workgroups finish sooner (measured on MI355X,
+    // the Qwen3-235B layer's 2 M pairs graph-replayed: 4 pairs 6.9 us, 8 pairs 7.5 us,
+    // 16 pairs 8.5 us)
+    const int per = 4;
     const int64_t chunks = ((int64_t)T * K + kRaThreads * per - 1) / (kRaThreads * per);
     const dim3 grid((unsigned)chunks, (unsigned)(r_end - r_begin));
     // rank r's table row in LDS when it is small enough for several workgroups per CU
@@ -364,9 +365,7 @@ extern "C" uep_status uep_reroute_assign(const int32_t* counts, const int32_t* t
     if (lds) UEP_RA(V, P, true);         \
     else UEP_RA(V, P, false);            \
   } while (0)
-    if (vec && per == 8) UEP_RA_L(true, 8);
-    else if (vec) UEP_RA_L(true, 4);
-    else if (per == 8) UEP_RA_L(false, 8);
+    if (vec) UEP_RA_L(true, 4);
     else UEP_RA_L(false, 4);
 #undef UEP_RA_L
 #undef UEP_RA
