@@ -140,6 +140,11 @@ __device__ __forceinline__ void stream_store(u32x4 v, span_t s, int off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, s, off, 0, kCpolStream);
 }
 
+// 4 bytes at byte offset `off` of the span, streaming like stream_store
+__device__ __forceinline__ void stream_store_b32(uint32_t v, span_t s, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, s, off, 0, kCpolStream);
+}
+
 // Non-temporal 16-byte load at byte offset `off` of the span; zeros at or past its end.
 // The span's bound replaces a per-lane guard, whose exec-mask branch around every load
 // and store of a row cost the permute 1.3 % (3.61 -> 3.56 ms, same box).
