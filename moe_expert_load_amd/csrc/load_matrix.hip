@@ -192,7 +192,7 @@ constexpr size_t kLmTileMaxLds = 64 * 1024;            // tiles only while the L
 
 // The ranking of chunk c of rank r by one 256-thread workgroup (lr_lds: the dynamic LDS
 // the launch sizes); counts may be NULL when the load matrix is already written.
-template <int kMaxK, bool kTile>
+template <int kMaxK, bool kTile, bool kStream>
 __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
                                              int32_t* __restrict__ bucket_pos,
                                              const int32_t* __restrict__ chunk_hist,
@@ -203,7 +203,9 @@ __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
   int32_t* whist = reinterpret_cast<int32_t*>(lr_lds + 4 * g.E);       // [4][E]
   int32_t* pre = whist + 4 * g.E;                                      // [E]
   int32_t* idt = pre + g.E;                        // kTile: [tok_per_chunk * K] ids
-  int32_t* pt = idt + g.tok_per_chunk * g.K;       // kTile: [tok_per_chunk * K] positions
+  // kTile or kStream: [tok_per_chunk * K] positions (after the ids, or in their place)
+  int32_t* pt = kTile ? idt + g.tok_per_chunk * g.K : idt;
+  constexpr bool kPt = kTile || kStream;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int32_t* ch = chunk_hist + (int64_t)r * g.n_chunks * g.E;
   const int t0 = c * g.tok_per_chunk, t1 = min(g.T, t0 + g.tok_per_chunk);
@@ -326,7 +328,7 @@ __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k) { v0[k] = v[k]; pos0[k] = pos[k]; }
     } else if (live) {
-      if (kTile) {
+      if (kPt) {
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k)
           if (k < g.K) pt[(t - t0) * g.K + k] = pos[k];
@@ -363,6 +365,11 @@ __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k)
         if (k < g.K) { v[k] = idt[(t - t0) * g.K + k]; pos[k] = pt[(t - t0) * g.K + k]; }
+    } else if (kStream) {
+      load_token(ids + base, g.K, vec, v);
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < g.K) pos[k] = pt[(t - t0) * g.K + k];
     } else {
       load_token(ids + base, g.K, vec, v);
       load_token(bucket_pos + base, g.K, vec, pos);
@@ -376,7 +383,7 @@ __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
         if (k2 < k) dup |= ok && v[k2] == v[k];
       if (ok) pos[k] += whist[w * g.E + v[k]];
     }
-    if (kTile) {
+    if (kPt) {
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k)
         if (k < g.K) pt[(t - t0) * g.K + k] = pos[k];
@@ -385,9 +392,21 @@ __device__ __forceinline__ void lm_rank_body(const int32_t* __restrict__ ids,
     }
   }
   if (dup) set_err(err, UEP_ERR_DUP_ID);
-  if (kTile) {          // the chunk's positions leave in one flat coalesced write
+  if (kPt) {            // the chunk's positions leave in one flat coalesced write
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) bucket_pos[chunk_base + i] = pt[i];
+    if (kStream) {
+      // streaming stores: nothing is left dirty in the L2 for the end of the launch to
+      // write back; 16-byte vectors when the chunk and the tile are 16-byte aligned
+      const span_t sp = span_of(bucket_pos + chunk_base, (int64_t)n * 4);
+      if (vec && g.E % 4 == 0) {
+        for (int i = threadIdx.x; 4 * i < n; i += 256)
+          stream_store(*reinterpret_cast<const u32x4*>(pt + 4 * i), sp, 16 * i);
+      } else {
+        for (int i = threadIdx.x; i < n; i += 256) stream_store_b32((uint32_t)pt[i], sp, 4 * i);
+      }
+    } else {
+      for (int i = threadIdx.x; i < n; i += 256) bucket_pos[chunk_base + i] = pt[i];
+    }
   }
 }
 
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
                                                int32_t* __restrict__ counts, int32_t* err,
                                                LmGeom g, bool vec, bool scanned) {
   extern __shared__ uint64_t lr_lds[];
-  lm_rank_body<kMaxK, kTile>(ids, bucket_pos, chunk_hist, counts, err, g, vec, scanned,
+  lm_rank_body<kMaxK, kTile, false>(ids, bucket_pos, chunk_hist, counts, err, g, vec, scanned,
                              blockIdx.x, blockIdx.y, lr_lds);
 }
 
@@ -406,7 +425,7 @@ __global__ __launch_bounds__(256) void lm_rank(const int32_t* __restrict__ ids,
 // before it finished (the solve needs the counts only), while blocks 1.. rank the
 // chunks as lm_rank does.  The solve is one workgroup's dependent chain, several times
 // longer than the ranking, so the ranking costs the plan no time of its own.
-template <int kMaxK, bool kTile, int kS>
+template <int kMaxK, bool kTile, int kS, bool kStream>
 __global__ __launch_bounds__(256) void plan_rank_solve(
     const int32_t* __restrict__ ids, int32_t* __restrict__ bucket_pos,
     const int32_t* __restrict__ chunk_hist, int32_t* err, LmGeom g, bool vec, bool scanned,
@@ -420,7 +439,7 @@ __global__ __launch_bounds__(256) void plan_rank_solve(
     return;
   }
   const int b = (int)blockIdx.x - 1;
-  lm_rank_body<kMaxK, kTile>(ids, bucket_pos, chunk_hist, nullptr, err, g, vec, scanned,
+  lm_rank_body<kMaxK, kTile, kStream>(ids, bucket_pos, chunk_hist, nullptr, err, g, vec, scanned,
                              b % g.n_chunks, b / g.n_chunks, pl_lds);
 }
 
@@ -707,26 +726,34 @@ extern "C" uep_status uep_plan(const int32_t* topk_ids, int32_t R, int32_t T, in
   const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
   const size_t lds_tile = lds + sizeof(int32_t) * 2 * (size_t)g.tok_per_chunk * K;
   const bool tile = !vec && lds_tile <= kLmTileMaxLds;
-  const size_t sh = std::max(tile ? lds_tile : lds, sizeof(int32_t) * (size_t)E);
+  // untiled, the positions leave through an LDS tile with streaming stores while the
+  // LDS still fits (lm_rank_body, kStream)
+  const size_t lds_pos = lds + sizeof(int32_t) * (size_t)g.tok_per_chunk * K;
+  const bool stream_pos = !tile && lds_pos <= kLmTileMaxLds;
+  const size_t sh = std::max(tile ? lds_tile : (stream_pos ? lds_pos : lds), sizeof(int32_t) * (size_t)E);
   const dim3 grid(1 + g.n_chunks * R);
-#define UEP_PLAN_FUSED(KM, TL, KS)                                                              \
-  hipLaunchKernelGGL((plan_rank_solve<KM, TL, KS>), grid, dim3(256), sh, s, topk_ids, bucket_pos, \
-                     (const int32_t*)hist, err, g, vec, scanned, (const int32_t*)counts, S, q_min, \
-                     slot_expert, inst_expert, inst_quota, rank_load, stats)
-#define UEP_PLAN_S(KM, TL)                        \
-  do {                                            \
-    if (S <= 1) UEP_PLAN_FUSED(KM, TL, 1);        \
-    else if (S <= 2) UEP_PLAN_FUSED(KM, TL, 2);   \
-    else if (S <= 4) UEP_PLAN_FUSED(KM, TL, 4);   \
-    else UEP_PLAN_FUSED(KM, TL, 8);               \
+#define UEP_PLAN_FUSED(KM, TL, KS, ST)                                                          \
+  hipLaunchKernelGGL((plan_rank_solve<KM, TL, KS, ST>), grid, dim3(256), sh, s, topk_ids,        \
+                     bucket_pos, (const int32_t*)hist, err, g, vec, scanned,                    \
+                     (const int32_t*)counts, S, q_min, slot_expert, inst_expert, inst_quota,    \
+                     rank_load, stats)
+#define UEP_PLAN_S(KM, TL, ST)                        \
+  do {                                                \
+    if (S <= 1) UEP_PLAN_FUSED(KM, TL, 1, ST);        \
+    else if (S <= 2) UEP_PLAN_FUSED(KM, TL, 2, ST);   \
+    else if (S <= 4) UEP_PLAN_FUSED(KM, TL, 4, ST);   \
+    else UEP_PLAN_FUSED(KM, TL, 8, ST);               \
   } while (0)
-  if (K <= 8) {
-    if (tile) UEP_PLAN_S(8, true); else UEP_PLAN_S(8, false);
-  } else if (K <= 12) {
-    if (tile) UEP_PLAN_S(12, true); else UEP_PLAN_S(12, false);
-  } else {
-    if (tile) UEP_PLAN_S(16, true); else UEP_PLAN_S(16, false);
-  }
+#define UEP_PLAN_K(KM)                                \
+  do {                                                \
+    if (tile) UEP_PLAN_S(KM, true, false);            \
+    else if (stream_pos) UEP_PLAN_S(KM, false, true); \
+    else UEP_PLAN_S(KM, false, false);                \
+  } while (0)
+  if (K <= 8) UEP_PLAN_K(8);
+  else if (K <= 12) UEP_PLAN_K(12);
+  else UEP_PLAN_K(16);
+#undef UEP_PLAN_K
 #undef UEP_PLAN_S
 #undef UEP_PLAN_FUSED
   UEP_CHECK_LAUNCH();
