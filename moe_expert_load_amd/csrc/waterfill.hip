@@ -181,8 +181,19 @@ __global__ __launch_bounds__(256) void wf_sample(const int32_t* __restrict__ ids
   }
   if (kStage && ext) {
     __syncthreads();
+    // streaming stores (nt sc1), 16-byte vectors when the rows and the tile allow: the
+    // next launch reads the fused rows from memory, and the end of this one has no
+    // dirty lines to write back
     int32_t* dst = ext + g_base * K1;
-    for (int j = threadIdx.x; j < n_tok * K1; j += 256) dst[j] = tile[j];
+    const int n = n_tok * K1;
+    const span_t sp = span_of(dst, (int64_t)n * 4);
+    int j0 = 0;
+    if (((reinterpret_cast<uintptr_t>(dst) | (uintptr_t)E * 4) & 15) == 0) {
+      for (int i = threadIdx.x; i < n / 4; i += 256)
+        stream_store(*reinterpret_cast<const u32x4*>(tile + 4 * i), sp, 16 * i);
+      j0 = n / 4 * 4;
+    }
+    for (int j = j0 + threadIdx.x; j < n; j += 256) stream_store_b32((uint32_t)tile[j], sp, 4 * j);
   }
 }
 
