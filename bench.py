@@ -864,7 +864,19 @@ def bench_lplb(args, torch, U, W, w):
     m = torch.empty(1, dtype=torch.float32, device=DEV)
     st = torch.zeros(4, dtype=torch.int32, device=DEV)
 
+    lp_ws = torch.empty(max(U.lplb_plan_workspace_size(w.R, w.T, w.K, w.E, ipr), 4),
+                        dtype=torch.uint8, device=DEV)
+    lp_out = {"counts": L.counts, "bucket_pos": L.bp, "x": x, "m": m,
+              "inst_quota": L.plan["inst_quota"], "stats": st, "xfer": L.xfer,
+              "inst_offset": L.ioff, "dest_inst": L.dinst, "dest_row": L.drow}
+
     def lp_plan(s, r_begin=0, r_end=None):
+        """The layer's plan in one uep_lplb_plan call (the LP overlapped with the ranking)."""
+        U.lplb_plan(L.ids, lp, L.plan["inst_expert"], args.lp_iters, r_begin, r_end, lp_out,
+                    None, lp_ws, s)
+
+    def lp_plan_separate(s, r_begin=0, r_end=None):
+        """The same plan as three calls: load matrix, LP split, reroute/assignment."""
         L.load(s)
         U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x, m, L.plan["inst_quota"], st,
                None, s)
@@ -896,6 +908,7 @@ def bench_lplb(args, torch, U, W, w):
     lp_us = graph_us(torch, lambda s: U.lplb(L.counts, lp, n_copies, len(inst), args.lp_iters, x,
                                              m, L.plan["inst_quota"], st, None, s), reps=5)
     plan_us = graph_us(torch, lambda s: lp_plan(s), reps=5)
+    plan_sep_us = graph_us(torch, lambda s: lp_plan_separate(s), reps=5)
     rank_us = graph_us(torch, lambda s, i: (lp_plan(s, i % w.R, i % w.R + 1),
                                             L.permute(s, i % w.R, i % w.R + 1, row_src=False)),
                        reps=8, replays=2, indexed=True)
@@ -914,7 +927,8 @@ def bench_lplb(args, torch, U, W, w):
     rri = torch.empty(max(U.reroute_workspace_size(w.R, I, ipr), 4), dtype=torch.uint8, device=DEV)
 
     def sample_plan(s):
-        L.load(s)
+        # the LP needs the loads only: the draws are ranked afterwards, as instance ids
+        U.load_matrix(L.ids, L.E, L.counts, None, None, L.lm_ws, s, counts_only=True)
         U.lplb(L.counts, lp, n_copies, I, args.lp_iters, x, m, L.plan["inst_quota"], st, None, s)
         U.lplb_sample(L.ids, lp, x, 99, 0, di, None, s)
         U.load_matrix(di, I, ci, bpi, None, wsi, s)
@@ -934,7 +948,7 @@ def bench_lplb(args, torch, U, W, w):
         for i in where:
             uni[i // ipr] += c[e] / len(where)
     out["extra"] = {**seq, "us_per_layer_rank_share": rank_us, "plan_us": plan_us,
-                    "lplb_us": lp_us,
+                    "plan_three_calls_us": plan_sep_us, "lplb_us": lp_us,
                     "load_matrix_us": graph_us(torch, L.load, reps=5),
                     "lp_iterations_run": int(st[2].item()), "m": float(m.item()),
                     "max_load_uniform_split": float(uni.max()), "mean_load": float(c.sum() / w.R),

@@ -386,6 +386,38 @@ uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t iters, float*
                     int32_t* inst_quota, int32_t* stats, int32_t* err, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * uep_lplb_plan -- uep_load_matrix, uep_lplb and uep_reroute_assign of one layer in one
+ * call ([BLOG] sections "从全局计数到LP求解的工程实现" and "从LP解决方案到Token调度": the LP
+ * runs on the global counts, then its split decides the token dispatch).  Outputs and
+ * errors are those of the three calls, bit for bit; the LP runs on the finished load
+ * matrix concurrently with the bucket-position ranking, which it does not need.
+ *
+ *   topk_ids, R, T, K, E              in   as uep_load_matrix
+ *   lp                                in   structure from uep_lplb_prepare for R, E and
+ *                                          inst_per_rank; iters as uep_lplb
+ *   inst_per_rank, inst_expert[I]     in   the static instance table the structure was
+ *                                          built from (I = R * inst_per_rank)
+ *   r_begin, r_end                    in   as uep_reroute_assign
+ *   counts, bucket_pos                out  as uep_load_matrix
+ *   x, m, inst_quota, stats           out  as uep_lplb
+ *   xfer, inst_offset, dest_inst,
+ *   dest_row                          out  as uep_reroute_assign
+ *   err                               out  optional; every bit the three calls set
+ *   ws, ws_bytes                           uep_lplb_plan_workspace_size()
+ * Geometries off the ranking fast path (E > 1024 or K > 16) run the three calls in
+ * sequence.
+ * ------------------------------------------------------------------------- */
+size_t uep_lplb_plan_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E,
+                                    int32_t inst_per_rank);
+uep_status uep_lplb_plan(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K, int32_t E,
+                         const void* lp, int32_t inst_per_rank, const int32_t* inst_expert,
+                         int32_t iters, int32_t r_begin, int32_t r_end, int32_t* counts,
+                         int32_t* bucket_pos, float* x, float* m, int32_t* inst_quota,
+                         int32_t* stats, int32_t* xfer, int32_t* inst_offset,
+                         int32_t* dest_inst, int32_t* dest_row, int32_t* err, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * uep_lplb_sample -- LPLB's per-token copy draw.
  * [BLOG] section "从LP解决方案到Token调度": the split, normalised per replicated expert,
  * is a probability distribution over its physical copies; every token routed to a

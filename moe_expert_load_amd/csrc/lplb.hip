@@ -29,6 +29,7 @@
 #include <vector>
 
 #include "common.h"
+#include "load_matrix.h"
 #include "philox.h"
 
 namespace uep {
@@ -685,14 +686,13 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
   return run;
 }
 
-__global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
-                                                          const int32_t* __restrict__ lpw,
-                                                          int iters, float* __restrict__ x_out,
-                                                          float* __restrict__ m_out,
-                                                          int32_t* __restrict__ inst_quota,
-                                                          int32_t* __restrict__ stats,
-                                                          int32_t* err) {
-  __shared__ LpShared S;                    // static LDS: no dynamic-base lookups
+// The whole LP solve for one 256-thread workgroup whose LDS state is S (lplb_kernel's,
+// or block 0's in the fused plan launch).
+__device__ __forceinline__ void lplb_body(LpShared& S, const int32_t* __restrict__ counts,
+                                          const int32_t* __restrict__ lpw, int iters,
+                                          float* __restrict__ x_out, float* __restrict__ m_out,
+                                          int32_t* __restrict__ inst_quota,
+                                          int32_t* __restrict__ stats, int32_t* err) {
   // a buffer that is not a structure from uep_lplb_prepare (or sizes beyond the LDS
   // tables) is refused whole: nothing but the error word is written
   if (lpw[0] != kLpMagic || lpw[1] < 1 || lpw[1] > kLpMaxR || lpw[2] < 1 || lpw[2] > kLpMaxE ||
@@ -841,6 +841,40 @@ __global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restr
     stats[2] = run;
     stats[3] = L.blk;
   }
+}
+
+__global__ __launch_bounds__(kLpThreads) void lplb_kernel(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ lpw,
+                                                          int iters, float* __restrict__ x_out,
+                                                          float* __restrict__ m_out,
+                                                          int32_t* __restrict__ inst_quota,
+                                                          int32_t* __restrict__ stats,
+                                                          int32_t* err) {
+  __shared__ LpShared S;                    // static LDS: no dynamic-base lookups
+  lplb_body(S, counts, lpw, iters, x_out, m_out, inst_quota, stats, err);
+}
+
+// Fused LPLB plan launch: block 0 solves the LP on the load matrix the launches before
+// it wrote (the LP needs the counts only), while blocks 1.. rank the chunks as lm_rank
+// does, in the same static LDS block (the ranking needs less than the LP's state).  The
+// LP is one workgroup's chain of iterations, several times longer than the ranking, so
+// the ranking costs the plan no time of its own.
+template <int kMaxK, bool kTile>
+__global__ __launch_bounds__(kLpThreads) void lplb_rank_kernel(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ bucket_pos,
+    const int32_t* __restrict__ chunk_hist, int32_t* err, LmGeom g, bool vec, bool scanned,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ lpw, int iters,
+    float* __restrict__ x_out, float* __restrict__ m_out, int32_t* __restrict__ inst_quota,
+    int32_t* __restrict__ stats) {
+  __shared__ LpShared S;
+  if (blockIdx.x == 0) {
+    lplb_body(S, counts, lpw, iters, x_out, m_out, inst_quota, stats, err);
+    return;
+  }
+  const int b = (int)blockIdx.x - 1;
+  lm_rank_body<kMaxK, kTile, false>(ids, bucket_pos, chunk_hist, nullptr, err, g, vec, scanned,
+                                    b % g.n_chunks, b / g.n_chunks,
+                                    reinterpret_cast<uint64_t*>(&S));
 }
 
 // LPLB's per-token copy draw (section "从LP解决方案到Token调度": the split,
@@ -1109,6 +1143,93 @@ extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t it
                      counts, static_cast<const int32_t*>(lp), iters, x, m, inst_quota, stats, err);
   UEP_CHECK_LAUNCH();
   return UEP_OK;
+}
+
+// uep_lplb_plan: uep_load_matrix, uep_lplb and uep_reroute_assign in one call, with the
+// LP solved concurrently with the bucket-position ranking (lplb_rank_kernel).  Launches:
+// lm_hist, lm_counts (the load matrix), lm_scan for long ranks, lplb_rank_kernel, then
+// the reroute and assignment of uep_reroute_assign.  Geometries off the ranking fast
+// path, or whose ranking would not fit the LP's LDS block, run the three calls in
+// sequence.
+static size_t lp_plan_align(size_t b) { return (b + 255) / 256 * 256; }
+
+extern "C" size_t uep_lplb_plan_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E,
+                                               int32_t inst_per_rank) {
+  if (R <= 0 || T < 0 || K <= 0 || E <= 0 || inst_per_rank <= 0) return 0;
+  return lp_plan_align(uep_load_matrix_workspace_size(R, T, K, E)) +
+         uep_reroute_workspace_size(R, E, inst_per_rank);
+}
+
+extern "C" uep_status uep_lplb_plan(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,
+                                    int32_t E, const void* lp, int32_t inst_per_rank,
+                                    const int32_t* inst_expert, int32_t iters, int32_t r_begin,
+                                    int32_t r_end, int32_t* counts, int32_t* bucket_pos,
+                                    float* x, float* m, int32_t* inst_quota, int32_t* stats,
+                                    int32_t* xfer, int32_t* inst_offset, int32_t* dest_inst,
+                                    int32_t* dest_row, int32_t* err, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (R <= 0 || T < 0 || K <= 0 || E <= 0 || inst_per_rank <= 0) return UEP_EINVAL;
+  if (r_begin < 0 || r_end > R || r_begin > r_end) return UEP_EINVAL;
+  if (R > kLpMaxR || K > 64 || E > kLmMaxE || (int64_t)R * T * K >= (1ll << 31) ||
+      (int64_t)R * inst_per_rank > (1 << 20))
+    return UEP_EGEOM;
+  // every check of the three calls, before anything is enqueued
+  if (!counts || !lp || !x || !m || !inst_quota || !inst_expert || !xfer || !inst_offset ||
+      iters < 0 || iters > 200 || (T > 0 && (!topk_ids || !bucket_pos)) ||
+      (T > 0 && r_end > r_begin && (!dest_inst || !dest_row)))
+    return UEP_EINVAL;
+  if (!ws || ws_bytes < uep_lplb_plan_workspace_size(R, T, K, E, inst_per_rank))
+    return UEP_EWORKSPACE;
+  const size_t lm_bytes = lp_plan_align(uep_load_matrix_workspace_size(R, T, K, E));
+  void* rr_ws = static_cast<char*>(ws) + lm_bytes;
+  const size_t rr_bytes = ws_bytes - lm_bytes;
+  LmGeom g = lm_geom(R, T, K, E);
+  const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(bucket_pos) % 16 == 0;
+  const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
+  const size_t lds_tile = lds + sizeof(int32_t) * 2 * (size_t)g.tok_per_chunk * K;
+  const bool tile = !vec && lds_tile <= kLmTileMaxLds;
+  if (!lm_bitmap(K, E) || T == 0 || (tile ? lds_tile : lds) > sizeof(LpShared)) {
+    uep_status st = uep_load_matrix(topk_ids, R, T, K, E, counts, bucket_pos, err, ws, lm_bytes,
+                                    stream);
+    if (st == UEP_OK) st = uep_lplb(counts, lp, iters, x, m, inst_quota, stats, err, stream);
+    if (st == UEP_OK)
+      st = uep_reroute_assign(counts, topk_ids, bucket_pos, R, T, K, E, inst_per_rank,
+                              inst_expert, inst_quota, r_begin, r_end, xfer, inst_offset,
+                              dest_inst, dest_row, err, rr_ws, rr_bytes, stream);
+    return st;
+  }
+  hipStream_t s = uep_stream(stream);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(lm_hist, dim3(g.n_chunks, R), dim3(256), sizeof(int32_t) * E, s, topk_ids,
+                     hist, err, g);
+  UEP_CHECK_LAUNCH();
+  hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
+  UEP_CHECK_LAUNCH();
+  const int per = E >= 256 ? 1 : 256 / E;
+  const bool scanned = g.n_chunks > 16 * per;
+  if (scanned) {
+    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, g);
+    UEP_CHECK_LAUNCH();
+  }
+  const dim3 grid(1 + g.n_chunks * R);
+  const int32_t* lpw = static_cast<const int32_t*>(lp);
+#define UEP_LP_FUSED(KM, TL)                                                                  \
+  hipLaunchKernelGGL((lplb_rank_kernel<KM, TL>), grid, dim3(kLpThreads), 0, s, topk_ids,      \
+                     bucket_pos, (const int32_t*)hist, err, g, vec, scanned,                  \
+                     (const int32_t*)counts, lpw, iters, x, m, inst_quota, stats)
+  if (K <= 8) {
+    if (tile) UEP_LP_FUSED(8, true); else UEP_LP_FUSED(8, false);
+  } else if (K <= 12) {
+    if (tile) UEP_LP_FUSED(12, true); else UEP_LP_FUSED(12, false);
+  } else {
+    if (tile) UEP_LP_FUSED(16, true); else UEP_LP_FUSED(16, false);
+  }
+#undef UEP_LP_FUSED
+  UEP_CHECK_LAUNCH();
+  return uep_reroute_assign(counts, topk_ids, bucket_pos, R, T, K, E, inst_per_rank, inst_expert,
+                            inst_quota, r_begin, r_end, xfer, inst_offset, dest_inst, dest_row,
+                            err, rr_ws, rr_bytes, stream);
 }
 
 extern "C" uep_status uep_lplb_sample(const int32_t* topk_ids, int32_t R, int32_t T, int32_t K,

@@ -56,6 +56,8 @@ SIGNATURES = {
     "uep_lplb_prepare": (_I, [_P, _I, _I, _I, _P, _SZ, _P]),
     "uep_lplb_sample": (_I, [_P, _I, _I, _I, _P, _P, _U64, _U64, _P, _P, _P]),
     "uep_lplb": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P]),
+    "uep_lplb_plan_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "uep_lplb_plan": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _I, _I, _I] + [_P] * 12 + [_SZ, _P]),
 }
 
 
@@ -439,6 +441,47 @@ def lplb(counts, lp, n_copies=None, n_inst=None, iters=30, x=None, m=None, inst_
     _check(LIB.uep_lplb(_p(counts), _p(lp.buf), iters, _p(x), _p(m), _p(inst_quota), _p(stats),
                         _p(err), _s(stream)), "uep_lplb")
     return x[:lp.n], m, inst_quota, stats
+
+
+def lplb_plan_workspace_size(R, T, K, E, inst_per_rank) -> int:
+    return int(LIB.uep_lplb_plan_workspace_size(R, T, K, E, inst_per_rank))
+
+
+def lplb_plan(topk_ids, lp, inst_expert, iters=30, r_begin=0, r_end=None, out=None, err=None,
+              ws=None, stream=None):
+    """uep_lplb_plan: load matrix, LP split and reroute/assignment in one call, with the
+    static instance table `inst_expert` [I] the structure was built from.  `out` may hold
+    preallocated buffers under the keys below; returns that dict."""
+    lp = _lp(lp)
+    _i32(topk_ids, "topk_ids")
+    R, T, K = topk_ids.shape
+    if R != lp.R:
+        raise TypeError(f"topk_ids has {R} ranks, the LP structure {lp.R}")
+    _buf(inst_expert, lp.I, "inst_expert")
+    r_end = R if r_end is None else r_end
+    E, I = lp.E, lp.I
+    shapes = {"counts": ((R, E), torch.int32), "bucket_pos": ((R, T, K), torch.int32),
+              "x": ((max(lp.n, 1),), torch.float32), "m": ((1,), torch.float32),
+              "inst_quota": ((I,), torch.int32), "stats": ((4,), torch.int32),
+              "xfer": ((R, I), torch.int32), "inst_offset": ((I + 1,), torch.int32),
+              "dest_inst": ((R, T, K), torch.int32), "dest_row": ((R, T, K), torch.int32)}
+    o = {} if out is None else dict(out)
+    for k, (shp, dt) in shapes.items():
+        n = 1
+        for d in shp:
+            n *= d
+        o[k] = _new(shp, topk_ids, dt) if o.get(k) is None else _buf(o[k], n, k, dt)
+    _buf(err, 1, "err")
+    need = lplb_plan_workspace_size(R, T, K, E, lp.inst_per_rank)
+    ws = _new((max(need, 4),), topk_ids, torch.uint8) if ws is None else ws
+    _check(LIB.uep_lplb_plan(_p(topk_ids), R, T, K, E, _p(lp.buf), lp.inst_per_rank,
+                             _p(inst_expert), iters, r_begin, r_end, _p(o["counts"]),
+                             _p(o["bucket_pos"]), _p(o["x"]), _p(o["m"]), _p(o["inst_quota"]),
+                             _p(o["stats"]), _p(o["xfer"]), _p(o["inst_offset"]),
+                             _p(o["dest_inst"]), _p(o["dest_row"]), _p(err), _p(ws),
+                             ws.numel() * ws.element_size(), _s(stream)), "uep_lplb_plan")
+    o["inst_per_rank"] = lp.inst_per_rank
+    return o
 
 
 def lplb_sample(topk_ids, lp, x, seed, layer, dest_inst=None, err=None, stream=None):

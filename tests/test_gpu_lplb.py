@@ -21,7 +21,8 @@ if not torch.cuda.is_available():
 import oracle as O                                       # noqa: E402
 from moe_expert_load_amd import uep as U                 # noqa: E402
 from moe_expert_load_amd import workload as W            # noqa: E402
-from tests.gpu_helpers import DEV, to_dev, host, err_word, say, compare_dispatch_rows  # noqa: E402
+from tests.gpu_helpers import (DEV, to_dev, host, err_word, say,  # noqa: E402
+                               compare_dispatch_rows, random_routing)
 from tests.test_oracle_reroute_permute import (check_reroute_properties,  # noqa: E402
                                                check_assign_properties)
 
@@ -469,3 +470,76 @@ def test_lplb_block_and_dense_solves():
         say(f"case: lplb solve path, {name}")
         res, x, m, q, st = check_lplb(counts, inst, ipr)
         assert st[3] == path, (name, st)
+
+
+def _placement(rng, R, E_loc, n_hot):
+    """Static instance table: E_loc mains per rank and one redundant slot per rank,
+    n_hot experts replicated on a rank other than their home."""
+    E, ipr = R * E_loc, E_loc + 1
+    inst = np.full(R * ipr, -1, dtype=np.int32)
+    for r in range(R):
+        inst[r * ipr:r * ipr + E_loc] = np.arange(r * E_loc, (r + 1) * E_loc)
+    free = list(rng.permutation(R))
+    for e in rng.choice(E, size=min(n_hot, R), replace=False):
+        for r in free:
+            if r != e // E_loc:
+                inst[r * ipr + E_loc] = e
+                free.remove(r)
+                break
+    return inst, ipr
+
+
+def _fused_vs_separate(ids, E, inst, ipr, r_begin=0, r_end=None):
+    R = ids.shape[0]
+    ids_d, inst_d = to_dev(ids), to_dev(inst)
+    lp = U.lplb_prepare(inst, R, E, ipr, DEV)
+    e1, e2 = err_word(), err_word()
+    counts, bp = U.load_matrix(ids_d, E, err=e1)
+    x, m, q, st = U.lplb(counts, lp, iters=30, err=e1)
+    xfer, ioff, di, dr = U.reroute_assign(counts, ids_d, bp, ipr, inst_d, q, r_begin, r_end,
+                                          err=e1)
+    o = U.lplb_plan(ids_d, lp, inst_d, iters=30, r_begin=r_begin, r_end=r_end, err=e2)
+    torch.cuda.synchronize()
+    assert int(host(e1)[0]) == 0 and int(host(e2)[0]) == 0
+    for key, ref in (("counts", counts), ("bucket_pos", bp), ("inst_quota", q), ("stats", st),
+                     ("xfer", xfer), ("inst_offset", ioff)):
+        assert torch.equal(o[key], ref), key
+    assert torch.equal(o["x"][:lp.n].view(torch.int32), x.view(torch.int32))
+    assert torch.equal(o["m"].view(torch.int32), m.view(torch.int32))
+    rb, re_ = r_begin, (R if r_end is None else r_end)
+    assert torch.equal(o["dest_inst"][rb:re_], di[rb:re_])
+    assert torch.equal(o["dest_row"][rb:re_], dr[rb:re_])
+    return o
+
+
+# (R, E_loc, T, K, replicated experts): 16-byte ids and the LDS-tiled ranking (K % 4 != 0),
+# ranks long enough for the scanned prefixes, a rank range
+LPLB_PLAN_GEOMS = [(4, 2, 600, 4, 3), (8, 4, 900, 8, 6), (16, 4, 1500, 6, 10),
+                   (5, 3, 700, 9, 4), (8, 2, 5000, 4, 5), (5, 4, 300, 16, 3)]
+
+
+@pytest.mark.parametrize("geom", LPLB_PLAN_GEOMS, ids=[str(g) for g in LPLB_PLAN_GEOMS])
+def test_lplb_plan_fused_matches_the_separate_calls(geom):
+    """uep_lplb_plan (load matrix, the LP overlapped with the ranking, reroute/assignment
+    in one call) gives the three separate calls' outputs bit for bit, the fp32 split and
+    objective included; with a rank range it assigns exactly that range."""
+    R, E_loc, T, K, n_hot = geom
+    rng = np.random.default_rng(sum(geom) * 13 + 5)
+    E = R * E_loc
+    say(f"case: fused lplb plan R={R} E={E} T={T} K={K} replicated={n_hot}")
+    inst, ipr = _placement(rng, R, E_loc, n_hot)
+    ids = random_routing(rng, R, T, K, E, empty_frac=0.02)
+    _fused_vs_separate(ids, E, inst, ipr)
+    if R >= 4:
+        _fused_vs_separate(ids, E, inst, ipr, r_begin=1, r_end=3)
+
+
+def test_lplb_plan_layer_full_size():
+    """The fused LPLB plan on the LPLB-shaped layer (R = 64, 256 experts + 32 static
+    replicas, 16384 tokens per rank): bit for bit the separate calls' outputs."""
+    w = W.LPLB_LAYER
+    say("case: fused lplb plan, layer full size", w)
+    ids = W.routing(w)
+    inst = W.static_replica_placement(w)
+    o = _fused_vs_separate(ids, w.E, inst, w.E_loc + 1)
+    say(f"fused lplb plan: m={float(host(o['m'])[0])} iterations={int(host(o['stats'])[2])}")
