@@ -1206,12 +1206,9 @@ extern "C" uep_status uep_lplb_plan(const int32_t* topk_ids, int32_t R, int32_t 
   UEP_CHECK_LAUNCH();
   hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
   UEP_CHECK_LAUNCH();
-  const int per = E >= 256 ? 1 : 256 / E;
-  const bool scanned = g.n_chunks > 16 * per;
-  if (scanned) {
-    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, g);
-    UEP_CHECK_LAUNCH();
-  }
+  // the ranking sums the earlier chunks' histograms itself (no lm_scan launch before the
+  // LP): it has the LP's whole solve to do it in
+  const bool scanned = false;
   const dim3 grid(1 + g.n_chunks * R);
   const int32_t* lpw = static_cast<const int32_t*>(lp);
 #define UEP_LP_FUSED(KM, TL)                                                                  \
