@@ -513,9 +513,11 @@ def _fused_vs_separate(ids, E, inst, ipr, r_begin=0, r_end=None):
 
 
 # (R, E_loc, T, K, replicated experts): 16-byte ids and the LDS-tiled ranking (K % 4 != 0),
-# ranks long enough for the scanned prefixes, a rank range
+# ranks long enough for many earlier chunks, a rank range, E = 1024 (the ranking's LDS
+# close to the LP's whole block) and beyond what fits (the three calls in sequence)
 LPLB_PLAN_GEOMS = [(4, 2, 600, 4, 3), (8, 4, 900, 8, 6), (16, 4, 1500, 6, 10),
-                   (5, 3, 700, 9, 4), (8, 2, 5000, 4, 5), (5, 4, 300, 16, 3)]
+                   (5, 3, 700, 9, 4), (8, 2, 5000, 4, 5), (5, 4, 300, 16, 3),
+                   (16, 64, 300, 8, 8), (16, 128, 200, 8, 4)]
 
 
 @pytest.mark.parametrize("geom", LPLB_PLAN_GEOMS, ids=[str(g) for g in LPLB_PLAN_GEOMS])

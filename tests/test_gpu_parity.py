@@ -922,7 +922,8 @@ def test_path_in_a_captured_graph_replays():
 FUSED_PLAN_GEOMS = [(4, 512, 2, 8, 1, 32), (8, 700, 8, 64, 2, 20), (16, 3000, 6, 128, 4, 50),
                     (5, 1000, 10, 40, 8, 5), (6, 800, 12, 48, 2, 3), (7, 900, 14, 70, 3, 0),
                     (4, 600, 16, 64, 1, 2), (4, 4500, 8, 256, 2, 10), (32, 300, 16, 2048, 1, 1),
-                    (1, 100, 4, 16, 2, 1), (4, 0, 2, 8, 1, 1), (3, 700, 4, 9, 1, 5)]
+                    (1, 100, 4, 16, 2, 1), (4, 0, 2, 8, 1, 1), (3, 700, 4, 9, 1, 5),
+                    (16, 300, 12, 1024, 2, 5), (16, 300, 16, 1024, 1, 5)]
 
 
 @pytest.mark.parametrize("geom", FUSED_PLAN_GEOMS, ids=[str(g) for g in FUSED_PLAN_GEOMS])
