@@ -124,7 +124,7 @@ struct LpShared {
   float v[kLpMaxNV], z[kLpMaxNV], dv[kLpMaxNV], dz[kLpMaxNV], rc[kLpMaxNV], tv[kLpMaxNV];
   float y[kLpMaxRows], dy[kLpMaxRows], rb[kLpMaxRows], rhs[kLpMaxRows];
   // normal equations (fp64)
-  double d[kLpMaxNV], beta[kLpMaxG], t64[kLpMaxRows], u64[kLpMaxR];
+  double d[kLpMaxNV], rbeta[kLpMaxG], cd[kLpMaxN], u64[kLpMaxR];
   double P[kLpMaxR][kLpMaxR + 1];
   double Dinv[kLpMaxR], d0[kLpMaxR];
   double colbuf[2][kLpMaxR];
@@ -275,18 +275,22 @@ __device__ __forceinline__ void lp_steps(int nv, LpShared& S, float& ap, float& 
   ad = b;
 }
 
-// dy = (A D A^T)^{-1} rhs with the factored rank matrix
-__device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
-  for (int g = threadIdx.x; g < G; g += kLpThreads) S.t64[g] = (double)S.rhs[R + g] / S.beta[g];
-  __syncthreads();
+// The right-hand side of the rank system: rank r's row plus, for every copy p on r,
+// d_p times its group's row divided by beta.
+__device__ __forceinline__ void lp_rank_rhs(int R, LpShared& S) {
   for (int r = threadIdx.x; r < R; r += kLpThreads) {
     double acc = S.rhs[r];
     for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-      const int p = S.rank_copy[k];
-      acc += S.d[p] * S.t64[S.copy_group[p]];
+      const int p = S.rank_copy[k], g = S.copy_group[p];
+      acc += S.d[p] * ((double)S.rhs[R + g] * S.rbeta[g]);
     }
     S.u64[r] = acc;
   }
+}
+
+// dy = (A D A^T)^{-1} rhs with the factored rank matrix
+__device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
+  lp_rank_rhs(R, S);
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
@@ -316,7 +320,7 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
       const int g = i - R;
       double acc = S.rhs[i];
       for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
-      S.dy[i] = (float)(acc / S.beta[g]);
+      S.dy[i] = (float)(acc * S.rbeta[g]);
     }
   }
   __syncthreads();
@@ -329,47 +333,79 @@ __device__ __forceinline__ double rcp_d(double x) {
   return fma(y, fma(-x, y, 1.0), y);
 }
 
-// d = v / z (the diagonal of the normal equations), each group's beta = sum of its
-// copies' d, and the dense coefficient delta = d_M + d_a of the rank matrix's 11^T term.
+// d = v / z (the diagonal of the normal equations); for every group g, 1 / beta_g with
+// beta_g the sum of its copies' d; for every copy p of g, cd_p = d_p * (the sum of the
+// other copies' d) / beta_g, its share of its rank's diagonal (a sum of positive terms:
+// no cancellation).  One thread per copy sums its group in index order, so every copy
+// of a group forms the same beta.  Returns the dense coefficient delta = d_M + d_a of
+// the rank matrix's 11^T term.
 __device__ __forceinline__ double lp_scaling(int n, int R, int G, LpShared& S) {
   const int nv = n + R + 2;
   for (int i = threadIdx.x; i < nv; i += kLpThreads) S.d[i] = (double)S.v[i] / (double)S.z[i];
   __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kLpThreads) {
-    double b = 0.0;
-    for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) b += S.d[p];
-    S.beta[g] = b;
+  for (int p = threadIdx.x; p < n; p += kLpThreads) {
+    const int g = S.copy_group[p], q0 = S.grp_start[g], q1 = S.grp_start[g + 1];
+    double b = 0.0, others = 0.0;
+    for (int q = q0; q < q1; ++q) {
+      const double dq = S.d[q];
+      b += dq;
+      if (q != p) others += dq;
+    }
+    const double rb = rcp_d(b);
+    S.cd[p] = S.d[p] * (others * rb);
+    if (p == q0) S.rbeta[g] = rb;
   }
   return S.d[n + R] + S.d[n + R + 1];
 }
 
-// rank r's diagonal entry of the rank matrix without the dense term: its slack's d plus,
-// for each copy p on r, d_p * (the other copies of p's group) / beta, a sum of positive
-// terms (no cancellation)
+// rank r's diagonal entry of the rank matrix without the dense term: its slack's d plus
+// cd of every copy on r
 __device__ __forceinline__ double lp_rank_diag(int n, int r, const LpShared& S) {
   double diag = S.d[n + r];
-  for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-    const int p = S.rank_copy[k], g = S.copy_group[p];
-    double others = 0.0;
-    for (int q = S.grp_start[g]; q < S.grp_start[g + 1]; ++q)
-      if (q != p) others += S.d[q];
-    diag += S.d[p] * (others / S.beta[g]);
-  }
+  for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) diag += S.cd[S.rank_copy[k]];
   return diag;
 }
 
-// an off-diagonal entry of the rank matrix without the dense term is -off: the copy
-// pairs of one group that touch both ranks
-__device__ __forceinline__ double lp_entry_off(int e, const LpView& L, const LpShared& S) {
-  double off = 0.0;
-  for (int k = L.ent_start[e]; k < L.ent_start[e + 1]; ++k) {
+// One off-diagonal entry of the rank matrix (r > r') as the thread that forms it every
+// iteration keeps it: its position, and the first of the pairs of copies of one group on
+// r and r' that it sums, with that pair's group, held in registers (the structure is
+// constant over the solve); further pairs are read from the structure.
+struct LpEnt {
+  int e;                 // entry index, -1: the thread has none
+  int rr;                // r * 64 + r'
+  int l1, l2;            // the lanes of r and r' in the block solve
+  int p, q, gp;          // first pair and the group of p
+  int k1, k_end;         // remaining pairs [k1, k_end)
+};
+
+__device__ __forceinline__ LpEnt lp_ent_load(int e, const LpView& L, const LpShared& S) {
+  LpEnt c;
+  c.e = e < L.n_ent ? e : -1;
+  if (c.e < 0) return c;
+  c.rr = L.ent_rr[e];
+  c.l1 = L.rank_lane[c.rr / kLpMaxR];
+  c.l2 = L.rank_lane[c.rr % kLpMaxR];
+  const int k0 = L.ent_start[e];
+  c.k_end = L.ent_start[e + 1];
+  c.k1 = k0 + 1;
+  c.p = L.ent_p[k0];
+  c.q = L.ent_q[k0];
+  c.gp = S.copy_group[c.p];
+  return c;
+}
+
+// the entry is -off: sum over its pairs of d_p d_q / beta
+__device__ __forceinline__ double lp_entry_off(const LpEnt& c, const LpView& L, const LpShared& S) {
+  double off = S.d[c.p] * (S.d[c.q] * S.rbeta[c.gp]);
+  for (int k = c.k1; k < c.k_end; ++k) {
     const int p = L.ent_p[k], q = L.ent_q[k];
-    off += S.d[p] * (S.d[q] / S.beta[S.copy_group[p]]);
+    off += S.d[p] * (S.d[q] * S.rbeta[S.copy_group[p]]);
   }
   return off;
 }
 
-__device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, LpShared& S) {
+__device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, const LpEnt& C,
+                                          LpShared& S) {
   const double delta = lp_scaling(n, R, G, S);
   // every entry starts at the dense M/a term; the matrix is padded to 64 x 64 with
   // identity rows and columns beyond R so the factorization has no bounds tests
@@ -379,15 +415,17 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
   }
   for (int r = R + threadIdx.x; r < kLpMaxR; r += kLpThreads) S.d0[r] = 1.0;
   __syncthreads();
-  // diagonal: slack term plus each copy's d_p * (other copies of its group) / beta
+  // diagonal: slack term plus each copy's cd
   for (int r = threadIdx.x; r < R; r += kLpThreads) {
     const double diag = delta + lp_rank_diag(n, r, S);
     S.P[r][r] = diag;
     S.d0[r] = diag;
   }
   // off-diagonal entries touched by copies of one group on both ranks
-  for (int e = threadIdx.x; e < L.n_ent; e += kLpThreads)
-    S.P[L.ent_rr[e] / kLpMaxR][L.ent_rr[e] % kLpMaxR] = delta - lp_entry_off(e, L, S);
+  for (int e = threadIdx.x; e < L.n_ent; e += kLpThreads) {
+    const LpEnt c = e == (int)threadIdx.x ? C : lp_ent_load(e, L, S);
+    S.P[c.rr / kLpMaxR][c.rr % kLpMaxR] = delta - lp_entry_off(c, L, S);
+  }
   __syncthreads();
   // Blocked right-looking LDL^T (Cholesky without square roots), panels of kLpPanel
   // columns.  Thread (ti, tk) keeps a 4x4 register tile of the trailing matrix: rows
@@ -482,15 +520,68 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
 // B (P without its dense term) is block diagonal over the components of the rank
 // coupling graph, packed into groups of kBlk lanes (lane_rank).  Every group factors
 // its block as U diag(p) U^T in registers, one row per lane, the rows broadcast within
-// the group by shuffles; all groups at once.  A solve is then one forward and one
+// the group by DPP moves; all groups at once.  A solve is then one forward and one
 // backward substitution per group and the rank-one correction of Sherman-Morrison:
 // P^-1 b = v - w (delta 1^T v) / (1 + delta 1^T w), v = B^-1 b, w = B^-1 1, both fp64.
 // Pivots that lost their precision are dropped as in the dense factorization.
-__device__ __forceinline__ double shfl_d(double v, int src) {
+
+// Lane J of every aligned group of kBlk (8 or 16) lanes, to every lane of its group, by
+// DPP moves (no trip through the LDS unit): quad_perm copies lane J % 4 of every quad
+// to its quad, then row_shr / row_shl by multiples of 4 lanes, each limited to one
+// bank (quad) of the 16-lane row, copy quad J / 4 to the group's other quads.  Every
+// source lane read is quad J / 4 of its own group, so bound_ctrl never applies.
+template <int kBlk, int J>
+__device__ __forceinline__ int grp_bcast_i(int x) {
+  static_assert(kBlk == 8 || kBlk == 16, "groups of 8 or 16 lanes");
+  const int q = __builtin_amdgcn_mov_dpp(x, (J % 4) * 0x55, 0xF, 0xF, false);
+  constexpr int Q = J / 4;
+  int r = q;
+  if constexpr (kBlk == 8) {
+    if constexpr (Q == 0) r = __builtin_amdgcn_update_dpp(r, q, 0x114, 0xF, 0xA, false);
+    else r = __builtin_amdgcn_update_dpp(r, q, 0x104, 0xF, 0x5, false);
+  } else {
+    if constexpr (Q != 0) r = __builtin_amdgcn_update_dpp(r, q, 0x100 + 4 * Q, 0xF, 0x1, false);
+    if constexpr (Q != 1) r = __builtin_amdgcn_update_dpp(r, q, Q < 1 ? 0x110 + 4 * (1 - Q) : 0x100 + 4 * (Q - 1), 0xF, 0x2, false);
+    if constexpr (Q != 2) r = __builtin_amdgcn_update_dpp(r, q, Q < 2 ? 0x110 + 4 * (2 - Q) : 0x100 + 4 * (Q - 2), 0xF, 0x4, false);
+    if constexpr (Q != 3) r = __builtin_amdgcn_update_dpp(r, q, 0x110 + 4 * (3 - Q), 0xF, 0x8, false);
+  }
+  return r;
+}
+
+template <int kBlk, int J>
+__device__ __forceinline__ double grp_bcast_j(double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const int lo = __shfl((int)(uint32_t)u, src, kWave);
-  const int hi = __shfl((int)(uint32_t)(u >> 32), src, kWave);
+  const int lo = grp_bcast_i<kBlk, J>((int)(uint32_t)u);
+  const int hi = grp_bcast_i<kBlk, J>((int)(uint32_t)(u >> 32));
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// the same with j a loop index of a fully unrolled loop (the switch folds away)
+template <int kBlk>
+__device__ __forceinline__ double grp_bcast(double v, int j) {
+  switch (j) {
+    case 0: return grp_bcast_j<kBlk, 0>(v);
+    case 1: return grp_bcast_j<kBlk, 1>(v);
+    case 2: return grp_bcast_j<kBlk, 2>(v);
+    case 3: return grp_bcast_j<kBlk, 3>(v);
+    case 4: return grp_bcast_j<kBlk, 4>(v);
+    case 5: return grp_bcast_j<kBlk, 5>(v);
+    case 6: return grp_bcast_j<kBlk, 6>(v);
+    case 7: return grp_bcast_j<kBlk, 7>(v);
+  }
+  if constexpr (kBlk == 16) {
+    switch (j) {
+      case 8: return grp_bcast_j<kBlk, 8>(v);
+      case 9: return grp_bcast_j<kBlk, 9>(v);
+      case 10: return grp_bcast_j<kBlk, 10>(v);
+      case 11: return grp_bcast_j<kBlk, 11>(v);
+      case 12: return grp_bcast_j<kBlk, 12>(v);
+      case 13: return grp_bcast_j<kBlk, 13>(v);
+      case 14: return grp_bcast_j<kBlk, 14>(v);
+      default: return grp_bcast_j<kBlk, 15>(v);
+    }
+  }
+  return v;
 }
 
 template <int kBlk>
@@ -507,7 +598,7 @@ __device__ __forceinline__ double lpb_subst(const LpBlk<kBlk>& B, double b, cons
   double z = b;
 #pragma unroll
   for (int j = 0; j < kBlk; ++j) {                      // U z = b
-    const double zj = shfl_d(z, B.base + j);
+    const double zj = grp_bcast<kBlk>(z, j);
     if (B.a > j) z = fma(-B.r[j], zj, z);
   }
   z *= B.dinv;
@@ -516,7 +607,7 @@ __device__ __forceinline__ double lpb_subst(const LpBlk<kBlk>& B, double b, cons
   for (int j = 0; j < kBlk; ++j) uc[j] = ust[(B.base + j) * kBlk + B.a];
 #pragma unroll
   for (int j = kBlk - 1; j >= 0; --j) {                 // U^T x = D^-1 z
-    const double xj = shfl_d(z, B.base + j);
+    const double xj = grp_bcast<kBlk>(z, j);
     if (B.a < j) z = fma(-uc[j], xj, z);
   }
   return z;
@@ -524,20 +615,21 @@ __device__ __forceinline__ double lpb_subst(const LpBlk<kBlk>& B, double b, cons
 
 template <int kBlk>
 __device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, const LpView& L,
-                                           LpShared& S) {
-  B.delta = lp_scaling(n, R, G, S);
+                                           const LpEnt& C, LpShared& S) {
   double* ust = &S.P[0][0];                 // kLpLanes rows of kBlk entries
   const int t = threadIdx.x;
-  __syncthreads();                          // beta and d complete
+  // every lane clears its own row (the last solve's reads of U ended at a barrier)
 #pragma unroll
   for (int b = 0; b < kBlk; ++b) ust[t * kBlk + b] = 0.0;
-  ust[t * kBlk + B.a] = B.rank >= 0 ? lp_rank_diag(n, B.rank, S) : 1.0;
-  __syncthreads();
+  B.delta = lp_scaling(n, R, G, S);
+  __syncthreads();                          // cd, 1 / beta and the cleared rows complete
+  if (B.rank >= 0) ust[t * kBlk + B.a] = lp_rank_diag(n, B.rank, S);
+  else ust[t * kBlk + B.a] = 1.0;
   for (int e = t; e < L.n_ent; e += kLpThreads) {
-    const double off = -lp_entry_off(e, L, S);
-    const int l1 = L.rank_lane[L.ent_rr[e] / kLpMaxR], l2 = L.rank_lane[L.ent_rr[e] % kLpMaxR];
-    ust[l1 * kBlk + l2 % kBlk] = off;
-    ust[l2 * kBlk + l1 % kBlk] = off;
+    const LpEnt c = e == t ? C : lp_ent_load(e, L, S);
+    const double off = -lp_entry_off(c, L, S);
+    ust[c.l1 * kBlk + c.l2 % kBlk] = off;
+    ust[c.l2 * kBlk + c.l1 % kBlk] = off;
   }
   __syncthreads();
   double d0 = 0.0;
@@ -549,11 +641,11 @@ __device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, 
   B.dinv = 0.0;
 #pragma unroll
   for (int j = 0; j < kBlk; ++j) {
-    const double pj = shfl_d(B.r[j], B.base + j);
-    const double thr = kPivTol * shfl_d(d0, B.base + j);
+    const double pj = grp_bcast<kBlk>(B.r[j], j);
+    const double thr = kPivTol * grp_bcast<kBlk>(d0, j);
     double ajb[kBlk];
 #pragma unroll
-    for (int b = j + 1; b < kBlk; ++b) ajb[b] = shfl_d(B.r[b], B.base + j);
+    for (int b = j + 1; b < kBlk; ++b) ajb[b] = grp_bcast<kBlk>(B.r[b], j);
     const bool bad = !(pj > thr);
     const double rc = bad ? 0.0 : rcp_d(pj);
     if (B.a == j) B.dinv = bad ? 1e-64 : rc;
@@ -574,16 +666,7 @@ __device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, 
 // dy = (A D A^T)^{-1} rhs with the block factors (the group rows as in lp_solve)
 template <int kBlk>
 __device__ __forceinline__ void lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G, LpShared& S) {
-  for (int g = threadIdx.x; g < G; g += kLpThreads) S.t64[g] = (double)S.rhs[R + g] / S.beta[g];
-  __syncthreads();
-  for (int r = threadIdx.x; r < R; r += kLpThreads) {
-    double acc = S.rhs[r];
-    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
-      const int p = S.rank_copy[k];
-      acc += S.d[p] * S.t64[S.copy_group[p]];
-    }
-    S.u64[r] = acc;
-  }
+  lp_rank_rhs(R, S);
   __syncthreads();
   const double v = lpb_subst<kBlk>(B, B.rank >= 0 ? S.u64[B.rank] : 0.0, &S.P[0][0]);
   const double sv = blk_sum(B.rank >= 0 ? v : 0.0, S);
@@ -597,7 +680,7 @@ __device__ __forceinline__ void lpb_solve(const LpBlk<kBlk>& B, int n, int R, in
       const int g = i - R;
       double acc = S.rhs[i];
       for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
-      S.dy[i] = (float)(acc / S.beta[g]);
+      S.dy[i] = (float)(acc * S.rbeta[g]);
     }
   }
   __syncthreads();
@@ -621,6 +704,7 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
   // Barriers below separate only accesses across threads: a loop over i that reads
   // what the same thread wrote at index i in the step before needs none.
   const auto plus_rb = [&](int i, float a) { return a + S.rb[i]; };
+  const LpEnt C = lp_ent_load(tid, L, S);
   for (int it = 0; it < iters; ++it) {
     // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
     lp_Av([&](int j) { return S.v[j]; },
@@ -637,8 +721,8 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
     // iterate, is below kGapRel of the objective (fp32 iterates gain nothing beyond)
     if (!(mu >= kMuStop) || gap <= kGapRel * fmax(1.0, (double)S.v[n + R])) break;
     ++run;
-    if constexpr (kBlk > 0) lpb_factor<kBlk>(B, n, R, G, L, S);
-    else lp_factor(n, R, G, L, S);
+    if constexpr (kBlk > 0) lpb_factor<kBlk>(B, n, R, G, L, C, S);
+    else lp_factor(n, R, G, L, C, S);
     // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
     lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
     __syncthreads();
