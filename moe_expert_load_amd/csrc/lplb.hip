@@ -131,6 +131,8 @@ struct LpShared {
   // reductions
   double red[kLpThreads / kWave];
   float redf[kLpThreads / kWave];
+  double redn[4][kLpThreads / kWave];
+  double ysum;                            // sum of the new rank duals (dense solve)
   int32_t Fi[kLpMaxR], hc[kLpMaxG];       // fixed load per rank, count per group
 };
 
@@ -224,6 +226,27 @@ __device__ __forceinline__ void blk_min2(float& x, float& y, LpShared& S) {
   y = ty;
 }
 
+// kN block sums in one pass (each summed in the same order as blk_sum)
+template <int kN>
+__device__ __forceinline__ void blk_sum_n(double (&x)[kN], LpShared& S) {
+#pragma unroll
+  for (int j = 0; j < kN; ++j) x[j] = wave_sum_d(x[j]);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+#pragma unroll
+    for (int j = 0; j < kN; ++j) S.redn[j][w] = x[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kN; ++j) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kLpThreads / kWave; ++i) t += S.redn[j][i];
+    x[j] = t;
+  }
+}
+
 // out[i] = fin(i, (A * vec)_i) for i < R + G, with vec(j) the j-th element (read from
 // LDS or formed on the fly).  Thread i writes out[i] only: a caller that next touches
 // out[i] in thread i needs no barrier in between.
@@ -245,18 +268,20 @@ __device__ __forceinline__ void lp_Av(Vec vec, Fin fin, float* out, int n, int R
   }
 }
 
-// out[nv] = A^T * y ; needs the sum of rank duals
+// (A^T y)_i, given ys = the sum of the rank duals (the M and a columns)
+__device__ __forceinline__ float lp_ATy_at(int i, const float* yv, float ys, int n, int R,
+                                           const LpShared& S) {
+  if (i < n) return -yv[S.copy_rank[i]] + yv[R + S.copy_group[i]];
+  if (i < n + R) return -yv[i - n];
+  return ys;
+}
+
+// out[nv] = A^T * y
 __device__ __forceinline__ void lp_ATy(const float* yv, float* out, int n, int R, int G, LpShared& S) {
   float part = 0.0f;
   for (int r = threadIdx.x; r < R; r += kLpThreads) part += yv[r];
   const float ys = (float)blk_sum((double)part, S);
-  for (int i = threadIdx.x; i < n + R + 2; i += kLpThreads) {
-    float val;
-    if (i < n) val = -yv[S.copy_rank[i]] + yv[R + S.copy_group[i]];
-    else if (i < n + R) val = -yv[i - n];
-    else val = ys;
-    out[i] = val;
-  }
+  for (int i = threadIdx.x; i < n + R + 2; i += kLpThreads) out[i] = lp_ATy_at(i, yv, ys, n, R, S);
 }
 
 __device__ inline float lp_cost(int i, int n, int R) {
@@ -288,8 +313,53 @@ __device__ __forceinline__ void lp_rank_rhs(int R, LpShared& S) {
   }
 }
 
-// dy = (A D A^T)^{-1} rhs with the factored rank matrix
-__device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
+// lp_steps, and in the same pass the sums that expand the affine complementarity
+// sum_i (v_i + ap dv_i)(z_i + ad dz_i) = vz + ap dvz + ad vdz + ap ad dvdz (fp64 products)
+__device__ __forceinline__ void lp_steps_aff(int nv, LpShared& S, float& ap, float& ad,
+                                             double (&sums)[4]) {
+  float a = 1.0f, b = 1.0f;
+  double x[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int i = threadIdx.x; i < nv; i += kLpThreads) {
+    const float v = S.v[i], z = S.z[i], dv = S.dv[i], dz = S.dz[i];
+    if (dv < 0.0f) a = fminf(a, -v / dv);
+    if (dz < 0.0f) b = fminf(b, -z / dz);
+    x[0] += (double)v * (double)z;
+    x[1] += (double)dv * (double)z;
+    x[2] += (double)v * (double)dz;
+    x[3] += (double)dv * (double)dz;
+  }
+  a = wave_min_f(a);
+  b = wave_min_f(b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = wave_sum_d(x[j]);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    S.redf[w] = a;
+    S.red[w] = b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S.redn[j][w] = x[j];
+  }
+  __syncthreads();
+  float ta = S.redf[0], tb = (float)S.red[0];
+#pragma unroll
+  for (int i = 1; i < kLpThreads / kWave; ++i) {
+    ta = fminf(ta, S.redf[i]);
+    tb = fminf(tb, (float)S.red[i]);
+  }
+  ap = ta;
+  ad = tb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kLpThreads / kWave; ++i) t += S.redn[j][i];
+    sums[j] = t;
+  }
+}
+
+// dy = (A D A^T)^{-1} rhs with the factored rank matrix; returns the sum of dy's rank part
+__device__ __forceinline__ double lp_solve(int n, int R, int G, LpShared& S) {
   lp_rank_rhs(R, S);
   __syncthreads();
   if (threadIdx.x < kWave) {
@@ -311,6 +381,8 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
 #pragma unroll
     for (int q = kLpMaxR - 1; q >= 0; --q) b = fma(-u[q], readlane_d(b, q), b);  // U^T u = w
     if (l < R) S.u64[l] = b;
+    const double ys = wave_sum_d(l < R ? b : 0.0);
+    if (l == 0) S.ysum = ys;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
@@ -323,7 +395,9 @@ __device__ __forceinline__ void lp_solve(int n, int R, int G, LpShared& S) {
       S.dy[i] = (float)(acc * S.rbeta[g]);
     }
   }
+  const double ys = S.ysum;
   __syncthreads();
+  return ys;
 }
 
 // The hardware reciprocal estimate is good to about 2^-24 relative; one Newton step
@@ -663,14 +737,16 @@ __device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, 
   B.s1 = blk_sum(B.rank >= 0 ? B.w : 0.0, S);
 }
 
-// dy = (A D A^T)^{-1} rhs with the block factors (the group rows as in lp_solve)
+// dy = (A D A^T)^{-1} rhs with the block factors (the group rows as in lp_solve); returns
+// the sum of dy's rank part, sum(v) - sum(w) c by the same correction
 template <int kBlk>
-__device__ __forceinline__ void lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G, LpShared& S) {
+__device__ __forceinline__ double lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G, LpShared& S) {
   lp_rank_rhs(R, S);
   __syncthreads();
   const double v = lpb_subst<kBlk>(B, B.rank >= 0 ? S.u64[B.rank] : 0.0, &S.P[0][0]);
   const double sv = blk_sum(B.rank >= 0 ? v : 0.0, S);
-  const double y = v - B.w * (B.delta * sv / (1.0 + B.delta * B.s1));
+  const double c = B.delta * sv / (1.0 + B.delta * B.s1);
+  const double y = v - B.w * c;
   if (B.rank >= 0) S.u64[B.rank] = y;
   __syncthreads();
   for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
@@ -684,6 +760,7 @@ __device__ __forceinline__ void lpb_solve(const LpBlk<kBlk>& B, int n, int R, in
     }
   }
   __syncthreads();
+  return sv - B.s1 * c;
 }
 
 // The interior-point loop: Mehrotra predictor-corrector from the starting point in S,
@@ -709,13 +786,19 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
     // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
     lp_Av([&](int j) { return S.v[j]; },
           [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, S);
-    lp_ATy(S.y, S.tv, n, R, G, S);
-    double cz = 0.0;
-    for (int i = tid; i < nv; i += kLpThreads) {
-      S.rc[i] = lp_cost(i, n, R) - S.tv[i] - S.z[i];
-      cz += (double)(S.v[i] * S.z[i]);
+    // the duality gap and the sum of the rank duals in one reduction
+    double gy[2] = {0.0, 0.0};
+    for (int i = tid; i < nv; i += kLpThreads) gy[0] += (double)(S.v[i] * S.z[i]);
+    {
+      float part = 0.0f;
+      for (int r = tid; r < R; r += kLpThreads) part += S.y[r];
+      gy[1] = part;
     }
-    const double gap = blk_sum(cz, S);
+    blk_sum_n<2>(gy, S);
+    const double gap = gy[0];
+    const float ys = (float)gy[1];
+    for (int i = tid; i < nv; i += kLpThreads)
+      S.rc[i] = lp_cost(i, n, R) - lp_ATy_at(i, S.y, ys, n, R, S) - S.z[i];
     const float mu = (float)(gap / nv);
     // stop once the duality gap, which bounds the objective error of a feasible
     // iterate, is below kGapRel of the objective (fp32 iterates gain nothing beyond)
@@ -726,19 +809,19 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
     // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
     lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
     __syncthreads();
-    if constexpr (kBlk > 0) lpb_solve<kBlk>(B, n, R, G, S);
-    else lp_solve(n, R, G, S);
-    lp_ATy(S.dy, S.tv, n, R, G, S);
+    double dys;
+    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, S);
+    else dys = lp_solve(n, R, G, S);
     for (int i = tid; i < nv; i += kLpThreads) {
-      S.dz[i] = S.rc[i] - S.tv[i];
+      S.dz[i] = S.rc[i] - lp_ATy_at(i, S.dy, (float)dys, n, R, S);
       S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
     }
     float ap, ad;
-    lp_steps(nv, S, ap, ad);
-    double ca = 0.0;
-    for (int i = tid; i < nv; i += kLpThreads)
-      ca += (double)((S.v[i] + ap * S.dv[i]) * (S.z[i] + ad * S.dz[i]));
-    const float mu_aff = (float)(blk_sum(ca, S) / nv);
+    double sums[4];
+    lp_steps_aff(nv, S, ap, ad, sums);
+    const double ca = sums[0] + (double)ap * sums[1] + (double)ad * sums[2] +
+                      (double)ap * (double)ad * sums[3];
+    const float mu_aff = (float)(fmax(ca, 0.0) / nv);
     const float ratio = mu_aff / mu;
     const float sg = ratio * ratio * ratio;
     // corrector: rmu = sg mu - v z - dv dz ; rhs = rb + A (D rc - rmu / z)
@@ -750,12 +833,11 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
     __syncthreads();
     lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, S);
     __syncthreads();
-    if constexpr (kBlk > 0) lpb_solve<kBlk>(B, n, R, G, S);
-    else lp_solve(n, R, G, S);
-    lp_ATy(S.dy, S.tv, n, R, G, S);
+    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, S);
+    else dys = lp_solve(n, R, G, S);
     for (int i = tid; i < nv; i += kLpThreads) {
       const float rmu = S.dv[i];
-      S.dz[i] = S.rc[i] - S.tv[i];
+      S.dz[i] = S.rc[i] - lp_ATy_at(i, S.dy, (float)dys, n, R, S);
       S.dv[i] = rmu / S.z[i] - (float)(S.d[i] * S.dz[i]);
     }
     float ap2, ad2;
