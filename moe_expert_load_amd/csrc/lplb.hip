@@ -600,26 +600,16 @@ __device__ __forceinline__ void lp_factor(int n, int R, int G, const LpView& L, 
 // Pivots that lost their precision are dropped as in the dense factorization.
 
 // Lane J of every aligned group of kBlk (8 or 16) lanes, to every lane of its group, by
-// DPP moves (no trip through the LDS unit): quad_perm copies lane J % 4 of every quad
-// to its quad, then row_shr / row_shl by multiples of 4 lanes, each limited to one
-// bank (quad) of the 16-lane row, copy quad J / 4 to the group's other quads.  Every
-// source lane read is quad J / 4 of its own group, so bound_ctrl never applies.
+// DPP moves (no trip through the LDS unit).  row_newbcast:N (DPP control 0x150 + N,
+// gfx90a and later) gives every lane of a 16-lane row the row's lane N: one move for
+// groups of 16; groups of 8 take lane J of the row, then, in banks 2 and 3 (the upper
+// 8 lanes), lane 8 + J.
 template <int kBlk, int J>
 __device__ __forceinline__ int grp_bcast_i(int x) {
   static_assert(kBlk == 8 || kBlk == 16, "groups of 8 or 16 lanes");
-  const int q = __builtin_amdgcn_mov_dpp(x, (J % 4) * 0x55, 0xF, 0xF, false);
-  constexpr int Q = J / 4;
-  int r = q;
-  if constexpr (kBlk == 8) {
-    if constexpr (Q == 0) r = __builtin_amdgcn_update_dpp(r, q, 0x114, 0xF, 0xA, false);
-    else r = __builtin_amdgcn_update_dpp(r, q, 0x104, 0xF, 0x5, false);
-  } else {
-    if constexpr (Q != 0) r = __builtin_amdgcn_update_dpp(r, q, 0x100 + 4 * Q, 0xF, 0x1, false);
-    if constexpr (Q != 1) r = __builtin_amdgcn_update_dpp(r, q, Q < 1 ? 0x110 + 4 * (1 - Q) : 0x100 + 4 * (Q - 1), 0xF, 0x2, false);
-    if constexpr (Q != 2) r = __builtin_amdgcn_update_dpp(r, q, Q < 2 ? 0x110 + 4 * (2 - Q) : 0x100 + 4 * (Q - 2), 0xF, 0x4, false);
-    if constexpr (Q != 3) r = __builtin_amdgcn_update_dpp(r, q, 0x110 + 4 * (3 - Q), 0xF, 0x8, false);
-  }
-  return r;
+  const int r = __builtin_amdgcn_mov_dpp(x, 0x150 + J, 0xF, 0xF, false);
+  if constexpr (kBlk == 16) return r;
+  return __builtin_amdgcn_update_dpp(r, x, 0x150 + 8 + J, 0xF, 0xC, false);
 }
 
 template <int kBlk, int J>
