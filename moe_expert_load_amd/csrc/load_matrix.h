@@ -305,6 +305,7 @@ __global__ __launch_bounds__(256) void lm_hist(const int32_t* __restrict__ ids,
                                                LmGeom g);
 __global__ __launch_bounds__(256) void lm_counts(const int32_t* __restrict__ chunk_hist,
                                                  int32_t* __restrict__ counts, LmGeom g);
-__global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist, LmGeom g);
+__global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts, LmGeom g);
 
 }  // namespace uep

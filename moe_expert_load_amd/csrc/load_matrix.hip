@@ -96,10 +96,13 @@ __global__ __launch_bounds__(256) void lm_counts(const int32_t* __restrict__ chu
 // workgroup loads one row instead of summing every earlier chunk's (which reads the
 // histograms about n_chunks / 2 times over).  Four threads per expert, each over a
 // quarter of the chunks: sums, an LDS exchange of the four partial sums, then the
-// prefixes written from the re-read (now cached) counts.
+// prefixes written from the re-read (now cached) counts.  With counts non-null the
+// last part's running sum, the rank's total, is also written there (the load matrix,
+// so no separate counts launch is needed).
 constexpr int kLmScanParts = 4;
 
-__global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist, LmGeom g) {
+__global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts, LmGeom g) {
   __shared__ int32_t part_sum[256];
   const int r = blockIdx.y;
   const int e = blockIdx.x * (256 / kLmScanParts) + threadIdx.x / kLmScanParts;
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(256) void lm_scan(int32_t* __restrict__ chunk_hist,
           run += acc[u];
         }
     }
+    if (counts && q == kLmScanParts - 1) counts[(int64_t)r * g.E + e] = run;
   }
 }
 
@@ -335,7 +339,8 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
     const int per = E >= 256 ? 1 : 256 / E;
     const bool scanned = T > 0 && g.n_chunks > 16 * per;
     if (scanned) {
-      hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, (int32_t*)ws, g);
+      hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, (int32_t*)ws,
+                         (int32_t*)nullptr, g);
       UEP_CHECK_LAUNCH();
     }
     const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;
@@ -371,7 +376,8 @@ extern "C" uep_status uep_load_matrix(const int32_t* topk_ids, int32_t R, int32_
 // ---------------------------------------------------------------------------------
 // uep_plan: uep_load_matrix, uep_solve_quota and uep_reroute_assign in one call, with
 // the solve overlapped with the ranking.  Launches: lm_hist, lm_counts (the load
-// matrix), lm_scan for long ranks, plan_rank_solve (solve || ranking), then the
+// matrix; for long ranks lm_scan, which also writes it), plan_rank_solve (solve ||
+// ranking), then the
 // reroute and assignment of uep_reroute_assign.  Geometries off the ranking fast path
 // (E > 1024 or K > 16) run the three calls one after the other instead.
 static size_t plan_align(size_t b) { return (b + 255) / 256 * 256; }
@@ -423,14 +429,14 @@ extern "C" uep_status uep_plan(const int32_t* topk_ids, int32_t R, int32_t T, in
   hipLaunchKernelGGL(lm_hist, dim3(g.n_chunks, R), dim3(256), sizeof(int32_t) * E, s, topk_ids,
                      hist, err, g);
   UEP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
-  UEP_CHECK_LAUNCH();
+  // long ranks: the scan also writes the load matrix (no counts launch)
   const int per = E >= 256 ? 1 : 256 / E;
   const bool scanned = g.n_chunks > 16 * per;
-  if (scanned) {
-    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, g);
-    UEP_CHECK_LAUNCH();
-  }
+  if (scanned)
+    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, counts, g);
+  else
+    hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
+  UEP_CHECK_LAUNCH();
   const bool vec = K % 4 == 0 && reinterpret_cast<uintptr_t>(topk_ids) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(bucket_pos) % 16 == 0;
   const size_t lds = sizeof(uint64_t) * 4 * E + sizeof(int32_t) * 5 * E;

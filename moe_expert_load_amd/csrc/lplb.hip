@@ -1303,10 +1303,10 @@ extern "C" uep_status uep_lplb(const int32_t* counts, const void* lp, int32_t it
 
 // uep_lplb_plan: uep_load_matrix, uep_lplb and uep_reroute_assign in one call, with the
 // LP solved concurrently with the bucket-position ranking (lplb_rank_kernel).  Launches:
-// lm_hist, lm_counts (the load matrix), lm_scan for long ranks, lplb_rank_kernel, then
-// the reroute and assignment of uep_reroute_assign.  Geometries off the ranking fast
-// path, or whose ranking would not fit the LP's LDS block, run the three calls in
-// sequence.
+// lm_hist, lm_counts (the load matrix; for long ranks lm_scan, which also writes it),
+// lplb_rank_kernel, then the reroute and assignment of uep_reroute_assign.  Geometries
+// off the ranking fast path, or whose ranking would not fit the LP's LDS block, run the
+// three calls in sequence.
 static size_t lp_plan_align(size_t b) { return (b + 255) / 256 * 256; }
 
 extern "C" size_t uep_lplb_plan_workspace_size(int32_t R, int32_t T, int32_t K, int32_t E,
@@ -1360,11 +1360,16 @@ extern "C" uep_status uep_lplb_plan(const int32_t* topk_ids, int32_t R, int32_t 
   hipLaunchKernelGGL(lm_hist, dim3(g.n_chunks, R), dim3(256), sizeof(int32_t) * E, s, topk_ids,
                      hist, err, g);
   UEP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
+  // long ranks: one scan of the chunk histograms, which also writes the load matrix,
+  // instead of every ranking workgroup summing the earlier chunks (on a 64-chunk rank
+  // that ranking outlasts the LP)
+  const int per = E >= 256 ? 1 : 256 / E;
+  const bool scanned = g.n_chunks > 16 * per;
+  if (scanned)
+    hipLaunchKernelGGL(lm_scan, dim3((E + 63) / 64, R), dim3(256), 0, s, hist, counts, g);
+  else
+    hipLaunchKernelGGL(lm_counts, dim3(R), dim3(256), 0, s, (const int32_t*)hist, counts, g);
   UEP_CHECK_LAUNCH();
-  // the ranking sums the earlier chunks' histograms itself (no lm_scan launch before the
-  // LP): it has the LP's whole solve to do it in
-  const bool scanned = false;
   const dim3 grid(1 + g.n_chunks * R);
   const int32_t* lpw = static_cast<const int32_t*>(lp);
 #define UEP_LP_FUSED(KM, TL)                                                                  \
