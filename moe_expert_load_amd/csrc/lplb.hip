@@ -139,6 +139,10 @@ struct LpShared {
 // Wave reductions by DPP (quad_perm xor 1, xor 2, row_ror 4 and 8 leave every row of
 // 16 lanes holding its row's total; the four rows are combined from lanes 0/16/32/48),
 // then across the 4 waves through LDS.  Every lane of the workgroup must take part.
+// A block reduction has one barrier, between the waves' partials and their reads: the
+// LP keeps at least one barrier between the reads of one reduction and the writes of
+// the next (every pair of consecutive reductions in it has one), so the partials of
+// the previous reduction are never overwritten while still being read.
 // Every lane has a source lane in its own row under these patterns, so mov_dpp's
 // bound_ctrl never applies; the form lets the compiler fold a move into its fp32 op.
 __device__ __forceinline__ double dpp_d(double v, int ctrl_sel) {
@@ -187,7 +191,6 @@ __device__ __forceinline__ float wave_min_f(float x) {
 __device__ __forceinline__ double blk_sum(double x, LpShared& S) {
   x = wave_sum_d(x);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
   if (threadIdx.x % kWave == 0) S.red[w] = x;
   __syncthreads();
   double t = 0.0;
@@ -199,7 +202,6 @@ __device__ __forceinline__ double blk_sum(double x, LpShared& S) {
 __device__ __forceinline__ float blk_min(float x, LpShared& S) {
   x = wave_min_f(x);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
   if (threadIdx.x % kWave == 0) S.redf[w] = x;
   __syncthreads();
   float t = S.redf[0];
@@ -213,7 +215,6 @@ __device__ __forceinline__ void blk_min2(float& x, float& y, LpShared& S) {
   x = wave_min_f(x);
   y = wave_min_f(y);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
   if (threadIdx.x % kWave == 0) { S.redf[w] = x; S.red[w] = y; }
   __syncthreads();
   float tx = S.redf[0], ty = (float)S.red[0];
@@ -232,7 +233,6 @@ __device__ __forceinline__ void blk_sum_n(double (&x)[kN], LpShared& S) {
 #pragma unroll
   for (int j = 0; j < kN; ++j) x[j] = wave_sum_d(x[j]);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
   if (threadIdx.x % kWave == 0) {
 #pragma unroll
     for (int j = 0; j < kN; ++j) S.redn[j][w] = x[j];
@@ -247,23 +247,35 @@ __device__ __forceinline__ void blk_sum_n(double (&x)[kN], LpShared& S) {
   }
 }
 
+// Row i of A (i < R + G) belongs to thread i, which holds the row's range for the whole
+// solve: rank_copy[lo, hi) for a rank row, the copies [lo, hi) for a group row.
+static_assert(kLpMaxR + kLpMaxG <= kLpThreads, "one row of A per thread");
+struct LpRow {
+  int lo, hi;
+};
+
+__device__ __forceinline__ LpRow lp_row(int R, int G, const LpShared& S) {
+  const int i = threadIdx.x;
+  if (i < R) return {S.rank_start[i], S.rank_start[i + 1]};
+  if (i < R + G) return {S.grp_start[i - R], S.grp_start[i - R + 1]};
+  return {0, 0};
+}
+
 // out[i] = fin(i, (A * vec)_i) for i < R + G, with vec(j) the j-th element (read from
 // LDS or formed on the fly).  Thread i writes out[i] only: a caller that next touches
 // out[i] in thread i needs no barrier in between.
 template <class Vec, class Fin>
 __device__ __forceinline__ void lp_Av(Vec vec, Fin fin, float* out, int n, int R, int G,
-                                      LpShared& S) {
+                                      const LpRow& W, LpShared& S) {
   const float Ma = vec(n + R) + vec(n + R + 1);
-  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
-    float acc;
-    if (i < R) {
-      acc = Ma - vec(n + i);
-      for (int k = S.rank_start[i]; k < S.rank_start[i + 1]; ++k) acc -= vec(S.rank_copy[k]);
-    } else {
-      const int g = i - R;
-      acc = 0.0f;
-      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += vec(p);
-    }
+  const int i = threadIdx.x;
+  if (i < R) {
+    float acc = Ma - vec(n + i);
+    for (int k = W.lo; k < W.hi; ++k) acc -= vec(S.rank_copy[k]);
+    out[i] = fin(i, acc);
+  } else if (i < R + G) {
+    float acc = 0.0f;
+    for (int p = W.lo; p < W.hi; ++p) acc += vec(p);
     out[i] = fin(i, acc);
   }
 }
@@ -302,14 +314,28 @@ __device__ __forceinline__ void lp_steps(int nv, LpShared& S, float& ap, float& 
 
 // The right-hand side of the rank system: rank r's row plus, for every copy p on r,
 // d_p times its group's row divided by beta.
-__device__ __forceinline__ void lp_rank_rhs(int R, LpShared& S) {
-  for (int r = threadIdx.x; r < R; r += kLpThreads) {
+__device__ __forceinline__ void lp_rank_rhs(int R, const LpRow& W, LpShared& S) {
+  const int r = threadIdx.x;
+  if (r < R) {
     double acc = S.rhs[r];
-    for (int k = S.rank_start[r]; k < S.rank_start[r + 1]; ++k) {
+    for (int k = W.lo; k < W.hi; ++k) {
       const int p = S.rank_copy[k], g = S.copy_group[p];
       acc += S.d[p] * ((double)S.rhs[R + g] * S.rbeta[g]);
     }
     S.u64[r] = acc;
+  }
+}
+
+// dy from the solved rank part u64: dy_r = u_r, and for group row g,
+// dy = (rhs_g + sum over its copies of d_p u_(rank of p)) / beta_g
+__device__ __forceinline__ void lp_dy(int R, int G, const LpRow& W, LpShared& S) {
+  const int i = threadIdx.x;
+  if (i < R) {
+    S.dy[i] = (float)S.u64[i];
+  } else if (i < R + G) {
+    double acc = S.rhs[i];
+    for (int p = W.lo; p < W.hi; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
+    S.dy[i] = (float)(acc * S.rbeta[i - R]);
   }
 }
 
@@ -333,7 +359,6 @@ __device__ __forceinline__ void lp_steps_aff(int nv, LpShared& S, float& ap, flo
 #pragma unroll
   for (int j = 0; j < 4; ++j) x[j] = wave_sum_d(x[j]);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
   if (threadIdx.x % kWave == 0) {
     S.redf[w] = a;
     S.red[w] = b;
@@ -359,8 +384,8 @@ __device__ __forceinline__ void lp_steps_aff(int nv, LpShared& S, float& ap, flo
 }
 
 // dy = (A D A^T)^{-1} rhs with the factored rank matrix; returns the sum of dy's rank part
-__device__ __forceinline__ double lp_solve(int n, int R, int G, LpShared& S) {
-  lp_rank_rhs(R, S);
+__device__ __forceinline__ double lp_solve(int n, int R, int G, const LpRow& W, LpShared& S) {
+  lp_rank_rhs(R, W, S);
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
@@ -385,16 +410,7 @@ __device__ __forceinline__ double lp_solve(int n, int R, int G, LpShared& S) {
     if (l == 0) S.ysum = ys;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
-    if (i < R) {
-      S.dy[i] = (float)S.u64[i];
-    } else {
-      const int g = i - R;
-      double acc = S.rhs[i];
-      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
-      S.dy[i] = (float)(acc * S.rbeta[g]);
-    }
-  }
+  lp_dy(R, G, W, S);
   const double ys = S.ysum;
   __syncthreads();
   return ys;
@@ -730,8 +746,9 @@ __device__ __forceinline__ void lpb_factor(LpBlk<kBlk>& B, int n, int R, int G, 
 // dy = (A D A^T)^{-1} rhs with the block factors (the group rows as in lp_solve); returns
 // the sum of dy's rank part, sum(v) - sum(w) c by the same correction
 template <int kBlk>
-__device__ __forceinline__ double lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G, LpShared& S) {
-  lp_rank_rhs(R, S);
+__device__ __forceinline__ double lpb_solve(const LpBlk<kBlk>& B, int n, int R, int G,
+                                            const LpRow& W, LpShared& S) {
+  lp_rank_rhs(R, W, S);
   __syncthreads();
   const double v = lpb_subst<kBlk>(B, B.rank >= 0 ? S.u64[B.rank] : 0.0, &S.P[0][0]);
   const double sv = blk_sum(B.rank >= 0 ? v : 0.0, S);
@@ -739,16 +756,7 @@ __device__ __forceinline__ double lpb_solve(const LpBlk<kBlk>& B, int n, int R, 
   const double y = v - B.w * c;
   if (B.rank >= 0) S.u64[B.rank] = y;
   __syncthreads();
-  for (int i = threadIdx.x; i < R + G; i += kLpThreads) {
-    if (i < R) {
-      S.dy[i] = (float)S.u64[i];
-    } else {
-      const int g = i - R;
-      double acc = S.rhs[i];
-      for (int p = S.grp_start[g]; p < S.grp_start[g + 1]; ++p) acc += S.d[p] * S.u64[S.copy_rank[p]];
-      S.dy[i] = (float)(acc * S.rbeta[g]);
-    }
-  }
+  lp_dy(R, G, W, S);
   __syncthreads();
   return sv - B.s1 * c;
 }
@@ -772,10 +780,11 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
   // what the same thread wrote at index i in the step before needs none.
   const auto plus_rb = [&](int i, float a) { return a + S.rb[i]; };
   const LpEnt C = lp_ent_load(tid, L, S);
+  const LpRow W = lp_row(R, G, S);
   for (int it = 0; it < iters; ++it) {
     // residuals and complementarity: rb = b - A v, rc = c - A^T y - z
     lp_Av([&](int j) { return S.v[j]; },
-          [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, S);
+          [&](int i, float a) { return (i < R ? S.f[i] : S.hh[i - R]) - a; }, S.rb, n, R, G, W, S);
     // the duality gap and the sum of the rank duals in one reduction
     double gy[2] = {0.0, 0.0};
     for (int i = tid; i < nv; i += kLpThreads) gy[0] += (double)(S.v[i] * S.z[i]);
@@ -797,11 +806,11 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
     if constexpr (kBlk > 0) lpb_factor<kBlk>(B, n, R, G, L, C, S);
     else lp_factor(n, R, G, L, C, S);
     // predictor: rhs = rb + A (v + D rc), the vector formed inside the product
-    lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, S);
+    lp_Av([&](int j) { return S.v[j] + (float)(S.d[j] * S.rc[j]); }, plus_rb, S.rhs, n, R, G, W, S);
     __syncthreads();
     double dys;
-    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, S);
-    else dys = lp_solve(n, R, G, S);
+    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, W, S);
+    else dys = lp_solve(n, R, G, W, S);
     for (int i = tid; i < nv; i += kLpThreads) {
       S.dz[i] = S.rc[i] - lp_ATy_at(i, S.dy, (float)dys, n, R, S);
       S.dv[i] = -S.v[i] - (float)(S.d[i] * S.dz[i]);
@@ -821,10 +830,10 @@ __device__ __forceinline__ int lp_ipm(int iters, int n, int R, int G, const LpVi
       S.tv[i] = (float)(S.d[i] * S.rc[i]) - rmu / S.z[i];
     }
     __syncthreads();
-    lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, S);
+    lp_Av([&](int j) { return S.tv[j]; }, plus_rb, S.rhs, n, R, G, W, S);
     __syncthreads();
-    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, S);
-    else dys = lp_solve(n, R, G, S);
+    if constexpr (kBlk > 0) dys = lpb_solve<kBlk>(B, n, R, G, W, S);
+    else dys = lp_solve(n, R, G, W, S);
     for (int i = tid; i < nv; i += kLpThreads) {
       const float rmu = S.dv[i];
       S.dz[i] = S.rc[i] - lp_ATy_at(i, S.dy, (float)dys, n, R, S);
