@@ -983,6 +983,7 @@ def bench_sweep(args, torch, U, W, w):
     s = torch.cuda.current_stream()
     fwd_t = Timer(torch, w.layers * (args.steps + args.warmup))
     bwd_t = Timer(torch, w.layers * (args.steps + args.warmup))
+    perm_t = Timer(torch, w.layers * (args.steps + args.warmup))
 
     def sweep(st, timers):
         for l in range(w.layers):
@@ -991,7 +992,9 @@ def bench_sweep(args, torch, U, W, w):
             fwd_t.start(st)
             L.plan_step(st)
             L.stage(st)
+            perm_t.start(st)
             L.permute(st)
+            perm_t.stop(st)
             fwd_t.stop(st)
             slots[l].copy_(L.plan["slot_expert"][:, :w.S])
         for l in reversed(range(w.layers)):
@@ -1007,7 +1010,10 @@ def bench_sweep(args, torch, U, W, w):
     b = np.array(bwd_t.all_ms()[w.layers * args.warmup:]) * 1e3
     out = base_line(w, W, w.N / (ms * 1e-3), ms, args, "int32",
                     {"layers": w.layers, "weight_sets_cycled": pool, "zipf_s": "0.8+0.6U per layer"})
-    out["roofline"] = None
+    # the dominant kernel: every layer's whole-group permute call, timed on the launch
+    # stream inside the sweep (no counter passes were taken on this command)
+    perm_ms = float(np.mean(perm_t.all_ms()[w.layers * args.warmup:]))
+    out["roofline"] = roofline(permute_bytes(w.N, w.P, w.H), perm_ms, PERMUTE_CALL)
     out["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
